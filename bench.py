@@ -1,0 +1,181 @@
+"""Benchmark of the MoE layer on one MI355X.
+
+One step = one 4096-token prefill of the uniform-routing layer (hidden 2048, 256 experts
+top-8 + 1 shared, intermediate 512, int4 group-64 weights) followed by a batch-1 decode
+sweep over 40 distinct weight sets of the same shape (so decode weights stream from HBM,
+not from cache).  Inputs are resident in HBM before timing starts.
+
+Prints one JSON line: value = prefill tokens/s; also decode microseconds per layer, the
+per-stage times from HIP events recorded by the library on its stream, roofline figures
+for the dominant kernel of each form, and the oracle's CPU throughput on the same
+workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s at 4K prefill + decode µs/layer; % of HBM/MFMA roofline"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-layers", type=int, default=40)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from sparse_moe_02_amd import binding as B
+    from sparse_moe_02_amd.layer import MoeLayer, bf16_tensor
+
+    if not os.path.exists(B.LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    sh2, sh1 = synth.shape_of(2), synth.shape_of(1)
+    T, H, I, E, k = sh2.T, sh2.H, sh2.I, sh2.E, sh2.k
+
+    log("bench: drawing the prefill layer")
+    Lp = synth.make_layer(2)
+    xp_bits = synth.make_x(2)
+    pre = MoeLayer(Lp, top_k=k, max_chunk_tokens=T, device=dev)
+    xp = bf16_tensor(xp_bits, dev)
+    outp = torch.empty_like(xp)
+
+    n_dec = 0 if args.prefill_only else args.decode_layers
+    dec_layers, dec_x, dec_out = [], [], []
+    Lb = None
+    for li in range(n_dec):
+        Lb = synth.make_layer(1, li, into=Lb)
+        dec_layers.append(MoeLayer(Lb, top_k=k, max_chunk_tokens=1, device=dev))
+        dec_x.append(bf16_tensor(synth.make_x(1, li)[0], dev))
+        dec_out.append(torch.empty_like(dec_x[-1]))
+        if li % 10 == 9:
+            log(f"bench: decode layers resident: {li + 1}")
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(ev_pre=None, ev_dec=None):
+        pre.prefill(xp, outp, events=ev_pre)
+        for li in range(n_dec):
+            dec_layers[li].decode(dec_x[li], dec_out[li], events=ev_dec[li] if ev_dec else None)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev_pre = [B.HipEvents(B.MOE_PREFILL_STAGES + 1) for _ in range(K)]
+    ev_dec = [[B.HipEvents(B.MOE_DECODE_STAGES + 1) for _ in range(n_dec)] for _ in range(K)]
+    marks = B.HipEvents(K + 1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    marks.record(0, stream)
+    for s in range(K):
+        step(ev_pre[s], ev_dec[s])
+        marks.record(s + 1, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    step_ms = [marks.elapsed_ms(s, s + 1) for s in range(K)]
+    pre_ms = np.array([e.elapsed_ms(0, B.MOE_PREFILL_STAGES) for e in ev_pre])
+    stage_ms = {name: float(np.mean([e.elapsed_ms(i, i + 1) for e in ev_pre]))
+                for i, name in enumerate(B.PREFILL_STAGE_NAMES)}
+    prefill_ms = float(np.median(pre_ms))
+    tok_s = T / (prefill_ms * 1e-3)
+
+    rows = T * (k + 1)
+    gateup_flop = 2.0 * (2 * I) * H * rows
+    down_flop = 2.0 * H * I * rows
+    router_flop = 2.0 * T * E * H
+    gu_ms = stage_ms["gateup"]
+    result = {
+        "metric": METRIC,
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"prefill {T} tokens (uniform routing) + batch-1 decode over {n_dec} weight sets",
+                   "tokens": T, "hidden": H, "experts": E, "top_k": k, "shared_experts": 1, "inter": I,
+                   "weights": "int4 affine group-64, fp16 scale/bias", "decode_layers": n_dec},
+        "prefill_us": round(prefill_ms * 1e3, 2),
+        "prefill_stage_us": {n: round(v * 1e3, 2) for n, v in stage_ms.items()},
+        "prefill_tflops": round((gateup_flop + down_flop + router_flop) / (prefill_ms * 1e-3) / 1e12, 1),
+        "roofline": {"kernel": "gemm_gateup (grouped GEMM gate/up + SwiGLU)", "bound": "mfma",
+                     "achieved": round(gateup_flop / (gu_ms * 1e-3) / 1e12, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gateup_flop / (gu_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flop_per_launch": gateup_flop},
+        "step_ms_events": round(float(np.mean(step_ms)), 4),
+    }
+    if n_dec:
+        dec_stage = {name: float(np.mean([e.elapsed_ms(i, i + 1) for es in ev_dec for e in es]))
+                     for i, name in enumerate(B.DECODE_STAGE_NAMES)}
+        dec_layer_ms = float(np.mean([e.elapsed_ms(0, B.MOE_DECODE_STAGES) for es in ev_dec for e in es]))
+        sweep_ms = np.array([m - p for m, p in zip(step_ms, pre_ms)])
+        us_layer = float(np.median(sweep_ms)) * 1e3 / n_dec
+        qmat_gu = I * H // 2 + 2 * 2 * I * (H // 64)
+        qmat_dn = H * I // 2 + 2 * 2 * H * (I // 64)
+        gu_bytes = (k + 1) * 2 * qmat_gu + 2 * H + (k + 1) * I * 4
+        layer_bytes = (k + 1) * (2 * qmat_gu + qmat_dn) + E * H * 2 + 2 * H * 2
+        result["decode_us_per_layer"] = round(us_layer, 3)
+        result["decode_stage_us"] = {n: round(v * 1e3, 3) for n, v in dec_stage.items()}
+        result["decode_layer_us_events"] = round(dec_layer_ms * 1e3, 3)
+        result["decode_hbm_frac"] = round(layer_bytes / (us_layer * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+        gu_gbs = gu_bytes / (dec_stage["gateup"] * 1e-3) / 1e9
+        result["decode_roofline"] = {"kernel": "decode_gateup (GEMV gate/up + SwiGLU, 9 experts)", "bound": "hbm",
+                                     "achieved": round(gu_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                     "frac": round(gu_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                                     "algorithmic_bytes_per_launch": gu_bytes}
+        result["decode_algorithmic_bytes_per_layer"] = layer_bytes
+
+    if not args.no_cpu_baseline:
+        import oracle
+
+        log("bench: oracle CPU baseline (full 4096-token prefill of the same layer)")
+        t1 = time.perf_counter()
+        oracle.forward(xp_bits, Lp, k)
+        dt = time.perf_counter() - t1
+        result["cpu_baseline"] = {"value": round(T / dt, 2), "unit": "tokens/s", "cores": oracle.threads(),
+                                  "kind": "oracle",
+                                  "sample": f"the full {T}-token prefill of the benchmark layer ({dt:.1f} s)"}
+    print(json.dumps(result), flush=True)
+    for layer in dec_layers + [pre]:
+        layer.close()
+
+
+if __name__ == "__main__":
+    main()

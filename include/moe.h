@@ -1,0 +1,193 @@
+/*
+ * moe.h -- C ABI of the MI355X sparse mixture-of-experts feed-forward layer.
+ *
+ * The layer ("Optimizing on-device inference for Apple Silicon", section "Qwen
+ * creates three different workload shapes"): a router scores E routed experts
+ * per token and keeps the top k; one shared expert processes every token.  Each
+ * expert is a SwiGLU feed-forward block whose weights are stored as 4-bit codes
+ * with one scale and one bias per group of 64 weights (section "Prefill >
+ * Dequantize weights during matmul").  The layer output is
+ *
+ *     out[t] = sum_{e in S_t} g_{t,e} * FFN_e(x_t) + FFN_shared(x_t)
+ *     FFN(v) = W_down * (silu(W_gate v) .* (W_up v)),   silu(a) = a*sigmoid(a)
+ *
+ * with S_t the k experts of largest router logit l[t][e] = x_t . Wr[e] (+ b[e])
+ * -- equal logits: the lower expert index wins -- and g_{t,.} the softmax of
+ * the chosen logits.  Logits are ranked as if computed exactly; the library
+ * certifies its fp32 ranking against a rigorous error bound and re-ranks
+ * uncertain tokens in binary64 (sequentially summed, ascending h, when even
+ * that cannot separate them).
+ *
+ * Two forms (section "Optimization strategy", first part: a matrix path for
+ * prefill, a vector path for batch-1 decode):
+ *   moe_forward_prefill -- T tokens: router, on-device histogram / prefix scan
+ *     / scatter / block map (section "Prefill > Keep expert routing on the
+ *     GPU"), grouped GEMMs that dequantise int4 tiles on chip and feed bf16
+ *     MFMA with fp32 accumulation, tile height chosen from each expert's row
+ *     count (section "Prefill > Match tile size to expert load"), SwiGLU fused
+ *     into the gate/up GEMM, gate-weighted combine fused into the down GEMM,
+ *     long prompts processed in bounded chunks (section "Prefill > Bound
+ *     temporary memory with prompt chunking");
+ *   moe_forward_decode -- one token: row-parallel dequant-GEMV over the k+1
+ *     active experts (section "Decode > Optimize the one-row weight path") with
+ *     the two input projections and the activation fused, and the output
+ *     projection fused with the routing weights and the shared expert (section
+ *     "Decode > Reduce intermediate and state traffic").
+ *
+ * Conventions
+ *   - Every pointer argument is a DEVICE pointer unless marked (host).
+ *   - The caller owns all device memory: weights, x, out and the workspace.  A
+ *     plan holds a host copy of the config and of the weight pointers only; it
+ *     allocates no device memory and launches nothing.  Weights must stay valid
+ *     and unmodified for the plan's lifetime.
+ *   - Forwards only enqueue work on `stream` (0 = null stream) and never
+ *     synchronise the host.  Device-side faults surface at the caller's next
+ *     synchronisation.  Calls that may run concurrently need distinct
+ *     workspaces.  A plan is immutable and may be shared between threads.
+ *   - Errors: host validation returns a status before anything is enqueued; a
+ *     failed launch returns MOE_ERR_HIP (hipGetLastError() is left for the
+ *     caller).  No C++ exception crosses this interface.
+ *   - x and out must not alias.  Device pointers must be 16-byte aligned.
+ *
+ * Layouts (row-major):
+ *   x, out           bf16 [T][H]
+ *   router weight    [E][H], bf16 (MOE_BF16) or float32 (MOE_FP32)
+ *   router bias      float32 [E], or NULL
+ *   quantised W[N][K]  q: uint32 [N][K/8]; element k of row n is the 4-bit code
+ *                    in bits 4*(k%8) of q[n][k/8] (low nibble first);
+ *                    scale, bias: fp16 [N][K/64]; w = scale*code + bias.
+ *   routed experts   stacked: gate, up [E][I][H]; down [E][H][I] (q, scale
+ *                    and bias each stacked on the leading axis)
+ *   shared expert    gate, up [I][H]; down [H][I]
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,      /* a required pointer is NULL */
+  MOE_ERR_SHAPE = 2,     /* unsupported sizes (see moe_config) */
+  MOE_ERR_DTYPE = 3,     /* unsupported dtype */
+  MOE_ERR_ALIGN = 4,     /* a device pointer is not 16-byte aligned */
+  MOE_ERR_WORKSPACE = 5, /* workspace missing or smaller than required */
+  MOE_ERR_TOKENS = 6,    /* T < 1 (prefill) */
+  MOE_ERR_DEVICE = 7,    /* current device is not gfx950, or device query failed */
+  MOE_ERR_HIP = 8,       /* a kernel launch failed */
+  MOE_ERR_ALIAS = 9,     /* x and out overlap */
+  MOE_ERR_ALLOC = 10     /* host allocation failed */
+} moe_status;
+
+typedef enum { MOE_BF16 = 0, MOE_FP16 = 1, MOE_FP32 = 2 } moe_dtype;
+
+/* Flags (moe_config.flags). */
+#define MOE_F_NONE 0u
+
+typedef struct {               /* (host) */
+  int32_t hidden;              /* H: multiple of 256, <= 16384 */
+  int32_t inter;               /* I: intermediate size of every expert (routed and
+                                  shared); multiple of 128, <= 4096 */
+  int32_t n_experts;           /* E: 1 <= E <= 256 */
+  int32_t top_k;               /* k: 1 <= k <= min(E, 16) */
+  int32_t group_size;          /* must be 64 */
+  moe_dtype router_dtype;      /* MOE_BF16 or MOE_FP32 */
+  moe_dtype qparam_dtype;      /* scale/bias dtype: MOE_FP16 */
+  int32_t max_chunk_tokens;    /* prefill chunk; fixes the workspace size; 1..65536 */
+  uint32_t flags;              /* MOE_F_* bits; unknown bits -> MOE_ERR_SHAPE */
+} moe_config;
+
+typedef struct {               /* (host struct of device pointers) */
+  const uint32_t *q;           /* [N][K/8] codes */
+  const void *scale;           /* fp16 [N][K/64] */
+  const void *bias;            /* fp16 [N][K/64] */
+} moe_qmat;
+
+typedef struct {               /* (host struct of device pointers) */
+  const void *router_w;        /* [E][H] bf16 or float32 */
+  const float *router_bias;    /* [E] or NULL */
+  moe_qmat gate, up;           /* routed, [E][I][H] */
+  moe_qmat down;               /* routed, [E][H][I] */
+  moe_qmat s_gate, s_up;       /* shared, [I][H] */
+  moe_qmat s_down;             /* shared, [H][I] */
+} moe_weights;
+
+typedef struct moe_plan_s *moe_plan_t;
+
+/* Prefill stages (indices into moe_debug_out.events). */
+enum {
+  MOE_STAGE_ROUTE = 0,   /* logits, top-k, gates, certification, fp64 re-rank */
+  MOE_STAGE_GROUP = 1,   /* histogram, prefix scan, scatter, block map */
+  MOE_STAGE_GATEUP = 2,  /* grouped GEMM gate/up + SwiGLU */
+  MOE_STAGE_DOWN = 3,    /* grouped GEMM down + gate-weighted combine */
+  MOE_STAGE_FINAL = 4,   /* fp32 accumulator -> bf16 output */
+  MOE_PREFILL_STAGES = 5
+};
+/* Decode stages. */
+enum {
+  MOE_DSTAGE_ROUTE = 0,  /* logits (binary64), top-k, gates */
+  MOE_DSTAGE_GATEUP = 1, /* k+1 experts: gate/up GEMV + SwiGLU */
+  MOE_DSTAGE_DOWN = 2,   /* down GEMV + routing weights + shared expert -> bf16 */
+  MOE_DECODE_STAGES = 3
+};
+
+/* Optional diagnostics of one forward (any field may be NULL).
+ * For prefill with T > max_chunk_tokens, topk_ids/gates cover all T tokens;
+ * counts/offsets are per chunk, concatenated ([n_chunks][E+1], [n_chunks][E+2]);
+ * row_token is per chunk, chunk c's rows starting at c*max_chunk_tokens*(k+1)
+ * and holding chunk-local token indices; n_refined[c] counts chunk c's tokens
+ * whose fp32 ranking was not certified and were re-ranked in binary64.
+ * events (host array of hipEvent_t): if non-NULL it must hold n_stages+1
+ * events; event i is recorded on the stream before stage i and event n_stages
+ * after the last stage (of the last chunk). */
+typedef struct {
+  int32_t *topk_ids;           /* [T][k], ascending expert index per token */
+  float *gates;                /* [T][k], gate of topk_ids[t][j] */
+  int32_t *counts;             /* [n_chunks][E+1]; bin E = shared expert */
+  int32_t *offsets;            /* [n_chunks][E+2] */
+  int32_t *row_token;          /* [n_chunks * max_chunk_tokens * (k+1)] */
+  int32_t *n_refined;          /* [n_chunks] */
+  hipEvent_t *events;          /* (host) */
+} moe_debug_out;
+
+/* Validate cfg and w (host checks only: no device work, no device memory) and
+ * create a plan.  *workspace_bytes receives the workspace size every forward
+ * with this plan needs (it depends only on cfg).  Queries the current device
+ * once; it must be a gfx950. */
+moe_status moe_plan_create(const moe_config *cfg, const moe_weights *w, moe_plan_t *plan,
+                           size_t *workspace_bytes);
+void moe_plan_destroy(moe_plan_t plan);
+
+/* Initialise a workspace's control words (enqueued on stream).  Required once
+ * per workspace before its first forward; forwards leave it initialised. */
+moe_status moe_workspace_init(moe_plan_t plan, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/* Prefill: x, out bf16 [T][H]; T >= 1.  Tokens are processed in chunks of at
+ * most max_chunk_tokens with one workspace. */
+moe_status moe_forward_prefill(moe_plan_t plan, const void *x, int64_t T, void *out,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream,
+                               const moe_debug_out *dbg);
+
+/* Decode: one token; x, out bf16 [H]. */
+moe_status moe_forward_decode(moe_plan_t plan, const void *x, void *out, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream,
+                              const moe_debug_out *dbg);
+
+const char *moe_status_string(moe_status s);
+
+/* Library build identification, e.g. "moe-mi355x gfx950". */
+const char *moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

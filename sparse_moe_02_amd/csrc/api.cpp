@@ -1,0 +1,313 @@
+// Host side of the C ABI declared in include/moe.h: validation, workspace layout, the
+// prefill chunk loop ("Optimizing on-device inference for Apple Silicon", section
+// "Prefill > Bound temporary memory with prompt chunking") and the launch sequences.
+// Every step is enqueued on the caller's stream with no host synchronisation in
+// between (section "Prefill > Keep expert routing on the GPU").
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "../../include/moe.h"
+#include "kernels.hpp"
+
+using namespace moe;
+
+struct moe_plan_s {
+  moe_config cfg;
+  moe_weights w;
+  int n_cu;
+  // workspace layout (byte offsets)
+  size_t off_ctrl, off_tokmask, off_ids, off_gates, off_counts, off_offsets, off_base, off_row_token,
+      off_row_gate, off_mblocks, off_h, off_acc, off_l64, off_a64, off_dids, off_dgates, off_dh, total;
+};
+
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+moe_status check_qmat(const moe_qmat &m) {
+  if (!m.q || !m.scale || !m.bias) return MOE_ERR_NULL;
+  if (!aligned16(m.q)) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+void layout(moe_plan_s &p) {
+  const size_t C = (size_t)p.cfg.max_chunk_tokens, E = p.cfg.n_experts, k = p.cfg.top_k;
+  const size_t H = p.cfg.hidden, I = p.cfg.inter;
+  const size_t nblk = (C + kRouteTokens - 1) / kRouteTokens;
+  const size_t rows = C * (k + 1);
+  const size_t max_mblocks = rows / kBM + E + 2;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  p.off_ctrl = take(sizeof(Ctrl));
+  p.off_tokmask = take(nblk * E * 4);
+  p.off_ids = take(C * k * 4);
+  p.off_gates = take(C * k * 4);
+  p.off_counts = take((E + 1) * 4);
+  p.off_offsets = take((E + 2) * 4);
+  p.off_base = take(nblk * E * 4);
+  p.off_row_token = take(rows * 4);
+  p.off_row_gate = take(rows * 4);
+  p.off_mblocks = take(max_mblocks * 16);
+  p.off_h = take(rows * I * 2);
+  p.off_acc = take(C * H * 4);
+  p.off_l64 = take(E * 8);
+  p.off_a64 = take(E * 8);
+  p.off_dids = take(k * 4);
+  p.off_dgates = take(k * 4);
+  p.off_dh = take((k + 1) * I * 4);
+  p.total = o;
+}
+
+template <class T>
+T *at(void *ws, size_t off) {
+  return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
+}
+
+QMat qm(const moe_qmat &m) {
+  return QMat{m.q, static_cast<const uint16_t *>(m.scale), static_cast<const uint16_t *>(m.bias)};
+}
+
+moe_status check_ws(const moe_plan_s *p, void *ws, size_t bytes) {
+  if (!ws) return MOE_ERR_WORKSPACE;
+  if (bytes < p->total) return MOE_ERR_WORKSPACE;
+  if (((uintptr_t)ws & 255u) != 0) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+hipError_t rec(const moe_debug_out *dbg, int i, hipStream_t s) {
+  if (dbg && dbg->events) return hipEventRecord(dbg->events[i], s);
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "unsupported shape or flags";
+    case MOE_ERR_DTYPE: return "unsupported dtype";
+    case MOE_ERR_ALIGN: return "pointer not aligned (16 B; workspace 256 B)";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_TOKENS: return "token count out of range";
+    case MOE_ERR_DEVICE: return "current device is not gfx950 or cannot be queried";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    case MOE_ERR_ALIAS: return "x and out overlap";
+    case MOE_ERR_ALLOC: return "host allocation failed";
+  }
+  return "unknown status";
+}
+
+const char *moe_version(void) { return "moe-mi355x gfx950 1"; }
+
+moe_status moe_plan_create(const moe_config *cfg, const moe_weights *w, moe_plan_t *plan,
+                           size_t *workspace_bytes) {
+  if (!cfg || !w || !plan) return MOE_ERR_NULL;
+  *plan = nullptr;
+  const moe_config &c = *cfg;
+  if (c.group_size != 64) return MOE_ERR_SHAPE;
+  if (c.hidden < 256 || c.hidden > 16384 || c.hidden % 256) return MOE_ERR_SHAPE;
+  if (c.inter < 128 || c.inter > 4096 || !is_pow2(c.inter)) return MOE_ERR_SHAPE;
+  if (c.n_experts < 1 || c.n_experts > kMaxExperts) return MOE_ERR_SHAPE;
+  if (c.top_k < 1 || c.top_k > c.n_experts || c.top_k > kMaxTopK) return MOE_ERR_SHAPE;
+  if (c.max_chunk_tokens < 1 || c.max_chunk_tokens > 65536) return MOE_ERR_SHAPE;
+  if (c.flags != 0) return MOE_ERR_SHAPE;
+  if (c.router_dtype != MOE_BF16 && c.router_dtype != MOE_FP32) return MOE_ERR_DTYPE;
+  if (c.qparam_dtype != MOE_FP16) return MOE_ERR_DTYPE;
+  if (!w->router_w) return MOE_ERR_NULL;
+  if (!aligned16(w->router_w) || (w->router_bias && ((uintptr_t)w->router_bias & 3u))) return MOE_ERR_ALIGN;
+  for (const moe_qmat *m : {&w->gate, &w->up, &w->down, &w->s_gate, &w->s_up, &w->s_down}) {
+    const moe_status st = check_qmat(*m);
+    if (st != MOE_OK) return st;
+  }
+  int dev = 0;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
+    return MOE_ERR_DEVICE;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MOE_ERR_DEVICE;
+  moe_plan_s *p = new (std::nothrow) moe_plan_s();
+  if (!p) return MOE_ERR_ALLOC;
+  p->cfg = c;
+  p->w = *w;
+  p->n_cu = prop.multiProcessorCount;
+  layout(*p);
+  if (workspace_bytes) *workspace_bytes = p->total;
+  *plan = p;
+  return MOE_OK;
+}
+
+void moe_plan_destroy(moe_plan_t plan) { delete plan; }
+
+moe_status moe_workspace_init(moe_plan_t p, void *ws, size_t bytes, hipStream_t stream) {
+  if (!p) return MOE_ERR_NULL;
+  const moe_status st = check_ws(p, ws, bytes);
+  if (st != MOE_OK) return st;
+  return launch_ctrl_init(at<Ctrl>(ws, p->off_ctrl), stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_forward_prefill(moe_plan_t p, const void *x, int64_t T, void *out, void *ws, size_t bytes,
+                               hipStream_t stream, const moe_debug_out *dbg) {
+  if (!p || !x || !out) return MOE_ERR_NULL;
+  if (T < 1 || T > ((int64_t)1 << 40)) return MOE_ERR_TOKENS;
+  if (!aligned16(x) || !aligned16(out)) return MOE_ERR_ALIGN;
+  moe_status st = check_ws(p, ws, bytes);
+  if (st != MOE_OK) return st;
+  const moe_config &c = p->cfg;
+  const size_t H = c.hidden, E = c.n_experts, k = c.top_k;
+  if (overlap(x, (size_t)T * H * 2, out, (size_t)T * H * 2)) return MOE_ERR_ALIAS;
+  const int64_t C = c.max_chunk_tokens;
+  const int gemm_blocks = p->n_cu * 2;
+  Ctrl *ctrl = at<Ctrl>(ws, p->off_ctrl);
+  const bool fp32_router = c.router_dtype == MOE_FP32;
+
+  for (int64_t c0 = 0, ci = 0; c0 < T; c0 += C, ++ci) {
+    const int Tc = (int)((T - c0 < C) ? (T - c0) : C);
+    const bool last = c0 + C >= T;
+    const moe_debug_out *d = last ? dbg : nullptr;
+    const uint16_t *xc = static_cast<const uint16_t *>(x) + (size_t)c0 * H;
+    uint16_t *oc = static_cast<uint16_t *>(out) + (size_t)c0 * H;
+
+    RouteArgs ra{};
+    ra.x = xc;
+    ra.wr16 = fp32_router ? nullptr : static_cast<const uint16_t *>(p->w.router_w);
+    ra.wr32 = fp32_router ? static_cast<const float *>(p->w.router_w) : nullptr;
+    ra.bias = p->w.router_bias;
+    ra.T = Tc;
+    ra.H = (int)H;
+    ra.E = (int)E;
+    ra.k = (int)k;
+    ra.ids = at<int32_t>(ws, p->off_ids);
+    ra.gates = at<float>(ws, p->off_gates);
+    ra.tokmask = at<uint32_t>(ws, p->off_tokmask);
+    ra.out_acc = at<float>(ws, p->off_acc);
+    ra.ctrl = ctrl;
+    if (dbg) {
+      ra.dbg_ids = dbg->topk_ids ? dbg->topk_ids + (size_t)c0 * k : nullptr;
+      ra.dbg_gates = dbg->gates ? dbg->gates + (size_t)c0 * k : nullptr;
+    }
+    if (rec(d, MOE_STAGE_ROUTE, stream) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_route(ra, stream) != hipSuccess) return MOE_ERR_HIP;
+
+    GroupArgs ga{};
+    ga.ids = ra.ids;
+    ga.gates = ra.gates;
+    ga.tokmask = ra.tokmask;
+    ga.T = Tc;
+    ga.E = (int)E;
+    ga.k = (int)k;
+    ga.counts = at<int32_t>(ws, p->off_counts);
+    ga.offsets = at<int32_t>(ws, p->off_offsets);
+    ga.base = at<int32_t>(ws, p->off_base);
+    ga.row_token = at<int32_t>(ws, p->off_row_token);
+    ga.row_gate = at<float>(ws, p->off_row_gate);
+    ga.mblocks = at<int4>(ws, p->off_mblocks);
+    ga.ctrl = ctrl;
+    if (dbg) {
+      ga.dbg_counts = dbg->counts ? dbg->counts + (size_t)ci * (E + 1) : nullptr;
+      ga.dbg_offsets = dbg->offsets ? dbg->offsets + (size_t)ci * (E + 2) : nullptr;
+      ga.dbg_row_token = dbg->row_token ? dbg->row_token + (size_t)c0 * (k + 1) : nullptr;
+      ga.dbg_n_refined = dbg->n_refined ? dbg->n_refined + ci : nullptr;
+    }
+    if (rec(d, MOE_STAGE_GROUP, stream) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_group(ga, stream) != hipSuccess) return MOE_ERR_HIP;
+
+    GemmArgs g1{};
+    g1.x = xc;
+    g1.mblocks = ga.mblocks;
+    g1.ctrl = ctrl;
+    g1.queue = &ctrl->q_gateup;
+    g1.row_token = ga.row_token;
+    g1.row_gate = ga.row_gate;
+    g1.w0 = qm(p->w.gate);
+    g1.w1 = qm(p->w.up);
+    g1.s0 = qm(p->w.s_gate);
+    g1.s1 = qm(p->w.s_up);
+    g1.E = (int)E;
+    g1.H = (int)H;
+    g1.I = c.inter;
+    g1.h = at<uint16_t>(ws, p->off_h);
+    if (rec(d, MOE_STAGE_GATEUP, stream) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_gemm_gateup(g1, gemm_blocks, stream) != hipSuccess) return MOE_ERR_HIP;
+
+    GemmArgs g2 = g1;
+    g2.x = g1.h;
+    g2.queue = &ctrl->q_down;
+    g2.w0 = qm(p->w.down);
+    g2.s0 = qm(p->w.s_down);
+    g2.w1 = QMat{};
+    g2.s1 = QMat{};
+    g2.out_acc = ra.out_acc;
+    if (rec(d, MOE_STAGE_DOWN, stream) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_gemm_down(g2, gemm_blocks, stream) != hipSuccess) return MOE_ERR_HIP;
+
+    if (rec(d, MOE_STAGE_FINAL, stream) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_finalize(ra.out_acc, oc, (int64_t)Tc * (int64_t)H, stream) != hipSuccess) return MOE_ERR_HIP;
+    if (rec(d, MOE_PREFILL_STAGES, stream) != hipSuccess) return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_forward_decode(moe_plan_t p, const void *x, void *out, void *ws, size_t bytes, hipStream_t stream,
+                              const moe_debug_out *dbg) {
+  if (!p || !x || !out) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(out)) return MOE_ERR_ALIGN;
+  moe_status st = check_ws(p, ws, bytes);
+  if (st != MOE_OK) return st;
+  const moe_config &c = p->cfg;
+  if (overlap(x, (size_t)c.hidden * 2, out, (size_t)c.hidden * 2)) return MOE_ERR_ALIAS;
+  DecodeArgs a{};
+  a.x = static_cast<const uint16_t *>(x);
+  const bool fp32_router = c.router_dtype == MOE_FP32;
+  a.wr16 = fp32_router ? nullptr : static_cast<const uint16_t *>(p->w.router_w);
+  a.wr32 = fp32_router ? static_cast<const float *>(p->w.router_w) : nullptr;
+  a.bias = p->w.router_bias;
+  a.gate = qm(p->w.gate);
+  a.up = qm(p->w.up);
+  a.down = qm(p->w.down);
+  a.s_gate = qm(p->w.s_gate);
+  a.s_up = qm(p->w.s_up);
+  a.s_down = qm(p->w.s_down);
+  a.H = c.hidden;
+  a.E = c.n_experts;
+  a.k = c.top_k;
+  a.I = c.inter;
+  a.l64 = at<double>(ws, p->off_l64);
+  a.a64 = at<double>(ws, p->off_a64);
+  a.ids = at<int32_t>(ws, p->off_dids);
+  a.gates = at<float>(ws, p->off_dgates);
+  a.hbuf = at<float>(ws, p->off_dh);
+  a.ctrl = at<Ctrl>(ws, p->off_ctrl);
+  a.out = static_cast<uint16_t *>(out);
+  if (dbg) {
+    a.dbg_ids = dbg->topk_ids;
+    a.dbg_gates = dbg->gates;
+  }
+  if (rec(dbg, MOE_DSTAGE_ROUTE, stream) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_decode_route(a, stream) != hipSuccess) return MOE_ERR_HIP;
+  if (rec(dbg, MOE_DSTAGE_GATEUP, stream) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_decode_gateup(a, stream) != hipSuccess) return MOE_ERR_HIP;
+  if (rec(dbg, MOE_DSTAGE_DOWN, stream) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_decode_down(a, stream) != hipSuccess) return MOE_ERR_HIP;
+  if (rec(dbg, MOE_DECODE_STAGES, stream) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// Device helpers shared by the MoE kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+// ---------------------------------------------------------------- number formats
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round to nearest even, packing (lo, hi) into one word (compiles to v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+  bf16x2 p;
+  p[0] = (__bf16)lo;
+  p[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)(pack_bf16x2(f, 0.f) & 0xffffu); }
+
+__device__ __forceinline__ float fp16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+// 4-bit code i (0..7) of a packed word as float.
+__device__ __forceinline__ float code_f(uint32_t w, int i) { return (float)((w >> (4 * i)) & 0xfu); }
+
+// Dequantise the 8 codes of one word with one (scale, bias) and pack to 4 bf16x2 words
+// (element order k, k+1, ... low half first): w = scale*code + bias in fp32, then RNE.
+__device__ __forceinline__ void dequant8_bf16(uint32_t w, float s, float b, uint32_t out[4]) {
+  const uint32_t lo = w & 0x0f0f0f0fu;         // codes 0,2,4,6 in bytes 0..3
+  const uint32_t hi = (w >> 4) & 0x0f0f0f0fu;  // codes 1,3,5,7
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float c0 = (float)((lo >> (8 * j)) & 0xffu);
+    const float c1 = (float)((hi >> (8 * j)) & 0xffu);
+    out[j] = pack_bf16x2(__builtin_fmaf(s, c0, b), __builtin_fmaf(s, c1, b));
+  }
+}
+
+// ---------------------------------------------------------------- wave reductions
+
+template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf, bool BOUND = false>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, BANK_MASK, BOUND));
+}
+
+// Sum over the 16 lanes of each DPP row; every lane of the row receives the row sum.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x124>(v);  // row_ror:4
+  v += dpp_f<0x128>(v);  // row_ror:8
+  return v;
+}
+
+// Sum over the whole wave, result broadcast to every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) v = fminf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Block until *flag reaches `target` (device-scope acquire), giving up after
+// `spins` polls; returns false on timeout.
+__device__ __forceinline__ bool wait_at_least(const int *flag, int target, int spins) {
+  for (int i = 0; i < spins; ++i) {
+    if (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) >= target) return true;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return false;
+}
+
+}  // namespace moe

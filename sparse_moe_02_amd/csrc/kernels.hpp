@@ -1,0 +1,105 @@
+// Launch interfaces of the MoE kernels (host side calls these from api.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kRouteTokens = 32;   // tokens per router workgroup
+constexpr int kMaxExperts = 256;
+constexpr int kMaxTopK = 16;
+constexpr int kBM = 128;           // max rows of one grouped-GEMM M-block
+constexpr int kGateUpCols = 128;   // h columns per gate/up work item (4 waves x 32)
+constexpr int kDownCols = 256;     // output columns per down work item (4 waves x 64)
+
+struct QMat {
+  const uint32_t *q;
+  const uint16_t *s;
+  const uint16_t *b;
+};
+
+// Control words at the start of the workspace.
+struct Ctrl {
+  int decode_ticket;   // decode router: blocks done (reset by the last block)
+  int q_gateup;        // grouped GEMM work queues (reset by the group kernel)
+  int q_down;
+  int n_mblocks;       // M-blocks in the block map
+  int n_refined;       // tokens re-ranked in binary64 this chunk (reset by the group kernel)
+  int pad[59];
+};
+
+struct RouteArgs {
+  const uint16_t *x;      // [T][H] bf16 (chunk)
+  const uint16_t *wr16;   // [E][H] bf16 router (or null)
+  const float *wr32;      // [E][H] fp32 router (or null)
+  const float *bias;      // [E] or null
+  int T, H, E, k;
+  int32_t *ids;           // [T][k] ascending
+  float *gates;           // [T][k]
+  uint32_t *tokmask;      // [ceil(T/32)][E] bit m: token 32*blk+m chose e
+  float *out_acc;         // [T][H]: zeroed here
+  Ctrl *ctrl;
+  int32_t *dbg_ids;       // optional [T][k] (chunk-offset)
+  float *dbg_gates;
+};
+
+struct GroupArgs {
+  const int32_t *ids;
+  const float *gates;
+  const uint32_t *tokmask;
+  int T, E, k;
+  int32_t *counts;        // [E+1]
+  int32_t *offsets;       // [E+2]
+  int32_t *base;          // [nblk][E] scratch
+  int32_t *row_token;     // [T*(k+1)]
+  float *row_gate;        // [T*(k+1)]
+  int4 *mblocks;          // {expert, row0, rows, mt}
+  Ctrl *ctrl;
+  int32_t *dbg_counts, *dbg_offsets, *dbg_row_token, *dbg_n_refined;
+};
+
+struct GemmArgs {
+  const uint16_t *x;        // gate/up: activations [T][H]; down: h [rows][I]
+  const int4 *mblocks;
+  const Ctrl *ctrl;
+  int *queue;
+  const int32_t *row_token;
+  const float *row_gate;
+  QMat w0, w1;              // routed stacked (gate, up) or (down, -)
+  QMat s0, s1;              // shared expert
+  int E, H, I;
+  uint16_t *h;              // gate/up output [rows][I]
+  float *out_acc;           // down output [T][H]
+};
+
+struct DecodeArgs {
+  const uint16_t *x;        // [H]
+  const uint16_t *wr16;
+  const float *wr32;
+  const float *bias;
+  QMat gate, up, down;      // routed stacked
+  QMat s_gate, s_up, s_down;
+  int H, E, k, I;
+  double *l64;              // [E]
+  double *a64;              // [E]  sum |x w|
+  int32_t *ids;             // [k]
+  float *gates;             // [k]
+  float *hbuf;              // [(k+1)][I]
+  Ctrl *ctrl;
+  uint16_t *out;            // [H]
+  int32_t *dbg_ids;
+  float *dbg_gates;
+};
+
+hipError_t launch_route(const RouteArgs &a, hipStream_t s);
+hipError_t launch_group(const GroupArgs &a, hipStream_t s);
+hipError_t launch_gemm_gateup(const GemmArgs &a, int n_blocks, hipStream_t s);
+hipError_t launch_gemm_down(const GemmArgs &a, int n_blocks, hipStream_t s);
+hipError_t launch_finalize(const float *acc, uint16_t *out, int64_t n, hipStream_t s);
+hipError_t launch_decode_route(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_decode_gateup(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_decode_down(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_ctrl_init(Ctrl *c, hipStream_t s);
+
+}  // namespace moe

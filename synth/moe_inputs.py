@@ -113,8 +113,12 @@ def _quant_matrix(rng: np.random.Generator, N: int, K: int):
     return q, s, b
 
 
-def make_layer(cfg: int, layer: int = 0, seed: int = 0) -> LayerWeights:
-    """Draw one layer's weights (router, E routed experts and the shared expert)."""
+def make_layer(cfg: int, layer: int = 0, seed: int = 0, into: Optional[LayerWeights] = None) -> LayerWeights:
+    """Draw one layer's weights (router, E routed experts and the shared expert).
+
+    ``into``: a LayerWeights of the same config whose arrays are overwritten (saves
+    the page faults of fresh memory when many layers are drawn one after another).
+    """
     sh = CONFIGS[cfg]
     wc = sh.weights_cfg if sh.weights_cfg >= 0 else cfg
     E, H, I = sh.E, sh.H, sh.I
@@ -128,9 +132,13 @@ def make_layer(cfg: int, layer: int = 0, seed: int = 0) -> LayerWeights:
         router_b = (-1.2 * np.log(rank.astype(np.float64))).astype(np.float32)
     mats = {}
     for m, (nm, N, K) in enumerate((("gate", I, H), ("up", I, H), ("down", H, I))):
-        q = np.empty((E + 1, N, K // 8), np.uint32)
-        s = np.empty((E + 1, N, K // 64), np.float16)
-        b = np.empty((E + 1, N, K // 64), np.float16)
+        if into is not None:
+            q, s, b = getattr(into, nm + "_q"), getattr(into, nm + "_s"), getattr(into, nm + "_b")
+            assert q.shape == (E + 1, N, K // 8)
+        else:
+            q = np.empty((E + 1, N, K // 8), np.uint32)
+            s = np.empty((E + 1, N, K // 64), np.float16)
+            b = np.empty((E + 1, N, K // 64), np.float16)
         for e in range(E + 1):
             q[e], s[e], b[e] = _quant_matrix(_rng(seed, wc, layer, TID_EXPERT0 + 3 * e + m), N, K)
         mats[nm] = (q, s, b)

@@ -1,0 +1,78 @@
+"""Shared helpers of the GPU parity tests: run the HIP library through its C ABI and
+compare with the oracle (bit-exact routing, max-abs-rel outputs)."""
+
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import oracle  # noqa: E402
+import synth  # noqa: E402
+
+TOL = 2e-2  # max|gpu - oracle| / max|oracle| over the output tensor
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+
+
+def ensure_lib():
+    from sparse_moe_02_amd import binding
+
+    if not os.path.exists(binding.LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    return binding
+
+
+def to_f64(bits: np.ndarray) -> np.ndarray:
+    return synth.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    return float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+
+
+def token_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    num = np.max(np.abs(got - ref), axis=1)
+    den = np.max(np.abs(ref), axis=1)
+    return float(np.max(num / den))
+
+
+def run_prefill(layer_w, x_bits, k, chunk, device="cuda:0"):
+    import torch
+
+    from sparse_moe_02_amd.layer import MoeLayer, bf16_bits, bf16_tensor
+
+    layer = MoeLayer(layer_w, top_k=k, max_chunk_tokens=chunk, device=device)
+    x = bf16_tensor(x_bits, device)
+    out, d = layer.prefill(x, debug=True)
+    torch.cuda.synchronize()
+    res = {key: v.cpu().numpy() for key, v in d.items()}
+    res["out"] = to_f64(bf16_bits(out))
+    layer.close()
+    return res
+
+
+def check_routing_prefill(res, ref_ids, ref_gates, x_len, E, k, chunk, group_of_chunk):
+    """ids bit-exact, gates close; per chunk counts/offsets/row_token bit-exact."""
+    assert np.array_equal(res["topk_ids"], ref_ids), "top-k ids differ from the oracle"
+    gerr = float(np.max(np.abs(res["gates"] - ref_gates)))
+    assert gerr <= 2e-5, f"gates differ by {gerr}"
+    nch = (x_len + chunk - 1) // chunk
+    for c in range(nch):
+        lo, hi = c * chunk, min(x_len, (c + 1) * chunk)
+        g = group_of_chunk(lo, hi)
+        n = (hi - lo) * (k + 1)
+        assert np.array_equal(res["counts"][c], g["counts"]), f"counts differ in chunk {c}"
+        assert np.array_equal(res["offsets"][c], g["offsets"]), f"offsets differ in chunk {c}"
+        rt = res["row_token"][c * chunk * (k + 1): c * chunk * (k + 1) + n]
+        assert np.array_equal(rt, g["row_token"]), f"row_token differs in chunk {c}"
+    return gerr

@@ -1,0 +1,228 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle.
+
+Routing (top-k ids, per-chunk counts, offsets and grouped row order) must match bit
+for bit; gates within 2e-5; outputs within max|gpu - oracle| / max|oracle| <= 2e-2.
+"""
+
+import numpy as np
+import pytest
+
+from gpu_helpers import (TOL, check_routing_prefill, ensure_lib, oracle, rel_err, run_prefill, say, synth,
+                         to_f64, token_rel_err)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ensure_lib()
+
+
+def _prefill_case(L, x, k, chunk, name):
+    say(f"[{name}] T={x.shape[0]} chunk={chunk}: oracle routing")
+    r = oracle.route(x, L.router_w, L.router_b, k)
+    E = L.gate_q.shape[0] - 1
+    say(f"[{name}] GPU prefill")
+    res = run_prefill(L, x, k, chunk)
+    gerr = check_routing_prefill(res, r["ids"], r["gates"], x.shape[0], E, k, chunk,
+                                 lambda lo, hi: oracle.group(r["ids"][lo:hi], E))
+    say(f"[{name}] routing exact; gate err {gerr:.2e}; refined per chunk {res['n_refined'].tolist()[:8]}")
+    return r, res
+
+
+def _check_out(name, got, ref):
+    e, et = rel_err(got, ref), token_rel_err(got, ref)
+    say(f"[{name}] out max-abs-rel {e:.3e} (worst token {et:.3e})")
+    assert e <= TOL, f"{name}: output error {e}"
+    return e
+
+
+def test_tiny_prefill_full_and_chunked():
+    L, x = synth.make_layer(0), synth.make_x(0)
+    ref = oracle.forward(x, L, 2)
+    for chunk in (8, 3, 1):
+        r, res = _prefill_case(L, x, 2, chunk, f"tiny/chunk{chunk}")
+        _check_out(f"tiny/chunk{chunk}", res["out"], ref["out"])
+        assert res["n_refined"].sum() == 8  # float32 router: every token ranked in binary64
+
+
+def test_tiny_decode_each_token():
+    import torch
+
+    from sparse_moe_02_amd.layer import MoeLayer, bf16_bits, bf16_tensor
+
+    L, x = synth.make_layer(0), synth.make_x(0)
+    ref = oracle.forward(x, L, 2)
+    layer = MoeLayer(L, top_k=2, max_chunk_tokens=8)
+    for t in range(8):
+        out, d = layer.decode(bf16_tensor(x[t], "cuda:0"), debug=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(d["topk_ids"].cpu().numpy()[0], ref["ids"][t])
+        assert np.max(np.abs(d["gates"].cpu().numpy()[0] - ref["gates"][t])) <= 2e-5
+        got = to_f64(bf16_bits(out))
+        assert rel_err(got[None], ref["out"][t][None]) <= TOL
+    layer.close()
+
+
+def test_prefill_uniform_4k():
+    L, x = synth.make_layer(2), synth.make_x(2)
+    r, res = _prefill_case(L, x, 8, 4096, "uniform-4k")
+    say("[uniform-4k] oracle experts")
+    ref = oracle.experts(x, L, r["ids"], r["gates"])
+    _check_out("uniform-4k", res["out"], ref)
+
+
+def test_prefill_zipf_4k():
+    L, x = synth.make_layer(3), synth.make_x(3)
+    r, res = _prefill_case(L, x, 8, 4096, "zipf-4k")
+    counts = res["counts"][0][:256]
+    assert counts.max() > 1000 and (counts == 0).sum() >= 50
+    say("[zipf-4k] oracle experts")
+    ref = oracle.experts(x, L, r["ids"], r["gates"])
+    _check_out("zipf-4k", res["out"], ref)
+
+
+def test_decode_40_layers():
+    import torch
+
+    from sparse_moe_02_amd.layer import MoeLayer, bf16_bits, bf16_tensor
+
+    L = None
+    worst = 0.0
+    for layer_i in range(40):
+        L = synth.make_layer(1, layer_i, into=L)
+        x = synth.make_x(1, layer_i)
+        r = oracle.route(x, L.router_w, None, 8)
+        ref = oracle.experts(x, L, r["ids"], r["gates"])
+        m = MoeLayer(L, top_k=8, max_chunk_tokens=1)
+        out, d = m.decode(bf16_tensor(x[0], "cuda:0"), debug=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(d["topk_ids"].cpu().numpy(), r["ids"]), f"layer {layer_i}: ids differ"
+        assert np.max(np.abs(d["gates"].cpu().numpy() - r["gates"])) <= 2e-5
+        e = rel_err(to_f64(bf16_bits(out))[None], ref)
+        worst = max(worst, e)
+        assert e <= TOL, f"layer {layer_i}: output error {e}"
+        m.close()
+        del m
+        if layer_i % 8 == 7:
+            say(f"[decode] layers 0..{layer_i} ok, worst max-abs-rel {worst:.3e}")
+
+
+def test_long_prompt_128k_chunked():
+    sh = synth.shape_of(4)
+    L = synth.make_layer(4)
+    say("[128k] drawing x")
+    x = synth.make_x(4)
+    T, chunk = sh.T, sh.chunk
+    r, res = _prefill_case(L, x, 8, chunk, "128k")
+    # outputs on a sample: first and last token of every chunk plus 4 seeded picks per chunk
+    rng = np.random.default_rng(0)
+    picks = set()
+    for c in range(T // chunk):
+        picks.update({c * chunk, c * chunk + chunk - 1})
+        picks.update((c * chunk + rng.integers(0, chunk, 4)).tolist())
+    idx = np.array(sorted(picks))
+    say(f"[128k] oracle experts on {idx.size} sampled tokens")
+    ref = oracle.experts(x[idx], L, r["ids"][idx], r["gates"][idx])
+    _check_out("128k", res["out"][idx], ref)
+
+
+def test_prefill_single_token_and_ragged_tail():
+    L = synth.make_layer(2)
+    x = synth.make_x(4, rows=slice(0, 4097))
+    for T, chunk in ((1, 4096), (4097, 4096), (77, 32)):
+        xs = x[:T]
+        r, res = _prefill_case(L, xs, 8, chunk, f"T{T}/c{chunk}")
+        sample = np.unique(np.r_[0:min(T, 40), T - 1])
+        ref = oracle.experts(xs[sample], L, r["ids"][sample], r["gates"][sample])
+        _check_out(f"T{T}/c{chunk}", res["out"][sample], ref)
+
+
+def test_exact_and_near_ties():
+    """Duplicated router rows (exact ties) and crafted near-ties below the fp32 and the
+    binary64 error bounds: the lower index must win exactly as in the oracle."""
+    L = synth.make_layer(2)
+    x = synth.make_x(2, rows=slice(0, 256)).copy()
+    rw = L.router_w.copy()
+    ref0 = oracle.route(x, rw, None, 8)
+    assert ref0["ranked"].shape == (256, 8)
+    # exact ties: expert 200 duplicates expert 17, 201 duplicates 99
+    rw[200] = rw[17]
+    rw[201] = rw[99]
+    # near ties on token 0: find its 8th and 9th experts, copy 8th's row into the 9th and
+    # nudge one weight where x is tiny so the logits differ by ~1e-7 (fp32 level)
+    l0 = np.argsort(-ref0["logits"][0])
+    e8, e9 = int(l0[7]), int(l0[8])
+    rw[e9] = rw[e8]
+    x[0, 5] = synth.f32_to_bf16_bits(np.float32(3e-4))
+    rw[e9, 5] = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(rw[e8, 5:6]) * np.float32(1.0 + 2 ** -7))[0]
+    # token 1: difference ~1e-16 (below the binary64 bound) via a denormal-range x entry
+    l1 = np.argsort(-ref0["logits"][1])
+    f8, f9 = int(l1[7]), int(l1[8])
+    if {f8, f9} & {e8, e9}:
+        f8, f9 = int(l1[5]), int(l1[6])
+    rw[f9] = rw[f8]
+    x[1, 9] = synth.f32_to_bf16_bits(np.float32(1e-14))
+    rw[f9, 9] = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(rw[f8, 9:10]) * np.float32(1.0 - 2 ** -7))[0]
+    L2 = synth.LayerWeights(rw, None, L.gate_q, L.gate_s, L.gate_b, L.up_q, L.up_s, L.up_b, L.down_q, L.down_s,
+                            L.down_b)
+    r, res = _prefill_case(L2, x, 8, 4096, "ties")
+    assert res["n_refined"][0] > 0
+    lg = r["logits"]
+    assert np.any(lg[:, 200] == lg[:, 17]) and 0 < abs(lg[0, e8] - lg[0, e9]) < 1e-5
+
+
+def test_bias_dominance_and_all_experts():
+    L = synth.make_layer(2)
+    x = synth.make_x(2, rows=slice(0, 300))
+    bias = np.zeros(256, np.float32)
+    bias[:8] = 100.0
+    L2 = synth.LayerWeights(L.router_w, bias, L.gate_q, L.gate_s, L.gate_b, L.up_q, L.up_s, L.up_b, L.down_q,
+                            L.down_s, L.down_b)
+    r, res = _prefill_case(L2, x, 8, 4096, "bias")
+    assert np.array_equal(res["topk_ids"], np.tile(np.arange(8), (300, 1)))
+    # k = E on a small layer: every expert chosen
+    Ls = synth.make_layer(0)
+    xs = synth.make_x(0)
+    ref = oracle.forward(xs, Ls, 16)
+    r2, res2 = _prefill_case(Ls, xs, 16, 8, "k=E")
+    _check_out("k=E", res2["out"], ref["out"])
+
+
+def test_routing_deterministic_across_runs():
+    L, x = synth.make_layer(2), synth.make_x(2, rows=slice(0, 1024))
+    a = run_prefill(L, x, 8, 1024)
+    b = run_prefill(L, x, 8, 1024)
+    for key in ("topk_ids", "counts", "offsets", "row_token"):
+        assert np.array_equal(a[key], b[key]), key
+    assert rel_err(a["out"], b["out"]) < 1e-2
+
+
+def test_abi_errors_on_device():
+    import torch
+
+    from sparse_moe_02_amd import binding as B
+    from sparse_moe_02_amd.layer import MoeLayer
+
+    L = synth.make_layer(0)
+    m = MoeLayer(L, top_k=2, max_chunk_tokens=8)
+    x = torch.zeros((8, 256), dtype=torch.bfloat16, device="cuda:0")
+    out = torch.empty_like(x)
+    s = m.stream()
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_forward_prefill(m.plan, x.data_ptr(), 8, out.data_ptr(), m.ws.data_ptr(), m.ws_bytes - 1, s)
+    assert ei.value.status == 5
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_forward_prefill(m.plan, x.data_ptr(), 8, x.data_ptr(), m.ws.data_ptr(), m.ws_bytes, s)
+    assert ei.value.status == 9
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_forward_prefill(m.plan, x.data_ptr() + 2, 8, out.data_ptr(), m.ws.data_ptr(), m.ws_bytes, s)
+    assert ei.value.status == 4
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_forward_prefill(m.plan, x.data_ptr(), 0, out.data_ptr(), m.ws.data_ptr(), m.ws_bytes, s)
+    assert ei.value.status == 6
+    torch.cuda.synchronize()
+    m.close()
