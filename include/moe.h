@@ -47,7 +47,8 @@
  *   - Errors: host validation returns a status before anything is enqueued; a
  *     failed launch returns MOE_ERR_HIP (hipGetLastError() is left for the
  *     caller).  No C++ exception crosses this interface.
- *   - x and out must not alias.  Device pointers must be 16-byte aligned.
+ *   - x and out must not alias.  x, out, router weight and code arrays must be
+ *     16-byte aligned, scale/bias arrays 4-byte aligned, the workspace 256-byte aligned.
  *
  * Layouts (row-major):
  *   x, out           bf16 [T][H]

@@ -34,6 +34,7 @@ bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 moe_status check_qmat(const moe_qmat &m) {
   if (!m.q || !m.scale || !m.bias) return MOE_ERR_NULL;
   if (!aligned16(m.q)) return MOE_ERR_ALIGN;
+  if (((uintptr_t)m.scale & 3u) || ((uintptr_t)m.bias & 3u)) return MOE_ERR_ALIGN;
   return MOE_OK;
 }
 
@@ -174,7 +175,7 @@ moe_status moe_forward_prefill(moe_plan_t p, const void *x, int64_t T, void *out
   const size_t H = c.hidden, E = c.n_experts, k = c.top_k;
   if (overlap(x, (size_t)T * H * 2, out, (size_t)T * H * 2)) return MOE_ERR_ALIAS;
   const int64_t C = c.max_chunk_tokens;
-  const int gemm_blocks = p->n_cu * 2;
+  const int gemm_blocks = p->n_cu;  // persistent: one 8-wave workgroup per CU
   Ctrl *ctrl = at<Ctrl>(ws, p->off_ctrl);
   const bool fp32_router = c.router_dtype == MOE_FP32;
 
@@ -233,7 +234,7 @@ moe_status moe_forward_prefill(moe_plan_t p, const void *x, int64_t T, void *out
     g1.x = xc;
     g1.mblocks = ga.mblocks;
     g1.ctrl = ctrl;
-    g1.queue = &ctrl->q_gateup;
+    g1.queue = ctrl->q_gateup;
     g1.row_token = ga.row_token;
     g1.row_gate = ga.row_gate;
     g1.w0 = qm(p->w.gate);
@@ -249,7 +250,7 @@ moe_status moe_forward_prefill(moe_plan_t p, const void *x, int64_t T, void *out
 
     GemmArgs g2 = g1;
     g2.x = g1.h;
-    g2.queue = &ctrl->q_down;
+    g2.queue = ctrl->q_down;
     g2.w0 = qm(p->w.down);
     g2.s0 = qm(p->w.s_down);
     g2.w1 = QMat{};

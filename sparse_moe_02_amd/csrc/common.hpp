@@ -18,6 +18,9 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+// 1/(1+exp(-a)) with the hardware reciprocal (about 1 ulp)
+__device__ __forceinline__ float sigmoid_fast(float a) { return __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
+
 // Round to nearest even, packing (lo, hi) into one word (compiles to v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
@@ -37,8 +40,11 @@ __device__ __forceinline__ float code_f(uint32_t w, int i) { return (float)((w >
 // Dequantise the 8 codes of one word with one (scale, bias) and pack to 4 bf16x2 words
 // (element order k, k+1, ... low half first): w = scale*code + bias in fp32, then RNE.
 __device__ __forceinline__ void dequant8_bf16(uint32_t w, float s, float b, uint32_t out[4]) {
-  const uint32_t lo = w & 0x0f0f0f0fu;         // codes 0,2,4,6 in bytes 0..3
-  const uint32_t hi = (w >> 4) & 0x0f0f0f0fu;  // codes 1,3,5,7
+  uint32_t lo = w & 0x0f0f0f0fu;         // codes 0,2,4,6 in bytes 0..3
+  uint32_t hi = (w >> 4) & 0x0f0f0f0fu;  // codes 1,3,5,7
+  // keep the byte layout opaque so each code converts with one v_cvt_f32_ubyteN
+  // (otherwise the extraction is re-derived from w with an extra shift/bfe per code)
+  asm("" : "+v"(lo), "+v"(hi));
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const float c0 = (float)((lo >> (8 * j)) & 0xffu);

@@ -19,7 +19,7 @@ namespace moe {
 namespace {
 
 constexpr int kGuRows = 4;   // gate/up rows per wave
-constexpr int kDnRows = 8;   // output rows per wave (at least)
+constexpr int kDnRows = 16;  // output rows per down workgroup
 
 __device__ __forceinline__ QMat expert_mat(const QMat &routed, const QMat &shared, int e, int E, int N, int K) {
   if (e == E) return shared;
@@ -36,7 +36,8 @@ __device__ __forceinline__ float dot_codes32(const uint4 &w, const float (&v)[32
   float s = 0.f;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const uint32_t lo = ws[q] & 0x0f0f0f0fu, hi = (ws[q] >> 4) & 0x0f0f0f0fu;
+    uint32_t lo = ws[q] & 0x0f0f0f0fu, hi = (ws[q] >> 4) & 0x0f0f0f0fu;
+    asm("" : "+v"(lo), "+v"(hi));  // one v_cvt_f32_ubyteN per code
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       s = __builtin_fmaf(v[8 * q + 2 * j], (float)((lo >> (8 * j)) & 0xffu), s);
@@ -100,30 +101,33 @@ __global__ __launch_bounds__(64) void k_decode_gateup(DecodeArgs a) {
 }
 
 // Down + combine: out[n] = sum_{j<k} gates[j] * Wd_{ids[j]}[n,:] . h_j + Wd_s[n,:] . h_k.
-// LPR lanes share one row (32 codes each per pass); a wave covers RW rows.
+// One workgroup of min(k+1, 16) waves per kDnRows output rows; wave j owns expert slot j
+// (and j + 16), keeps
+// its 32-element chunk of h_j in registers and issues all its weight loads at once.
+// LPR lanes share a row (32 codes each); per-slot partial sums meet in LDS.
 template <int LPR>
-__global__ __launch_bounds__(64) void k_decode_down(DecodeArgs a) {
-  constexpr int RPP = kWave / LPR;                       // rows per pass
-  constexpr int RW = RPP > kDnRows ? RPP : kDnRows;      // rows per wave
-  constexpr int P = RW / RPP;
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(1024) void k_decode_down(DecodeArgs a) {
+  constexpr int RPP = kWave / LPR;           // rows per pass
+  constexpr int P = kDnRows / RPP;           // passes (kDnRows is a multiple of RPP)
+  __shared__ float s_part[kMaxTopK + 1][kDnRows];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int H = a.H, I = a.I, E = a.E, k = a.k;
   const int sub = lane / LPR, cl = lane % LPR;
-  const int n0 = blockIdx.x * RW;
-  float acc[P] = {};
-  for (int j = 0; j <= k; ++j) {
+  const int n0 = blockIdx.x * kDnRows;
+  for (int j = wv; j <= k; j += nw) {
     const int e = j < k ? a.ids[j] : E;
     const float gj = j < k ? a.gates[j] : 1.0f;
     const QMat D = expert_mat(a.down, a.s_down, e, E, H, I);
+    float acc[P] = {};
     for (int c = cl; c < I / 32; c += LPR) {
       uint4 w[P];
-      float s[P], b[P];
+      float sc[P], bi[P];
 #pragma unroll
       for (int p = 0; p < P; ++p) {
         const size_t n = (size_t)(n0 + p * RPP + sub);
         w[p] = *(const uint4 *)(D.q + n * (I / 8) + 4 * c);
-        s[p] = fp16_to_f32(D.s[n * (I / 64) + c / 2]);
-        b[p] = fp16_to_f32(D.b[n * (I / 64) + c / 2]);
+        sc[p] = fp16_to_f32(D.s[n * (I / 64) + c / 2]);
+        bi[p] = fp16_to_f32(D.b[n * (I / 64) + c / 2]);
       }
       float hv[32];
       const float4 *hp = (const float4 *)(a.hbuf + (size_t)j * I + 32 * c);
@@ -139,15 +143,21 @@ __global__ __launch_bounds__(64) void k_decode_down(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 32; ++i) hs += hv[i];
 #pragma unroll
-      for (int p = 0; p < P; ++p) acc[p] += gj * (s[p] * dot_codes32(w[p], hv) + b[p] * hs);
+      for (int p = 0; p < P; ++p) acc[p] += sc[p] * dot_codes32(w[p], hv) + bi[p] * hs;
+    }
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      float v = acc[p];
+#pragma unroll
+      for (int o = 1; o < LPR; o <<= 1) v += __shfl_xor(v, o);
+      if (cl == 0) s_part[j][p * RPP + sub] = gj * v;
     }
   }
-#pragma unroll
-  for (int p = 0; p < P; ++p) {
-    float v = acc[p];
-#pragma unroll
-    for (int o = 1; o < LPR; o <<= 1) v += __shfl_xor(v, o);
-    if (cl == 0) a.out[n0 + p * RPP + sub] = f32_to_bf16(v);
+  __syncthreads();
+  if (threadIdx.x < kDnRows) {
+    float v = 0.f;
+    for (int jj = 0; jj <= k; ++jj) v += s_part[jj][threadIdx.x];
+    a.out[n0 + threadIdx.x] = f32_to_bf16(v);
   }
 }
 
@@ -162,15 +172,14 @@ hipError_t launch_decode_gateup(const DecodeArgs &a, hipStream_t s) {
 hipError_t launch_decode_down(const DecodeArgs &a, hipStream_t s) {
   const int cpr = a.I / 32;
   const int lpr = cpr < kWave ? cpr : kWave;
-  const int rpp = kWave / lpr;
-  const int rw = rpp > kDnRows ? rpp : kDnRows;
-  const dim3 grid(a.H / rw);
+  const int nw = a.k + 1 < 16 ? a.k + 1 : 16;  // waves; each loops over its expert slots
+  const dim3 grid(a.H / kDnRows), block(64 * nw);
   switch (lpr) {
-    case 4: hipLaunchKernelGGL(k_decode_down<4>, grid, dim3(64), 0, s, a); break;
-    case 8: hipLaunchKernelGGL(k_decode_down<8>, grid, dim3(64), 0, s, a); break;
-    case 16: hipLaunchKernelGGL(k_decode_down<16>, grid, dim3(64), 0, s, a); break;
-    case 32: hipLaunchKernelGGL(k_decode_down<32>, grid, dim3(64), 0, s, a); break;
-    default: hipLaunchKernelGGL(k_decode_down<64>, grid, dim3(64), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(k_decode_down<4>, grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL(k_decode_down<8>, grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL(k_decode_down<16>, grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL(k_decode_down<32>, grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL(k_decode_down<64>, grid, block, 0, s, a); break;
   }
   return hipGetLastError();
 }

@@ -11,6 +11,9 @@
 // rows of an expert are in ascending token order without atomics.  Bin E is the shared
 // expert, which every token visits.
 //
+// One workgroup per 256 tokens; each rereads every mask (popcounts are cheap), so no
+// workgroup waits for another.
+//
 // Block map: an expert with n rows is split into ceil(n/128) M-blocks of balanced height
 // (section "Prefill > Match tile size to expert load": the tile height follows the
 // expert's actual row count); each M-block records its height in 32-row MFMA tiles.
@@ -23,31 +26,53 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 1024;
+constexpr int kSubs = 8;                                 // router workgroups per group workgroup
+constexpr int kTokensPerBlock = kSubs * kRouteTokens;   // 256
+constexpr int kParts = kThreads / kMaxExperts;          // 4 threads per expert column
 
+// Workgroup g handles tokens [256 g, 256 g + 256) = router workgroups 8g .. 8g+7.  Every
+// workgroup reads all bit masks to get the expert totals (hence the offsets) and the
+// count of earlier tokens per expert; workgroup 0 also writes the offsets and the block
+// map and resets the work queues.
 __global__ __launch_bounds__(kThreads) void k_group(GroupArgs a) {
-  __shared__ int s_cnt[kMaxExperts + 1];
+  __shared__ int s_tot[kParts][kMaxExperts];
+  __shared__ int s_pre[kParts][kMaxExperts];
   __shared__ int s_off[kMaxExperts + 2];
-  __shared__ int s_cls[5];     // M-blocks per tile-height class (1..4 tiles of 32 rows)
-  __shared__ int s_clsoff[5];
-  __shared__ int s_clspos[5];
+  __shared__ int s_cnt[kMaxExperts + 1];
+  __shared__ uint32_t s_msk[kSubs][kMaxExperts];
+  __shared__ int s_base[kSubs][kMaxExperts];
+  __shared__ int s_cls[5], s_clsoff[5], s_clspos[5];
   const int tid = threadIdx.x;
   const int T = a.T, E = a.E, k = a.k;
   const int nblk = (T + kRouteTokens - 1) / kRouteTokens;
+  const int sb0 = blockIdx.x * kSubs;
+  const uint32_t *__restrict__ mask = a.tokmask;
 
-  // 1. histogram and per-workgroup bases (thread per expert, sequential over workgroups)
-  if (tid < E) {
-    int run = 0;
-    for (int b = 0; b < nblk; ++b) {
-      a.base[(size_t)b * E + tid] = run;
-      run += __popc(a.tokmask[(size_t)b * E + tid]);
+  // 1. per expert: total count, and count over router workgroups before sb0
+  {
+    const int e = tid % kMaxExperts, part = tid / kMaxExperts;
+    int tot = 0, pre = 0;
+    if (e < E) {
+      for (int b = part; b < nblk; b += kParts) {
+        const int c = __popc(mask[(size_t)b * E + e]);
+        tot += c;
+        pre += b < sb0 ? c : 0;
+      }
     }
-    s_cnt[tid] = run;
+    s_tot[part][e] = tot;
+    s_pre[part][e] = pre;
   }
-  if (tid == E) s_cnt[E] = T;
   if (tid < 5) {
     s_cls[tid] = 0;
     s_clspos[tid] = 0;
   }
+  __syncthreads();
+  if (tid < E) {
+    int tot = 0;
+    for (int p = 0; p < kParts; ++p) tot += s_tot[p][tid];
+    s_cnt[tid] = tot;
+  }
+  if (tid == E) s_cnt[E] = T;
   __syncthreads();
 
   // 2. exclusive prefix scan over the E+1 bins (one wave; lane takes a contiguous run)
@@ -69,7 +94,48 @@ __global__ __launch_bounds__(kThreads) void k_group(GroupArgs a) {
     }
     if (tid == kWave - 1) s_off[E + 1] = incl;
   }
+  // masks of this workgroup's router workgroups
+  for (int i = tid; i < kSubs * kMaxExperts; i += kThreads) {
+    const int j = i / kMaxExperts, e = i % kMaxExperts;
+    s_msk[j][e] = (e < E && sb0 + j < nblk) ? mask[(size_t)(sb0 + j) * E + e] : 0u;
+  }
   __syncthreads();
+  if (tid < E) {
+    int run = s_off[tid];
+    for (int p = 0; p < kParts; ++p) run += s_pre[p][tid];
+    for (int j = 0; j < kSubs; ++j) {
+      s_base[j][tid] = run;
+      run += __popc(s_msk[j][tid]);
+    }
+  }
+  __syncthreads();
+
+  // 3. scatter: grouped row of every (token, chosen expert) and of the shared slot
+  const int t0 = blockIdx.x * kTokensPerBlock;
+  for (int i = tid; i < kTokensPerBlock * (k + 1); i += kThreads) {
+    const int lt = i / (k + 1), j = i - lt * (k + 1);
+    const int t = t0 + lt;
+    if (t >= T) continue;
+    int pos;
+    float g;
+    if (j < k) {
+      const int e = a.ids[(size_t)t * k + j];
+      if ((unsigned)e >= (unsigned)E) continue;  // cannot happen for router output
+      const int sj = lt / kRouteTokens;
+      const uint32_t below = (1u << (lt % kRouteTokens)) - 1u;
+      pos = s_base[sj][e] + __popc(s_msk[sj][e] & below);
+      if (pos < s_off[e] || pos >= s_off[e + 1]) continue;
+      g = a.gates[(size_t)t * k + j];
+    } else {
+      pos = s_off[E] + t;
+      g = 1.0f;
+    }
+    a.row_token[pos] = t;
+    a.row_gate[pos] = g;
+    if (a.dbg_row_token) a.dbg_row_token[pos] = t;
+  }
+  if (blockIdx.x != 0) return;
+
   for (int e = tid; e <= E; e += kThreads) {
     a.counts[e] = s_cnt[e];
     if (a.dbg_counts) a.dbg_counts[e] = s_cnt[e];
@@ -77,26 +143,6 @@ __global__ __launch_bounds__(kThreads) void k_group(GroupArgs a) {
   for (int e = tid; e <= E + 1; e += kThreads) {
     a.offsets[e] = s_off[e];
     if (a.dbg_offsets) a.dbg_offsets[e] = s_off[e];
-  }
-
-  // 3. scatter: grouped row of every (token, chosen expert) and of the shared slot
-  for (int t = tid; t < T; t += kThreads) {
-    const int b = t / kRouteTokens;
-    const uint32_t below = (1u << (t % kRouteTokens)) - 1u;
-    for (int j = 0; j < k; ++j) {
-      const int e = a.ids[(size_t)t * k + j];
-      if ((unsigned)e >= (unsigned)E) continue;  // cannot happen for router output
-      const size_t be = (size_t)b * E + e;
-      const int pos = s_off[e] + a.base[be] + __popc(a.tokmask[be] & below);
-      if (pos < s_off[e] || pos >= s_off[e + 1]) continue;
-      a.row_token[pos] = t;
-      a.row_gate[pos] = a.gates[(size_t)t * k + j];
-      if (a.dbg_row_token) a.dbg_row_token[pos] = t;
-    }
-    const int pos = s_off[E] + t;
-    a.row_token[pos] = t;
-    a.row_gate[pos] = 1.0f;
-    if (a.dbg_row_token) a.dbg_row_token[pos] = t;
   }
 
   // 4. block map: balanced M-blocks per expert, ordered tallest class first
@@ -120,8 +166,10 @@ __global__ __launch_bounds__(kThreads) void k_group(GroupArgs a) {
       run += s_cls[c];
     }
     a.ctrl->n_mblocks = run;
-    a.ctrl->q_gateup = 0;
-    a.ctrl->q_down = 0;
+    for (int x = 0; x < kXcds; ++x) {
+      a.ctrl->q_gateup[x] = 0;
+      a.ctrl->q_down[x] = 0;
+    }
     if (a.dbg_n_refined) *a.dbg_n_refined = a.ctrl->n_refined;
     a.ctrl->n_refined = 0;
   }
@@ -141,7 +189,8 @@ __global__ __launch_bounds__(kThreads) void k_group(GroupArgs a) {
 }  // namespace
 
 hipError_t launch_group(const GroupArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(k_group, dim3(1), dim3(kThreads), 0, s, a);
+  const int nb = (a.T + kTokensPerBlock - 1) / kTokensPerBlock;
+  hipLaunchKernelGGL(k_group, dim3(nb), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -10,8 +10,9 @@ constexpr int kRouteTokens = 32;   // tokens per router workgroup
 constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 16;
 constexpr int kBM = 128;           // max rows of one grouped-GEMM M-block
-constexpr int kGateUpCols = 128;   // h columns per gate/up work item (4 waves x 32)
-constexpr int kDownCols = 256;     // output columns per down work item (4 waves x 64)
+constexpr int kGemmThreads = 512;  // grouped GEMM workgroup: 8 waves
+constexpr int kGateUpCols = 256;   // h columns per gate/up work item (8 waves x 32)
+constexpr int kDownCols = 512;     // output columns per down work item (8 waves x 64)
 
 struct QMat {
   const uint32_t *q;
@@ -19,14 +20,17 @@ struct QMat {
   const uint16_t *b;
 };
 
+constexpr int kXcds = 8;           // MI355X: 8 accelerator complex dies, one L2 each
+
 // Control words at the start of the workspace.
 struct Ctrl {
-  int decode_ticket;   // decode router: blocks done (reset by the last block)
-  int q_gateup;        // grouped GEMM work queues (reset by the group kernel)
-  int q_down;
-  int n_mblocks;       // M-blocks in the block map
-  int n_refined;       // tokens re-ranked in binary64 this chunk (reset by the group kernel)
-  int pad[59];
+  int decode_ticket;     // decode router: blocks done (reset by the last block)
+  int n_mblocks;         // M-blocks in the block map
+  int n_refined;         // tokens re-ranked in binary64 this chunk (reset by the group kernel)
+  int pad0;
+  int q_gateup[kXcds];   // grouped GEMM work queues, one per XCD (reset by the group kernel)
+  int q_down[kXcds];
+  int pad[44];
 };
 
 struct RouteArgs {
@@ -63,7 +67,7 @@ struct GemmArgs {
   const uint16_t *x;        // gate/up: activations [T][H]; down: h [rows][I]
   const int4 *mblocks;
   const Ctrl *ctrl;
-  int *queue;
+  int *queue;               // kXcds counters
   const int32_t *row_token;
   const float *row_gate;
   QMat w0, w1;              // routed stacked (gate, up) or (down, -)

@@ -140,17 +140,26 @@ __device__ void resolve64(Sel64 &S, int r, const uint16_t *x, const uint16_t *w1
   __syncthreads();
 }
 
-// Compact S.chosen (E experts) into ascending S.list and write ids/gates (softmax of
-// S.gl over the chosen experts).
+// Compact the chosen experts into ascending S.list and write ids/gates (softmax of S.gl
+// over them).  Experts are gathered unordered, then each of the k entries finds its
+// rank among the k.
 __device__ void emit_selection(Sel64 &S, int E, int k, int32_t *ids, float *gates, int32_t *dbg_ids,
                                float *dbg_gates, int tid, int nthr) {
-  if (tid < k) S.list[tid] = 0;
+  if (tid == 0) S.nin = 0;
+  if (tid < kMaxTopK) S.list[tid] = 0;
   __syncthreads();
-  for (int e = tid; e < E; e += nthr) {
-    if (!S.chosen[e]) continue;
+  for (int e = tid; e < E; e += nthr)
+    if (S.chosen[e]) {
+      const int at = atomicAdd(&S.nin, 1);
+      if (at < kMaxTopK) S.cand[at] = e;
+    }
+  __syncthreads();
+  const int n = min(S.nin, k);
+  if (tid < n) {
+    const int e = S.cand[tid];
     int pos = 0;
-    for (int j = 0; j < e; ++j) pos += S.chosen[j];
-    if (pos < k) S.list[pos] = e;
+    for (int j = 0; j < n; ++j) pos += S.cand[j] < e;
+    S.list[pos] = e;
   }
   __syncthreads();
   if (tid < k) {
@@ -169,10 +178,19 @@ __device__ void emit_selection(Sel64 &S, int E, int k, int32_t *ids, float *gate
 
 // ---------------------------------------------------------------------------- prefill
 
-__global__ __launch_bounds__(256) void k_route(RouteArgs a) {
+constexpr int kRouteThreads = 512;   // 8 waves: wave w owns experts 32w..32w+31
+constexpr int kKC = 256;             // k per staged chunk of x
+constexpr int kXRow = kKC * 2;       // bytes per staged row (32 slots of 16 B)
+
+// swizzled position of 16-byte slot `slot` of staged row `r`
+__device__ __forceinline__ int xoff(int r, int slot) { return r * kXRow + ((slot ^ (r & 15)) << 4); }
+
+__global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
   __shared__ float s_l[kRouteTokens][kMaxExperts];   // fp32 logit (+bias)
   __shared__ float s_r[kRouteTokens][kMaxExperts];   // its error radius
-  __shared__ int s_sel[kRouteTokens][kMaxTopK];      // chosen experts (any order)
+  __shared__ __attribute__((aligned(16))) uint8_t s_x[2][kRouteTokens * kXRow];
+  __shared__ int s_sel[kRouteTokens][kMaxTopK];      // chosen experts (rank order)
+  __shared__ float s_min_in[kRouteTokens], s_max_out[kRouteTokens];
   __shared__ int s_flag[kRouteTokens];
   __shared__ uint32_t s_mask[kMaxExperts];
   __shared__ Sel64 S;
@@ -182,77 +200,106 @@ __global__ __launch_bounds__(256) void k_route(RouteArgs a) {
   const int t0 = blockIdx.x * kRouteTokens;
   const int nt = min(kRouteTokens, a.T - t0);
 
-  {  // the combine accumulator of these tokens starts at zero
-    float4 *oa = (float4 *)(a.out_acc + (size_t)t0 * H);
-    const int n4 = nt * H / 4;
-    for (int i = tid; i < n4; i += 256) oa[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  for (int e = tid; e < kMaxExperts; e += 256) s_mask[e] = 0;
+  for (int e = tid; e < kMaxExperts; e += kRouteThreads) s_mask[e] = 0;
   if (tid < kRouteTokens) s_flag[tid] = 0;
 
   if (a.wr16) {
-    // 32 tokens x 32 experts per MFMA tile; wave wv takes expert tiles wv and wv+4.
     const int m = lane & 31, hf = lane >> 5;
-    const int tok = t0 + min(m, nt - 1);
-    const uint16_t *xr = a.x + (size_t)tok * H + 8 * hf;
     const int nct = (E + 31) / 32;
-    const int ct0 = wv, ct1 = wv + 4;
-    const bool has1 = ct1 < nct;
-    if (ct0 < nct) {
-      const uint16_t *w0 = a.wr16 + (size_t)min(ct0 * 32 + m, E - 1) * H + 8 * hf;
-      const uint16_t *w1 = a.wr16 + (size_t)min(ct1 * 32 + m, E - 1) * H + 8 * hf;
-      f32x16 acc0 = {}, acc1 = {}, abs0 = {}, abs1 = {};
-      const u32x4 msk = {0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu};
-#pragma unroll 4
-      for (int kk = 0; kk < H; kk += 16) {
-        const u32x4 av = *(const u32x4 *)(xr + kk);
-        const u32x4 b0 = *(const u32x4 *)(w0 + kk);
-        const u32x4 aa = av & msk;
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, b0), acc0, 0, 0, 0);
-        abs0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, aa), __builtin_bit_cast(bf16x8, (u32x4)(b0 & msk)), abs0, 0, 0, 0);
-        if (has1) {
-          const u32x4 b1 = *(const u32x4 *)(w1 + kk);
-          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, b1), acc1, 0, 0, 0);
-          abs1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, aa), __builtin_bit_cast(bf16x8, (u32x4)(b1 & msk)), abs1, 0, 0, 0);
-        }
+    const bool active = wv < nct;
+    const uint16_t *wrow = a.wr16 + (size_t)min(wv * 32 + m, E - 1) * H + 8 * hf;
+    // x chunk loader: wave-load j fills staged rows 2j, 2j+1; lane L -> row 2j+L/32,
+    // physical slot L%32 holding logical slot (L%32) ^ (row & 15)
+    const int xr0 = 2 * wv + (lane >> 5), xr1 = xr0 + 16;
+    const uint16_t *xg0 = a.x + (size_t)(t0 + min(xr0, nt - 1)) * H + 8 * ((lane & 31) ^ (xr0 & 15));
+    const uint16_t *xg1 = a.x + (size_t)(t0 + min(xr1, nt - 1)) * H + 8 * ((lane & 31) ^ (xr1 & 15));
+    auto load_x = [&](int c, int buf) {
+      __builtin_amdgcn_global_load_lds((const void *)(xg0 + c * kKC),
+                                       (__attribute__((address_space(3))) void *)(s_x[buf] + wv * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(xg1 + c * kKC),
+                                       (__attribute__((address_space(3))) void *)(s_x[buf] + (wv + 8) * 1024), 16, 0,
+                                       0);
+    };
+    u32x4 w0[kKC / 16], w1[kKC / 16];
+    auto load_w = [&](int c, u32x4(&dst)[kKC / 16]) {
+#pragma unroll
+      for (int s2 = 0; s2 < kKC / 16; ++s2) dst[s2] = *(const u32x4 *)(wrow + c * kKC + 16 * s2);
+    };
+    const int nch = H / kKC;
+    f32x16 acc = {}, aab = {};
+    const u32x4 msk = {0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu};
+    auto compute = [&](int buf, const u32x4(&wb)[kKC / 16]) {
+#pragma unroll
+      for (int s2 = 0; s2 < kKC / 16; ++s2) {
+        const u32x4 av = *(const u32x4 *)(s_x[buf] + xoff(m, 2 * s2 + hf));
+        const u32x4 bv = wb[s2];
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv),
+                                                      acc, 0, 0, 0);
+        aab = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, (u32x4)(av & msk)),
+                                                      __builtin_bit_cast(bf16x8, (u32x4)(bv & msk)), aab, 0, 0, 0);
       }
+    };
+    // two-stage pipeline: chunk c+1 (x into LDS, router rows into registers) is in
+    // flight while chunk c is multiplied
+    load_x(0, 0);
+    if (active) load_w(0, w0);
+    for (int c = 0; c < nch; c += 2) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (c + 1 < nch) {
+        load_x(c + 1, 1);
+        if (active) load_w(c + 1, w1);
+      }
+      if (active) compute(0, w0);
+      if (c + 1 >= nch) break;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (c + 2 < nch) {
+        load_x(c + 2, 0);
+        if (active) load_w(c + 2, w0);
+      }
+      if (active) compute(1, w1);
+    }
+    if (active) {
       // fp32 error of an MFMA chain of H/16 steps of 16 exact products: at most
       // (H/16 + 15) roundings of sum|p|; doubled for margin, plus the bias addition,
       // the sequential binary64 reference's own error and product underflow.
       const float c32 = 2.0f * (float)(H / 16 + 16) + 4.0f;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        if (t == 1 && !has1) break;
-        const int e = (t ? ct1 : ct0) * 32 + m;
-        if (e >= E) continue;
+      const int e = wv * 32 + m;
+      if (e < E) {
         const float bb = a.bias ? a.bias[e] : 0.0f;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int row = 8 * (j >> 2) + 4 * hf + (j & 3);
-          const float l = (t ? acc1[j] : acc0[j]) + bb;
-          const float ab = (t ? abs1[j] : abs0[j]);
+          const float l = acc[j] + bb;
           s_l[row][e] = l;
-          s_r[row][e] = c32 * kU32 * ab * 1.01f + 2.0f * kU32 * fabsf(l) + 1e-12f * ab + 1e-30f;
+          s_r[row][e] = c32 * kU32 * aab[j] * 1.01f + 2.0f * kU32 * fabsf(l) + 1e-12f * aab[j] + 1e-30f;
         }
       }
     }
   } else {
     // float32 router weights: no fp32 ranking; every expert is re-ranked in binary64.
-    for (int i = tid; i < kRouteTokens * kMaxExperts; i += 256) {
+    for (int i = tid; i < kRouteTokens * kMaxExperts; i += kRouteThreads) {
       (&s_l[0][0])[i] = 0.0f;
       (&s_r[0][0])[i] = INFINITY;
     }
   }
+  {  // the combine accumulator of these tokens starts at zero
+    float4 *oa = (float4 *)(a.out_acc + (size_t)t0 * H);
+    const int n4 = nt * H / 4;
+    for (int i = tid; i < n4; i += kRouteThreads) oa[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   __syncthreads();
 
-  // fp32 selection: wave wv takes tokens 8wv..8wv+7, eight lanes per token.
+  // fp32 selection: wave wv takes tokens 4wv..4wv+3, sixteen lanes per token.
   {
-    const int g = lane >> 3, q = lane & 7;
-    const int m = wv * 8 + g;
-    float lv[kMaxExperts / 8], rv[kMaxExperts / 8];
+    const int g = lane >> 4, q = lane & 15;
+    const int m = wv * 4 + g;
+    constexpr int NV = kMaxExperts / 16;
+    float lv[NV], rv[NV];
 #pragma unroll
-    for (int i = 0; i < kMaxExperts / 8; ++i) {
-      const int e = q + 8 * i;
+    for (int i = 0; i < NV; ++i) {
+      const int e = q + 16 * i;
       lv[i] = e < E ? s_l[m][e] : -INFINITY;
       rv[i] = e < E ? s_r[m][e] : 0.0f;
     }
@@ -261,16 +308,15 @@ __global__ __launch_bounds__(256) void k_route(RouteArgs a) {
       float bv = -INFINITY;
       int bi = 0x7fffffff;
 #pragma unroll
-      for (int i = 0; i < kMaxExperts / 8; ++i) {
-        const int e = q + 8 * i;
-        const bool ok = e < E && !((taken >> i) & 1u);
-        if (ok && (lv[i] > bv || (lv[i] == bv && e < bi))) {
+      for (int i = 0; i < NV; ++i) {
+        const int e = q + 16 * i;
+        if (e < E && !((taken >> i) & 1u) && (lv[i] > bv || (lv[i] == bv && e < bi))) {
           bv = lv[i];
           bi = e;
         }
       }
 #pragma unroll
-      for (int o = 1; o < 8; o <<= 1) {
+      for (int o = 1; o < 16; o <<= 1) {
         const float ov = __shfl_xor(bv, o);
         const int oi = __shfl_xor(bi, o);
         if (ov > bv || (ov == bv && oi < bi)) {
@@ -278,13 +324,13 @@ __global__ __launch_bounds__(256) void k_route(RouteArgs a) {
           bi = oi;
         }
       }
-      if (bi < E && (bi & 7) == q) taken |= 1u << (bi >> 3);
+      if (bi < E && (bi & 15) == q) taken |= 1u << (bi >> 4);
       if (q == 0) s_sel[m][r] = bi < E ? bi : 0;
     }
     float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < kMaxExperts / 8; ++i) {
-      const int e = q + 8 * i;
+    for (int i = 0; i < NV; ++i) {
+      const int e = q + 16 * i;
       if (e >= E) continue;
       if ((taken >> i) & 1u)
         mn = fminf(mn, lv[i] - rv[i]);
@@ -292,39 +338,29 @@ __global__ __launch_bounds__(256) void k_route(RouteArgs a) {
         mx = fmaxf(mx, lv[i] + rv[i]);
     }
 #pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
+    for (int o = 1; o < 16; o <<= 1) {
       mn = fminf(mn, __shfl_xor(mn, o));
       mx = fmaxf(mx, __shfl_xor(mx, o));
     }
-    const bool cert = mn > mx;  // false for NaN or infinite radius
+    const bool cert = mn > mx;  // false for NaN or an infinite radius
+    if (q == 0) {
+      s_min_in[m] = mn;
+      s_max_out[m] = mx;
+    }
     __syncthreads();
     if (m < nt && cert) {
       const float top = s_l[m][s_sel[m][0]];
-      float ex[2] = {0.f, 0.f};
-      int ee[2] = {0, 0};
-      float den = 0.f;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int r = q + 8 * u;
-        if (r < k) {
-          ee[u] = s_sel[m][r];
-          ex[u] = __expf(s_l[m][ee[u]] - top);
-          den += ex[u];
-        }
-      }
-#pragma unroll
-      for (int o = 1; o < 8; o <<= 1) den += __shfl_xor(den, o);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int r = q + 8 * u;
-        if (r >= k) continue;
+      if (q < k) {
+        const int e = s_sel[m][q];
+        float ex = __expf(s_l[m][e] - top), den = 0.f;
+        for (int j = 0; j < k; ++j) den += __expf(s_l[m][s_sel[m][j]] - top);
         int pos = 0;
-        for (int j = 0; j < k; ++j) pos += s_sel[m][j] < ee[u];
+        for (int j = 0; j < k; ++j) pos += s_sel[m][j] < e;
         const size_t o = (size_t)(t0 + m) * k + pos;
-        const float gt = ex[u] / den;
-        a.ids[o] = ee[u];
+        const float gt = ex / den;
+        a.ids[o] = e;
         a.gates[o] = gt;
-        if (a.dbg_ids) a.dbg_ids[o] = ee[u];
+        if (a.dbg_ids) a.dbg_ids[o] = e;
         if (a.dbg_gates) a.dbg_gates[o] = gt;
       }
     } else if (m < nt && q == 0) {
@@ -333,36 +369,33 @@ __global__ __launch_bounds__(256) void k_route(RouteArgs a) {
   }
   __syncthreads();
 
-  // binary64 re-ranking of the tokens the fp32 certificate did not settle
+  // re-ranking of the tokens the fp32 certificate did not settle.  With S~ the fp32
+  // top-k, lo = min over S~ of (l - r) and hi = max outside of (l + r): a chosen expert
+  // with l - r > hi is in for sure, an outside one with l + r < lo is out for sure; the
+  // rest get binary64 logits and are resolved in resolve64.
   int n_ref = 0;
   for (int m = 0; m < nt; ++m) {
     if (!s_flag[m]) continue;
     ++n_ref;
     const uint16_t *xrow = a.x + (size_t)(t0 + m) * H;
-    for (int e = tid; e < E; e += 256) {
-      S.v[e] = s_l[m][e];
-      S.rad[e] = s_r[m][e];
-      S.gl[e] = s_l[m][e];
-      S.chosen[e] = 0;
-    }
-    __syncthreads();
-    if (a.wr16) {
-      classify(S.v, S.rad, E, k, S.state, tid, 256);
-    } else {
-      // no fp32 logits: every expert is a binary64 candidate
-      for (int e = tid; e < E; e += 256) S.state[e] = 0;
-    }
+    const float lo = s_min_in[m], hi = s_max_out[m];
     if (tid == 0) S.n = 0;
     __syncthreads();
-    for (int e = tid; e < E; e += 256) {
-      if (S.state[e] == 1) S.chosen[e] = 1;
-      if (S.state[e] == 0) S.cand[atomicAdd(&S.n, 1)] = e;
+    for (int e = tid; e < E; e += kRouteThreads) {
+      S.gl[e] = s_l[m][e];
+      S.chosen[e] = 0;
+      bool in_sel = false;
+      for (int j = 0; j < k; ++j) in_sel |= s_sel[m][j] == e;
+      const float L = s_l[m][e] - s_r[m][e], U = s_l[m][e] + s_r[m][e];
+      const bool sure_in = a.wr16 && in_sel && L > hi;
+      const bool sure_out = a.wr16 && !in_sel && U < lo;
+      if (sure_in) S.chosen[e] = 1;
+      if (!sure_in && !sure_out) S.cand[atomicAdd(&S.n, 1)] = e;
     }
     __syncthreads();
     int nin1 = 0;
-    for (int e = 0; e < E; ++e) nin1 += S.chosen[e];
-    // binary64 logits of the undecided experts, one wave each
-    for (int c = wv; c < S.n; c += 4) {
+    for (int j = 0; j < k; ++j) nin1 += S.chosen[s_sel[m][j]];
+    for (int c = wv; c < S.n; c += kRouteThreads / kWave) {
       const int e = S.cand[c];
       double l, ab;
       wave_dot64(xrow, a.wr16 ? a.wr16 + (size_t)e * H : nullptr, a.wr32 ? a.wr32 + (size_t)e * H : nullptr, H,
@@ -375,54 +408,124 @@ __global__ __launch_bounds__(256) void k_route(RouteArgs a) {
       }
     }
     __syncthreads();
-    resolve64(S, k - nin1, xrow, a.wr16, a.wr32, a.bias, H, tid, 256);
+    resolve64(S, k - nin1, xrow, a.wr16, a.wr32, a.bias, H, tid, kRouteThreads);
     emit_selection(S, E, k, a.ids + (size_t)(t0 + m) * k, a.gates + (size_t)(t0 + m) * k,
                    a.dbg_ids ? a.dbg_ids + (size_t)(t0 + m) * k : nullptr,
-                   a.dbg_gates ? a.dbg_gates + (size_t)(t0 + m) * k : nullptr, tid, 256);
+                   a.dbg_gates ? a.dbg_gates + (size_t)(t0 + m) * k : nullptr, tid, kRouteThreads);
     if (tid < k) s_sel[m][tid] = S.list[tid];
     __syncthreads();
   }
 
   // per-expert bit masks of this workgroup's tokens (histogram / rank source)
-  for (int i = tid; i < nt * k; i += 256) {
+  for (int i = tid; i < nt * k; i += kRouteThreads) {
     const int m = i / k, r = i - m * k;
     atomicOr(&s_mask[s_sel[m][r]], 1u << m);
   }
   __syncthreads();
-  for (int e = tid; e < E; e += 256) a.tokmask[(size_t)blockIdx.x * E + e] = s_mask[e];
+  for (int e = tid; e < E; e += kRouteThreads) a.tokmask[(size_t)blockIdx.x * E + e] = s_mask[e];
   if (tid == 0 && n_ref) atomicAdd(&a.ctrl->n_refined, n_ref);
 }
 
 // ---------------------------------------------------------------------------- decode
 
+// One wave per expert computes the binary64 logit; the last workgroup to finish selects
+// the top k with one wave (k rounds of a wave arg-max), certifies the choice against the
+// binary64 error radii, and resolves uncertain experts with sequential sums.
 __global__ __launch_bounds__(64) void k_decode_route(DecodeArgs a) {
   __shared__ Sel64 S;
   __shared__ int s_last;
   const int lane = threadIdx.x;
-  const int e = blockIdx.x, H = a.H, E = a.E, k = a.k;
-  double l, ab;
-  wave_dot64(a.x, a.wr16 ? a.wr16 + (size_t)e * H : nullptr, a.wr32 ? a.wr32 + (size_t)e * H : nullptr, H, lane, l,
-             ab);
-  if (a.bias) l += (double)a.bias[e];
-  if (lane == 0) {
-    a.l64[e] = l;
-    a.a64[e] = radius64(l, ab, H);
-    const int t = __hip_atomic_fetch_add(&a.ctrl->decode_ticket, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (t == E - 1);
+  const int e0 = blockIdx.x, H = a.H, E = a.E, k = a.k;
+  {
+    double l, ab;
+    wave_dot64(a.x, a.wr16 ? a.wr16 + (size_t)e0 * H : nullptr, a.wr32 ? a.wr32 + (size_t)e0 * H : nullptr, H,
+               lane, l, ab);
+    if (a.bias) l += (double)a.bias[e0];
+    if (lane == 0) {
+      a.l64[e0] = l;
+      a.a64[e0] = radius64(l, ab, H);
+      const int t = __hip_atomic_fetch_add(&a.ctrl->decode_ticket, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = (t == E - 1);
+    }
   }
   __syncthreads();
   if (!s_last) return;
   __threadfence();
-  for (int i = lane; i < E; i += kWave) {
-    S.v[i] = __hip_atomic_load(&a.l64[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    S.rad[i] = __hip_atomic_load(&a.a64[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    S.gl[i] = S.v[i];
-    S.cand[i] = i;
-    S.chosen[i] = 0;
+  constexpr int NV = kMaxExperts / kWave;
+  double v[NV], rd[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = lane + kWave * i;
+    v[i] = e < E ? __hip_atomic_load(&a.l64[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : -INFINITY;
+    rd[i] = e < E ? __hip_atomic_load(&a.a64[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0;
+    if (e < E) {
+      S.gl[e] = v[i];
+      S.chosen[e] = 0;
+    }
   }
-  if (lane == 0) S.n = E;
+  uint32_t taken = 0;
+  for (int r = 0; r < k; ++r) {
+    double bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = lane + kWave * i;
+      if (e < E && !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < bi))) {
+        bv = v[i];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const double ov = __shfl_xor(bv, o);
+      const int oi = __shfl_xor(bi, o);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (bi < E && (bi % kWave) == lane) taken |= 1u << (bi / kWave);
+  }
+  double mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = lane + kWave * i;
+    if (e >= E) continue;
+    if ((taken >> i) & 1u)
+      mn = fmin(mn, v[i] - rd[i]);
+    else
+      mx = fmax(mx, v[i] + rd[i]);
+  }
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    mn = fmin(mn, __shfl_xor(mn, o));
+    mx = fmax(mx, __shfl_xor(mx, o));
+  }
+  if (lane == 0) S.n = 0;
   __syncthreads();
-  resolve64(S, k, a.x, a.wr16, a.wr32, a.bias, H, lane, kWave);
+  int nin1 = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = lane + kWave * i;
+    if (e >= E) continue;
+    const bool in_sel = (taken >> i) & 1u;
+    const bool sure_in = in_sel && v[i] - rd[i] > mx;
+    const bool sure_out = !in_sel && v[i] + rd[i] < mn;
+    if (sure_in) {
+      S.chosen[e] = 1;
+      ++nin1;
+    }
+    if (!sure_in && !sure_out) {
+      const int c = atomicAdd(&S.n, 1);
+      S.cand[c] = e;
+      S.v[c] = v[i];
+      S.rad[c] = rd[i];
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) nin1 += __shfl_xor(nin1, o);
+  __syncthreads();
+  if (S.n > 0) resolve64(S, k - nin1, a.x, a.wr16, a.wr32, a.bias, H, lane, kWave);
   emit_selection(S, E, k, a.ids, a.gates, a.dbg_ids, a.dbg_gates, lane, kWave);
   if (lane == 0) __hip_atomic_store(&a.ctrl->decode_ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -436,7 +539,7 @@ __global__ void k_ctrl_init(Ctrl *c) {
 
 hipError_t launch_route(const RouteArgs &a, hipStream_t s) {
   const int nb = (a.T + kRouteTokens - 1) / kRouteTokens;
-  hipLaunchKernelGGL(k_route, dim3(nb), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_route, dim3(nb), dim3(kRouteThreads), 0, s, a);
   return hipGetLastError();
 }
 
