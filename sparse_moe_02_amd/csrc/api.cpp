@@ -19,8 +19,8 @@ struct moe_plan_s {
   moe_weights w;
   int n_cu;
   // workspace layout (byte offsets)
-  size_t off_ctrl, off_tokmask, off_ids, off_gates, off_counts, off_offsets, off_base, off_row_token,
-      off_row_gate, off_mblocks, off_h, off_acc, off_l64, off_a64, off_dids, off_dgates, off_dh, total;
+  size_t off_ctrl, off_tokmask, off_ids, off_gates, off_counts, off_offsets, off_row_token,
+      off_row_gate, off_slot_row, off_mblocks, off_h, off_y, off_l64, off_a64, off_dids, off_dgates, off_dh, total;
 };
 
 namespace {
@@ -56,12 +56,12 @@ void layout(moe_plan_s &p) {
   p.off_gates = take(C * k * 4);
   p.off_counts = take((E + 1) * 4);
   p.off_offsets = take((E + 2) * 4);
-  p.off_base = take(nblk * E * 4);
   p.off_row_token = take(rows * 4);
   p.off_row_gate = take(rows * 4);
+  p.off_slot_row = take(rows * 4);
   p.off_mblocks = take(max_mblocks * 16);
   p.off_h = take(rows * I * 2);
-  p.off_acc = take(C * H * 4);
+  p.off_y = take(rows * H * 2);
   p.off_l64 = take(E * 8);
   p.off_a64 = take(E * 8);
   p.off_dids = take(k * 4);
@@ -198,7 +198,6 @@ moe_status moe_forward_prefill(moe_plan_t p, const void *x, int64_t T, void *out
     ra.ids = at<int32_t>(ws, p->off_ids);
     ra.gates = at<float>(ws, p->off_gates);
     ra.tokmask = at<uint32_t>(ws, p->off_tokmask);
-    ra.out_acc = at<float>(ws, p->off_acc);
     ra.ctrl = ctrl;
     if (dbg) {
       ra.dbg_ids = dbg->topk_ids ? dbg->topk_ids + (size_t)c0 * k : nullptr;
@@ -216,9 +215,9 @@ moe_status moe_forward_prefill(moe_plan_t p, const void *x, int64_t T, void *out
     ga.k = (int)k;
     ga.counts = at<int32_t>(ws, p->off_counts);
     ga.offsets = at<int32_t>(ws, p->off_offsets);
-    ga.base = at<int32_t>(ws, p->off_base);
     ga.row_token = at<int32_t>(ws, p->off_row_token);
     ga.row_gate = at<float>(ws, p->off_row_gate);
+    ga.slot_row = at<int32_t>(ws, p->off_slot_row);
     ga.mblocks = at<int4>(ws, p->off_mblocks);
     ga.ctrl = ctrl;
     if (dbg) {
@@ -255,12 +254,12 @@ moe_status moe_forward_prefill(moe_plan_t p, const void *x, int64_t T, void *out
     g2.s0 = qm(p->w.s_down);
     g2.w1 = QMat{};
     g2.s1 = QMat{};
-    g2.out_acc = ra.out_acc;
+    g2.y = at<uint16_t>(ws, p->off_y);
     if (rec(d, MOE_STAGE_DOWN, stream) != hipSuccess) return MOE_ERR_HIP;
     if (launch_gemm_down(g2, gemm_blocks, stream) != hipSuccess) return MOE_ERR_HIP;
 
     if (rec(d, MOE_STAGE_FINAL, stream) != hipSuccess) return MOE_ERR_HIP;
-    if (launch_finalize(ra.out_acc, oc, (int64_t)Tc * (int64_t)H, stream) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_finalize(g2.y, ga.slot_row, oc, Tc, (int)H, (int)k, stream) != hipSuccess) return MOE_ERR_HIP;
     if (rec(d, MOE_PREFILL_STAGES, stream) != hipSuccess) return MOE_ERR_HIP;
   }
   return MOE_OK;

@@ -95,6 +95,22 @@ __device__ __forceinline__ float wave_min(float v) {
   return v;
 }
 
+// Cross-workgroup hand-off without cache maintenance: agent-scope relaxed atomic
+// stores/loads are coherent across XCDs; draining vmcnt after the data stores orders
+// them before a following relaxed ticket update.
+template <class T>
+__device__ __forceinline__ void st_agent(T *p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class T>
+__device__ __forceinline__ T ld_agent(const T *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0xF70); }  // vmcnt(0)
+__device__ __forceinline__ int ticket(int *p) {
+  return __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Block until *flag reaches `target` (device-scope acquire), giving up after
 // `spins` polls; returns false on timeout.
 __device__ __forceinline__ bool wait_at_least(const int *flag, int target, int spins) {

@@ -7,12 +7,13 @@
 // fp32; the expanded weight array never exists in memory.  Section "Decode > Reduce
 // intermediate and state traffic" fuses the gated activation with the input
 // projections and the routing score and shared expert with the output projection; the
-// same fusions are applied here: SwiGLU in the gate/up epilogue, gate-weighted
-// scatter-add in the down epilogue.
+// same fusions are applied here: SwiGLU in the gate/up epilogue, the routing weight in
+// the down epilogue (the k+1 rows of a token are summed by a short gather kernel).
 //
-// MI355X mapping.  A work item is (M-block of one expert, N-block).  Eight waves split
-// the N-block; each wave covers all rows of the M-block (1..4 tiles of 32), so a weight
-// element is dequantised once per work item.  For a 128-wide K super-step, lane l of a
+// MI355X mapping.  A work item is (M-block of one expert, N-block).  Eight waves (two
+// per SIMD) split the N-block; each wave covers all rows of the M-block (1..4 tiles of
+// 32), so a weight element is dequantised once per work item, and each wave interleaves
+// its dequant VALU work between its own MFMAs (k-slice software pipeline).  For a 128-wide K super-step, lane l of a
 // wave owns weight row n = l%32 and the 64 consecutive k of half h = l/32: exactly eight
 // packed words and one (scale, bias) pair.  Word j feeds MFMA j of the super-step, whose
 // B operand wants 8 consecutive k per lane; the activation operand uses the same k
@@ -35,9 +36,9 @@ namespace {
 
 constexpr int kRowBytes = 256;                 // 128 bf16 per staged activation row
 constexpr int kAStage = kBM * kRowBytes;       // 32 KiB: up to 128 activation rows
-constexpr int kBSet = 256 * 64;                // 16 KiB: 256 weight rows x 64 B (128 codes)
-constexpr int kSArr = 256 * 4;                 // 1 KiB: 256 rows x (2 fp16 of one array)
-constexpr int kStageBytes = kAStage + 2 * kBSet + 4 * kSArr;  // 68 KiB
+constexpr int kBStage = 512 * 64;              // 32 KiB: 512 weight rows x 64 B (128 codes)
+constexpr int kSStage = 2 * 512 * 4;           // 4 KiB: scales then biases, 2 fp16 per row
+constexpr int kStageBytes = kAStage + kBStage + kSStage;  // 68 KiB
 
 template <int N>
 __device__ __forceinline__ void vm_wait() {
@@ -65,7 +66,7 @@ __device__ __forceinline__ QMat expert_mat(const QMat &routed, const QMat &share
 
 // activation tile: row r at r*256, 16-byte chunk c at slot c ^ (r & 15)
 __device__ __forceinline__ int a_off(int row, int chunk) { return row * kRowBytes + ((chunk ^ (row & 15)) << 4); }
-// weight set: weight slot w (= 32*wave + lane%32) at w*64, 16-byte part p at p ^ ((w >> 2) & 3)
+// weights: slot w (one weight row) at w*64, 16-byte part p at p ^ ((w >> 2) & 3)
 __device__ __forceinline__ int b_off(int slot, int part) { return slot * 64 + ((part ^ ((slot >> 2) & 3)) << 4); }
 
 __device__ __forceinline__ f32x16 mfma(const u32x4 &a, const uint32_t (&b)[4], const f32x16 &c) {
@@ -74,31 +75,32 @@ __device__ __forceinline__ f32x16 mfma(const u32x4 &a, const uint32_t (&b)[4], c
                                                  0, 0);
 }
 
-// One work item.  GU: gate/up + SwiGLU (K = H; weight set 0 = gate rows, set 1 = up rows,
-// both row n of the lane).  Otherwise down + combine (K = I; sets 0/1 = rows n, n + 32).
+// One work item, eight waves (two per SIMD).  Each wave owns two 32-column MFMA tiles of
+// weight rows: GU (gate/up + SwiGLU, K = H): tile 0 = gate row n, tile 1 = up row n with
+// n = nb*256 + 32*wave + lane%32; down (K = I): tile i = row nb*512 + 64*wave + 32 i +
+// lane%32.  Weight slot (0..511) = 64*wave + 32*tile + lane%32.
 template <int MT, bool GU>
-__device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, int *s_tok, float *s_gate, int e,
-                          int row0, int rows, int nb) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, hf = lane >> 5;
+__device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, float *s_gate, int e, int row0,
+                          int rows, int nb) {
+  const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5;
+  const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.H, I = a.I;
   const int K = GU ? H : I;
   const int N = GU ? I : H;  // rows of each weight matrix
   const int nss = K / 128;
   const QMat M0 = GU ? expert_mat(a.w0, a.s0, e, a.E, I, H) : expert_mat(a.w0, a.s0, e, a.E, H, I);
   const QMat M1 = GU ? expert_mat(a.w1, a.s1, e, a.E, I, H) : M0;
-  // weight row of (set, slot): slot = 32*wave + j, j < 32
-  auto wrow = [&](int set, int slot) {
-    const int w = slot >> 5, j = slot & 31;
-    const int n = GU ? nb * kGateUpCols + slot : nb * kDownCols + 64 * w + 32 * set + j;
+  auto slot_mat = [&](int slot) -> const QMat & { return (GU && ((slot >> 5) & 1)) ? M1 : M0; };
+  auto slot_row = [&](int slot) {
+    const int w = slot >> 6, t = (slot >> 5) & 1, j = slot & 31;
+    const int n = GU ? nb * kGateUpCols + 32 * w + j : nb * kDownCols + 64 * w + 32 * t + j;
     return min(n, N - 1);  // idle waves of a narrow layer load a valid row
   };
-  const int n_lane = GU ? nb * kGateUpCols + 32 * wv + (lane & 31) : nb * kDownCols + 64 * wv + (lane & 31);
-  const bool active = (GU ? nb * kGateUpCols + 32 * wv : nb * kDownCols + 64 * wv) < N;
+  const int wcol0 = GU ? nb * kGateUpCols + 32 * wu : nb * kDownCols + 64 * wu;
+  const bool active = wcol0 < N;
 
-  // --- this wave's share of each stage's loads: wave-uniform bases (scalar registers)
-  // plus 32-bit per-lane byte offsets
-  const int wu = __builtin_amdgcn_readfirstlane(wv);
-  // A: MT wave-loads of 1 KiB (4 rows), index i -> rows 4(wu + 8i) .. +3
+  // --- this wave's share of each stage's loads: wave-uniform bases + 32-bit offsets
+  // A: MT*8 wave-loads of 1 KiB (4 rows each); wave takes v = wu + 8i, i < MT
   const char *abase = (const char *)a.x;
   uint32_t aoff[MT];
 #pragma unroll
@@ -108,27 +110,27 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, i
     const uint32_t row_elem = GU ? (uint32_t)a.row_token[rr] * (uint32_t)H : (uint32_t)rr * (uint32_t)I;
     aoff[i] = 2u * (row_elem + 8u * (uint32_t)((lane & 15) ^ (r & 15)));
   }
-  // B: 4 wave-loads of 1 KiB (16 weight slots), v = wu + 8i: set v/16, slots 16(v%16) ..
+  // B: 32 wave-loads of 1 KiB (16 slots x 64 B); wave takes v = wu + 8i, i < 4
   const char *bbase[4];
   uint32_t boff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int v = wu + 8 * i, set = v >> 4;
-    const int slot = 16 * (v & 15) + (lane >> 2);
-    bbase[i] = (const char *)(set ? M1.q : M0.q);
-    boff[i] = 4u * ((uint32_t)wrow(set, slot) * (uint32_t)(K / 8) + 4u * (uint32_t)((lane & 3) ^ ((slot >> 2) & 3)));
+    const int v = wu + 8 * i;
+    const int slot = 16 * v + (lane >> 2);
+    bbase[i] = (const char *)slot_mat(16 * v).q;
+    boff[i] = 4u * ((uint32_t)slot_row(slot) * (uint32_t)(K / 8) + 4u * (uint32_t)((lane & 3) ^ ((slot >> 2) & 3)));
   }
-  // S: 2 wave-loads of 256 B (64 slots x 2 fp16), v = wu + 8i: array v/4 in
-  // (scale set 0, bias set 0, scale set 1, bias set 1), slots 64(v%4) + lane
+  // S: 16 wave-loads of 256 B (64 slots x 2 fp16): scales (v < 8) then biases; wave
+  // takes v = wu + 8i, i < 2
   const char *sbase[2];
   uint32_t soff[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int v = wu + 8 * i, arr = v >> 2, set = arr >> 1;
-    const int slot = 64 * (v & 3) + lane;
-    const QMat &M = set ? M1 : M0;
-    sbase[i] = (const char *)((arr & 1) ? M.b : M.s);
-    soff[i] = 2u * (uint32_t)wrow(set, slot) * (uint32_t)(K / 64);
+    const int v = wu + 8 * i;
+    const int slot = 64 * (v & 7) + lane;
+    const QMat &M = slot_mat(64 * (v & 7) + 32 * (lane >> 5));
+    sbase[i] = (const char *)((v >> 3) ? M.b : M.s);
+    soff[i] = 2u * (uint32_t)slot_row(slot) * (uint32_t)(K / 64);
   }
   auto issue = [&](int ss, uint8_t *st) {
 #pragma unroll
@@ -136,46 +138,79 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, i
 #pragma unroll
     for (int i = 0; i < 4; ++i) g2l16(bbase[i] + boff[i] + ss * 64, st + kAStage + (wu + 8 * i) * 1024);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) g2l4(sbase[i] + soff[i] + ss * 4, st + kAStage + 2 * kBSet + (wu + 8 * i) * 256);
+    for (int i = 0; i < 2; ++i) g2l4(sbase[i] + soff[i] + ss * 4, st + kAStage + kBStage + (wu + 8 * i) * 256);
   };
 
-  if (!GU && tid < MT * 32) {  // token and gate of every row, read back by the epilogue
-    const int rr = row0 + min(tid, rows - 1);
-    s_tok[tid] = a.row_token[rr];
-    s_gate[tid] = a.row_gate[rr];
-  }
-  f32x16 acc0[MT], acc1[MT];
+  if (!GU && tid < MT * 32) s_gate[tid] = a.row_gate[row0 + min(tid, rows - 1)];  // read by the epilogue
+  f32x16 acc[MT][2];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    acc0[t] = (f32x16){};
-    acc1[t] = (f32x16){};
-  }
-  const int myslot = 32 * wv + (lane & 31);
-  // multiply super-step ss from stage `st`
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) acc[t][i] = (f32x16){};
+
+  // multiply one super-step (128 k) from stage `st`
+  const int l15 = lane & 15;
+  const int a_lane = (lane & 31) * kRowBytes;       // + t*32*256 (immediate) per row tile
+  const int a_c0 = (hf * 8) ^ l15;                   // swizzled chunk of slice j: a_c0 ^ j
+  int b_lane[2];                                     // this lane's weight slot per tile
+#pragma unroll
+  for (int i = 0; i < 2; ++i) b_lane[i] = (64 * wu + 32 * i + (lane & 31));
   auto compute = [&](const uint8_t *st) {
-    const uint8_t *b0 = st + kAStage, *b1 = b0 + kBSet;
-    const uint16_t *sp = (const uint16_t *)(b1 + kBSet);
-    const float sa = fp16_to_f32(sp[myslot * 2 + hf]);
-    const float ba = fp16_to_f32(sp[kSArr / 2 + myslot * 2 + hf]);
-    const float sb = fp16_to_f32(sp[kSArr + myslot * 2 + hf]);
-    const float bb = fp16_to_f32(sp[3 * kSArr / 2 + myslot * 2 + hf]);
-    const uint4 w00 = *(const uint4 *)(b0 + b_off(myslot, 2 * hf));
-    const uint4 w01 = *(const uint4 *)(b0 + b_off(myslot, 2 * hf + 1));
-    const uint4 w10 = *(const uint4 *)(b1 + b_off(myslot, 2 * hf));
-    const uint4 w11 = *(const uint4 *)(b1 + b_off(myslot, 2 * hf + 1));
-    const uint32_t wa[8] = {w00.x, w00.y, w00.z, w00.w, w01.x, w01.y, w01.z, w01.w};
-    const uint32_t wb[8] = {w10.x, w10.y, w10.z, w10.w, w11.x, w11.y, w11.z, w11.w};
+    const uint8_t *bb = st + kAStage;
+    const uint16_t *sp = (const uint16_t *)(st + kAStage + kBStage);
+    float sc[2], bi[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      sc[i] = fp16_to_f32(sp[2 * b_lane[i] + hf]);
+      bi[i] = fp16_to_f32(sp[kSStage / 4 + 2 * b_lane[i] + hf]);
+    }
+    // word j of the lane's 8 (16-byte part 2*hf + j/4, dword j%4) of its slot in tile i
+    auto word = [&](int i, int j) {
+      return *(const uint32_t *)(bb + b_off(b_lane[i], 2 * hf + (j >> 2)) + 4 * (j & 3));
+    };
+    auto afrag = [&](int t, int j) {
+      return *(const u32x4 *)(st + t * 32 * kRowBytes + a_lane + ((a_c0 ^ j) << 4));
+    };
+    // software pipeline over the eight k-slices: activation fragments, packed words and
+    // dequantised weights of slice j+1 are prepared while the MFMAs of slice j run
+    u32x4 av[2][MT];
+    uint32_t d[2][2][4];
+    uint32_t wn[2];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) av[0][t] = afrag(t, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dequant8_bf16(word(i, 0), sc[i], bi[i], d[0][i]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) wn[i] = word(i, 1);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      uint32_t d0[4], d1[4];
-      dequant8_bf16(wa[j], sa, ba, d0);
-      dequant8_bf16(wb[j], sb, bb, d1);
+      const int c = j & 1, nx = c ^ 1;
+      if (j < 7) {
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const int row = t * 32 + (lane & 31);
-        const u32x4 av = *(const u32x4 *)(st + a_off(row, hf * 8 + j));
-        acc0[t] = mfma(av, d0, acc0[t]);
-        acc1[t] = mfma(av, d1, acc1[t]);
+        for (int t = 0; t < MT; ++t) av[nx][t] = afrag(t, j + 1);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) dequant8_bf16(wn[i], sc[i], bi[i], d[nx][i]);
+        if (j < 6) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) wn[i] = word(i, j + 2);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) acc[t][i] = mfma(av[c][t], d[c][i], acc[t][i]);
+      if (j < 7) {
+        // the next slices' LDS reads first, then each MFMA followed by its share of the
+        // dequant VALU work (2 words, 46 instructions)
+        if (j < 6)
+          __builtin_amdgcn_sched_group_barrier(0x100, MT + 2, 0);
+        else
+          __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * MT; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, (46 + 2 * MT - 1) / (2 * MT), 0);
+        }
       }
     }
   };
@@ -193,39 +228,42 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, i
     if (ss + 2 < nss) issue(ss + 2, stage0);
     if (active) compute(stage1);
   }
-  // every wave is past its last LDS read before the next item refills the ring
+  // every wave is past its last LDS read before the epilogue reuses stage0
   __builtin_amdgcn_s_barrier();
-  if (!active) return;
-  const int n0 = n_lane, n1 = n_lane + 32;
-
-  if (GU) {
-    // SwiGLU epilogue: h = silu(gate) * up, bf16
+  if (active) {
+    // Epilogue, one 32-row tile at a time: the wave converts its tile to bf16 in its own
+    // LDS area (GU: 32 x 32 h values; down: 32 x 64 gate-weighted outputs), then
+    // writes whole rows with 16-byte stores.
+    constexpr int COLS = GU ? 32 : 64;
+    uint16_t *tile = (uint16_t *)(stage0 + wu * (32 * 64 * 2));
+    const int lc = lane & 31;
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int r = t * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
-        if (r < rows) {
-          const float gv = acc0[t][v], uv = acc1[t][v];
-          a.h[(size_t)(row0 + r) * I + n0] = f32_to_bf16(gv * sigmoid_fast(gv) * uv);
+        const int r = 8 * (v >> 2) + 4 * hf + (v & 3);
+        if (GU) {
+          const float gv = acc[t][0][v], uv = acc[t][1][v];
+          tile[r * COLS + lc] = f32_to_bf16(gv * sigmoid_fast(gv) * uv);
+        } else {
+          const float g = s_gate[t * 32 + r];
+#pragma unroll
+          for (int i = 0; i < 2; ++i) tile[r * COLS + 32 * i + lc] = f32_to_bf16(g * acc[t][i][v]);
         }
       }
-    }
-  } else {
-    // combine: out_acc[token] += gate * y (the shared expert's rows carry gate 1)
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's tile writes are done
+      constexpr int LPR = COLS / 8;        // lanes per row (16 B each)
+      constexpr int RPI = 64 / LPR;        // rows per store instruction
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = t * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
-        if (r < rows) {
-          const int tok = s_tok[r];
-          const float g = s_gate[r];
-          float *o = a.out_acc + (size_t)tok * H;
-          unsafeAtomicAdd(o + n0, g * acc0[t][v]);
-          unsafeAtomicAdd(o + n1, g * acc1[t][v]);
+      for (int rr = 0; rr < 32; rr += RPI) {
+        const int r = rr + lane / LPR;
+        if (t * 32 + r < rows) {
+          const uint4 v = *(const uint4 *)(tile + r * COLS + 8 * (lane % LPR));
+          uint16_t *dst = GU ? a.h + (size_t)(row0 + t * 32 + r) * I : a.y + (size_t)(row0 + t * 32 + r) * H;
+          *(uint4 *)(dst + wcol0 + 8 * (lane % LPR)) = v;
         }
       }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next tile overwrites
     }
   }
 }
@@ -237,7 +275,6 @@ template <bool GU>
 __device__ void gemm_persistent(const GemmArgs &a) {
   __shared__ __attribute__((aligned(16))) uint8_t stage0[kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t stage1[kStageBytes];
-  __shared__ int s_tok[kBM];
   __shared__ float s_gate[kBM];
   __shared__ int s_item;
   const int NB = GU ? (a.I + kGateUpCols - 1) / kGateUpCols : (a.H + kDownCols - 1) / kDownCols;
@@ -249,16 +286,16 @@ __device__ void gemm_persistent(const GemmArgs &a) {
     for (;;) {
       if (threadIdx.x == 0) s_item = atomicAdd(&a.queue[x], 1);
       __syncthreads();
-      const int item = s_item;
+      const int item = __builtin_amdgcn_readfirstlane(s_item);  // uniform: keeps item state scalar
       __syncthreads();
       if (item >= n_items) break;
       const int4 mb = a.mblocks[x + kXcds * (item / NB)];
       const int nb = item % NB;
       switch (mb.w) {
-        case 1: gemm_item<1, GU>(a, stage0, stage1, s_tok, s_gate, mb.x, mb.y, mb.z, nb); break;
-        case 2: gemm_item<2, GU>(a, stage0, stage1, s_tok, s_gate, mb.x, mb.y, mb.z, nb); break;
-        case 3: gemm_item<3, GU>(a, stage0, stage1, s_tok, s_gate, mb.x, mb.y, mb.z, nb); break;
-        default: gemm_item<4, GU>(a, stage0, stage1, s_tok, s_gate, mb.x, mb.y, mb.z, nb); break;
+        case 1: gemm_item<1, GU>(a, stage0, stage1, s_gate, mb.x, mb.y, mb.z, nb); break;
+        case 2: gemm_item<2, GU>(a, stage0, stage1, s_gate, mb.x, mb.y, mb.z, nb); break;
+        case 3: gemm_item<3, GU>(a, stage0, stage1, s_gate, mb.x, mb.y, mb.z, nb); break;
+        default: gemm_item<4, GU>(a, stage0, stage1, s_gate, mb.x, mb.y, mb.z, nb); break;
       }
     }
   }
@@ -267,17 +304,29 @@ __device__ void gemm_persistent(const GemmArgs &a) {
 __global__ __launch_bounds__(kGemmThreads) void k_gemm_gateup(GemmArgs a) { gemm_persistent<true>(a); }
 __global__ __launch_bounds__(kGemmThreads) void k_gemm_down(GemmArgs a) { gemm_persistent<false>(a); }
 
-// fp32 accumulator -> bf16 output, eight elements per thread
-__global__ __launch_bounds__(256) void k_finalize(const float *acc, uint16_t *out, int64_t n8) {
-  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
-    const float4 a0 = ((const float4 *)acc)[2 * i];
-    const float4 a1 = ((const float4 *)acc)[2 * i + 1];
+// Combine: out[t] = sum over the k+1 grouped rows of token t (already gate-weighted),
+// fp32 sum, bf16 result.  One workgroup per token, eight columns per thread.
+__global__ __launch_bounds__(256) void k_finalize(const uint16_t *y, const int32_t *slot_row, uint16_t *out, int H,
+                                                  int k) {
+  const int t = blockIdx.x;
+  const int32_t *sr = slot_row + (size_t)t * (k + 1);
+  for (int c = threadIdx.x; c < H / 8; c += 256) {
+    float acc[8] = {};
+    for (int j = 0; j <= k; ++j) {
+      const uint4 v = *(const uint4 *)(y + (size_t)sr[j] * H + 8 * c);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += bf16_lo(w[i]);
+        acc[2 * i + 1] += bf16_hi(w[i]);
+      }
+    }
     uint4 o;
-    o.x = pack_bf16x2(a0.x, a0.y);
-    o.y = pack_bf16x2(a0.z, a0.w);
-    o.z = pack_bf16x2(a1.x, a1.y);
-    o.w = pack_bf16x2(a1.z, a1.w);
-    ((uint4 *)out)[i] = o;
+    o.x = pack_bf16x2(acc[0], acc[1]);
+    o.y = pack_bf16x2(acc[2], acc[3]);
+    o.z = pack_bf16x2(acc[4], acc[5]);
+    o.w = pack_bf16x2(acc[6], acc[7]);
+    *(uint4 *)(out + (size_t)t * H + 8 * c) = o;
   }
 }
 
@@ -293,12 +342,9 @@ hipError_t launch_gemm_down(const GemmArgs &a, int n_blocks, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_finalize(const float *acc, uint16_t *out, int64_t n, hipStream_t s) {
-  const int64_t n8 = n / 8;
-  int64_t nb = (n8 + 255) / 256;
-  if (nb > 4096) nb = 4096;
-  if (nb < 1) nb = 1;
-  hipLaunchKernelGGL(k_finalize, dim3((unsigned)nb), dim3(256), 0, s, acc, out, n8);
+hipError_t launch_finalize(const uint16_t *y, const int32_t *slot_row, uint16_t *out, int T, int H, int k,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(k_finalize, dim3(T), dim3(256), 0, s, y, slot_row, out, H, k);
   return hipGetLastError();
 }
 

@@ -132,6 +132,7 @@ __global__ __launch_bounds__(kThreads) void k_group(GroupArgs a) {
     }
     a.row_token[pos] = t;
     a.row_gate[pos] = g;
+    a.slot_row[(size_t)t * (k + 1) + j] = pos;
     if (a.dbg_row_token) a.dbg_row_token[pos] = t;
   }
   if (blockIdx.x != 0) return;

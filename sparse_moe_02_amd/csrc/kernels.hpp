@@ -10,7 +10,7 @@ constexpr int kRouteTokens = 32;   // tokens per router workgroup
 constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 16;
 constexpr int kBM = 128;           // max rows of one grouped-GEMM M-block
-constexpr int kGemmThreads = 512;  // grouped GEMM workgroup: 8 waves
+constexpr int kGemmThreads = 512;  // grouped GEMM workgroup: 8 waves, two per SIMD
 constexpr int kGateUpCols = 256;   // h columns per gate/up work item (8 waves x 32)
 constexpr int kDownCols = 512;     // output columns per down work item (8 waves x 64)
 
@@ -42,7 +42,6 @@ struct RouteArgs {
   int32_t *ids;           // [T][k] ascending
   float *gates;           // [T][k]
   uint32_t *tokmask;      // [ceil(T/32)][E] bit m: token 32*blk+m chose e
-  float *out_acc;         // [T][H]: zeroed here
   Ctrl *ctrl;
   int32_t *dbg_ids;       // optional [T][k] (chunk-offset)
   float *dbg_gates;
@@ -55,9 +54,9 @@ struct GroupArgs {
   int T, E, k;
   int32_t *counts;        // [E+1]
   int32_t *offsets;       // [E+2]
-  int32_t *base;          // [nblk][E] scratch
   int32_t *row_token;     // [T*(k+1)]
   float *row_gate;        // [T*(k+1)]
+  int32_t *slot_row;      // [T][k+1] grouped row of (token, slot); slot k = shared
   int4 *mblocks;          // {expert, row0, rows, mt}
   Ctrl *ctrl;
   int32_t *dbg_counts, *dbg_offsets, *dbg_row_token, *dbg_n_refined;
@@ -74,7 +73,7 @@ struct GemmArgs {
   QMat s0, s1;              // shared expert
   int E, H, I;
   uint16_t *h;              // gate/up output [rows][I]
-  float *out_acc;           // down output [T][H]
+  uint16_t *y;              // down output, gate-weighted, per grouped row [rows][H]
 };
 
 struct DecodeArgs {
@@ -100,7 +99,8 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t s);
 hipError_t launch_group(const GroupArgs &a, hipStream_t s);
 hipError_t launch_gemm_gateup(const GemmArgs &a, int n_blocks, hipStream_t s);
 hipError_t launch_gemm_down(const GemmArgs &a, int n_blocks, hipStream_t s);
-hipError_t launch_finalize(const float *acc, uint16_t *out, int64_t n, hipStream_t s);
+hipError_t launch_finalize(const uint16_t *y, const int32_t *slot_row, uint16_t *out, int T, int H, int k,
+                           hipStream_t s);
 hipError_t launch_decode_route(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_gateup(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_down(const DecodeArgs &a, hipStream_t s);

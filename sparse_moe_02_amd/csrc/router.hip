@@ -103,6 +103,7 @@ struct Sel64 {
   int state[kMaxExperts];
   int chosen[kMaxExperts];   // per expert: 1 if selected
   int list[kMaxTopK];
+  float ex[kMaxTopK];
   int n, nin;
 };
 
@@ -162,12 +163,17 @@ __device__ void emit_selection(Sel64 &S, int E, int k, int32_t *ids, float *gate
     S.list[pos] = e;
   }
   __syncthreads();
-  if (tid < k) {
-    double mx = -INFINITY, den = 0.0;
+  if (tid < k) {  // each chosen expert's exponential once
+    double mx = -INFINITY;
     for (int j = 0; j < k; ++j) mx = fmax(mx, S.gl[S.list[j]]);
-    for (int j = 0; j < k; ++j) den += exp(S.gl[S.list[j]] - mx);
+    S.ex[tid] = __expf((float)(S.gl[S.list[tid]] - mx));
+  }
+  __syncthreads();
+  if (tid < k) {
+    float den = 0.f;
+    for (int j = 0; j < k; ++j) den += S.ex[j];
     const int e = S.list[tid];
-    const float g = (float)(exp(S.gl[e] - mx) / den);
+    const float g = S.ex[tid] / den;
     ids[tid] = e;
     gates[tid] = g;
     if (dbg_ids) dbg_ids[tid] = e;
@@ -283,11 +289,6 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
       (&s_l[0][0])[i] = 0.0f;
       (&s_r[0][0])[i] = INFINITY;
     }
-  }
-  {  // the combine accumulator of these tokens starts at zero
-    float4 *oa = (float4 *)(a.out_acc + (size_t)t0 * H);
-    const int n4 = nt * H / 4;
-    for (int i = tid; i < n4; i += kRouteThreads) oa[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   __syncthreads();
 
@@ -442,22 +443,21 @@ __global__ __launch_bounds__(64) void k_decode_route(DecodeArgs a) {
                lane, l, ab);
     if (a.bias) l += (double)a.bias[e0];
     if (lane == 0) {
-      a.l64[e0] = l;
-      a.a64[e0] = radius64(l, ab, H);
-      const int t = __hip_atomic_fetch_add(&a.ctrl->decode_ticket, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = (t == E - 1);
+      st_agent(&a.l64[e0], l);
+      st_agent(&a.a64[e0], radius64(l, ab, H));
+      vm_drain();
+      s_last = ticket(&a.ctrl->decode_ticket) == E - 1;
     }
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
   constexpr int NV = kMaxExperts / kWave;
   double v[NV], rd[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int e = lane + kWave * i;
-    v[i] = e < E ? __hip_atomic_load(&a.l64[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : -INFINITY;
-    rd[i] = e < E ? __hip_atomic_load(&a.a64[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0;
+    v[i] = e < E ? ld_agent(&a.l64[e]) : -INFINITY;
+    rd[i] = e < E ? ld_agent(&a.a64[e]) : 0.0;
     if (e < E) {
       S.gl[e] = v[i];
       S.chosen[e] = 0;
@@ -527,7 +527,7 @@ __global__ __launch_bounds__(64) void k_decode_route(DecodeArgs a) {
   __syncthreads();
   if (S.n > 0) resolve64(S, k - nin1, a.x, a.wr16, a.wr32, a.bias, H, lane, kWave);
   emit_selection(S, E, k, a.ids, a.gates, a.dbg_ids, a.dbg_gates, lane, kWave);
-  if (lane == 0) __hip_atomic_store(&a.ctrl->decode_ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0) st_agent(&a.ctrl->decode_ticket, 0);
 }
 
 __global__ void k_ctrl_init(Ctrl *c) {
