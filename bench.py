@@ -29,6 +29,37 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "prefill4k_decode40_hbm_traffic.md")
+
+
+def profiled_traffic(kernel):
+    """HBM bytes per dispatch of `kernel` from the committed FETCH_SIZE/WRITE_SIZE profile
+    (scaled by the copy-kernel calibration it records), or None when the kernel sources have
+    changed since the counters were taken."""
+    import hashlib
+
+    try:
+        lines = open(TRAFFIC_PROFILE).read().split("\n")
+    except OSError:
+        return None
+    srcs, want, val = [], None, None
+    for line in lines:
+        f = line.split()
+        if len(f) >= 2 and f[0] == "sources:":
+            srcs = f[1:]
+        elif len(f) == 2 and f[0] == "sources_sha256:":
+            want = f[1]
+        elif len(f) == 3 and f[0] == "traffic_bytes" and f[1] == kernel:
+            val = float(f[2])
+    if not srcs or want is None or val is None:
+        return None
+    h = hashlib.sha256()
+    for s in srcs:
+        with open(os.path.join(ROOT, s), "rb") as fh:
+            h.update(fh.read())
+    return val if h.hexdigest() == want else None
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -41,6 +72,9 @@ def main():
     ap.add_argument("--decode-layers", type=int, default=40)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB, 5 times "
+                         "(calibrates the HBM byte counters of a profiler run)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -59,6 +93,15 @@ def main():
         __graft_entry__.build()
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 5}), flush=True)
+        return
     sh2, sh1 = synth.shape_of(2), synth.shape_of(1)
     T, H, I, E, k = sh2.T, sh2.H, sh2.I, sh2.E, sh2.k
 
@@ -138,7 +181,8 @@ def main():
         "roofline": {"kernel": "gemm_gateup (grouped GEMM gate/up + SwiGLU)", "bound": "mfma",
                      "achieved": round(gateup_flop / (gu_ms * 1e-3) / 1e12, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gateup_flop / (gu_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "algorithmic_flop_per_launch": gateup_flop},
+                     "traffic": profiled_traffic("k_gemm_gateup"), "traffic_unit": "bytes per launch",
+                     "algorithmic_flop_per_launch": gateup_flop},
         "step_ms_events": round(float(np.mean(step_ms)), 4),
     }
     if n_dec:
