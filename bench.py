@@ -193,17 +193,17 @@ def main():
         us_layer = float(np.median(sweep_ms)) * 1e3 / n_dec
         qmat_gu = I * H // 2 + 2 * 2 * I * (H // 64)
         qmat_dn = H * I // 2 + 2 * 2 * H * (I // 64)
-        gu_bytes = (k + 1) * 2 * qmat_gu + 2 * H + (k + 1) * I * 4
         layer_bytes = (k + 1) * (2 * qmat_gu + qmat_dn) + E * H * 2 + 2 * H * 2
         result["decode_us_per_layer"] = round(us_layer, 3)
         result["decode_stage_us"] = {n: round(v * 1e3, 3) for n, v in dec_stage.items()}
         result["decode_layer_us_events"] = round(dec_layer_ms * 1e3, 3)
         result["decode_hbm_frac"] = round(layer_bytes / (us_layer * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
-        gu_gbs = gu_bytes / (dec_stage["gateup"] * 1e-3) / 1e9
-        result["decode_roofline"] = {"kernel": "decode_gateup (GEMV gate/up + SwiGLU, 9 experts)", "bound": "hbm",
-                                     "achieved": round(gu_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                     "frac": round(gu_gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                                     "algorithmic_bytes_per_launch": gu_bytes}
+        k_gbs = layer_bytes / (dec_stage["layer"] * 1e-3) / 1e9
+        result["decode_roofline"] = {"kernel": "k_decode (whole decode layer: router, top-k, 9 expert GEMVs)",
+                                     "bound": "hbm", "achieved": round(k_gbs, 1), "peak": PEAK_HBM_GBS,
+                                     "unit": "GB/s", "frac": round(k_gbs / PEAK_HBM_GBS, 4),
+                                     "traffic": profiled_traffic("k_decode"), "traffic_unit": "bytes per launch",
+                                     "algorithmic_bytes_per_launch": layer_bytes}
         result["decode_algorithmic_bytes_per_layer"] = layer_bytes
 
     if not args.no_cpu_baseline:

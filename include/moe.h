@@ -128,15 +128,14 @@ enum {
   MOE_STAGE_GROUP = 1,   /* histogram, prefix scan, scatter, block map */
   MOE_STAGE_GATEUP = 2,  /* grouped GEMM gate/up + SwiGLU */
   MOE_STAGE_DOWN = 3,    /* grouped GEMM down + gate-weighted combine */
-  MOE_STAGE_FINAL = 4,   /* fp32 accumulator -> bf16 output */
+  MOE_STAGE_FINAL = 4,   /* per token: sum of its k+1 gate-weighted rows -> bf16 */
   MOE_PREFILL_STAGES = 5
 };
-/* Decode stages. */
+/* Decode stages: the whole token (logits, top-k, gates, gate/up GEMV + SwiGLU,
+ * down GEMV + routing weights + shared expert) is one launch. */
 enum {
-  MOE_DSTAGE_ROUTE = 0,  /* logits (binary64), top-k, gates */
-  MOE_DSTAGE_GATEUP = 1, /* k+1 experts: gate/up GEMV + SwiGLU */
-  MOE_DSTAGE_DOWN = 2,   /* down GEMV + routing weights + shared expert -> bf16 */
-  MOE_DECODE_STAGES = 3
+  MOE_DSTAGE_LAYER = 0,
+  MOE_DECODE_STAGES = 1
 };
 
 /* Optional diagnostics of one forward (any field may be NULL).
@@ -177,7 +176,11 @@ moe_status moe_forward_prefill(moe_plan_t plan, const void *x, int64_t T, void *
                                void *workspace, size_t workspace_bytes, hipStream_t stream,
                                const moe_debug_out *dbg);
 
-/* Decode: one token; x, out bf16 [H]. */
+/* Decode: one token; x, out bf16 [H].  One launch whose workgroups hand results to
+ * each other inside the launch (section "Decode > Keep every decode step on the
+ * GPU"); requires E <= 256.  If an internal wait ever exceeded its poll budget, the
+ * control word at byte offset 88 of the workspace (int32) becomes non-zero (the output of
+ * that call is then invalid); moe_workspace_init clears it. */
 moe_status moe_forward_decode(moe_plan_t plan, const void *x, void *out, void *workspace,
                               size_t workspace_bytes, hipStream_t stream,
                               const moe_debug_out *dbg);

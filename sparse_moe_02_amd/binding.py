@@ -18,10 +18,11 @@ MOE_BF16, MOE_FP16, MOE_FP32 = 0, 1, 2
 MOE_OK = 0
 MOE_STAGE_ROUTE, MOE_STAGE_GROUP, MOE_STAGE_GATEUP, MOE_STAGE_DOWN, MOE_STAGE_FINAL = range(5)
 MOE_PREFILL_STAGES = 5
-MOE_DSTAGE_ROUTE, MOE_DSTAGE_GATEUP, MOE_DSTAGE_DOWN = range(3)
-MOE_DECODE_STAGES = 3
+MOE_DSTAGE_LAYER = 0
+MOE_DECODE_STAGES = 1
 PREFILL_STAGE_NAMES = ("route", "group", "gateup", "down", "final")
-DECODE_STAGE_NAMES = ("route", "gateup", "down")
+DECODE_STAGE_NAMES = ("layer",)
+CTRL_DECODE_ERR_OFFSET = 88  # byte offset of the decode wait-failure word in the workspace
 
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE", 4: "MOE_ERR_ALIGN",
                 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_TOKENS", 7: "MOE_ERR_DEVICE", 8: "MOE_ERR_HIP",

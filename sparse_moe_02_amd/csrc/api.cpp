@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <atomic>
 #include <cstring>
 #include <new>
 
@@ -18,9 +19,10 @@ struct moe_plan_s {
   moe_config cfg;
   moe_weights w;
   int n_cu;
+  int dec_grid;  // workgroups of the decode launch (all resident at once)
   // workspace layout (byte offsets)
   size_t off_ctrl, off_tokmask, off_ids, off_gates, off_counts, off_offsets, off_row_token,
-      off_row_gate, off_slot_row, off_mblocks, off_h, off_y, off_l64, off_a64, off_dids, off_dgates, off_dh, total;
+      off_row_gate, off_slot_row, off_mblocks, off_h, off_y, off_lrec, off_hrec, off_hint, off_dend, total;
 };
 
 namespace {
@@ -62,11 +64,10 @@ void layout(moe_plan_s &p) {
   p.off_mblocks = take(max_mblocks * 16);
   p.off_h = take(rows * I * 2);
   p.off_y = take(rows * H * 2);
-  p.off_l64 = take(E * 8);
-  p.off_a64 = take(E * 8);
-  p.off_dids = take(k * 4);
-  p.off_dgates = take(k * 4);
-  p.off_dh = take((k + 1) * I * 4);
+  p.off_lrec = take(E * 3 * 8);  // decode records: cleared by moe_workspace_init
+  p.off_hrec = take((k + 1) * I * 8);
+  p.off_hint = take((k + 1) * I / 4 * 4);
+  p.off_dend = o;
   p.total = o;
 }
 
@@ -89,6 +90,17 @@ moe_status check_ws(const moe_plan_s *p, void *ws, size_t bytes) {
 bool overlap(const void *a, size_t na, const void *b, size_t nb) {
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
   return x < y + nb && y < x + na;
+}
+
+// Tag of one decode call's hand-off records.  Process-wide and increasing, so a call
+// never accepts a record left in its workspace by an earlier call (records are cleared
+// to tag 0 by moe_workspace_init; 0 is never issued).
+std::atomic<uint32_t> g_epoch{0};
+
+uint32_t next_epoch() {
+  uint32_t e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+  while (e == 0) e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+  return e;
 }
 
 hipError_t rec(const moe_debug_out *dbg, int i, hipStream_t s) {
@@ -149,6 +161,14 @@ moe_status moe_plan_create(const moe_config *cfg, const moe_weights *w, moe_plan
   p->cfg = c;
   p->w = *w;
   p->n_cu = prop.multiProcessorCount;
+  {
+    DecodeArgs da{};
+    da.H = c.hidden;
+    da.E = c.n_experts;
+    da.k = c.top_k;
+    da.I = c.inter;
+    p->dec_grid = decode_grid(da, p->n_cu);
+  }
   layout(*p);
   if (workspace_bytes) *workspace_bytes = p->total;
   *plan = p;
@@ -161,7 +181,10 @@ moe_status moe_workspace_init(moe_plan_t p, void *ws, size_t bytes, hipStream_t 
   if (!p) return MOE_ERR_NULL;
   const moe_status st = check_ws(p, ws, bytes);
   if (st != MOE_OK) return st;
-  return launch_ctrl_init(at<Ctrl>(ws, p->off_ctrl), stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  return launch_ctrl_init(at<Ctrl>(ws, p->off_ctrl), at<char>(ws, p->off_lrec), p->off_dend - p->off_lrec, stream) ==
+                 hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
 }
 
 moe_status moe_forward_prefill(moe_plan_t p, const void *x, int64_t T, void *out, void *ws, size_t bytes,
@@ -289,23 +312,18 @@ moe_status moe_forward_decode(moe_plan_t p, const void *x, void *out, void *ws, 
   a.E = c.n_experts;
   a.k = c.top_k;
   a.I = c.inter;
-  a.l64 = at<double>(ws, p->off_l64);
-  a.a64 = at<double>(ws, p->off_a64);
-  a.ids = at<int32_t>(ws, p->off_dids);
-  a.gates = at<float>(ws, p->off_dgates);
-  a.hbuf = at<float>(ws, p->off_dh);
+  a.epoch = next_epoch();
+  a.lrec = at<uint64_t>(ws, p->off_lrec);
+  a.hrec = at<uint64_t>(ws, p->off_hrec);
+  a.hint = at<uint32_t>(ws, p->off_hint);
   a.ctrl = at<Ctrl>(ws, p->off_ctrl);
   a.out = static_cast<uint16_t *>(out);
   if (dbg) {
     a.dbg_ids = dbg->topk_ids;
     a.dbg_gates = dbg->gates;
   }
-  if (rec(dbg, MOE_DSTAGE_ROUTE, stream) != hipSuccess) return MOE_ERR_HIP;
-  if (launch_decode_route(a, stream) != hipSuccess) return MOE_ERR_HIP;
-  if (rec(dbg, MOE_DSTAGE_GATEUP, stream) != hipSuccess) return MOE_ERR_HIP;
-  if (launch_decode_gateup(a, stream) != hipSuccess) return MOE_ERR_HIP;
-  if (rec(dbg, MOE_DSTAGE_DOWN, stream) != hipSuccess) return MOE_ERR_HIP;
-  if (launch_decode_down(a, stream) != hipSuccess) return MOE_ERR_HIP;
+  if (rec(dbg, MOE_DSTAGE_LAYER, stream) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_decode(a, p->dec_grid, stream) != hipSuccess) return MOE_ERR_HIP;
   if (rec(dbg, MOE_DECODE_STAGES, stream) != hipSuccess) return MOE_ERR_HIP;
   return MOE_OK;
 }

@@ -1,25 +1,54 @@
-// Decode form (one token): row-parallel dequant-GEMV over the k routed experts and the
-// shared expert, no MFMA.
+// Decode form (one token) in a single launch: router logits, top-k selection, the
+// gate/up GEMVs with SwiGLU and the down GEMVs with the gate-weighted combine.
 //
 // "Optimizing on-device inference for Apple Silicon", section "Decode > Optimize the
-// one-row weight path": a group of lanes cooperates on one output while reading
-// different parts of the weight row in parallel.  Section "Decode > Reduce intermediate
-// and state traffic": the two input projections and the gated activation form one
-// kernel; the output projection, the routing weights and the shared expert's result form
-// another.  Batch-1 decode moves every active weight byte once, so both kernels are
-// bound by HBM reads: each lane issues 16-byte loads of packed codes and the dot product
-// is taken against the codes directly,
-//     sum_k x_k (s q_k + b) = s * sum_k x_k q_k + b * sum_k x_k   (per group of 64),
-// in fp32, then reduced across the lanes of the row.
+// one-row weight path": a group of lanes shares one output row, each lane reading a
+// different part of the packed weight row.  Section "Decode > Reduce intermediate and
+// state traffic": the two input projections and the gated activation are one step; the
+// output projection, the routing weights and the shared expert's result are another.
+// Section "Decode > Keep every decode step on the GPU": the token's whole layer runs
+// without the host.
+//
+// Batch-1 decode moves every active weight byte once, so the layer is bound by HBM reads
+// and by the latency of its dependency chain (logits -> selection -> gate/up -> down).
+// One launch covers the chain.  Workgroups hand results to each other as tagged
+// records: an 8-byte word holding a 32-bit value and the call's 32-bit epoch, written
+// with one device-scope store and read with device-scope loads, so a reader accepts a
+// value exactly when its tag is this call's epoch; there are no counters and no atomic
+// read-modify-writes (those serialise on one address).
+//   1. workgroup b computes the binary64 logits of experts b, b+G, ... and publishes
+//      each as three records (the two halves of the logit and its error radius);
+//   2. every workgroup that needs the routing reads all E logits and selects the top k
+//      itself (same values, same arithmetic, same result): a threshold from each wave's
+//      q-th largest logit leaves a few candidates, ranked exactly, then certified
+//      against the radii; undecided experts are summed sequentially in binary64;
+//   3. gate/up task g (16 rows of one expert slot) runs on workgroup g mod G and
+//      publishes h as records plus one hint word per 4 rows; tasks of the shared expert
+//      run before the routing is known; a workgroup's first down task has its weight
+//      loads issued together with its routed gate/up loads;
+//   4. down task d (8 output rows, every slot) waits for the hints of the h rows it
+//      needs, reads the records into LDS and sums gate * (W_down h) in slot order.
+// Every workgroup of the grid is resident at once (the grid is capped by the occupancy
+// of this kernel), so each wait ends; a wait that exceeds its poll budget sets an error
+// word instead of hanging.  The dot products use the packed codes directly:
+//     sum_k v_k (s q_k + b) = s * sum_k v_k q_k + b * sum_k v_k   (per group of 64).
 #include "common.hpp"
 #include "kernels.hpp"
+#include "select64.hpp"
 
 namespace moe {
 
 namespace {
 
-constexpr int kGuRows = 4;   // gate/up rows per wave
-constexpr int kDnRows = 16;  // output rows per down workgroup
+constexpr int kDecThreads = 256;        // four waves
+constexpr int kGuRows = 4;              // gate/up rows per wave in one task
+constexpr int kGuTask = 4 * kGuRows;    // rows of one gate/up task
+constexpr int kDnRows = 8;              // output rows of one down task
+constexpr int kDnUnits = 5;             // (row, slot) units per 16-lane group per round
+constexpr int kDnSlots = 10;            // slots per down round: 8 rows x 10 = 16 groups x 5
+constexpr int kHStage = 5120;           // h floats staged in LDS per down round
+constexpr int kSpins = 1 << 20;         // polls before a wait gives up (about a second)
+constexpr int kRecSpins = 1 << 12;      // re-reads of one h record after its hint was seen
 
 __device__ __forceinline__ QMat expert_mat(const QMat &routed, const QMat &shared, int e, int E, int N, int K) {
   if (e == E) return shared;
@@ -47,140 +76,474 @@ __device__ __forceinline__ float dot_codes32(const uint4 &w, const float (&v)[32
   return s;
 }
 
-// Gate/up for expert slot j (j < k: routed ids[j]; j == k: shared), rows i0..i0+3.
-// Lane takes 32-element chunks c = lane + 64 p of the H-long rows.
-__global__ __launch_bounds__(64) void k_decode_gateup(DecodeArgs a) {
-  const int lane = threadIdx.x;
-  const int H = a.H, I = a.I, E = a.E, k = a.k;
-  const int per = I / kGuRows;
-  const int j = blockIdx.x / per;
-  const int i0 = (blockIdx.x - j * per) * kGuRows;
-  const int e = j < k ? a.ids[j] : E;
-  const QMat G = expert_mat(a.gate, a.s_gate, e, E, I, H);
-  const QMat U = expert_mat(a.up, a.s_up, e, E, I, H);
-  float accg[kGuRows] = {}, accu[kGuRows] = {};
-  for (int c = lane; c < H / 32; c += kWave) {
-    uint4 wg[kGuRows], wu[kGuRows];
-    float sg[kGuRows], bg[kGuRows], su[kGuRows], bu[kGuRows];
-#pragma unroll
-    for (int r = 0; r < kGuRows; ++r) {
-      const size_t row = (size_t)(i0 + r);
-      wg[r] = *(const uint4 *)(G.q + row * (H / 8) + 4 * c);
-      wu[r] = *(const uint4 *)(U.q + row * (H / 8) + 4 * c);
-      sg[r] = fp16_to_f32(G.s[row * (H / 64) + c / 2]);
-      bg[r] = fp16_to_f32(G.b[row * (H / 64) + c / 2]);
-      su[r] = fp16_to_f32(U.s[row * (H / 64) + c / 2]);
-      bu[r] = fp16_to_f32(U.b[row * (H / 64) + c / 2]);
+__device__ __forceinline__ uint64_t tagged(uint32_t epoch, uint32_t v) { return ((uint64_t)epoch << 32) | v; }
+__device__ __forceinline__ uint32_t tag_of(uint64_t r) { return (uint32_t)(r >> 32); }
+
+struct DecShared {
+  Sel64 S;
+  double red[2][4];
+  int ids[kMaxTopK];
+  float gates[kMaxTopK];
+  float unit[kDnRows * kDnSlots];
+  __attribute__((aligned(16))) float h[kHStage];
+};
+
+// ------------------------------------------------------------------ router (binary64)
+
+// Additions on any path of router_logit's sum: 8 per 2048 elements per lane, a 6-level
+// butterfly, 3 across the four waves.
+__device__ __forceinline__ int router_depth(int H) { return 8 * ((H + 2047) / 2048) + 9; }
+
+// Binary64 logit of expert e (exact products, summed lane-sequentially, then over the
+// wave, then over the four waves in order) and sum |x w|, in every thread.
+__device__ void router_logit(const DecodeArgs &a, DecShared &sh, int e, double &l, double &ab) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, H = a.H;
+  double s = 0.0, sa = 0.0;
+  for (int c = tid; c < H / 8; c += kDecThreads) {
+    const uint4 xv = *(const uint4 *)(a.x + 8 * c);
+    const float xf[8] = {bf16_lo(xv.x), bf16_hi(xv.x), bf16_lo(xv.y), bf16_hi(xv.y),
+                         bf16_lo(xv.z), bf16_hi(xv.z), bf16_lo(xv.w), bf16_hi(xv.w)};
+    float wf[8];
+    if (a.wr16) {
+      const uint4 wv4 = *(const uint4 *)(a.wr16 + (size_t)e * H + 8 * c);
+      wf[0] = bf16_lo(wv4.x); wf[1] = bf16_hi(wv4.x); wf[2] = bf16_lo(wv4.y); wf[3] = bf16_hi(wv4.y);
+      wf[4] = bf16_lo(wv4.z); wf[5] = bf16_hi(wv4.z); wf[6] = bf16_lo(wv4.w); wf[7] = bf16_hi(wv4.w);
+    } else {
+      const float4 w0 = *(const float4 *)(a.wr32 + (size_t)e * H + 8 * c);
+      const float4 w1 = *(const float4 *)(a.wr32 + (size_t)e * H + 8 * c + 4);
+      wf[0] = w0.x; wf[1] = w0.y; wf[2] = w0.z; wf[3] = w0.w;
+      wf[4] = w1.x; wf[5] = w1.y; wf[6] = w1.z; wf[7] = w1.w;
     }
-    float xf[32];
-    float xs = 0.f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 xv = *(const uint4 *)(a.x + 32 * c + 8 * q);
-      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xf[8 * q + 2 * i] = bf16_lo(xw[i]);
-        xf[8 * q + 2 * i + 1] = bf16_hi(xw[i]);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 32; ++i) xs += xf[i];
-#pragma unroll
-    for (int r = 0; r < kGuRows; ++r) {
-      accg[r] += sg[r] * dot_codes32(wg[r], xf) + bg[r] * xs;
-      accu[r] += su[r] * dot_codes32(wu[r], xf) + bu[r] * xs;
+    for (int i = 0; i < 8; ++i) {
+      const double p = (double)xf[i] * (double)wf[i];  // exact
+      s += p;
+      sa += fabs(p);
     }
   }
-#pragma unroll
-  for (int r = 0; r < kGuRows; ++r) {
-    const float g = wave_sum(accg[r]);
-    const float u = wave_sum(accu[r]);
-    if (lane == 0) a.hbuf[(size_t)j * I + i0 + r] = g / (1.0f + __expf(-g)) * u;
+  s = wave_sum_f64(s);
+  sa = wave_sum_f64(sa);
+  if (lane == 0) {
+    sh.red[0][wv] = s;
+    sh.red[1][wv] = sa;
+  }
+  __syncthreads();
+  l = ((sh.red[0][0] + sh.red[0][1]) + sh.red[0][2]) + sh.red[0][3];
+  ab = ((sh.red[1][0] + sh.red[1][1]) + sh.red[1][2]) + sh.red[1][3];
+  if (a.bias) l += (double)a.bias[e];
+  __syncthreads();
+}
+
+// Wait for expert e's three logit records of this call.
+__device__ void read_logit(const DecodeArgs &a, int e, double &v, double &r) {
+  const uint64_t *rec = a.lrec + 3 * (size_t)e;
+  for (int i = 0;; ++i) {
+    const uint64_t r0 = ld_agent(&rec[0]), r1 = ld_agent(&rec[1]), r2 = ld_agent(&rec[2]);
+    if (tag_of(r0) == a.epoch && tag_of(r1) == a.epoch && tag_of(r2) == a.epoch) {
+      v = __longlong_as_double((long long)(((uint64_t)(uint32_t)r1 << 32) | (uint32_t)r0));
+      r = (double)__uint_as_float((uint32_t)r2);
+      return;
+    }
+    if (i == kSpins) {
+      st_agent(&a.ctrl->d_err, 1);
+      v = -INFINITY;
+      r = 0.0;
+      return;
+    }
+    __builtin_amdgcn_s_sleep(2);
   }
 }
 
-// Down + combine: out[n] = sum_{j<k} gates[j] * Wd_{ids[j]}[n,:] . h_j + Wd_s[n,:] . h_k.
-// One workgroup of min(k+1, 16) waves per kDnRows output rows; wave j owns expert slot j
-// (and j + 16), keeps
-// its 32-element chunk of h_j in registers and issues all its weight loads at once.
-// LPR lanes share a row (32 codes each); per-slot partial sums meet in LDS.
-template <int LPR>
-__global__ __launch_bounds__(1024) void k_decode_down(DecodeArgs a) {
-  constexpr int RPP = kWave / LPR;           // rows per pass
-  constexpr int P = kDnRows / RPP;           // passes (kDnRows is a multiple of RPP)
-  __shared__ float s_part[kMaxTopK + 1][kDnRows];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  const int H = a.H, I = a.I, E = a.E, k = a.k;
-  const int sub = lane / LPR, cl = lane % LPR;
-  const int n0 = blockIdx.x * kDnRows;
-  for (int j = wv; j <= k; j += nw) {
-    const int e = j < k ? a.ids[j] : E;
-    const float gj = j < k ? a.gates[j] : 1.0f;
-    const QMat D = expert_mat(a.down, a.s_down, e, E, H, I);
-    float acc[P] = {};
-    for (int c = cl; c < I / 32; c += LPR) {
-      uint4 w[P];
-      float sc[P], bi[P];
+__device__ double block_min_f64(double v, DecShared &sh) {
 #pragma unroll
-      for (int p = 0; p < P; ++p) {
-        const size_t n = (size_t)(n0 + p * RPP + sub);
-        w[p] = *(const uint4 *)(D.q + n * (I / 8) + 4 * c);
-        sc[p] = fp16_to_f32(D.s[n * (I / 64) + c / 2]);
-        bi[p] = fp16_to_f32(D.b[n * (I / 64) + c / 2]);
-      }
-      float hv[32];
-      const float4 *hp = (const float4 *)(a.hbuf + (size_t)j * I + 32 * c);
+  for (int o = 1; o < kWave; o <<= 1) v = fmin(v, __shfl_xor(v, o));
+  if ((threadIdx.x & 63) == 0) sh.red[0][threadIdx.x >> 6] = v;
+  __syncthreads();
+  v = fmin(fmin(sh.red[0][0], sh.red[0][1]), fmin(sh.red[0][2], sh.red[0][3]));
+  __syncthreads();
+  return v;
+}
+
+__device__ double block_max_f64(double v, DecShared &sh) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float4 v = hp[q];
-        hv[4 * q] = v.x;
-        hv[4 * q + 1] = v.y;
-        hv[4 * q + 2] = v.z;
-        hv[4 * q + 3] = v.w;
-      }
-      float hs = 0.f;
+  for (int o = 1; o < kWave; o <<= 1) v = fmax(v, __shfl_xor(v, o));
+  if ((threadIdx.x & 63) == 0) sh.red[0][threadIdx.x >> 6] = v;
+  __syncthreads();
+  v = fmax(fmax(sh.red[0][0], sh.red[0][1]), fmax(sh.red[0][2], sh.red[0][3]));
+  __syncthreads();
+  return v;
+}
+
+// Top-k of the E logits of this call (value descending, index ascending) into sh.ids
+// (ascending) and sh.gates.  One expert per thread (E <= 256).
+__device__ void select_topk(const DecodeArgs &a, DecShared &sh, bool write_debug) {
+  Sel64 &S = sh.S;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, E = a.E, k = a.k;
+  const bool mine = tid < E;
+  double v = -INFINITY, r = 0.0;
+  if (mine) {
+    read_logit(a, tid, v, r);
+    S.gl[tid] = v;
+    S.chosen[tid] = 0;
+  }
+  // Threshold: wave w's q-th largest logit t_w (q = ceil(k / waves)).  At least k logits
+  // are >= min_w t_w, so every chosen expert is among those.
+  const int nw = (E + kWave - 1) / kWave, q = (k + nw - 1) / nw;
+  if (wv < nw) {
+    double cur = v, qth = -INFINITY;
+    for (int i = 0; i < q; ++i) {
+      double m = cur;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) hs += hv[i];
-#pragma unroll
-      for (int p = 0; p < P; ++p) acc[p] += sc[p] * dot_codes32(w[p], hv) + bi[p] * hs;
+      for (int o = 1; o < kWave; o <<= 1) m = fmax(m, __shfl_xor(m, o));
+      qth = m;
+      const unsigned long long hit = __ballot(cur == m);
+      if (lane == __ffsll(hit) - 1) cur = -INFINITY;  // take out one instance
     }
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-      float v = acc[p];
-#pragma unroll
-      for (int o = 1; o < LPR; o <<= 1) v += __shfl_xor(v, o);
-      if (cl == 0) s_part[j][p * RPP + sub] = gj * v;
-    }
+    if (lane == 0) sh.red[1][wv] = qth;
+  }
+  if (tid == 0) S.n = 0;
+  __syncthreads();
+  double tau = INFINITY;
+  for (int w = 0; w < nw; ++w) tau = fmin(tau, sh.red[1][w]);
+  if (mine && v >= tau) {
+    const int c = atomicAdd(&S.n, 1);
+    S.cand[c] = tid;
+    S.v[c] = v;
   }
   __syncthreads();
-  if (threadIdx.x < kDnRows) {
-    float v = 0.f;
-    for (int jj = 0; jj <= k; ++jj) v += s_part[jj][threadIdx.x];
-    a.out[n0 + threadIdx.x] = f32_to_bf16(v);
+  const int nc = S.n;
+  for (int c = tid; c < nc; c += kDecThreads) {
+    const double vc = S.v[c];
+    const int ec = S.cand[c];
+    int rank = 0;
+    for (int j = 0; j < nc; ++j) {
+      const double vj = S.v[j];
+      rank += (vj > vc) || (vj == vc && S.cand[j] < ec);
+    }
+    if (rank < k) S.chosen[ec] = 1;
+  }
+  __syncthreads();
+  const bool sel = mine && S.chosen[tid];
+  // certification: every chosen logit minus its radius above every other plus its radius
+  const double mn = block_min_f64(sel ? v - r : INFINITY, sh);
+  const double mx = block_max_f64((mine && !sel) ? v + r : -INFINITY, sh);
+  const bool sure_in = sel && v - r > mx;
+  const bool sure_out = mine && !sel && v + r < mn;
+  if (!__syncthreads_and(!mine || sure_in || sure_out)) {
+    if (mine) S.chosen[tid] = sure_in ? 1 : 0;
+    if (tid == 0) S.n = 0;
+    __syncthreads();
+    if (mine && !sure_in && !sure_out) {
+      const int c = atomicAdd(&S.n, 1);
+      S.cand[c] = tid;
+      S.v[c] = v;
+      S.rad[c] = r;
+    }
+    const int nin1 = __syncthreads_count(sure_in);
+    resolve64(S, k - nin1, a.x, a.wr16, a.wr32, a.bias, a.H, tid, kDecThreads);
+  }
+  emit_selection<false>(S, E, k, sh.ids, sh.gates, write_debug ? a.dbg_ids : nullptr,
+                        write_debug ? a.dbg_gates : nullptr, tid, kDecThreads);
+  if (tid < k) sh.ids[tid] = min(max(sh.ids[tid], 0), E - 1);  // keep reads in bounds even after a failed wait
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------ gate/up
+
+// One round of a gate/up task for the calling wave: rows r0..r0+3 of slot j, the
+// 32-element chunk c = lane + 64 p of the H-long rows.
+struct GuLoad {
+  uint4 wg[kGuRows], wu[kGuRows];
+  uint32_t sg[kGuRows], bg[kGuRows], su[kGuRows], bu[kGuRows];
+  uint4 x[4];
+  bool ok;
+};
+
+__device__ __forceinline__ void gu_issue(const DecodeArgs &a, const QMat &Gm, const QMat &Um, int r0, int c,
+                                         GuLoad &L) {
+  const int H = a.H;
+  L.ok = c < H / 32;
+  const int cc = L.ok ? c : 0;
+#pragma unroll
+  for (int r = 0; r < kGuRows; ++r) {
+    const size_t row = (size_t)(r0 + r);
+    L.wg[r] = *(const uint4 *)(Gm.q + row * (H / 8) + 4 * cc);
+    L.wu[r] = *(const uint4 *)(Um.q + row * (H / 8) + 4 * cc);
+    L.sg[r] = Gm.s[row * (H / 64) + cc / 2];
+    L.bg[r] = Gm.b[row * (H / 64) + cc / 2];
+    L.su[r] = Um.s[row * (H / 64) + cc / 2];
+    L.bu[r] = Um.b[row * (H / 64) + cc / 2];
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) L.x[q] = *(const uint4 *)(a.x + 32 * cc + 8 * q);
+}
+
+__device__ __forceinline__ void gu_accumulate(const GuLoad &L, float (&ag)[kGuRows], float (&au)[kGuRows]) {
+  if (!L.ok) return;
+  float xf[32];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t xw[4] = {L.x[q].x, L.x[q].y, L.x[q].z, L.x[q].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xf[8 * q + 2 * i] = bf16_lo(xw[i]);
+      xf[8 * q + 2 * i + 1] = bf16_hi(xw[i]);
+    }
+  }
+  float xs = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) xs += xf[i];
+#pragma unroll
+  for (int r = 0; r < kGuRows; ++r) {
+    ag[r] += fp16_to_f32((uint16_t)L.sg[r]) * dot_codes32(L.wg[r], xf) + fp16_to_f32((uint16_t)L.bg[r]) * xs;
+    au[r] += fp16_to_f32((uint16_t)L.su[r]) * dot_codes32(L.wu[r], xf) + fp16_to_f32((uint16_t)L.bu[r]) * xs;
+  }
+}
+
+__device__ __forceinline__ int gu_expert(const DecodeArgs &a, const DecShared &sh, int j) {
+  return j < a.k ? sh.ids[j] : a.E;
+}
+
+__device__ __forceinline__ void gu_start(const DecodeArgs &a, const DecShared &sh, int g, GuLoad &L) {
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tpe = a.I / kGuTask;
+  const int j = g / tpe, r0 = (g - j * tpe) * kGuTask + kGuRows * wv;
+  const int e = gu_expert(a, sh, j);
+  gu_issue(a, expert_mat(a.gate, a.s_gate, e, a.E, a.I, a.H), expert_mat(a.up, a.s_up, e, a.E, a.I, a.H), r0,
+           lane, L);
+}
+
+// Gate/up task g: slot j = g / (I/16), rows i0 .. i0+15 (wave w: i0+4w .. i0+4w+3).
+// `first` holds the already-issued first round.  Publishes this wave's 4 h records,
+// then its hint.
+__device__ void gu_task(const DecodeArgs &a, const DecShared &sh, int g, const GuLoad &first) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int I = a.I, H = a.H;
+  const int tpe = I / kGuTask;
+  const int j = g / tpe, r0 = (g - j * tpe) * kGuTask + kGuRows * wv;
+  float ag[kGuRows] = {}, au[kGuRows] = {};
+  gu_accumulate(first, ag, au);
+  const int np = (H / 32 + kWave - 1) / kWave;
+  if (np > 1) {
+    const int e = gu_expert(a, sh, j);
+    const QMat Gm = expert_mat(a.gate, a.s_gate, e, a.E, I, H);
+    const QMat Um = expert_mat(a.up, a.s_up, e, a.E, I, H);
+    for (int p = 1; p < np; ++p) {
+      GuLoad L;
+      gu_issue(a, Gm, Um, r0, lane + kWave * p, L);
+      gu_accumulate(L, ag, au);
+    }
+  }
+  float hv = 0.f;
+#pragma unroll
+  for (int r = 0; r < kGuRows; ++r) {
+    const float gs = wave_sum(ag[r]);
+    const float us = wave_sum(au[r]);
+    if (lane == r) hv = gs / (1.0f + __expf(-gs)) * us;
+  }
+  const size_t row = (size_t)j * I + r0;
+  if (lane < kGuRows) st_agent(&a.hrec[row + lane], tagged(a.epoch, __float_as_uint(hv)));
+  if (lane == 0) st_agent(&a.hint[row / kGuRows], a.epoch);
+}
+
+// ------------------------------------------------------------------ down
+
+// Units of a down round: u = r * nb + jj (row r of the task, slot j0 + jj).  16-lane
+// group q (lane/16 + 4*wave) takes u = q + 16 m; lane cl = lane % 16 takes the
+// 32-element chunk c = cl + 16 p of the I-long rows.
+struct DnLoad {
+  uint4 w[kDnUnits];
+  uint32_t s[kDnUnits], b[kDnUnits];
+};
+
+__device__ __forceinline__ void dn_issue(const DecodeArgs &a, const DecShared &sh, int n0, int j0, int nb, int c,
+                                         DnLoad &L) {
+  const int I = a.I, k = a.k, q = (threadIdx.x >> 4);
+  const int cc = c < I / 32 ? c : 0;
+#pragma unroll
+  for (int m = 0; m < kDnUnits; ++m) {
+    int u = q + 16 * m;
+    u = u < kDnRows * nb ? u : 0;  // surplus units read unit 0 (result discarded)
+    const int r = u / nb, slot = j0 + (u - r * nb);
+    const int e = slot < k ? sh.ids[slot] : a.E;
+    const QMat D = expert_mat(a.down, a.s_down, e, a.E, a.H, I);
+    const size_t n = (size_t)(n0 + r);
+    L.w[m] = *(const uint4 *)(D.q + n * (I / 8) + 4 * cc);
+    L.s[m] = D.s[n * (I / 64) + cc / 2];
+    L.b[m] = D.b[n * (I / 64) + cc / 2];
+  }
+}
+
+// h of slots j0 .. j0+nb-1 into LDS: wait for their hints, then take the records,
+// re-reading any whose tag is not yet this call's.
+__device__ void stage_h(const DecodeArgs &a, DecShared &sh, int j0, int nb) {
+  const int tid = threadIdx.x;
+  const int n = nb * a.I;
+  const size_t base = (size_t)j0 * a.I;
+  bool ok = false;
+  for (int i = 0; !ok; ++i) {
+    bool mine = true;
+    for (int t = tid; t < n / kGuRows; t += kDecThreads) mine &= ld_agent(&a.hint[base / kGuRows + t]) == a.epoch;
+    ok = __syncthreads_and(mine);
+    if (!ok) {
+      if (i == kSpins) {
+        if (tid == 0) st_agent(&a.ctrl->d_err, 1);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  for (int t = tid; t < n; t += kDecThreads) {
+    uint64_t rv = ld_agent(&a.hrec[base + t]);
+    for (int i = 0; tag_of(rv) != a.epoch; ++i) {
+      if (i == kRecSpins) {
+        st_agent(&a.ctrl->d_err, 1);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+      rv = ld_agent(&a.hrec[base + t]);
+    }
+    sh.h[t] = __uint_as_float((uint32_t)rv);
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void dn_accumulate(const DecodeArgs &a, DecShared &sh, const DnLoad &L, int nb, int c,
+                                              float (&acc)[kDnUnits]) {
+  const int I = a.I, q = threadIdx.x >> 4;
+  if (c >= I / 32) return;
+#pragma unroll
+  for (int m = 0; m < kDnUnits; ++m) {
+    const int u = q + 16 * m;
+    if (u >= kDnRows * nb) continue;
+    const int jj = u % nb;
+    const float4 *hp = (const float4 *)&sh.h[jj * I + 32 * c];
+    float hv[32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 v = hp[i];
+      hv[4 * i] = v.x;
+      hv[4 * i + 1] = v.y;
+      hv[4 * i + 2] = v.z;
+      hv[4 * i + 3] = v.w;
+    }
+    float hs = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) hs += hv[i];
+    acc[m] += fp16_to_f32((uint16_t)L.s[m]) * dot_codes32(L.w[m], hv) + fp16_to_f32((uint16_t)L.b[m]) * hs;
+  }
+}
+
+// Down task d: output rows n0 = 8d .. 8d+7 over every slot, rounds of nb slots and
+// chunk passes; `pre` (if given) is round 0's first pass, already issued.
+__device__ void dn_task(const DecodeArgs &a, DecShared &sh, int d, const DnLoad *pre) {
+  const int tid = threadIdx.x, q = tid >> 4, cl = tid & 15;
+  const int I = a.I, k = a.k, n0 = d * kDnRows;
+  const int nbmax = min(min(k + 1, kDnSlots), kHStage / I);
+  const int npass = (I / 32 + 15) / 16;
+  float out_acc = 0.f;  // thread t < 8: row n0 + t
+  for (int j0 = 0; j0 <= k; j0 += nbmax) {
+    const int nb = min(nbmax, k + 1 - j0);
+    stage_h(a, sh, j0, nb);
+    float acc[kDnUnits] = {};
+    for (int p = 0; p < npass; ++p) {
+      const int c = cl + 16 * p;
+      if (pre && j0 == 0 && p == 0) {
+        dn_accumulate(a, sh, *pre, nb, c, acc);
+      } else {
+        DnLoad L;
+        dn_issue(a, sh, n0, j0, nb, c, L);
+        dn_accumulate(a, sh, L, nb, c, acc);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < kDnUnits; ++m) {
+      const float v = row16_sum(acc[m]);
+      const int u = q + 16 * m;
+      if (cl == 0 && u < kDnRows * nb) {
+        const int slot = j0 + u % nb;
+        sh.unit[u] = (slot < k ? sh.gates[slot] : 1.0f) * v;
+      }
+    }
+    __syncthreads();
+    if (tid < kDnRows)
+      for (int jj = 0; jj < nb; ++jj) out_acc += sh.unit[tid * nb + jj];
+    __syncthreads();
+  }
+  if (tid < kDnRows) a.out[n0 + tid] = f32_to_bf16(out_acc);
+}
+
+// ------------------------------------------------------------------ the layer
+
+__global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
+  __shared__ DecShared sh;
+  const int b = blockIdx.x, G = gridDim.x, tid = threadIdx.x;
+  const int E = a.E, k = a.k;
+  const int n_gu = (k + 1) * (a.I / kGuTask), n_dn = a.H / kDnRows;
+  const int first_shared = k * (a.I / kGuTask);  // gate/up tasks from here on are the shared expert's
+
+  // The shared expert needs no routing: issue its gate/up loads before the router work.
+  GuLoad gl;
+  const bool gu_early = b < n_gu && b >= first_shared;
+  if (gu_early) gu_start(a, sh, b, gl);
+
+  // 1. router logits, published as records
+  for (int e = b; e < E; e += G) {
+    double l, ab;
+    router_logit(a, sh, e, l, ab);
+    if (tid == 0) {
+      const uint64_t lb = (uint64_t)__double_as_longlong(l);
+      const float rad = __double2float_ru(radius64(l, ab, a.H, router_depth(a.H)));
+      uint64_t *rec = a.lrec + 3 * (size_t)e;
+      st_agent(&rec[0], tagged(a.epoch, (uint32_t)lb));
+      st_agent(&rec[1], tagged(a.epoch, (uint32_t)(lb >> 32)));
+      st_agent(&rec[2], tagged(a.epoch, __float_as_uint(rad)));
+    }
+  }
+
+  if (gu_early) gu_task(a, sh, b, gl);
+
+  // 2. the selection, in every workgroup that uses it
+  int g0 = gu_early ? b + G : b;
+  const bool routed_gu = g0 < first_shared;
+  if (routed_gu || b < n_dn || b == 0) select_topk(a, sh, b == 0);
+
+  // 3. routed gate/up tasks; the first down task's loads go out with the first of them
+  DnLoad dl;
+  bool dn_pre = false;
+  const int nbmax = min(min(k + 1, kDnSlots), kHStage / a.I);
+  for (int g = g0; g < n_gu; g += G) {
+    gu_start(a, sh, g, gl);
+    if (!dn_pre && b < n_dn) {
+      dn_issue(a, sh, b * kDnRows, 0, min(nbmax, k + 1), tid & 15, dl);
+      dn_pre = true;
+    }
+    gu_task(a, sh, g, gl);
+  }
+
+  // 4. down tasks
+  for (int d = b; d < n_dn; d += G) {
+    dn_task(a, sh, d, dn_pre ? &dl : nullptr);
+    dn_pre = false;
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode_gateup(const DecodeArgs &a, hipStream_t s) {
-  const int nb = (a.k + 1) * (a.I / kGuRows);
-  hipLaunchKernelGGL(k_decode_gateup, dim3(nb), dim3(64), 0, s, a);
-  return hipGetLastError();
+int decode_grid(const DecodeArgs &a, int n_cu) {
+  const int n_gu = (a.k + 1) * (a.I / kGuTask), n_dn = a.H / kDnRows;
+  int want = a.E;
+  want = want > n_gu ? want : n_gu;
+  want = want > n_dn ? want : n_dn;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode, kDecThreads, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  const int cap = per_cu * n_cu;
+  return want < cap ? want : cap;
 }
 
-hipError_t launch_decode_down(const DecodeArgs &a, hipStream_t s) {
-  const int cpr = a.I / 32;
-  const int lpr = cpr < kWave ? cpr : kWave;
-  const int nw = a.k + 1 < 16 ? a.k + 1 : 16;  // waves; each loops over its expert slots
-  const dim3 grid(a.H / kDnRows), block(64 * nw);
-  switch (lpr) {
-    case 4: hipLaunchKernelGGL(k_decode_down<4>, grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL(k_decode_down<8>, grid, block, 0, s, a); break;
-    case 16: hipLaunchKernelGGL(k_decode_down<16>, grid, block, 0, s, a); break;
-    case 32: hipLaunchKernelGGL(k_decode_down<32>, grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL(k_decode_down<64>, grid, block, 0, s, a); break;
-  }
+hipError_t launch_decode(const DecodeArgs &a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(k_decode, dim3(grid), dim3(kDecThreads), 0, s, a);
   return hipGetLastError();
 }
 

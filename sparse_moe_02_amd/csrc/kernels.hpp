@@ -24,14 +24,18 @@ constexpr int kXcds = 8;           // MI355X: 8 accelerator complex dies, one L2
 
 // Control words at the start of the workspace.
 struct Ctrl {
-  int decode_ticket;     // decode router: blocks done (reset by the last block)
+  int pad0;
   int n_mblocks;         // M-blocks in the block map
   int n_refined;         // tokens re-ranked in binary64 this chunk (reset by the group kernel)
-  int pad0;
+  int pad1;
   int q_gateup[kXcds];   // grouped GEMM work queues, one per XCD (reset by the group kernel)
   int q_down[kXcds];
-  int pad[44];
+  int pad2[2];
+  int d_err;             // decode: a wait ran out of polls (sticky; cleared by workspace init)
+  int pad[41];
 };
+static_assert(sizeof(Ctrl) == 256, "control block is one 256-byte slot");
+static_assert(__builtin_offsetof(Ctrl, d_err) == 88, "documented offset of the decode error word");
 
 struct RouteArgs {
   const uint16_t *x;      // [T][H] bf16 (chunk)
@@ -84,11 +88,10 @@ struct DecodeArgs {
   QMat gate, up, down;      // routed stacked
   QMat s_gate, s_up, s_down;
   int H, E, k, I;
-  double *l64;              // [E]
-  double *a64;              // [E]  sum |x w|
-  int32_t *ids;             // [k]
-  float *gates;             // [k]
-  float *hbuf;              // [(k+1)][I]
+  uint32_t epoch;           // tag of this call's records: nonzero, new for every call
+  uint64_t *lrec;           // [E][3] tagged records: low and high word of the binary64 logit, radius
+  uint64_t *hrec;           // [(k+1)*I] tagged h values
+  uint32_t *hint;           // [(k+1)*I/4] one per 4 h rows: their records have been stored
   Ctrl *ctrl;
   uint16_t *out;            // [H]
   int32_t *dbg_ids;
@@ -101,9 +104,8 @@ hipError_t launch_gemm_gateup(const GemmArgs &a, int n_blocks, hipStream_t s);
 hipError_t launch_gemm_down(const GemmArgs &a, int n_blocks, hipStream_t s);
 hipError_t launch_finalize(const uint16_t *y, const int32_t *slot_row, uint16_t *out, int T, int H, int k,
                            hipStream_t s);
-hipError_t launch_decode_route(const DecodeArgs &a, hipStream_t s);
-hipError_t launch_decode_gateup(const DecodeArgs &a, hipStream_t s);
-hipError_t launch_decode_down(const DecodeArgs &a, hipStream_t s);
-hipError_t launch_ctrl_init(Ctrl *c, hipStream_t s);
+int decode_grid(const DecodeArgs &a, int n_cu);  // workgroups of the decode launch
+hipError_t launch_decode(const DecodeArgs &a, int grid, hipStream_t s);
+hipError_t launch_ctrl_init(Ctrl *c, void *clear, size_t clear_bytes, hipStream_t s);
 
 }  // namespace moe

@@ -11,177 +11,15 @@
 // undecided experts get binary64 logits (wave-parallel), and experts that even these
 // cannot order are summed sequentially in ascending h in binary64, which reproduces the
 // exact-product sequential sum bit for bit.
-//
-// Decode: one wave per expert computes binary64 logits; the last workgroup to finish
-// (ticket counter) selects, falling back to sequential sums for undecided experts.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "select64.hpp"
 
 namespace moe {
 
 namespace {
 
 constexpr float kU32 = 5.9604644775390625e-8f;       // 2^-24
-constexpr double kU64 = 1.1102230246251565404e-16;   // 2^-53
-
-// Binary64 dot product of x with one router row, by one wave.  Lane `lane` takes the
-// 8-element chunks c = lane + 64 i (ascending i) and sums its exact products
-// sequentially; a butterfly over the wave gives every lane the same total.  Also
-// returns sum |x_h w_h|.  Each product passes through at most seq + 6 roundings with
-// seq = 8*ceil(H/512).
-__device__ void wave_dot64(const uint16_t *x, const uint16_t *w16, const float *w32, int H,
-                           int lane, double &l, double &a) {
-  double s = 0.0, sa = 0.0;
-  for (int c = lane; c < H / 8; c += kWave) {
-    const uint4 xv = *(const uint4 *)(x + 8 * c);
-    float xf[8] = {bf16_lo(xv.x), bf16_hi(xv.x), bf16_lo(xv.y), bf16_hi(xv.y),
-                   bf16_lo(xv.z), bf16_hi(xv.z), bf16_lo(xv.w), bf16_hi(xv.w)};
-    float wf[8];
-    if (w16) {
-      const uint4 wv = *(const uint4 *)(w16 + 8 * c);
-      wf[0] = bf16_lo(wv.x); wf[1] = bf16_hi(wv.x); wf[2] = bf16_lo(wv.y); wf[3] = bf16_hi(wv.y);
-      wf[4] = bf16_lo(wv.z); wf[5] = bf16_hi(wv.z); wf[6] = bf16_lo(wv.w); wf[7] = bf16_hi(wv.w);
-    } else {
-      const float4 w0 = *(const float4 *)(w32 + 8 * c);
-      const float4 w1 = *(const float4 *)(w32 + 8 * c + 4);
-      wf[0] = w0.x; wf[1] = w0.y; wf[2] = w0.z; wf[3] = w0.w;
-      wf[4] = w1.x; wf[5] = w1.y; wf[6] = w1.z; wf[7] = w1.w;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const double p = (double)xf[i] * (double)wf[i];  // exact
-      s += p;
-      sa += fabs(p);
-    }
-  }
-  l = wave_sum_f64(s);
-  a = wave_sum_f64(sa);
-}
-
-// Error radius of a wave_dot64 logit (plus bias) relative to the sequential
-// ascending-h binary64 sum (plus bias), whose own error to the exact value is at most
-// H roundings of sum|p|.
-__device__ __forceinline__ double radius64(double lb, double a, int H) {
-  const double seq = 8.0 * ((H + 511) / 512);
-  return (seq + 8.0 + (double)H) * kU64 * a * 1.001 + 4.0 * kU64 * fabs(lb) + 1e-300;
-}
-
-// Sequential ascending-h binary64 logit: the same arithmetic as the plain definition.
-__device__ double seq_dot64(const uint16_t *x, const uint16_t *w16, const float *w32, int H) {
-  double acc = 0.0;
-  for (int h = 0; h < H; ++h) {
-    const double w = w16 ? (double)bf16_to_f32(w16[h]) : (double)w32[h];
-    acc = __builtin_fma((double)bf16_to_f32(x[h]), w, acc);  // product exact: fma == mul+add
-  }
-  return acc;
-}
-
-// Membership in the best r of n candidates (order: value descending, index ascending)
-// from values v with error radius rad: state 1 = certainly in, 2 = certainly out,
-// 0 = undecided.  Candidate j may outrank i if v_j + rad_j >= v_i - rad_i, and
-// certainly outranks i if v_j - rad_j > v_i + rad_i.
-__device__ void classify(const double *v, const double *rad, int n, int r, int *state, int tid,
-                         int nthr) {
-  for (int i = tid; i < n; i += nthr) {
-    const double lo = v[i] - rad[i], hi = v[i] + rad[i];
-    int poss = 0, cert = 0;
-    for (int j = 0; j < n; ++j) {
-      if (j == i) continue;
-      poss += (v[j] + rad[j] >= lo);
-      cert += (v[j] - rad[j] > hi);
-    }
-    state[i] = (poss < r) ? 1 : (cert >= r ? 2 : 0);
-  }
-}
-
-// Shared per-workgroup scratch of the binary64 selection.
-struct Sel64 {
-  double v[kMaxExperts];
-  double rad[kMaxExperts];
-  double gl[kMaxExperts];    // logit used for the gate of each expert
-  int cand[kMaxExperts];     // candidate -> expert
-  int state[kMaxExperts];
-  int chosen[kMaxExperts];   // per expert: 1 if selected
-  int list[kMaxTopK];
-  float ex[kMaxTopK];
-  int n, nin;
-};
-
-// Resolve the candidates S.cand[0..S.n) for `r` remaining slots with binary64 logits
-// already in S.v/S.rad; undecided ones are summed sequentially.  Marks S.chosen.
-__device__ void resolve64(Sel64 &S, int r, const uint16_t *x, const uint16_t *w16,
-                          const float *w32, const float *bias, int H, int tid, int nthr) {
-  classify(S.v, S.rad, S.n, r, S.state, tid, nthr);
-  __syncthreads();
-  if (tid == 0) S.nin = 0;
-  __syncthreads();
-  for (int c = tid; c < S.n; c += nthr) {
-    if (S.state[c] == 1) {
-      S.chosen[S.cand[c]] = 1;
-      atomicAdd(&S.nin, 1);
-    } else if (S.state[c] == 0) {
-      const int e = S.cand[c];
-      double l = seq_dot64(x, w16 ? w16 + (size_t)e * H : nullptr, w32 ? w32 + (size_t)e * H : nullptr, H);
-      if (bias) l += (double)bias[e];
-      S.v[c] = l;  // exact canonical value
-    }
-  }
-  __syncthreads();
-  const int rr = r - S.nin;
-  for (int c = tid; c < S.n; c += nthr) {
-    if (S.state[c] != 0) continue;
-    const int e = S.cand[c];
-    int rank = 0;
-    for (int j = 0; j < S.n; ++j)
-      if (j != c && S.state[j] == 0)
-        rank += (S.v[j] > S.v[c]) || (S.v[j] == S.v[c] && S.cand[j] < e);
-    if (rank < rr) S.chosen[e] = 1;
-    S.gl[e] = S.v[c];
-  }
-  __syncthreads();
-}
-
-// Compact the chosen experts into ascending S.list and write ids/gates (softmax of S.gl
-// over them).  Experts are gathered unordered, then each of the k entries finds its
-// rank among the k.
-__device__ void emit_selection(Sel64 &S, int E, int k, int32_t *ids, float *gates, int32_t *dbg_ids,
-                               float *dbg_gates, int tid, int nthr) {
-  if (tid == 0) S.nin = 0;
-  if (tid < kMaxTopK) S.list[tid] = 0;
-  __syncthreads();
-  for (int e = tid; e < E; e += nthr)
-    if (S.chosen[e]) {
-      const int at = atomicAdd(&S.nin, 1);
-      if (at < kMaxTopK) S.cand[at] = e;
-    }
-  __syncthreads();
-  const int n = min(S.nin, k);
-  if (tid < n) {
-    const int e = S.cand[tid];
-    int pos = 0;
-    for (int j = 0; j < n; ++j) pos += S.cand[j] < e;
-    S.list[pos] = e;
-  }
-  __syncthreads();
-  if (tid < k) {  // each chosen expert's exponential once
-    double mx = -INFINITY;
-    for (int j = 0; j < k; ++j) mx = fmax(mx, S.gl[S.list[j]]);
-    S.ex[tid] = __expf((float)(S.gl[S.list[tid]] - mx));
-  }
-  __syncthreads();
-  if (tid < k) {
-    float den = 0.f;
-    for (int j = 0; j < k; ++j) den += S.ex[j];
-    const int e = S.list[tid];
-    const float g = S.ex[tid] / den;
-    ids[tid] = e;
-    gates[tid] = g;
-    if (dbg_ids) dbg_ids[tid] = e;
-    if (dbg_gates) dbg_gates[tid] = g;
-  }
-  __syncthreads();
-}
-
 // ---------------------------------------------------------------------------- prefill
 
 constexpr int kRouteThreads = 512;   // 8 waves: wave w owns experts 32w..32w+31
@@ -404,7 +242,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
       if (a.bias) l += (double)a.bias[e];
       if (lane == 0) {
         S.v[c] = l;
-        S.rad[c] = radius64(l, ab, H);
+        S.rad[c] = radius64(l, ab, H, wave_dot64_depth(H));
         S.gl[e] = l;
       }
     }
@@ -427,112 +265,11 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
   if (tid == 0 && n_ref) atomicAdd(&a.ctrl->n_refined, n_ref);
 }
 
-// ---------------------------------------------------------------------------- decode
-
-// One wave per expert computes the binary64 logit; the last workgroup to finish selects
-// the top k with one wave (k rounds of a wave arg-max), certifies the choice against the
-// binary64 error radii, and resolves uncertain experts with sequential sums.
-__global__ __launch_bounds__(64) void k_decode_route(DecodeArgs a) {
-  __shared__ Sel64 S;
-  __shared__ int s_last;
-  const int lane = threadIdx.x;
-  const int e0 = blockIdx.x, H = a.H, E = a.E, k = a.k;
-  {
-    double l, ab;
-    wave_dot64(a.x, a.wr16 ? a.wr16 + (size_t)e0 * H : nullptr, a.wr32 ? a.wr32 + (size_t)e0 * H : nullptr, H,
-               lane, l, ab);
-    if (a.bias) l += (double)a.bias[e0];
-    if (lane == 0) {
-      st_agent(&a.l64[e0], l);
-      st_agent(&a.a64[e0], radius64(l, ab, H));
-      vm_drain();
-      s_last = ticket(&a.ctrl->decode_ticket) == E - 1;
-    }
-  }
-  __syncthreads();
-  if (!s_last) return;
-  constexpr int NV = kMaxExperts / kWave;
-  double v[NV], rd[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int e = lane + kWave * i;
-    v[i] = e < E ? ld_agent(&a.l64[e]) : -INFINITY;
-    rd[i] = e < E ? ld_agent(&a.a64[e]) : 0.0;
-    if (e < E) {
-      S.gl[e] = v[i];
-      S.chosen[e] = 0;
-    }
-  }
-  uint32_t taken = 0;
-  for (int r = 0; r < k; ++r) {
-    double bv = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int e = lane + kWave * i;
-      if (e < E && !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < bi))) {
-        bv = v[i];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const double ov = __shfl_xor(bv, o);
-      const int oi = __shfl_xor(bi, o);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if (bi < E && (bi % kWave) == lane) taken |= 1u << (bi / kWave);
-  }
-  double mn = INFINITY, mx = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int e = lane + kWave * i;
-    if (e >= E) continue;
-    if ((taken >> i) & 1u)
-      mn = fmin(mn, v[i] - rd[i]);
-    else
-      mx = fmax(mx, v[i] + rd[i]);
-  }
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    mn = fmin(mn, __shfl_xor(mn, o));
-    mx = fmax(mx, __shfl_xor(mx, o));
-  }
-  if (lane == 0) S.n = 0;
-  __syncthreads();
-  int nin1 = 0;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int e = lane + kWave * i;
-    if (e >= E) continue;
-    const bool in_sel = (taken >> i) & 1u;
-    const bool sure_in = in_sel && v[i] - rd[i] > mx;
-    const bool sure_out = !in_sel && v[i] + rd[i] < mn;
-    if (sure_in) {
-      S.chosen[e] = 1;
-      ++nin1;
-    }
-    if (!sure_in && !sure_out) {
-      const int c = atomicAdd(&S.n, 1);
-      S.cand[c] = e;
-      S.v[c] = v[i];
-      S.rad[c] = rd[i];
-    }
-  }
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) nin1 += __shfl_xor(nin1, o);
-  __syncthreads();
-  if (S.n > 0) resolve64(S, k - nin1, a.x, a.wr16, a.wr32, a.bias, H, lane, kWave);
-  emit_selection(S, E, k, a.ids, a.gates, a.dbg_ids, a.dbg_gates, lane, kWave);
-  if (lane == 0) st_agent(&a.ctrl->decode_ticket, 0);
-}
-
-__global__ void k_ctrl_init(Ctrl *c) {
+__global__ void k_ctrl_init(Ctrl *c, uint32_t *clear, int n_words) {
   int *p = (int *)c;
-  for (int i = threadIdx.x; i < (int)(sizeof(Ctrl) / sizeof(int)); i += blockDim.x) p[i] = 0;
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < (int)(sizeof(Ctrl) / sizeof(int)); i += blockDim.x) p[i] = 0;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n_words; i += gridDim.x * blockDim.x) clear[i] = 0;
 }
 
 }  // namespace
@@ -543,13 +280,9 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_decode_route(const DecodeArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(k_decode_route, dim3(a.E), dim3(64), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_ctrl_init(Ctrl *c, hipStream_t s) {
-  hipLaunchKernelGGL(k_ctrl_init, dim3(1), dim3(64), 0, s, c);
+hipError_t launch_ctrl_init(Ctrl *c, void *clear, size_t clear_bytes, hipStream_t s) {
+  const int n = (int)(clear_bytes / 4);
+  hipLaunchKernelGGL(k_ctrl_init, dim3(n > 0 ? (n + 255) / 256 : 1), dim3(256), 0, s, c, (uint32_t *)clear, n);
   return hipGetLastError();
 }
 

@@ -1,0 +1,184 @@
+// Binary64 ranking shared by the prefill router and the decode kernel: exact-product
+// dot products, their error radii, and the selection of the top k experts with the
+// lowest-index tie-break when the binary64 values alone cannot order them.
+#pragma once
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr double kU64 = 1.1102230246251565404e-16;   // 2^-53
+
+// Binary64 dot product of x with one router row, by one wave.  Lane `lane` takes the
+// 8-element chunks c = lane + 64 i (ascending i) and sums its exact products
+// sequentially; a butterfly over the wave gives every lane the same total.  Also
+// returns sum |x_h w_h|.  Each product passes through at most seq + 6 roundings with
+// seq = 8*ceil(H/512).
+__device__ void wave_dot64(const uint16_t *x, const uint16_t *w16, const float *w32, int H,
+                           int lane, double &l, double &a) {
+  double s = 0.0, sa = 0.0;
+  for (int c = lane; c < H / 8; c += kWave) {
+    const uint4 xv = *(const uint4 *)(x + 8 * c);
+    float xf[8] = {bf16_lo(xv.x), bf16_hi(xv.x), bf16_lo(xv.y), bf16_hi(xv.y),
+                   bf16_lo(xv.z), bf16_hi(xv.z), bf16_lo(xv.w), bf16_hi(xv.w)};
+    float wf[8];
+    if (w16) {
+      const uint4 wv = *(const uint4 *)(w16 + 8 * c);
+      wf[0] = bf16_lo(wv.x); wf[1] = bf16_hi(wv.x); wf[2] = bf16_lo(wv.y); wf[3] = bf16_hi(wv.y);
+      wf[4] = bf16_lo(wv.z); wf[5] = bf16_hi(wv.z); wf[6] = bf16_lo(wv.w); wf[7] = bf16_hi(wv.w);
+    } else {
+      const float4 w0 = *(const float4 *)(w32 + 8 * c);
+      const float4 w1 = *(const float4 *)(w32 + 8 * c + 4);
+      wf[0] = w0.x; wf[1] = w0.y; wf[2] = w0.z; wf[3] = w0.w;
+      wf[4] = w1.x; wf[5] = w1.y; wf[6] = w1.z; wf[7] = w1.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const double p = (double)xf[i] * (double)wf[i];  // exact
+      s += p;
+      sa += fabs(p);
+    }
+  }
+  l = wave_sum_f64(s);
+  a = wave_sum_f64(sa);
+}
+
+// Error radius of a binary64 logit (plus bias) summed in any order with at most `depth`
+// additions on the path of every product, relative to the sequential ascending-h
+// binary64 sum (plus bias), whose own error to the exact value is at most H roundings of
+// sum|p|.  `a` is the computed sum |x_h w_h|.
+__device__ __forceinline__ double radius64(double lb, double a, int H, int depth) {
+  return ((double)depth + 2.0 + (double)H) * kU64 * a * 1.001 + 4.0 * kU64 * fabs(lb) + 1e-300;
+}
+
+// Additions on any path of wave_dot64's sum.
+__device__ __forceinline__ int wave_dot64_depth(int H) { return 8 * ((H + 511) / 512) + 6; }
+
+// Sequential ascending-h binary64 logit: the same arithmetic as the plain definition.
+__device__ double seq_dot64(const uint16_t *x, const uint16_t *w16, const float *w32, int H) {
+  double acc = 0.0;
+  for (int h = 0; h < H; ++h) {
+    const double w = w16 ? (double)bf16_to_f32(w16[h]) : (double)w32[h];
+    acc = __builtin_fma((double)bf16_to_f32(x[h]), w, acc);  // product exact: fma == mul+add
+  }
+  return acc;
+}
+
+// Membership in the best r of n candidates (order: value descending, index ascending)
+// from values v with error radius rad: state 1 = certainly in, 2 = certainly out,
+// 0 = undecided.  Candidate j may outrank i if v_j + rad_j >= v_i - rad_i, and
+// certainly outranks i if v_j - rad_j > v_i + rad_i.
+__device__ void classify(const double *v, const double *rad, int n, int r, int *state, int tid,
+                         int nthr) {
+  for (int i = tid; i < n; i += nthr) {
+    const double lo = v[i] - rad[i], hi = v[i] + rad[i];
+    int poss = 0, cert = 0;
+    for (int j = 0; j < n; ++j) {
+      if (j == i) continue;
+      poss += (v[j] + rad[j] >= lo);
+      cert += (v[j] - rad[j] > hi);
+    }
+    state[i] = (poss < r) ? 1 : (cert >= r ? 2 : 0);
+  }
+}
+
+// Shared per-workgroup scratch of the binary64 selection.
+struct Sel64 {
+  double v[kMaxExperts];
+  double rad[kMaxExperts];
+  double gl[kMaxExperts];    // logit used for the gate of each expert
+  int cand[kMaxExperts];     // candidate -> expert
+  int state[kMaxExperts];
+  int chosen[kMaxExperts];   // per expert: 1 if selected
+  int list[kMaxTopK];
+  float ex[kMaxTopK];
+  int n, nin;
+};
+
+// Resolve the candidates S.cand[0..S.n) for `r` remaining slots with binary64 logits
+// already in S.v/S.rad; undecided ones are summed sequentially.  Marks S.chosen.
+__device__ void resolve64(Sel64 &S, int r, const uint16_t *x, const uint16_t *w16,
+                          const float *w32, const float *bias, int H, int tid, int nthr) {
+  classify(S.v, S.rad, S.n, r, S.state, tid, nthr);
+  __syncthreads();
+  if (tid == 0) S.nin = 0;
+  __syncthreads();
+  for (int c = tid; c < S.n; c += nthr) {
+    if (S.state[c] == 1) {
+      S.chosen[S.cand[c]] = 1;
+      atomicAdd(&S.nin, 1);
+    } else if (S.state[c] == 0) {
+      const int e = S.cand[c];
+      double l = seq_dot64(x, w16 ? w16 + (size_t)e * H : nullptr, w32 ? w32 + (size_t)e * H : nullptr, H);
+      if (bias) l += (double)bias[e];
+      S.v[c] = l;  // exact canonical value
+    }
+  }
+  __syncthreads();
+  const int rr = r - S.nin;
+  for (int c = tid; c < S.n; c += nthr) {
+    if (S.state[c] != 0) continue;
+    const int e = S.cand[c];
+    int rank = 0;
+    for (int j = 0; j < S.n; ++j)
+      if (j != c && S.state[j] == 0)
+        rank += (S.v[j] > S.v[c]) || (S.v[j] == S.v[c] && S.cand[j] < e);
+    if (rank < rr) S.chosen[e] = 1;
+    S.gl[e] = S.v[c];
+  }
+  __syncthreads();
+}
+
+// Compact the chosen experts into ascending S.list and write ids/gates (softmax of S.gl
+// over them; AGENT: with device-coherent stores).  Experts are gathered unordered, then
+// each of the k entries finds its rank among the k.
+template <bool AGENT = false>
+__device__ void emit_selection(Sel64 &S, int E, int k, int32_t *ids, float *gates, int32_t *dbg_ids,
+                               float *dbg_gates, int tid, int nthr) {
+  if (tid == 0) S.nin = 0;
+  if (tid < kMaxTopK) S.list[tid] = 0;
+  __syncthreads();
+  for (int e = tid; e < E; e += nthr)
+    if (S.chosen[e]) {
+      const int at = atomicAdd(&S.nin, 1);
+      if (at < kMaxTopK) S.cand[at] = e;
+    }
+  __syncthreads();
+  const int n = min(S.nin, k);
+  if (tid < n) {
+    const int e = S.cand[tid];
+    int pos = 0;
+    for (int j = 0; j < n; ++j) pos += S.cand[j] < e;
+    S.list[pos] = e;
+  }
+  __syncthreads();
+  if (tid < k) {  // each chosen expert's exponential once
+    double mx = -INFINITY;
+    for (int j = 0; j < k; ++j) mx = fmax(mx, S.gl[S.list[j]]);
+    S.ex[tid] = __expf((float)(S.gl[S.list[tid]] - mx));
+  }
+  __syncthreads();
+  if (tid < k) {
+    float den = 0.f;
+    for (int j = 0; j < k; ++j) den += S.ex[j];
+    const int e = S.list[tid];
+    const float g = S.ex[tid] / den;
+    if (AGENT) {  // read by other workgroups of the same launch
+      st_agent(&ids[tid], e);
+      st_agent(&gates[tid], g);
+    } else {
+      ids[tid] = e;
+      gates[tid] = g;
+    }
+    if (dbg_ids) dbg_ids[tid] = e;
+    if (dbg_gates) dbg_gates[tid] = g;
+  }
+  __syncthreads();
+}
+
+}  // namespace
+
+}  // namespace moe

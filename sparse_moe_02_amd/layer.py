@@ -110,6 +110,13 @@ class MoeLayer:
                              self.stream(), dbg)
         return (out, d) if debug else out
 
+    def decode_error(self) -> int:
+        """The decode kernel's wait-failure word (0 = every call so far completed its
+        internal hand-offs); synchronises the device."""
+        torch.cuda.synchronize()
+        o = B.CTRL_DECODE_ERR_OFFSET
+        return int(self.ws[o:o + 4].cpu().view(torch.int32).item())
+
 
 def bf16_tensor(bits: np.ndarray, device) -> torch.Tensor:
     """bf16 bit patterns (uint16 numpy) -> bf16 device tensor."""

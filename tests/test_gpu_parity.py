@@ -64,6 +64,7 @@ def test_tiny_decode_each_token():
         assert np.max(np.abs(d["gates"].cpu().numpy()[0] - ref["gates"][t])) <= 2e-5
         got = to_f64(bf16_bits(out))
         assert rel_err(got[None], ref["out"][t][None]) <= TOL
+    assert layer.decode_error() == 0
     layer.close()
 
 
@@ -105,10 +106,38 @@ def test_decode_40_layers():
         e = rel_err(to_f64(bf16_bits(out))[None], ref)
         worst = max(worst, e)
         assert e <= TOL, f"layer {layer_i}: output error {e}"
+        assert m.decode_error() == 0
         m.close()
         del m
         if layer_i % 8 == 7:
             say(f"[decode] layers 0..{layer_i} ok, worst max-abs-rel {worst:.3e}")
+
+
+def test_decode_back_to_back_same_workspace():
+    """Many decode calls on one workspace with no host sync in between (the launch
+    re-arms its own hand-off counters): every output bitwise equal, in tolerance, and
+    no wait ran out of polls."""
+    import torch
+
+    from sparse_moe_02_amd.layer import MoeLayer, bf16_bits, bf16_tensor
+
+    L = synth.make_layer(1, 3)
+    xs = [synth.make_x(1, 3)[0], synth.make_x(1, 4)[0]]
+    refs = []
+    for x in xs:
+        r = oracle.route(x[None], L.router_w, None, 8)
+        refs.append(oracle.experts(x[None], L, r["ids"], r["gates"]))
+    m = MoeLayer(L, top_k=8, max_chunk_tokens=1)
+    xd = [bf16_tensor(x, "cuda:0") for x in xs]
+    outs = [m.decode(xd[i % 2]) for i in range(40)]
+    torch.cuda.synchronize()
+    got = [bf16_bits(o) for o in outs]
+    for i in range(40):
+        assert np.array_equal(got[i], got[i % 2]), f"call {i} differs from call {i % 2}"
+    for i in range(2):
+        assert rel_err(to_f64(got[i])[None], refs[i]) <= TOL
+    assert m.decode_error() == 0
+    m.close()
 
 
 def test_long_prompt_128k_chunked():
