@@ -53,6 +53,43 @@ __device__ __forceinline__ void dequant8_bf16(uint32_t w, float s, float b, uint
   }
 }
 
+// ---------------------------------------------------------------- direct-to-LDS loads
+
+// 16 bytes per lane from gbase + voff into LDS: lane i's bytes land at lds + 16 i (lds is
+// wave-uniform).  Issued from inline asm so the compiler neither waits for it nor orders
+// LDS reads behind it on its own: the caller counts its loads, waits with vm_wait_dyn and
+// publishes the data with a barrier.
+__device__ __forceinline__ void dma16(const void *gbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n" ::"s"(
+                   __builtin_amdgcn_readfirstlane(lds)),
+               "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0xF70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// s_waitcnt vmcnt(m) for the largest m <= n of a small ladder (n: loads that may stay in
+// flight; a smaller count only waits longer).
+__device__ __forceinline__ void vm_wait_dyn(int n) {
+  if (n >= 16) {
+    if (n >= 32) vm_wait_n<32>(); else if (n >= 24) vm_wait_n<24>(); else vm_wait_n<16>();
+  } else if (n >= 8) {
+    if (n >= 12) vm_wait_n<12>(); else if (n >= 10) vm_wait_n<10>(); else vm_wait_n<8>();
+  } else if (n >= 4) {
+    if (n >= 6) { if (n >= 7) vm_wait_n<7>(); else vm_wait_n<6>(); } else { if (n >= 5) vm_wait_n<5>(); else vm_wait_n<4>(); }
+  } else {
+    if (n >= 2) { if (n >= 3) vm_wait_n<3>(); else vm_wait_n<2>(); } else { if (n >= 1) vm_wait_n<1>(); else vm_wait_n<0>(); }
+  }
+}
+
 // ---------------------------------------------------------------- wave reductions
 
 template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf, bool BOUND = false>

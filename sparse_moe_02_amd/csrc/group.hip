@@ -53,10 +53,21 @@ __global__ __launch_bounds__(kThreads) void k_group(GroupArgs a) {
     const int e = tid % kMaxExperts, part = tid / kMaxExperts;
     int tot = 0, pre = 0;
     if (e < E) {
-      for (int b = part; b < nblk; b += kParts) {
-        const int c = __popc(mask[(size_t)b * E + e]);
-        tot += c;
-        pre += b < sb0 ? c : 0;
+      // batches of kBatch independent loads in flight per thread
+      constexpr int kBatch = 16;
+      for (int b0 = part; b0 < nblk; b0 += kParts * kBatch) {
+        uint32_t mv[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+          const int b = b0 + kParts * i;
+          mv[i] = b < nblk ? mask[(size_t)b * E + e] : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+          const int c = __popc(mv[i]);
+          tot += c;
+          pre += b0 + kParts * i < sb0 ? c : 0;
+        }
       }
     }
     s_tot[part][e] = tot;

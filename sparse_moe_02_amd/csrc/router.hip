@@ -7,8 +7,8 @@
 // Prefill: one workgroup per 32 tokens.  Logits and the bound sum_h |x_h w_eh| come
 // from two bf16 MFMA chains with fp32 accumulation (bf16 x bf16 products are exact in
 // fp32).  A token's fp32 ranking is certified when every chosen logit minus its error
-// radius exceeds every other logit plus its radius; otherwise the token is re-ranked:
-// undecided experts get binary64 logits (wave-parallel), and experts that even these
+// radius exceeds every other logit plus its radius; otherwise one wave re-ranks it:
+// undecided experts get binary64 logits (wave-parallel sums), and experts that even these
 // cannot order are summed sequentially in ascending h in binary64, which reproduces the
 // exact-product sequential sum bit for bit.
 #include "common.hpp"
@@ -23,21 +23,46 @@ constexpr float kU32 = 5.9604644775390625e-8f;       // 2^-24
 // ---------------------------------------------------------------------------- prefill
 
 constexpr int kRouteThreads = 512;   // 8 waves: wave w owns experts 32w..32w+31
-constexpr int kKC = 256;             // k per staged chunk of x
-constexpr int kXRow = kKC * 2;       // bytes per staged row (32 slots of 16 B)
+constexpr int kKC = 64;              // k per chunk (one LDS stage)
+constexpr int kKP = 128;             // k per fresh fp32 partial sum (two chunks)
+constexpr int kRStages = 4;          // chunks in flight
+constexpr int kXStage = kRouteTokens * kKC * 2;           // 4 KiB: 32 token rows
+constexpr int kWStage = kMaxExperts * kKC * 2;            // 32 KiB: 256 router rows
+constexpr int kStage = kXStage + kWStage;
 
-// swizzled position of 16-byte slot `slot` of staged row `r`
-__device__ __forceinline__ int xoff(int r, int slot) { return r * kXRow + ((slot ^ (r & 15)) << 4); }
+// 16-byte piece `c` (0..7) of staged 128-byte row r: swizzled so that the MFMA operand
+// reads (16 rows, same piece) hit distinct banks
+__device__ __forceinline__ int roff(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
+struct RouteSmem {
+  union {
+    uint8_t stage[kRStages][kStage];  // logits phase
+    struct {                          // selection and re-ranking phase
+      float l[kRouteTokens][kMaxExperts];  // fp32 logit (+bias)
+      float r[kRouteTokens][kMaxExperts];  // its error radius
+      WaveSel ws[kRouteThreads / kWave];
+    } sel;
+  };
+};
+
+// One workgroup per 32 tokens.
+//  1. logits: for each 64-k chunk, the 32 token rows and all router rows go global ->
+//     LDS with direct-to-LDS loads (8 rows x 128 bytes per instruction), four chunks in
+//     flight; wave w multiplies its 32 experts with the 32 tokens.  Each 128-k partial is
+//     a fresh MFMA chain added to the running fp32 total, so a product passes through at
+//     most kKP/16 + 15 roundings in its partial and H/kKP in the total.  A second MFMA
+//     chain over sign-cleared operands gives sum |x w| for the error radius.
+//  2. fp32 selection, sixteen lanes per token, certified against the radii.
+//  3. tokens the certificate does not settle are re-ranked by one wave each, in parallel.
 __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
-  __shared__ float s_l[kRouteTokens][kMaxExperts];   // fp32 logit (+bias)
-  __shared__ float s_r[kRouteTokens][kMaxExperts];   // its error radius
-  __shared__ __attribute__((aligned(16))) uint8_t s_x[2][kRouteTokens * kXRow];
-  __shared__ int s_sel[kRouteTokens][kMaxTopK];      // chosen experts (rank order)
+  __shared__ __attribute__((aligned(16))) RouteSmem sm;
+  __shared__ int s_sel[kRouteTokens][kMaxTopK];      // chosen experts
   __shared__ float s_min_in[kRouteTokens], s_max_out[kRouteTokens];
-  __shared__ int s_flag[kRouteTokens];
+  __shared__ int s_list[kRouteTokens];
+  __shared__ int s_nflag;
   __shared__ uint32_t s_mask[kMaxExperts];
-  __shared__ Sel64 S;
+  auto &s_l = sm.sel.l;
+  auto &s_r = sm.sel.r;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = a.H, E = a.E, k = a.k;
@@ -45,77 +70,77 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
   const int nt = min(kRouteTokens, a.T - t0);
 
   for (int e = tid; e < kMaxExperts; e += kRouteThreads) s_mask[e] = 0;
-  if (tid < kRouteTokens) s_flag[tid] = 0;
+  if (tid == 0) s_nflag = 0;
 
   if (a.wr16) {
     const int m = lane & 31, hf = lane >> 5;
     const int nct = (E + 31) / 32;
     const bool active = wv < nct;
-    const uint16_t *wrow = a.wr16 + (size_t)min(wv * 32 + m, E - 1) * H + 8 * hf;
-    // x chunk loader: wave-load j fills staged rows 2j, 2j+1; lane L -> row 2j+L/32,
-    // physical slot L%32 holding logical slot (L%32) ^ (row & 15)
-    const int xr0 = 2 * wv + (lane >> 5), xr1 = xr0 + 16;
-    const uint16_t *xg0 = a.x + (size_t)(t0 + min(xr0, nt - 1)) * H + 8 * ((lane & 31) ^ (xr0 & 15));
-    const uint16_t *xg1 = a.x + (size_t)(t0 + min(xr1, nt - 1)) * H + 8 * ((lane & 31) ^ (xr1 & 15));
-    auto load_x = [&](int c, int buf) {
-      __builtin_amdgcn_global_load_lds((const void *)(xg0 + c * kKC),
-                                       (__attribute__((address_space(3))) void *)(s_x[buf] + wv * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void *)(xg1 + c * kKC),
-                                       (__attribute__((address_space(3))) void *)(s_x[buf] + (wv + 8) * 1024), 16, 0,
-                                       0);
-    };
-    u32x4 w0[kKC / 16], w1[kKC / 16];
-    auto load_w = [&](int c, u32x4(&dst)[kKC / 16]) {
+    // loads of one chunk: waves 0..3 each bring 8 token rows, every wave brings its own
+    // 32 router rows (4 instructions of 8 rows); lane L -> row base + L/8, physical piece
+    // L%8 holding logical piece (L%8) ^ f(row)
+    const int xr = 8 * wv + (lane >> 3);
+    const uint32_t xoff0 =
+        (uint32_t)(t0 + min(xr, nt - 1)) * (uint32_t)H * 2u + 16u * (uint32_t)((lane & 7) ^ ((xr >> 1) & 7));
+    uint32_t woff0[4];
 #pragma unroll
-      for (int s2 = 0; s2 < kKC / 16; ++s2) dst[s2] = *(const u32x4 *)(wrow + c * kKC + 16 * s2);
+    for (int u = 0; u < 4; ++u) {
+      const int e = 32 * wv + 8 * u + (lane >> 3);
+      woff0[u] = (uint32_t)min(e, E - 1) * (uint32_t)H * 2u + 16u * (uint32_t)((lane & 7) ^ ((e >> 1) & 7));
+    }
+    const int per_chunk = 4 + (wv < 4 ? 1 : 0);
+    auto issue = [&](int c, int st) {
+      const uint32_t base = lds_addr(&sm.stage[st][0]);
+      if (wv < 4) dma16(a.x, xoff0 + 128u * (uint32_t)c, base + (uint32_t)wv * 1024u);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        dma16(a.wr16, woff0[u] + 128u * (uint32_t)c, base + (uint32_t)kXStage + (uint32_t)(4 * wv + u) * 1024u);
     };
     const int nch = H / kKC;
-    f32x16 acc = {}, aab = {};
+    f32x16 tot = {}, acc = {}, aab = {};
     const u32x4 msk = {0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu};
-    auto compute = [&](int buf, const u32x4(&wb)[kKC / 16]) {
+    auto compute = [&](int c, int st) {
+      const uint8_t *xs = &sm.stage[st][0];
+      const uint8_t *ws = xs + kXStage;
+      if ((c & 1) == 0) acc = (f32x16){};
 #pragma unroll
-      for (int s2 = 0; s2 < kKC / 16; ++s2) {
-        const u32x4 av = *(const u32x4 *)(s_x[buf] + xoff(m, 2 * s2 + hf));
-        const u32x4 bv = wb[s2];
+      for (int j = 0; j < kKC / 16; ++j) {
+        const u32x4 av = *(const u32x4 *)(xs + roff(m, 2 * j + hf));
+        const u32x4 bv = *(const u32x4 *)(ws + roff(32 * wv + m, 2 * j + hf));
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv),
                                                       acc, 0, 0, 0);
         aab = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, (u32x4)(av & msk)),
                                                       __builtin_bit_cast(bf16x8, (u32x4)(bv & msk)), aab, 0, 0, 0);
       }
+      if (c & 1) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) tot[j] += acc[j];
+      }
     };
-    // two-stage pipeline: chunk c+1 (x into LDS, router rows into registers) is in
-    // flight while chunk c is multiplied
-    load_x(0, 0);
-    if (active) load_w(0, w0);
-    for (int c = 0; c < nch; c += 2) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (c + 1 < nch) {
-        load_x(c + 1, 1);
-        if (active) load_w(c + 1, w1);
-      }
-      if (active) compute(0, w0);
-      if (c + 1 >= nch) break;
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (c + 2 < nch) {
-        load_x(c + 2, 0);
-        if (active) load_w(c + 2, w0);
-      }
-      if (active) compute(1, w1);
+    // prologue: chunks 0..kRStages-2 in flight
+    for (int c = 0; c < kRStages - 1 && c < nch; ++c) issue(c, c);
+    for (int c = 0; c < nch; ++c) {
+      const int st = c % kRStages;
+      // chunk c's loads are complete once only the later chunks' loads remain
+      vm_wait_dyn(per_chunk * min(kRStages - 2, nch - 1 - c));
+      __syncthreads();  // chunk c visible to every wave; chunk c-1's stage is free
+      if (c + kRStages - 1 < nch) issue(c + kRStages - 1, (c + kRStages - 1) % kRStages);
+      if (active) compute(c, st);
     }
+    __syncthreads();  // every wave is past its last stage read before the logits reuse it
     if (active) {
-      // fp32 error of an MFMA chain of H/16 steps of 16 exact products: at most
-      // (H/16 + 15) roundings of sum|p|; doubled for margin, plus the bias addition,
-      // the sequential binary64 reference's own error and product underflow.
-      const float c32 = 2.0f * (float)(H / 16 + 16) + 4.0f;
+      // Error radius of the fp32 logit: a product passes through at most kKP/16 + 15
+      // roundings in its partial's MFMA chain and H/kKP in the running total; doubled
+      // for margin, plus the bias addition, the sequential binary64 reference's own
+      // error and product underflow.
+      const float c32 = 2.0f * (float)(kKP / 16 + 15 + H / kKP) + 4.0f;
       const int e = wv * 32 + m;
       if (e < E) {
         const float bb = a.bias ? a.bias[e] : 0.0f;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int row = 8 * (j >> 2) + 4 * hf + (j & 3);
-          const float l = acc[j] + bb;
+          const float l = tot[j] + bb;
           s_l[row][e] = l;
           s_r[row][e] = c32 * kU32 * aab[j] * 1.01f + 2.0f * kU32 * fabsf(l) + 1e-12f * aab[j] + 1e-30f;
         }
@@ -203,57 +228,39 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
         if (a.dbg_gates) a.dbg_gates[o] = gt;
       }
     } else if (m < nt && q == 0) {
-      s_flag[m] = 1;
+      s_list[atomicAdd(&s_nflag, 1)] = m;
     }
   }
   __syncthreads();
 
-  // re-ranking of the tokens the fp32 certificate did not settle.  With S~ the fp32
-  // top-k, lo = min over S~ of (l - r) and hi = max outside of (l + r): a chosen expert
-  // with l - r > hi is in for sure, an outside one with l + r < lo is out for sure; the
-  // rest get binary64 logits and are resolved in resolve64.
-  int n_ref = 0;
-  for (int m = 0; m < nt; ++m) {
-    if (!s_flag[m]) continue;
-    ++n_ref;
-    const uint16_t *xrow = a.x + (size_t)(t0 + m) * H;
-    const float lo = s_min_in[m], hi = s_max_out[m];
-    if (tid == 0) S.n = 0;
-    __syncthreads();
-    for (int e = tid; e < E; e += kRouteThreads) {
-      S.gl[e] = s_l[m][e];
-      S.chosen[e] = 0;
-      bool in_sel = false;
-      for (int j = 0; j < k; ++j) in_sel |= s_sel[m][j] == e;
-      const float L = s_l[m][e] - s_r[m][e], U = s_l[m][e] + s_r[m][e];
-      const bool sure_in = a.wr16 && in_sel && L > hi;
-      const bool sure_out = a.wr16 && !in_sel && U < lo;
-      if (sure_in) S.chosen[e] = 1;
-      if (!sure_in && !sure_out) S.cand[atomicAdd(&S.n, 1)] = e;
+  // Re-ranking of the tokens the fp32 certificate did not settle, one wave per token.
+  // With S~ the fp32 top-k, lo = min over S~ of (l - r) and hi = max outside of (l + r):
+  // a chosen expert with l - r > hi is in for sure, an outside one with l + r < lo is
+  // out for sure; the rest are candidates for rerank_wave.
+  const int nflag = s_nflag;
+  if (nflag) {
+    WaveSel &W = sm.sel.ws[wv];
+    for (int f = wv; f < nflag; f += kRouteThreads / kWave) {
+      const int m = s_list[f];
+      const float lo = s_min_in[m], hi = s_max_out[m];
+      const bool fp32_ok = a.wr16 != nullptr;
+      auto in_sel = [&](int e) {
+        bool r = false;
+        for (int j = 0; j < k; ++j) r |= s_sel[m][j] == e;
+        return r;
+      };
+      auto known_in = [&](int e) { return fp32_ok && in_sel(e) && s_l[m][e] - s_r[m][e] > hi; };
+      auto known_out = [&](int e) { return fp32_ok && !in_sel(e) && s_l[m][e] + s_r[m][e] < lo; };
+      auto l32 = [&](int e) { return s_l[m][e]; };
+      const size_t o = (size_t)(t0 + m) * k;
+      rerank_wave(W, known_in, known_out, l32, E, k, a.x + (size_t)(t0 + m) * H, a.wr16, a.wr32, a.bias, H, lane,
+                  a.ids + o, a.gates + o, a.dbg_ids ? a.dbg_ids + o : nullptr,
+                  a.dbg_gates ? a.dbg_gates + o : nullptr);
+      if (lane < k) s_sel[m][lane] = W.in_ids[lane];
+      wave_sync();
     }
-    __syncthreads();
-    int nin1 = 0;
-    for (int j = 0; j < k; ++j) nin1 += S.chosen[s_sel[m][j]];
-    for (int c = wv; c < S.n; c += kRouteThreads / kWave) {
-      const int e = S.cand[c];
-      double l, ab;
-      wave_dot64(xrow, a.wr16 ? a.wr16 + (size_t)e * H : nullptr, a.wr32 ? a.wr32 + (size_t)e * H : nullptr, H,
-                 lane, l, ab);
-      if (a.bias) l += (double)a.bias[e];
-      if (lane == 0) {
-        S.v[c] = l;
-        S.rad[c] = radius64(l, ab, H, wave_dot64_depth(H));
-        S.gl[e] = l;
-      }
-    }
-    __syncthreads();
-    resolve64(S, k - nin1, xrow, a.wr16, a.wr32, a.bias, H, tid, kRouteThreads);
-    emit_selection(S, E, k, a.ids + (size_t)(t0 + m) * k, a.gates + (size_t)(t0 + m) * k,
-                   a.dbg_ids ? a.dbg_ids + (size_t)(t0 + m) * k : nullptr,
-                   a.dbg_gates ? a.dbg_gates + (size_t)(t0 + m) * k : nullptr, tid, kRouteThreads);
-    if (tid < k) s_sel[m][tid] = S.list[tid];
-    __syncthreads();
   }
+  __syncthreads();
 
   // per-expert bit masks of this workgroup's tokens (histogram / rank source)
   for (int i = tid; i < nt * k; i += kRouteThreads) {
@@ -262,7 +269,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
   }
   __syncthreads();
   for (int e = tid; e < E; e += kRouteThreads) a.tokmask[(size_t)blockIdx.x * E + e] = s_mask[e];
-  if (tid == 0 && n_ref) atomicAdd(&a.ctrl->n_refined, n_ref);
+  if (tid == 0 && nflag) atomicAdd(&a.ctrl->n_refined, nflag);
 }
 
 __global__ void k_ctrl_init(Ctrl *c, uint32_t *clear, int n_words) {

@@ -182,3 +182,157 @@ __device__ void emit_selection(Sel64 &S, int E, int k, int32_t *ids, float *gate
 }  // namespace
 
 }  // namespace moe
+
+namespace moe {
+
+namespace {
+
+// ------------------------------------------------------------------ wave-level re-ranking
+
+// Scratch of one wave's re-ranking of one token (candidates in first-seen order).
+struct WaveSel {
+  double v[kMaxExperts];   // binary64 logit (+ bias) of candidate c
+  float rad[kMaxExperts];  // its radius (rounded up to fp32)
+  int16_t cand[kMaxExperts];  // candidate -> expert
+  uint8_t state[kMaxExperts];  // 1 in, 2 out, 0 undecided
+  int in_ids[kMaxTopK];        // chosen experts (any order)
+  float in_l[kMaxTopK];    // the logit each chosen expert's gate uses
+  int n_in;
+};
+
+// Orders this wave's LDS accesses before and after (lanes of one wave read each other's
+// LDS writes).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ int lane_rank(unsigned long long mask, int lane) {
+  return __popcll(mask & ((1ull << lane) - 1ull));
+}
+
+// Re-rank one token with one wave.  `known_in(e)` / `known_out(e)` classify experts that
+// the fp32 certificate already settles; every other expert is a candidate and gets a
+// binary64 logit; candidates the binary64 radii cannot order are summed sequentially in
+// ascending h (the plain definition's arithmetic, bit for bit).  Writes ids (ascending)
+// and softmax gates, and returns the chosen ids (ascending) in W.in_ids[0..k).
+template <class KnownIn, class KnownOut, class Fp32Logit>
+__device__ void rerank_wave(WaveSel &W, KnownIn known_in, KnownOut known_out, Fp32Logit l32, int E, int k,
+                            const uint16_t *xrow, const uint16_t *wr16, const float *wr32, const float *bias, int H,
+                            int lane, int32_t *ids, float *gates, int32_t *dbg_ids, float *dbg_gates) {
+  // 1. settled-in experts and the candidate list
+  int n_in = 0, n_c = 0;
+  for (int e0 = 0; e0 < E; e0 += kWave) {
+    const int e = e0 + lane;
+    const bool valid = e < E;
+    const bool in = valid && known_in(e);
+    const bool cand = valid && !in && !known_out(e);
+    const unsigned long long bi = __ballot(in), bc = __ballot(cand);
+    if (in) {
+      const int p = n_in + lane_rank(bi, lane);
+      if (p < kMaxTopK) {
+        W.in_ids[p] = e;
+        W.in_l[p] = l32(e);
+      }
+    }
+    if (cand) W.cand[n_c + lane_rank(bc, lane)] = (int16_t)e;
+    n_in += __popcll(bi);
+    n_c += __popcll(bc);
+  }
+  n_in = min(n_in, k);
+  // 2. binary64 logits of the candidates, one wave-wide dot product each
+  for (int c = 0; c < n_c; ++c) {
+    const int e = W.cand[c];
+    double l, ab;
+    wave_dot64(xrow, wr16 ? wr16 + (size_t)e * H : nullptr, wr32 ? wr32 + (size_t)e * H : nullptr, H, lane, l, ab);
+    if (bias) l += (double)bias[e];
+    if (lane == 0) {
+      W.v[c] = l;
+      W.rad[c] = __double2float_ru(radius64(l, ab, H, wave_dot64_depth(H)));
+    }
+  }
+  wave_sync();
+  // 3. membership among the candidates for the r remaining places
+  const int r = k - n_in;
+  for (int i = lane; i < n_c; i += kWave) {
+    const double lo = W.v[i] - W.rad[i], hi = W.v[i] + W.rad[i];
+    int poss = 0, cert = 0;
+    for (int j = 0; j < n_c; ++j) {
+      if (j == i) continue;
+      poss += (W.v[j] + W.rad[j] >= lo);
+      cert += (W.v[j] - W.rad[j] > hi);
+    }
+    W.state[i] = (uint8_t)((poss < r) ? 1 : (cert >= r ? 2 : 0));
+  }
+  wave_sync();
+  // undecided candidates: exact canonical value, one lane each
+  int n_cin = 0;
+  for (int i0 = 0; i0 < n_c; i0 += kWave) {
+    const int i = i0 + lane;
+    const bool und = i < n_c && W.state[i] == 0;
+    if (und) {
+      const int e = W.cand[i];
+      double l = seq_dot64(xrow, wr16 ? wr16 + (size_t)e * H : nullptr, wr32 ? wr32 + (size_t)e * H : nullptr, H);
+      if (bias) l += (double)bias[e];
+      W.v[i] = l;
+    }
+    n_cin += __popcll(__ballot(i < n_c && W.state[i] == 1));
+  }
+  wave_sync();
+  const int rr = r - n_cin;  // places left for the undecided ones
+  for (int i0 = 0; i0 < n_c; i0 += kWave) {
+    const int i = i0 + lane;
+    bool take = false;
+    if (i < n_c) {
+      if (W.state[i] == 1) {
+        take = true;
+      } else if (W.state[i] == 0) {
+        int rank = 0;
+        for (int j = 0; j < n_c; ++j)
+          if (j != i && W.state[j] == 0) rank += (W.v[j] > W.v[i]) || (W.v[j] == W.v[i] && W.cand[j] < W.cand[i]);
+        take = rank < rr;
+      }
+    }
+    const unsigned long long bt = __ballot(take);
+    if (take) {
+      const int p = n_in + lane_rank(bt, lane);
+      if (p < kMaxTopK) {
+        W.in_ids[p] = W.cand[i];
+        W.in_l[p] = (float)W.v[i];
+      }
+    }
+    n_in += __popcll(bt);
+  }
+  wave_sync();
+  // 4. ascending ids and softmax gates
+  const int n = min(n_in, k);
+  int my_e = 0x7fffffff;
+  float my_l = -INFINITY;
+  if (lane < n) {
+    my_e = W.in_ids[lane];
+    my_l = W.in_l[lane];
+  }
+  float mx = my_l;
+#pragma unroll
+  for (int o = 1; o < kMaxTopK; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  const float ex = lane < n ? __expf(my_l - mx) : 0.f;
+  float den = ex;
+#pragma unroll
+  for (int o = 1; o < kMaxTopK; o <<= 1) den += __shfl_xor(den, o);
+  int pos = 0;
+  for (int j = 0; j < n; ++j) pos += __shfl(my_e, j) < my_e;
+  wave_sync();
+  if (lane < n) {
+    const float g = ex / den;
+    ids[pos] = my_e;
+    gates[pos] = g;
+    if (dbg_ids) dbg_ids[pos] = my_e;
+    if (dbg_gates) dbg_gates[pos] = g;
+    W.in_ids[pos] = my_e;
+  }
+  wave_sync();
+}
+
+}  // namespace
+
+}  // namespace moe
