@@ -106,6 +106,15 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// Maximum over the 16 lanes of each DPP row, broadcast to the row.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x124>(v));
+  v = fmaxf(v, dpp_f<0x128>(v));
+  return v;
+}
+
 // Sum over the whole wave, result broadcast to every lane.
 __device__ __forceinline__ float wave_sum(float v) {
   v = row16_sum(v);

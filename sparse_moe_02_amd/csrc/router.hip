@@ -11,6 +11,8 @@
 // undecided experts get binary64 logits (wave-parallel sums), and experts that even these
 // cannot order are summed sequentially in ascending h in binary64, which reproduces the
 // exact-product sequential sum bit for bit.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "select64.hpp"
@@ -25,10 +27,10 @@ constexpr float kU32 = 5.9604644775390625e-8f;       // 2^-24
 constexpr int kRouteThreads = 512;   // 8 waves: wave w owns experts 32w..32w+31
 constexpr int kKC = 64;              // k per chunk (one LDS stage)
 constexpr int kKP = 128;             // k per fresh fp32 partial sum (two chunks)
-constexpr int kRStages = 4;          // chunks in flight
+constexpr int kWStages = 3;          // router-row chunks in LDS (two loaded ahead: they hit L2)
+constexpr int kXStages = 12;         // token-row chunks in LDS (eleven ahead: they come from HBM)
 constexpr int kXStage = kRouteTokens * kKC * 2;           // 4 KiB: 32 token rows
 constexpr int kWStage = kMaxExperts * kKC * 2;            // 32 KiB: 256 router rows
-constexpr int kStage = kXStage + kWStage;
 
 // 16-byte piece `c` (0..7) of staged 128-byte row r: swizzled so that the MFMA operand
 // reads (16 rows, same piece) hit distinct banks
@@ -36,7 +38,10 @@ __device__ __forceinline__ int roff(int r, int c) { return r * 128 + ((c ^ ((r >
 
 struct RouteSmem {
   union {
-    uint8_t stage[kRStages][kStage];  // logits phase
+    struct {                          // logits phase
+      uint8_t w[kWStages][kWStage];
+      uint8_t x[kXStages][kXStage];
+    } st;
     struct {                          // selection and re-ranking phase
       float l[kRouteTokens][kMaxExperts];  // fp32 logit (+bias)
       float r[kRouteTokens][kMaxExperts];  // its error radius
@@ -47,8 +52,9 @@ struct RouteSmem {
 
 // One workgroup per 32 tokens.
 //  1. logits: for each 64-k chunk, the 32 token rows and all router rows go global ->
-//     LDS with direct-to-LDS loads (8 rows x 128 bytes per instruction), four chunks in
-//     flight; wave w multiplies its 32 experts with the 32 tokens.  Each 128-k partial is
+//     LDS with direct-to-LDS loads (8 rows x 128 bytes per instruction); token rows are
+//     loaded eleven chunks ahead, router rows (shared by every workgroup, so L2 hits)
+//     two ahead; wave w multiplies its 32 experts with the 32 tokens.  Each 128-k partial is
 //     a fresh MFMA chain added to the running fp32 total, so a product passes through at
 //     most kKP/16 + 15 roundings in its partial and H/kKP in the total.  A second MFMA
 //     chain over sign-cleared operands gives sum |x w| for the error radius.
@@ -88,44 +94,66 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
       const int e = 32 * wv + 8 * u + (lane >> 3);
       woff0[u] = (uint32_t)min(e, E - 1) * (uint32_t)H * 2u + 16u * (uint32_t)((lane & 7) ^ ((e >> 1) & 7));
     }
-    const int per_chunk = 4 + (wv < 4 ? 1 : 0);
-    auto issue = [&](int c, int st) {
-      const uint32_t base = lds_addr(&sm.stage[st][0]);
-      if (wv < 4) dma16(a.x, xoff0 + 128u * (uint32_t)c, base + (uint32_t)wv * 1024u);
+    auto issue_x = [&](int c) {
+      if (wv < 4) dma16(a.x, xoff0 + 128u * (uint32_t)c, lds_addr(&sm.st.x[c % kXStages][0]) + (uint32_t)wv * 1024u);
+    };
+    auto issue_w = [&](int c) {
+      const uint32_t base = lds_addr(&sm.st.w[c % kWStages][0]);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        dma16(a.wr16, woff0[u] + 128u * (uint32_t)c, base + (uint32_t)kXStage + (uint32_t)(4 * wv + u) * 1024u);
+      for (int u = 0; u < 4; ++u) dma16(a.wr16, woff0[u] + 128u * (uint32_t)c, base + (uint32_t)(4 * wv + u) * 1024u);
     };
     const int nch = H / kKC;
     f32x16 tot = {}, acc = {}, aab = {};
     const u32x4 msk = {0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu};
-    auto compute = [&](int c, int st) {
-      const uint8_t *xs = &sm.stage[st][0];
-      const uint8_t *ws = xs + kXStage;
-      if ((c & 1) == 0) acc = (f32x16){};
+    f32x16 acc1 = {}, aab1 = {};
+    auto compute = [&](int c) {
+      const uint8_t *xs = &sm.st.x[c % kXStages][0];
+      const uint8_t *ws = &sm.st.w[c % kWStages][0];
+      if ((c & 1) == 0) {
+        acc = (f32x16){};
+        acc1 = (f32x16){};
+      }
+      // all four slices' fragments first, then two independent chains per quantity
+      u32x4 av[kKC / 16], bv[kKC / 16];
 #pragma unroll
       for (int j = 0; j < kKC / 16; ++j) {
-        const u32x4 av = *(const u32x4 *)(xs + roff(m, 2 * j + hf));
-        const u32x4 bv = *(const u32x4 *)(ws + roff(32 * wv + m, 2 * j + hf));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv),
-                                                      acc, 0, 0, 0);
-        aab = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, (u32x4)(av & msk)),
-                                                      __builtin_bit_cast(bf16x8, (u32x4)(bv & msk)), aab, 0, 0, 0);
+        av[j] = *(const u32x4 *)(xs + roff(m, 2 * j + hf));
+        bv[j] = *(const u32x4 *)(ws + roff(32 * wv + m, 2 * j + hf));
+      }
+#pragma unroll
+      for (int j = 0; j < kKC / 16; ++j) {
+        f32x16 &ac = (j & 1) ? acc1 : acc;
+        f32x16 &ab = (j & 1) ? aab1 : aab;
+        ac = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[j]), __builtin_bit_cast(bf16x8, bv[j]),
+                                                     ac, 0, 0, 0);
+        ab = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, (u32x4)(av[j] & msk)),
+                                                     __builtin_bit_cast(bf16x8, (u32x4)(bv[j] & msk)), ab, 0, 0, 0);
       }
       if (c & 1) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) tot[j] += acc[j];
+        for (int j = 0; j < 16; ++j) tot[j] += acc[j] + acc1[j];
       }
     };
-    // prologue: chunks 0..kRStages-2 in flight
-    for (int c = 0; c < kRStages - 1 && c < nch; ++c) issue(c, c);
+    // prologue: token rows of chunks 0..kXStages-2, router rows of chunks 0..kWStages-2.
+    // Step c issues the token rows of chunk c+kXStages-1 and then the router rows of
+    // chunk c+kWStages-1; chunk c's loads are complete once only the loads issued at
+    // step c-1 and later remain.
+    for (int c = 0; c < kXStages - 1 && c < nch; ++c) issue_x(c);
+    for (int c = 0; c < kWStages - 1 && c < nch; ++c) issue_w(c);
+    int last_step = 0;  // loads issued by the previous step
     for (int c = 0; c < nch; ++c) {
-      const int st = c % kRStages;
-      // chunk c's loads are complete once only the later chunks' loads remain
-      vm_wait_dyn(per_chunk * min(kRStages - 2, nch - 1 - c));
-      __syncthreads();  // chunk c visible to every wave; chunk c-1's stage is free
-      if (c + kRStages - 1 < nch) issue(c + kRStages - 1, (c + kRStages - 1) % kRStages);
-      if (active) compute(c, st);
+      vm_wait_dyn(c == 0 ? 0 : last_step);
+      __syncthreads();  // chunk c visible to every wave; chunk c-1's stages are free
+      last_step = 0;
+      if (c + kXStages - 1 < nch) {
+        issue_x(c + kXStages - 1);
+        last_step += wv < 4 ? 1 : 0;
+      }
+      if (c + kWStages - 1 < nch) {
+        issue_w(c + kWStages - 1);
+        last_step += 4;
+      }
+      if (active) compute(c);
     }
     __syncthreads();  // every wave is past its last stage read before the logits reuse it
     if (active) {
@@ -134,6 +162,8 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
       // for margin, plus the bias addition, the sequential binary64 reference's own
       // error and product underflow.
       const float c32 = 2.0f * (float)(kKP / 16 + 15 + H / kKP) + 4.0f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) aab[j] += aab1[j];
       const int e = wv * 32 + m;
       if (e < E) {
         const float bb = a.bias ? a.bias[e] : 0.0f;
@@ -155,76 +185,84 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
   }
   __syncthreads();
 
-  // fp32 selection: wave wv takes tokens 4wv..4wv+3, sixteen lanes per token.
+  // fp32 selection: wave wv takes tokens 4wv..4wv+3, sixteen lanes (one DPP row) per
+  // token, lane q holding experts q, q+16, ...  Each (logit, expert) pair is one 32-bit
+  // key: the order-preserving bits of the logit with the low 8 replaced by the
+  // complemented index, so the largest key is the largest logit, ties (and logits equal
+  // in their top 24 bits) to the lower index; k rounds of a row maximum pick the top k,
+  // clearing each winner.  Truncating the keys only changes the choice between logits
+  // closer than their error radii, and such a token fails the certificate below, which
+  // uses the exact fp32 values.
   {
     const int g = lane >> 4, q = lane & 15;
     const int m = wv * 4 + g;
     constexpr int NV = kMaxExperts / 16;
+    uint32_t key[NV];
     float lv[NV], rv[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int e = q + 16 * i;
       lv[i] = e < E ? s_l[m][e] : -INFINITY;
       rv[i] = e < E ? s_r[m][e] : 0.0f;
+      const uint32_t b = __float_as_uint(lv[i]);
+      const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+      key[i] = e < E ? ((ord & 0xffffff00u) | (uint32_t)(255 - e)) : 0u;
+    }
+    auto row_max_u32 = [](uint32_t v) {
+      v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
+      v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
+      v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, false));  // row_ror:4
+      v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false));  // row_ror:8
+      return v;
+    };
+    int my_e = 0;
+    for (int r = 0; r < k; ++r) {
+      uint32_t best = 0;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) best = max(best, key[i]);
+      best = row_max_u32(best);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) key[i] = key[i] == best ? 0u : key[i];
+      if (q == r) my_e = 255 - (int)(best & 0xffu);
     }
     uint32_t taken = 0;
-    for (int r = 0; r < k; ++r) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
 #pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const int e = q + 16 * i;
-        if (e < E && !((taken >> i) & 1u) && (lv[i] > bv || (lv[i] == bv && e < bi))) {
-          bv = lv[i];
-          bi = e;
-        }
-      }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const float ov = __shfl_xor(bv, o);
-        const int oi = __shfl_xor(bi, o);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      if (bi < E && (bi & 15) == q) taken |= 1u << (bi >> 4);
-      if (q == 0) s_sel[m][r] = bi < E ? bi : 0;
-    }
+    for (int i = 0; i < NV; ++i) taken |= (key[i] == 0u && q + 16 * i < E) ? (1u << i) : 0u;
+    const float my_l = q < k ? s_l[m][my_e] : -INFINITY;
     float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int e = q + 16 * i;
-      if (e >= E) continue;
-      if ((taken >> i) & 1u)
-        mn = fminf(mn, lv[i] - rv[i]);
-      else
-        mx = fmaxf(mx, lv[i] + rv[i]);
+      const bool in = (taken >> i) & 1u;
+      mn = (e < E && in) ? fminf(mn, lv[i] - rv[i]) : mn;
+      mx = (e < E && !in) ? fmaxf(mx, lv[i] + rv[i]) : mx;
     }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      mn = fminf(mn, __shfl_xor(mn, o));
-      mx = fmaxf(mx, __shfl_xor(mx, o));
-    }
+    mn = -row16_max(-mn);
+    mx = row16_max(mx);
     const bool cert = mn > mx;  // false for NaN or an infinite radius
+    if (q < k) s_sel[m][q] = my_e;
     if (q == 0) {
       s_min_in[m] = mn;
       s_max_out[m] = mx;
     }
-    __syncthreads();
     if (m < nt && cert) {
-      const float top = s_l[m][s_sel[m][0]];
+      // gates: softmax of the chosen logits (lane q < k holds choice q; choice 0 is the
+      // largest); ids in ascending order
+      const float top = __shfl(my_l, lane & ~15);
+      const float ex = q < k ? __expf(my_l - top) : 0.0f;
+      const float den = row16_sum(ex);
+      int pos = 0;
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) {
+        const int ej = __shfl(my_e, (lane & ~15) + j);
+        pos += (j < k && ej < my_e) ? 1 : 0;
+      }
       if (q < k) {
-        const int e = s_sel[m][q];
-        float ex = __expf(s_l[m][e] - top), den = 0.f;
-        for (int j = 0; j < k; ++j) den += __expf(s_l[m][s_sel[m][j]] - top);
-        int pos = 0;
-        for (int j = 0; j < k; ++j) pos += s_sel[m][j] < e;
         const size_t o = (size_t)(t0 + m) * k + pos;
         const float gt = ex / den;
-        a.ids[o] = e;
+        a.ids[o] = my_e;
         a.gates[o] = gt;
-        if (a.dbg_ids) a.dbg_ids[o] = e;
+        if (a.dbg_ids) a.dbg_ids[o] = my_e;
         if (a.dbg_gates) a.dbg_gates[o] = gt;
       }
     } else if (m < nt && q == 0) {

@@ -20,26 +20,42 @@ constexpr double kU64 = 1.1102230246251565404e-16;   // 2^-53
 __device__ void wave_dot64(const uint16_t *x, const uint16_t *w16, const float *w32, int H,
                            int lane, double &l, double &a) {
   double s = 0.0, sa = 0.0;
-  for (int c = lane; c < H / 8; c += kWave) {
-    const uint4 xv = *(const uint4 *)(x + 8 * c);
-    float xf[8] = {bf16_lo(xv.x), bf16_hi(xv.x), bf16_lo(xv.y), bf16_hi(xv.y),
-                   bf16_lo(xv.z), bf16_hi(xv.z), bf16_lo(xv.w), bf16_hi(xv.w)};
-    float wf[8];
-    if (w16) {
-      const uint4 wv = *(const uint4 *)(w16 + 8 * c);
-      wf[0] = bf16_lo(wv.x); wf[1] = bf16_hi(wv.x); wf[2] = bf16_lo(wv.y); wf[3] = bf16_hi(wv.y);
-      wf[4] = bf16_lo(wv.z); wf[5] = bf16_hi(wv.z); wf[6] = bf16_lo(wv.w); wf[7] = bf16_hi(wv.w);
-    } else {
-      const float4 w0 = *(const float4 *)(w32 + 8 * c);
-      const float4 w1 = *(const float4 *)(w32 + 8 * c + 4);
-      wf[0] = w0.x; wf[1] = w0.y; wf[2] = w0.z; wf[3] = w0.w;
-      wf[4] = w1.x; wf[5] = w1.y; wf[6] = w1.z; wf[7] = w1.w;
+  // four chunks' loads in flight before their products are summed (in ascending order)
+  for (int c0 = lane; c0 < H / 8; c0 += 4 * kWave) {
+    uint4 xv[4], wa[4], wb[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + u * kWave;
+      const int cc = c < H / 8 ? c : lane;
+      xv[u] = *(const uint4 *)(x + 8 * cc);
+      if (w16) {
+        wa[u] = *(const uint4 *)(w16 + 8 * cc);
+      } else {
+        wa[u] = *(const uint4 *)(w32 + 8 * cc);
+        wb[u] = *(const uint4 *)(w32 + 8 * cc + 4);
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const double p = (double)xf[i] * (double)wf[i];  // exact
-      s += p;
-      sa += fabs(p);
+    for (int u = 0; u < 4; ++u) {
+      if (c0 + u * kWave >= H / 8) break;
+      const float xf[8] = {bf16_lo(xv[u].x), bf16_hi(xv[u].x), bf16_lo(xv[u].y), bf16_hi(xv[u].y),
+                           bf16_lo(xv[u].z), bf16_hi(xv[u].z), bf16_lo(xv[u].w), bf16_hi(xv[u].w)};
+      float wf[8];
+      if (w16) {
+        wf[0] = bf16_lo(wa[u].x); wf[1] = bf16_hi(wa[u].x); wf[2] = bf16_lo(wa[u].y); wf[3] = bf16_hi(wa[u].y);
+        wf[4] = bf16_lo(wa[u].z); wf[5] = bf16_hi(wa[u].z); wf[6] = bf16_lo(wa[u].w); wf[7] = bf16_hi(wa[u].w);
+      } else {
+        wf[0] = __uint_as_float(wa[u].x); wf[1] = __uint_as_float(wa[u].y);
+        wf[2] = __uint_as_float(wa[u].z); wf[3] = __uint_as_float(wa[u].w);
+        wf[4] = __uint_as_float(wb[u].x); wf[5] = __uint_as_float(wb[u].y);
+        wf[6] = __uint_as_float(wb[u].z); wf[7] = __uint_as_float(wb[u].w);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const double p = (double)xf[i] * (double)wf[i];  // exact
+        s += p;
+        sa += fabs(p);
+      }
     }
   }
   l = wave_sum_f64(s);
