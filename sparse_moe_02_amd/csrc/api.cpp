@@ -22,7 +22,7 @@ struct moe_plan_s {
   int dec_grid;  // workgroups of the decode launch (all resident at once)
   // workspace layout (byte offsets)
   size_t off_ctrl, off_tokmask, off_ids, off_gates, off_counts, off_offsets, off_row_token,
-      off_row_gate, off_slot_row, off_mblocks, off_h, off_y, off_lrec, off_hrec, off_hint, off_dend, total;
+      off_row_gate, off_slot_row, off_mblocks, off_h, off_y, off_lrec, off_hrec, off_dend, total;
 };
 
 namespace {
@@ -66,7 +66,6 @@ void layout(moe_plan_s &p) {
   p.off_y = take(rows * H * 2);
   p.off_lrec = take(E * 3 * 8);  // decode records: cleared by moe_workspace_init
   p.off_hrec = take((k + 1) * I * 8);
-  p.off_hint = take((k + 1) * I / 4 * 4);
   p.off_dend = o;
   p.total = o;
 }
@@ -315,7 +314,6 @@ moe_status moe_forward_decode(moe_plan_t p, const void *x, void *out, void *ws, 
   a.epoch = next_epoch();
   a.lrec = at<uint64_t>(ws, p->off_lrec);
   a.hrec = at<uint64_t>(ws, p->off_hrec);
-  a.hint = at<uint32_t>(ws, p->off_hint);
   a.ctrl = at<Ctrl>(ws, p->off_ctrl);
   a.out = static_cast<uint16_t *>(out);
   if (dbg) {

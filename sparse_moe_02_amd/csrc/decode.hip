@@ -23,15 +23,18 @@
 //      q-th largest logit leaves a few candidates, ranked exactly, then certified
 //      against the radii; undecided experts are summed sequentially in binary64;
 //   3. gate/up task g (16 rows of one expert slot) runs on workgroup g mod G and
-//      publishes h as records plus one hint word per 4 rows; tasks of the shared expert
-//      run before the routing is known; a workgroup's first down task has its weight
-//      loads issued together with its routed gate/up loads;
-//   4. down task d (8 output rows, every slot) waits for the hints of the h rows it
-//      needs, reads the records into LDS and sums gate * (W_down h) in slot order.
+//      publishes h as records; tasks of the shared expert run before the routing is
+//      known; a workgroup's first down task has its weight loads issued together with
+//      its routed gate/up loads;
+//   4. down task d (8 output rows, every slot) reads the h records into LDS (all loads
+//      in flight at once, re-reading only records not yet published) and sums
+//      gate * (W_down h) in slot order.
 // Every workgroup of the grid is resident at once (the grid is capped by the occupancy
 // of this kernel), so each wait ends; a wait that exceeds its poll budget sets an error
 // word instead of hanging.  The dot products use the packed codes directly:
 //     sum_k v_k (s q_k + b) = s * sum_k v_k q_k + b * sum_k v_k   (per group of 64).
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "select64.hpp"
@@ -48,7 +51,6 @@ constexpr int kDnUnits = 5;             // (row, slot) units per 16-lane group p
 constexpr int kDnSlots = 10;            // slots per down round: 8 rows x 10 = 16 groups x 5
 constexpr int kHStage = 5120;           // h floats staged in LDS per down round
 constexpr int kSpins = 1 << 20;         // polls before a wait gives up (about a second)
-constexpr int kRecSpins = 1 << 12;      // re-reads of one h record after its hint was seen
 
 __device__ __forceinline__ QMat expert_mat(const QMat &routed, const QMat &shared, int e, int E, int N, int K) {
   if (e == E) return shared;
@@ -81,6 +83,7 @@ __device__ __forceinline__ uint32_t tag_of(uint64_t r) { return (uint32_t)(r >> 
 
 struct DecShared {
   Sel64 S;
+  uint64_t cand[kDecThreads / kWave][kMaxTopK];  // each wave's top-k keys
   double red[2][4];
   int ids[kMaxTopK];
   float gates[kMaxTopK];
@@ -174,8 +177,44 @@ __device__ double block_max_f64(double v, DecShared &sh) {
   return v;
 }
 
+// Maximum of a 64-bit value over the wave, in every lane: DPP maxima inside each row of
+// 16 lanes, then the four row results through scalar registers.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  auto dpp64 = [](uint64_t x, auto ctrl) {
+    constexpr int C = decltype(ctrl)::value;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, C, 0xf, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), C, 0xf, 0xf, false);
+    return ((uint64_t)hi << 32) | lo;
+  };
+  auto mx = [](uint64_t p, uint64_t q) { return q > p ? q : p; };
+  v = mx(v, dpp64(v, std::integral_constant<int, 0xB1>{}));   // quad_perm [1,0,3,2]
+  v = mx(v, dpp64(v, std::integral_constant<int, 0x4E>{}));   // quad_perm [2,3,0,1]
+  v = mx(v, dpp64(v, std::integral_constant<int, 0x124>{}));  // row_ror:4
+  v = mx(v, dpp64(v, std::integral_constant<int, 0x128>{}));  // row_ror:8
+  uint64_t r = 0;
+#pragma unroll
+  for (int row = 0; row < 4; ++row) {
+    const uint64_t rv = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * row) << 32) |
+                        (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * row);
+    r = mx(r, rv);
+  }
+  return r;
+}
+
+// Order-preserving 64-bit key of a binary64 logit of expert e: the low 8 bits carry the
+// complemented index, so the largest key is the largest logit, ties (and logits equal in
+// all but their last 8 bits, far inside the error radii) to the lower index.
+__device__ __forceinline__ uint64_t logit_key(double v, int e) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint64_t ord = (b >> 63) ? ~b : (b | (1ull << 63));
+  return (ord & ~0xffull) | (uint64_t)(255 - e);
+}
+
 // Top-k of the E logits of this call (value descending, index ascending) into sh.ids
-// (ascending) and sh.gates.  One expert per thread (E <= 256).
+// (ascending) and sh.gates.  One expert per thread (E <= 256): each wave takes its top k
+// by k rounds of a wave maximum, wave 0 merges the four lists the same way; the choice
+// is then certified against the binary64 error radii (experts closer than their radii
+// are re-ranked by resolve64).
 __device__ void select_topk(const DecodeArgs &a, DecShared &sh, bool write_debug) {
   Sel64 &S = sh.S;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, E = a.E, k = a.k;
@@ -186,41 +225,21 @@ __device__ void select_topk(const DecodeArgs &a, DecShared &sh, bool write_debug
     S.gl[tid] = v;
     S.chosen[tid] = 0;
   }
-  // Threshold: wave w's q-th largest logit t_w (q = ceil(k / waves)).  At least k logits
-  // are >= min_w t_w, so every chosen expert is among those.
-  const int nw = (E + kWave - 1) / kWave, q = (k + nw - 1) / nw;
-  if (wv < nw) {
-    double cur = v, qth = -INFINITY;
-    for (int i = 0; i < q; ++i) {
-      double m = cur;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) m = fmax(m, __shfl_xor(m, o));
-      qth = m;
-      const unsigned long long hit = __ballot(cur == m);
-      if (lane == __ffsll(hit) - 1) cur = -INFINITY;  // take out one instance
-    }
-    if (lane == 0) sh.red[1][wv] = qth;
-  }
-  if (tid == 0) S.n = 0;
-  __syncthreads();
-  double tau = INFINITY;
-  for (int w = 0; w < nw; ++w) tau = fmin(tau, sh.red[1][w]);
-  if (mine && v >= tau) {
-    const int c = atomicAdd(&S.n, 1);
-    S.cand[c] = tid;
-    S.v[c] = v;
+  uint64_t key = mine ? logit_key(v, tid) : 0ull;
+  for (int rr = 0; rr < k; ++rr) {
+    const uint64_t best = wave_max_u64(key);
+    key = key == best ? 0ull : key;
+    if (lane == 0) sh.cand[wv][rr] = best;
   }
   __syncthreads();
-  const int nc = S.n;
-  for (int c = tid; c < nc; c += kDecThreads) {
-    const double vc = S.v[c];
-    const int ec = S.cand[c];
-    int rank = 0;
-    for (int j = 0; j < nc; ++j) {
-      const double vj = S.v[j];
-      rank += (vj > vc) || (vj == vc && S.cand[j] < ec);
+  if (wv == 0) {
+    const int cw = lane >> 4, cr = lane & 15;
+    uint64_t c = (cr < k) ? sh.cand[cw][cr] : 0ull;
+    for (int rr = 0; rr < k; ++rr) {
+      const uint64_t best = wave_max_u64(c);
+      c = c == best ? 0ull : c;
+      if (lane == 0 && best != 0ull) S.chosen[255 - (int)(best & 0xffull)] = 1;
     }
-    if (rank < k) S.chosen[ec] = 1;
   }
   __syncthreads();
   const bool sel = mine && S.chosen[tid];
@@ -314,9 +333,8 @@ __device__ __forceinline__ void gu_start(const DecodeArgs &a, const DecShared &s
 }
 
 // Gate/up task g: slot j = g / (I/16), rows i0 .. i0+15 (wave w: i0+4w .. i0+4w+3).
-// `first` holds the already-issued first round.  Publishes this wave's 4 h records,
-// then its hint.
-__device__ void gu_task(const DecodeArgs &a, const DecShared &sh, int g, const GuLoad &first) {
+// `first` holds the already-issued first round.  Publishes this wave's 4 h records.
+__device__ __forceinline__ void gu_task(const DecodeArgs &a, const DecShared &sh, int g, const GuLoad &first) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int I = a.I, H = a.H;
   const int tpe = I / kGuTask;
@@ -343,7 +361,6 @@ __device__ void gu_task(const DecodeArgs &a, const DecShared &sh, int g, const G
   }
   const size_t row = (size_t)j * I + r0;
   if (lane < kGuRows) st_agent(&a.hrec[row + lane], tagged(a.epoch, __float_as_uint(hv)));
-  if (lane == 0) st_agent(&a.hint[row / kGuRows], a.epoch);
 }
 
 // ------------------------------------------------------------------ down
@@ -374,36 +391,35 @@ __device__ __forceinline__ void dn_issue(const DecodeArgs &a, const DecShared &s
   }
 }
 
-// h of slots j0 .. j0+nb-1 into LDS: wait for their hints, then take the records,
-// re-reading any whose tag is not yet this call's.
-__device__ void stage_h(const DecodeArgs &a, DecShared &sh, int j0, int nb) {
+// h of slots j0 .. j0+nb-1 into LDS from their tagged records: each thread issues the
+// loads of up to 16 records at once, then re-reads (one by one) the few whose tag is not
+// yet this call's.
+__device__ __forceinline__ void stage_h(const DecodeArgs &a, DecShared &sh, int j0, int nb) {
   const int tid = threadIdx.x;
   const int n = nb * a.I;
-  const size_t base = (size_t)j0 * a.I;
-  bool ok = false;
-  for (int i = 0; !ok; ++i) {
-    bool mine = true;
-    for (int t = tid; t < n / kGuRows; t += kDecThreads) mine &= ld_agent(&a.hint[base / kGuRows + t]) == a.epoch;
-    ok = __syncthreads_and(mine);
-    if (!ok) {
-      if (i == kSpins) {
-        if (tid == 0) st_agent(&a.ctrl->d_err, 1);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
+  const uint64_t *rec = a.hrec + (size_t)j0 * a.I;
+  constexpr int kBatch = 16;
+  for (int t0 = tid; t0 < n; t0 += kDecThreads * kBatch) {
+    uint64_t rv[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int t = t0 + u * kDecThreads;
+      rv[u] = t < n ? ld_agent(&rec[t]) : tagged(a.epoch, 0u);
     }
-  }
-  for (int t = tid; t < n; t += kDecThreads) {
-    uint64_t rv = ld_agent(&a.hrec[base + t]);
-    for (int i = 0; tag_of(rv) != a.epoch; ++i) {
-      if (i == kRecSpins) {
-        st_agent(&a.ctrl->d_err, 1);
-        break;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int t = t0 + u * kDecThreads;
+      if (t >= n) continue;
+      for (int i = 0; tag_of(rv[u]) != a.epoch; ++i) {
+        if (i == kSpins) {
+          st_agent(&a.ctrl->d_err, 1);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        rv[u] = ld_agent(&rec[t]);
       }
-      __builtin_amdgcn_s_sleep(1);
-      rv = ld_agent(&a.hrec[base + t]);
+      sh.h[t] = __uint_as_float((uint32_t)rv[u]);
     }
-    sh.h[t] = __uint_as_float((uint32_t)rv);
   }
   __syncthreads();
 }
@@ -436,7 +452,7 @@ __device__ __forceinline__ void dn_accumulate(const DecodeArgs &a, DecShared &sh
 
 // Down task d: output rows n0 = 8d .. 8d+7 over every slot, rounds of nb slots and
 // chunk passes; `pre` (if given) is round 0's first pass, already issued.
-__device__ void dn_task(const DecodeArgs &a, DecShared &sh, int d, const DnLoad *pre) {
+__device__ __forceinline__ void dn_task(const DecodeArgs &a, DecShared &sh, int d, const DnLoad &pre, bool has_pre) {
   const int tid = threadIdx.x, q = tid >> 4, cl = tid & 15;
   const int I = a.I, k = a.k, n0 = d * kDnRows;
   const int nbmax = min(min(k + 1, kDnSlots), kHStage / I);
@@ -448,8 +464,8 @@ __device__ void dn_task(const DecodeArgs &a, DecShared &sh, int d, const DnLoad 
     float acc[kDnUnits] = {};
     for (int p = 0; p < npass; ++p) {
       const int c = cl + 16 * p;
-      if (pre && j0 == 0 && p == 0) {
-        dn_accumulate(a, sh, *pre, nb, c, acc);
+      if (has_pre && j0 == 0 && p == 0) {
+        dn_accumulate(a, sh, pre, nb, c, acc);
       } else {
         DnLoad L;
         dn_issue(a, sh, n0, j0, nb, c, L);
@@ -523,7 +539,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
 
   // 4. down tasks
   for (int d = b; d < n_dn; d += G) {
-    dn_task(a, sh, d, dn_pre ? &dl : nullptr);
+    dn_task(a, sh, d, dl, dn_pre);
     dn_pre = false;
   }
 }

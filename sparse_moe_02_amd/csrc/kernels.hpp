@@ -91,7 +91,6 @@ struct DecodeArgs {
   uint32_t epoch;           // tag of this call's records: nonzero, new for every call
   uint64_t *lrec;           // [E][3] tagged records: low and high word of the binary64 logit, radius
   uint64_t *hrec;           // [(k+1)*I] tagged h values
-  uint32_t *hint;           // [(k+1)*I/4] one per 4 h rows: their records have been stored
   Ctrl *ctrl;
   uint16_t *out;            // [H]
   int32_t *dbg_ids;
