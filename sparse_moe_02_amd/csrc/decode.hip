@@ -83,7 +83,9 @@ __device__ __forceinline__ uint32_t tag_of(uint64_t r) { return (uint32_t)(r >> 
 
 struct DecShared {
   Sel64 S;
-  uint64_t cand[kDecThreads / kWave][kMaxTopK];  // each wave's top-k keys
+  uint32_t cand[kDecThreads / kWave][kMaxTopK];  // each wave's top-k keys
+  int wcnt[kDecThreads / kWave];
+  float wf[kDecThreads / kWave];
   double red[2][4];
   int ids[kMaxTopK];
   float gates[kMaxTopK];
@@ -177,44 +179,57 @@ __device__ double block_max_f64(double v, DecShared &sh) {
   return v;
 }
 
-// Maximum of a 64-bit value over the wave, in every lane: DPP maxima inside each row of
-// 16 lanes, then the four row results through scalar registers.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  auto dpp64 = [](uint64_t x, auto ctrl) {
-    constexpr int C = decltype(ctrl)::value;
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, C, 0xf, 0xf, false);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), C, 0xf, 0xf, false);
-    return ((uint64_t)hi << 32) | lo;
-  };
-  auto mx = [](uint64_t p, uint64_t q) { return q > p ? q : p; };
-  v = mx(v, dpp64(v, std::integral_constant<int, 0xB1>{}));   // quad_perm [1,0,3,2]
-  v = mx(v, dpp64(v, std::integral_constant<int, 0x4E>{}));   // quad_perm [2,3,0,1]
-  v = mx(v, dpp64(v, std::integral_constant<int, 0x124>{}));  // row_ror:4
-  v = mx(v, dpp64(v, std::integral_constant<int, 0x128>{}));  // row_ror:8
-  uint64_t r = 0;
-#pragma unroll
-  for (int row = 0; row < 4; ++row) {
-    const uint64_t rv = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * row) << 32) |
-                        (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * row);
-    r = mx(r, rv);
-  }
-  return r;
+// DPP row maxima / minima (16 lanes), then the four row results through scalar registers:
+// the wave-wide result in every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, false));  // row_ror:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false));  // row_ror:8
+  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+  return max(a, b);
 }
 
-// Order-preserving 64-bit key of a binary64 logit of expert e: the low 8 bits carry the
-// complemented index, so the largest key is the largest logit, ties (and logits equal in
-// all but their last 8 bits, far inside the error radii) to the lower index.
-__device__ __forceinline__ uint64_t logit_key(double v, int e) {
-  const uint64_t b = (uint64_t)__double_as_longlong(v);
-  const uint64_t ord = (b >> 63) ? ~b : (b | (1ull << 63));
-  return (ord & ~0xffull) | (uint64_t)(255 - e);
+template <int C>
+__device__ __forceinline__ double dpp_d(double x) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, C, 0xf, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), C, 0xf, 0xf, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ double readlane_d(double x, int l) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// wave minimum of mn and maximum of mx together
+__device__ __forceinline__ void wave_minmax_f64(double &mn, double &mx) {
+  mn = fmin(mn, dpp_d<0xB1>(mn)); mx = fmax(mx, dpp_d<0xB1>(mx));
+  mn = fmin(mn, dpp_d<0x4E>(mn)); mx = fmax(mx, dpp_d<0x4E>(mx));
+  mn = fmin(mn, dpp_d<0x124>(mn)); mx = fmax(mx, dpp_d<0x124>(mx));
+  mn = fmin(mn, dpp_d<0x128>(mn)); mx = fmax(mx, dpp_d<0x128>(mx));
+  mn = fmin(fmin(readlane_d(mn, 0), readlane_d(mn, 16)), fmin(readlane_d(mn, 32), readlane_d(mn, 48)));
+  mx = fmax(fmax(readlane_d(mx, 0), readlane_d(mx, 16)), fmax(readlane_d(mx, 32), readlane_d(mx, 48)));
+}
+
+// Order-preserving 32-bit key of a logit of expert e: the fp32 value's ordered bits with
+// the low 8 replaced by the complemented index, so the largest key is the largest logit,
+// ties (and logits equal in their top 24 bits) to the lower index.  The truncation only
+// changes the choice between logits much closer than 2^-15 relative; the certificate
+// below, on the binary64 values and radii, catches any such choice.
+__device__ __forceinline__ uint32_t logit_key(double v, int e) {
+  const uint32_t b = __float_as_uint((float)v);
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return (ord & 0xffffff00u) | (uint32_t)(255 - e);
 }
 
 // Top-k of the E logits of this call (value descending, index ascending) into sh.ids
 // (ascending) and sh.gates.  One expert per thread (E <= 256): each wave takes its top k
-// by k rounds of a wave maximum, wave 0 merges the four lists the same way; the choice
-// is then certified against the binary64 error radii (experts closer than their radii
-// are re-ranked by resolve64).
+// by k rounds of a wave maximum; a chosen candidate is one of the 4k whose rank among
+// them is below k.  The choice is certified against the binary64 error radii; experts
+// closer than their radii are re-ranked by resolve64.
 __device__ void select_topk(const DecodeArgs &a, DecShared &sh, bool write_debug) {
   Sel64 &S = sh.S;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, E = a.E, k = a.k;
@@ -223,29 +238,34 @@ __device__ void select_topk(const DecodeArgs &a, DecShared &sh, bool write_debug
   if (mine) {
     read_logit(a, tid, v, r);
     S.gl[tid] = v;
-    S.chosen[tid] = 0;
   }
-  uint64_t key = mine ? logit_key(v, tid) : 0ull;
+  uint32_t key = mine ? logit_key(v, tid) : 0u;
+  const uint32_t key0 = key;
   for (int rr = 0; rr < k; ++rr) {
-    const uint64_t best = wave_max_u64(key);
-    key = key == best ? 0ull : key;
+    const uint32_t best = wave_max_u32(key);
+    key = key == best ? 0u : key;
     if (lane == 0) sh.cand[wv][rr] = best;
   }
   __syncthreads();
-  if (wv == 0) {
-    const int cw = lane >> 4, cr = lane & 15;
-    uint64_t c = (cr < k) ? sh.cand[cw][cr] : 0ull;
-    for (int rr = 0; rr < k; ++rr) {
-      const uint64_t best = wave_max_u64(c);
-      c = c == best ? 0ull : c;
-      if (lane == 0 && best != 0ull) S.chosen[255 - (int)(best & 0xffull)] = 1;
-    }
+  {
+    // rank of my key among the 4k wave candidates (keys are distinct)
+    int rank = 0;
+    for (int w2 = 0; w2 < kDecThreads / kWave; ++w2)
+      for (int rr = 0; rr < k; ++rr) rank += sh.cand[w2][rr] > key0 ? 1 : 0;
+    S.chosen[tid] = (mine && key == 0u && rank < k) ? 1 : 0;  // key cleared: one of my wave's k
   }
   __syncthreads();
   const bool sel = mine && S.chosen[tid];
   // certification: every chosen logit minus its radius above every other plus its radius
-  const double mn = block_min_f64(sel ? v - r : INFINITY, sh);
-  const double mx = block_max_f64((mine && !sel) ? v + r : -INFINITY, sh);
+  double mn = sel ? v - r : INFINITY, mx = (mine && !sel) ? v + r : -INFINITY;
+  wave_minmax_f64(mn, mx);
+  if (lane == 0) {
+    sh.red[0][wv] = mn;
+    sh.red[1][wv] = mx;
+  }
+  __syncthreads();
+  mn = fmin(fmin(sh.red[0][0], sh.red[0][1]), fmin(sh.red[0][2], sh.red[0][3]));
+  mx = fmax(fmax(sh.red[1][0], sh.red[1][1]), fmax(sh.red[1][2], sh.red[1][3]));
   const bool sure_in = sel && v - r > mx;
   const bool sure_out = mine && !sel && v + r < mn;
   if (!__syncthreads_and(!mine || sure_in || sure_out)) {
@@ -261,8 +281,38 @@ __device__ void select_topk(const DecodeArgs &a, DecShared &sh, bool write_debug
     const int nin1 = __syncthreads_count(sure_in);
     resolve64(S, k - nin1, a.x, a.wr16, a.wr32, a.bias, a.H, tid, kDecThreads);
   }
-  emit_selection<false>(S, E, k, sh.ids, sh.gates, write_debug ? a.dbg_ids : nullptr,
-                        write_debug ? a.dbg_gates : nullptr, tid, kDecThreads);
+  // ids ascending (rank of each chosen expert = chosen experts below it) and softmax
+  // gates of the chosen logits
+  const bool ch = mine && S.chosen[tid];
+  const float gl = ch ? (float)S.gl[tid] : -INFINITY;
+  const uint64_t bal = __ballot(ch);
+  const uint32_t gb = __float_as_uint(gl);
+  const uint32_t wo = wave_max_u32((gb & 0x80000000u) ? ~gb : (gb | 0x80000000u));  // ordered bits
+  if (lane == 0) {
+    sh.wcnt[wv] = __popcll(bal);
+    sh.wf[wv] = __uint_as_float((wo & 0x80000000u) ? (wo & 0x7fffffffu) : ~wo);
+  }
+  __syncthreads();
+  int below = __popcll(bal & ((1ull << lane) - 1ull));
+  float gmax = -INFINITY;
+  for (int w2 = 0; w2 < kDecThreads / kWave; ++w2) {
+    below += w2 < wv ? sh.wcnt[w2] : 0;
+    gmax = fmaxf(gmax, sh.wf[w2]);
+  }
+  const float ex = ch ? __expf(gl - gmax) : 0.0f;
+  const float ws = wave_sum(ex);
+  __syncthreads();  // every thread has read sh.wf / sh.wcnt
+  if (lane == 0) sh.wf[wv] = ws;
+  __syncthreads();
+  const float den = (sh.wf[0] + sh.wf[1]) + (sh.wf[2] + sh.wf[3]);
+  if (ch && below < kMaxTopK) {
+    const float g = ex / den;
+    sh.ids[below] = tid;
+    sh.gates[below] = g;
+    if (write_debug && a.dbg_ids) a.dbg_ids[below] = tid;
+    if (write_debug && a.dbg_gates) a.dbg_gates[below] = g;
+  }
+  __syncthreads();
   if (tid < k) sh.ids[tid] = min(max(sh.ids[tid], 0), E - 1);  // keep reads in bounds even after a failed wait
   __syncthreads();
 }
