@@ -66,6 +66,14 @@ __device__ __forceinline__ void dma16(const void *gbase, uint32_t voff, uint32_t
                : "memory", "m0");
 }
 
+// The same with 4 bytes per lane (lane i's bytes land at lds + 4 i).
+__device__ __forceinline__ void dma4(const void *gbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2\n" ::"s"(
+                   __builtin_amdgcn_readfirstlane(lds)),
+               "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
 }

@@ -46,15 +46,6 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt(0xF70 | (N & 15) | ((N >> 4) << 14));  // vmcnt(N), others free
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ void g2l16(const void *g, uint8_t *l) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void *)l, 16, 0, 0);
-}
-__device__ __forceinline__ void g2l4(const void *g, uint8_t *l) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void *)l, 4, 0, 0);
-}
-
 __device__ __forceinline__ QMat expert_mat(const QMat &routed, const QMat &shared, int e, int E, int N, int K) {
   if (e == E) return shared;
   QMat m;
@@ -69,9 +60,12 @@ __device__ __forceinline__ int a_off(int row, int chunk) { return row * kRowByte
 // weights: slot w (one weight row) at w*64, 16-byte part p at p ^ ((w >> 2) & 3)
 __device__ __forceinline__ int b_off(int slot, int part) { return slot * 64 + ((part ^ ((slot >> 2) & 3)) << 4); }
 
-__device__ __forceinline__ f32x16 mfma(const u32x4 &a, const uint32_t (&b)[4], const f32x16 &c) {
-  const u32x4 bv = {b[0], b[1], b[2], b[3]};
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, bv), c, 0,
+// D += W X^T for a 32x32 tile: the weights are the row operand and the activations the
+// column operand, so lane l holds token row l%32 of the tile and output columns
+// 8q + 4(l/32) + {0,1,2,3} in accumulator entries 4q..4q+3 (four consecutive columns).
+__device__ __forceinline__ f32x16 mfma(const uint32_t (&w)[4], const u32x4 &x, const f32x16 &c) {
+  const u32x4 wv = {w[0], w[1], w[2], w[3]};
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wv), __builtin_bit_cast(bf16x8, x), c, 0,
                                                  0, 0);
 }
 
@@ -120,27 +114,29 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
     bbase[i] = (const char *)slot_mat(16 * v).q;
     boff[i] = 4u * ((uint32_t)slot_row(slot) * (uint32_t)(K / 8) + 4u * (uint32_t)((lane & 3) ^ ((slot >> 2) & 3)));
   }
-  // S: 16 wave-loads of 256 B (64 slots x 2 fp16): scales (v < 8) then biases; wave
-  // takes v = wu + 8i, i < 2
+  // S: 16 wave-loads of 256 B (64 slots x 2 fp16): v < 8 scales, v >= 8 biases.  Wave-load
+  // v covers tile t = (v >> 2) & 1 of the wave pair m = v & 3, so its rows come from one
+  // matrix: lane l takes slot 64 (2m + l/32) + 32 t + l%32.  Wave wu takes v = wu + 8i.
   const char *sbase[2];
   uint32_t soff[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int v = wu + 8 * i;
-    const int slot = 64 * (v & 7) + lane;
-    const QMat &M = slot_mat(64 * (v & 7) + 32 * (lane >> 5));
+    const int t = (v >> 2) & 1, m = v & 3;
+    const int slot = 64 * (2 * m + (lane >> 5)) + 32 * t + (lane & 31);
+    const QMat &M = slot_mat(32 * t);
     sbase[i] = (const char *)((v >> 3) ? M.b : M.s);
     soff[i] = 2u * (uint32_t)slot_row(slot) * (uint32_t)(K / 64);
   }
   auto issue = [&](int ss, uint8_t *st) {
+    const uint32_t l = lds_addr(st);
 #pragma unroll
-    for (int i = 0; i < MT; ++i) g2l16(abase + aoff[i] + ss * 256, st + (wu + 8 * i) * 1024);
+    for (int i = 0; i < MT; ++i) dma16(abase + ss * 256, aoff[i], l + (wu + 8 * i) * 1024);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) g2l16(bbase[i] + boff[i] + ss * 64, st + kAStage + (wu + 8 * i) * 1024);
+    for (int i = 0; i < 4; ++i) dma16(bbase[i] + ss * 64, boff[i], l + kAStage + (wu + 8 * i) * 1024);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) g2l4(sbase[i] + soff[i] + ss * 4, st + kAStage + kBStage + (wu + 8 * i) * 256);
+    for (int i = 0; i < 2; ++i) dma4(sbase[i] + ss * 4, soff[i], l + kAStage + kBStage + (wu + 8 * i) * 256);
   };
-
   if (!GU && tid < MT * 32) s_gate[tid] = a.row_gate[row0 + min(tid, rows - 1)];  // read by the epilogue
   f32x16 acc[MT][2];
 #pragma unroll
@@ -153,16 +149,20 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
   const int a_lane = (lane & 31) * kRowBytes;       // + t*32*256 (immediate) per row tile
   const int a_c0 = (hf * 8) ^ l15;                   // swizzled chunk of slice j: a_c0 ^ j
   int b_lane[2];                                     // this lane's weight slot per tile
+  int s_lane[2];                                     // fp16 index of its scale (biases + 1024)
 #pragma unroll
-  for (int i = 0; i < 2; ++i) b_lane[i] = (64 * wu + 32 * i + (lane & 31));
+  for (int i = 0; i < 2; ++i) {
+    b_lane[i] = (64 * wu + 32 * i + (lane & 31));
+    s_lane[i] = 128 * ((i << 2) | (wu >> 1)) + 2 * (32 * (wu & 1) + (lane & 31)) + hf;
+  }
   auto compute = [&](const uint8_t *st) {
     const uint8_t *bb = st + kAStage;
     const uint16_t *sp = (const uint16_t *)(st + kAStage + kBStage);
     float sc[2], bi[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      sc[i] = fp16_to_f32(sp[2 * b_lane[i] + hf]);
-      bi[i] = fp16_to_f32(sp[kSStage / 4 + 2 * b_lane[i] + hf]);
+      sc[i] = fp16_to_f32(sp[s_lane[i]]);
+      bi[i] = fp16_to_f32(sp[kSStage / 4 + s_lane[i]]);
     }
     // word j of the lane's 8 (16-byte part 2*hf + j/4, dword j%4) of its slot in tile i
     auto word = [&](int i, int j) {
@@ -171,13 +171,15 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
     auto afrag = [&](int t, int j) {
       return *(const u32x4 *)(st + t * 32 * kRowBytes + a_lane + ((a_c0 ^ j) << 4));
     };
-    // software pipeline over the eight k-slices: activation fragments, packed words and
-    // dequantised weights of slice j+1 are prepared while the MFMAs of slice j run
-    u32x4 av[2][MT];
+    // software pipeline over the eight k-slices: the packed words and dequantised weights
+    // of slice j+1 are prepared while the MFMAs of slice j run, and each row tile's
+    // activation fragment of slice j+1 is read as soon as slice j's two MFMAs have
+    // issued with it (one fragment register set per row tile)
+    u32x4 av[MT];
     uint32_t d[2][2][4];
     uint32_t wn[2];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) av[0][t] = afrag(t, 0);
+    for (int t = 0; t < MT; ++t) av[t] = afrag(t, 0);
 #pragma unroll
     for (int i = 0; i < 2; ++i) dequant8_bf16(word(i, 0), sc[i], bi[i], d[0][i]);
 #pragma unroll
@@ -187,8 +189,6 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
       const int c = j & 1, nx = c ^ 1;
       if (j < 7) {
 #pragma unroll
-        for (int t = 0; t < MT; ++t) av[nx][t] = afrag(t, j + 1);
-#pragma unroll
         for (int i = 0; i < 2; ++i) dequant8_bf16(wn[i], sc[i], bi[i], d[nx][i]);
         if (j < 6) {
 #pragma unroll
@@ -196,35 +196,41 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
         }
       }
 #pragma unroll
-      for (int t = 0; t < MT; ++t)
+      for (int t = 0; t < MT; ++t) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) acc[t][i] = mfma(av[c][t], d[c][i], acc[t][i]);
+        for (int i = 0; i < 2; ++i) acc[t][i] = mfma(d[c][i], av[t], acc[t][i]);
+        if (j < 7) av[t] = afrag(t, j + 1);
+      }
       if (j < 7) {
-        // the next slices' LDS reads first, then each MFMA followed by its share of the
-        // dequant VALU work (2 words, 46 instructions)
-        if (j < 6)
-          __builtin_amdgcn_sched_group_barrier(0x100, MT + 2, 0);
-        else
-          __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);
+        // order: the next packed words, then per row tile two MFMAs, each followed by its
+        // share of the dequant VALU work (2 words, 46 instructions), then the tile's next
+        // activation fragment
+        if (j < 6) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-        for (int i = 0; i < 2 * MT; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, (46 + 2 * MT - 1) / (2 * MT), 0);
+        for (int t = 0; t < MT; ++t) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, (46 + 2 * MT - 1) / (2 * MT), 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
       }
     }
   };
-  // two-stage ring, unrolled by two so each read names one stage object and the
-  // copies in flight name the other
+  // Two-stage ring, unrolled by two so each read names one stage object and the copies
+  // in flight name the other.  The stage loads are issued from inline asm, so the
+  // compiler adds no waits of its own for them; each wave waits for its loads, then the
+  // barrier publishes every wave's.
   issue(0, stage0);
   for (int ss = 0; ss < nss; ss += 2) {
     vm_wait<0>();
-    __builtin_amdgcn_s_barrier();  // stage0 holds step ss for every wave; stage1 is free
+    __syncthreads();  // stage0 holds step ss for every wave; stage1 is free
     if (ss + 1 < nss) issue(ss + 1, stage1);
     if (active) compute(stage0);
     if (ss + 1 >= nss) break;
     vm_wait<0>();
-    __builtin_amdgcn_s_barrier();  // stage1 holds step ss+1; stage0 is free
+    __syncthreads();  // stage1 holds step ss+1; stage0 is free
     if (ss + 2 < nss) issue(ss + 2, stage0);
     if (active) compute(stage1);
   }
@@ -232,23 +238,39 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
   __builtin_amdgcn_s_barrier();
   if (active) {
     // Epilogue, one 32-row tile at a time: the wave converts its tile to bf16 in its own
-    // LDS area (GU: 32 x 32 h values; down: 32 x 64 gate-weighted outputs), then
-    // writes whole rows with 16-byte stores.
+    // LDS area (GU: 32 rows x 32 h values; down: 32 rows x 64 gate-weighted outputs; rows
+    // padded by 16 bytes so the 8-byte writes of 32 rows spread over the banks), then
+    // writes whole row segments with 16-byte stores.
     constexpr int COLS = GU ? 32 : 64;
-    uint16_t *tile = (uint16_t *)(stage0 + wu * (32 * 64 * 2));
-    const int lc = lane & 31;
+    constexpr int RB = COLS * 2 + 16;  // bytes per staged row
+    uint8_t *tile = stage0 + wu * (32 * RB);
+    // lane index made opaque here so its row/column arithmetic is not hoisted out of the
+    // persistent loop (where it would occupy registers through the main loop)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lr = ln & 31, lh = ln >> 5;
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
+      const float g = GU ? 1.0f : s_gate[t * 32 + lr];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = 8 * (v >> 2) + 4 * hf + (v & 3);
+      for (int q = 0; q < 4; ++q) {
         if (GU) {
-          const float gv = acc[t][0][v], uv = acc[t][1][v];
-          tile[r * COLS + lc] = f32_to_bf16(gv * sigmoid_fast(gv) * uv);
-        } else {
-          const float g = s_gate[t * 32 + r];
+          float hv[4];
 #pragma unroll
-          for (int i = 0; i < 2; ++i) tile[r * COLS + 32 * i + lc] = f32_to_bf16(g * acc[t][i][v]);
+          for (int u = 0; u < 4; ++u) {
+            const float gv = acc[t][0][4 * q + u], uv = acc[t][1][4 * q + u];
+            hv[u] = gv * sigmoid_fast(gv) * uv;
+          }
+          const uint2 pk = {pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
+          *(uint2 *)(tile + lr * RB + 2 * (8 * q + 4 * lh)) = pk;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const f32x16 &ac = acc[t][i];
+            const uint2 pk = {pack_bf16x2(g * ac[4 * q], g * ac[4 * q + 1]),
+                              pack_bf16x2(g * ac[4 * q + 2], g * ac[4 * q + 3])};
+            *(uint2 *)(tile + lr * RB + 2 * (32 * i + 8 * q + 4 * lh)) = pk;
+          }
         }
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's tile writes are done
@@ -256,11 +278,11 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
       constexpr int RPI = 64 / LPR;        // rows per store instruction
 #pragma unroll
       for (int rr = 0; rr < 32; rr += RPI) {
-        const int r = rr + lane / LPR;
+        const int r = rr + ln / LPR;
         if (t * 32 + r < rows) {
-          const uint4 v = *(const uint4 *)(tile + r * COLS + 8 * (lane % LPR));
+          const uint4 v = *(const uint4 *)(tile + r * RB + 16 * (ln % LPR));
           uint16_t *dst = GU ? a.h + (size_t)(row0 + t * 32 + r) * I : a.y + (size_t)(row0 + t * 32 + r) * H;
-          *(uint4 *)(dst + wcol0 + 8 * (lane % LPR)) = v;
+          *(uint4 *)(dst + wcol0 + 8 * (ln % LPR)) = v;
         }
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next tile overwrites
@@ -295,7 +317,8 @@ __device__ void gemm_persistent(const GemmArgs &a) {
         case 1: gemm_item<1, GU>(a, stage0, stage1, s_gate, mb.x, mb.y, mb.z, nb); break;
         case 2: gemm_item<2, GU>(a, stage0, stage1, s_gate, mb.x, mb.y, mb.z, nb); break;
         case 3: gemm_item<3, GU>(a, stage0, stage1, s_gate, mb.x, mb.y, mb.z, nb); break;
-        default: gemm_item<4, GU>(a, stage0, stage1, s_gate, mb.x, mb.y, mb.z, nb); break;
+        case 4: gemm_item<4, GU>(a, stage0, stage1, s_gate, mb.x, mb.y, mb.z, nb); break;
+        default: gemm_item<5, GU>(a, stage0, stage1, s_gate, mb.x, mb.y, mb.z, nb); break;
       }
     }
   }

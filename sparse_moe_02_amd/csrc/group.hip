@@ -14,7 +14,7 @@
 // One workgroup per 256 tokens; each rereads every mask (popcounts are cheap), so no
 // workgroup waits for another.
 //
-// Block map: an expert with n rows is split into ceil(n/128) M-blocks of balanced height
+// Block map: an expert with n rows is split into ceil(n/160) M-blocks of balanced height
 // (section "Prefill > Match tile size to expert load": the tile height follows the
 // expert's actual row count); each M-block records its height in 32-row MFMA tiles.
 // Empty experts emit nothing, so their weights are never read.
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kThreads) void k_group(GroupArgs a) {
   __shared__ int s_cnt[kMaxExperts + 1];
   __shared__ uint32_t s_msk[kSubs][kMaxExperts];
   __shared__ int s_base[kSubs][kMaxExperts];
-  __shared__ int s_cls[5], s_clsoff[5], s_clspos[5];
+  __shared__ int s_cls[6], s_clsoff[6], s_clspos[6];
   const int tid = threadIdx.x;
   const int T = a.T, E = a.E, k = a.k;
   const int nblk = (T + kRouteTokens - 1) / kRouteTokens;
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void k_group(GroupArgs a) {
     s_tot[part][e] = tot;
     s_pre[part][e] = pre;
   }
-  if (tid < 5) {
+  if (tid < 6) {
     s_cls[tid] = 0;
     s_clspos[tid] = 0;
   }
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void k_group(GroupArgs a) {
   __syncthreads();
   if (tid == 0) {
     int run = 0;
-    for (int c = 4; c >= 1; --c) {
+    for (int c = kBM / 32; c >= 1; --c) {
       s_clsoff[c] = run;
       run += s_cls[c];
     }

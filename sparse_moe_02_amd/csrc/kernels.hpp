@@ -9,7 +9,7 @@ namespace moe {
 constexpr int kRouteTokens = 32;   // tokens per router workgroup
 constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 16;
-constexpr int kBM = 128;           // max rows of one grouped-GEMM M-block
+constexpr int kBM = 160;           // max rows of one grouped-GEMM M-block (5 MFMA row tiles)
 constexpr int kGemmThreads = 512;  // grouped GEMM workgroup: 8 waves, two per SIMD
 constexpr int kGateUpCols = 256;   // h columns per gate/up work item (8 waves x 32)
 constexpr int kDownCols = 512;     // output columns per down work item (8 waves x 64)
