@@ -59,10 +59,18 @@ __device__ __forceinline__ void dequant8_bf16(uint32_t w, float s, float b, uint
 // wave-uniform).  Issued from inline asm so the compiler neither waits for it nor orders
 // LDS reads behind it on its own: the caller counts its loads, waits with vm_wait_dyn and
 // publishes the data with a barrier.
+// gbase must be wave-uniform; it is read from the first lane, so the compiler keeps it in
+// scalar registers even where it cannot prove the uniformity itself.
+__device__ __forceinline__ const void *uniform_ptr(const void *p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ void dma16(const void *gbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n" ::"s"(
                    __builtin_amdgcn_readfirstlane(lds)),
-               "v"(voff), "s"(gbase)
+               "v"(voff), "s"(uniform_ptr(gbase))
                : "memory", "m0");
 }
 
@@ -70,7 +78,7 @@ __device__ __forceinline__ void dma16(const void *gbase, uint32_t voff, uint32_t
 __device__ __forceinline__ void dma4(const void *gbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2\n" ::"s"(
                    __builtin_amdgcn_readfirstlane(lds)),
-               "v"(voff), "s"(gbase)
+               "v"(voff), "s"(uniform_ptr(gbase))
                : "memory", "m0");
 }
 

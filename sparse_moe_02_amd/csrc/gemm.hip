@@ -76,7 +76,12 @@ __device__ __forceinline__ f32x16 mfma(const uint32_t (&w)[4], const u32x4 &x, c
 template <int MT, bool GU>
 __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, float *s_gate, int e, int row0,
                           int rows, int nb) {
-  const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5;
+  // thread index made opaque so per-lane address arithmetic is computed per item instead
+  // of being hoisted out of the persistent loop (where every row-tile variant's copy
+  // would hold registers for the whole kernel)
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, hf = lane >> 5;
   const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.H, I = a.I;
   const int K = GU ? H : I;
@@ -164,58 +169,59 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
       sc[i] = fp16_to_f32(sp[s_lane[i]]);
       bi[i] = fp16_to_f32(sp[kSStage / 4 + s_lane[i]]);
     }
+    auto afrag = [&](int t, int j) {
+      return *(const u32x4 *)(st + t * 32 * kRowBytes + a_lane + ((a_c0 ^ j) << 4));
+    };
     // word j of the lane's 8 (16-byte part 2*hf + j/4, dword j%4) of its slot in tile i
     auto word = [&](int i, int j) {
       return *(const uint32_t *)(bb + b_off(b_lane[i], 2 * hf + (j >> 2)) + 4 * (j & 3));
     };
-    auto afrag = [&](int t, int j) {
-      return *(const u32x4 *)(st + t * 32 * kRowBytes + a_lane + ((a_c0 ^ j) << 4));
-    };
-    // software pipeline over the eight k-slices: the packed words and dequantised weights
-    // of slice j+1 are prepared while the MFMAs of slice j run, and each row tile's
-    // activation fragment of slice j+1 is read as soon as slice j's two MFMAs have
-    // issued with it (one fragment register set per row tile)
-    u32x4 av[MT];
-    uint32_t d[2][2][4];
-    uint32_t wn[2];
+    // Software pipeline over the eight k-slices.  At the start of slice j the LDS reads
+    // for later slices are issued as one group (activation fragments of slice j+1, packed
+    // words of slice j+1 for tile 1 and j+2 for tile 0).  The slice's MFMAs run tile 0
+    // first, then tile 1; tile 1's weights of slice j are dequantised between the tile-0
+    // MFMAs and tile 0's weights of slice j+1 between the tile-1 MFMAs, so each tile needs
+    // one register set of dequantised weights.
+    u32x4 av[2][MT];
+    uint32_t d0[4], d1[4];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) av[t] = afrag(t, 0);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) dequant8_bf16(word(i, 0), sc[i], bi[i], d[0][i]);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) wn[i] = word(i, 1);
+    for (int t = 0; t < MT; ++t) av[0][t] = afrag(t, 0);
+    dequant8_bf16(word(0, 0), sc[0], bi[0], d0);
+    uint32_t q1 = word(1, 0), q0 = word(0, 1);
+    constexpr int kV = (23 + MT - 1) / MT;  // dequant VALU instructions per MFMA
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int c = j & 1, nx = c ^ 1;
+      uint32_t n1 = 0, n0 = 0;
       if (j < 7) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) dequant8_bf16(wn[i], sc[i], bi[i], d[nx][i]);
-        if (j < 6) {
-#pragma unroll
-          for (int i = 0; i < 2; ++i) wn[i] = word(i, j + 2);
-        }
+        for (int t = 0; t < MT; ++t) av[nx][t] = afrag(t, j + 1);
+        n1 = word(1, j + 1);
       }
+      if (j < 6) n0 = word(0, j + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      dequant8_bf16(q1, sc[1], bi[1], d1);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc[t][0] = mfma(d0, av[c][t], acc[t][0]);
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) acc[t][i] = mfma(d[c][i], av[t], acc[t][i]);
-        if (j < 7) av[t] = afrag(t, j + 1);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      if (j < 7) dequant8_bf16(q0, sc[0], bi[0], d0);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc[t][1] = mfma(d1, av[c][t], acc[t][1]);
       if (j < 7) {
-        // order: the next packed words, then per row tile two MFMAs, each followed by its
-        // share of the dequant VALU work (2 words, 46 instructions), then the tile's next
-        // activation fragment
-        if (j < 6) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-#pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, (46 + 2 * MT - 1) / (2 * MT), 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
+      q1 = n1;
+      q0 = n0;
     }
   };
   // Two-stage ring, unrolled by two so each read names one stage object and the copies
