@@ -21,7 +21,7 @@ struct moe_plan_s {
   int n_cu;
   int dec_grid;  // workgroups of the decode launch (all resident at once)
   // workspace layout (byte offsets)
-  size_t off_ctrl, off_tokmask, off_ids, off_gates, off_counts, off_offsets, off_row_token,
+  size_t off_ctrl, off_tokmask, off_lg, off_rd, off_ids, off_gates, off_counts, off_offsets, off_row_token,
       off_row_gate, off_slot_row, off_mblocks, off_h, off_y, off_lrec, off_hrec, off_dend, total;
 };
 
@@ -54,6 +54,8 @@ void layout(moe_plan_s &p) {
   };
   p.off_ctrl = take(sizeof(Ctrl));
   p.off_tokmask = take(nblk * E * 4);
+  p.off_lg = take(C * E * 4);
+  p.off_rd = take(C * E * 4);
   p.off_ids = take(C * k * 4);
   p.off_gates = take(C * k * 4);
   p.off_counts = take((E + 1) * 4);
@@ -220,6 +222,8 @@ moe_status moe_forward_prefill(moe_plan_t p, const void *x, int64_t T, void *out
     ra.ids = at<int32_t>(ws, p->off_ids);
     ra.gates = at<float>(ws, p->off_gates);
     ra.tokmask = at<uint32_t>(ws, p->off_tokmask);
+    ra.lg = at<float>(ws, p->off_lg);
+    ra.rd = at<float>(ws, p->off_rd);
     ra.ctrl = ctrl;
     if (dbg) {
       ra.dbg_ids = dbg->topk_ids ? dbg->topk_ids + (size_t)c0 * k : nullptr;

@@ -4,13 +4,15 @@
 // different workload shapes": the router scores every routed expert and keeps eight
 // per token.  The selection is defined on exact logits (ties: lower index wins).
 //
-// Prefill: one workgroup per 32 tokens.  Logits and the bound sum_h |x_h w_eh| come
-// from two bf16 MFMA chains with fp32 accumulation (bf16 x bf16 products are exact in
-// fp32).  A token's fp32 ranking is certified when every chosen logit minus its error
-// radius exceeds every other logit plus its radius; otherwise one wave re-ranks it:
-// undecided experts get binary64 logits (wave-parallel sums), and experts that even these
-// cannot order are summed sequentially in ascending h in binary64, which reproduces the
-// exact-product sequential sum bit for bit.
+// Prefill, two launches.  k_route_logits tiles (64 tokens x 64 experts) over the whole
+// grid so every CU works and the router rows are read from L2 only T/64 times; logits
+// and the bound sum_h |x_h w_eh| come from two bf16 MFMA chains with fp32 accumulation
+// (bf16 x bf16 products are exact in fp32) and go to the workspace.  k_route then takes
+// 32 tokens per workgroup: a token's fp32 ranking is certified when every chosen logit
+// minus its error radius exceeds every other logit plus its radius; otherwise one wave
+// re-ranks it: undecided experts get binary64 logits (wave-parallel sums), and experts
+// that even these cannot order are summed sequentially in ascending h in binary64, which
+// reproduces the exact-product sequential sum bit for bit.
 #include <type_traits>
 
 #include "common.hpp"
@@ -24,40 +26,137 @@ namespace {
 constexpr float kU32 = 5.9604644775390625e-8f;       // 2^-24
 // ---------------------------------------------------------------------------- prefill
 
-constexpr int kRouteThreads = 512;   // 8 waves: wave w owns experts 32w..32w+31
+constexpr int kRouteThreads = 512;   // selection: 8 waves, four tokens each
 constexpr int kKC = 64;              // k per chunk (one LDS stage)
 constexpr int kKP = 128;             // k per fresh fp32 partial sum (two chunks)
-constexpr int kWStages = 3;          // router-row chunks in LDS (two loaded ahead: they hit L2)
-constexpr int kXStages = 12;         // token-row chunks in LDS (eleven ahead: they come from HBM)
-constexpr int kXStage = kRouteTokens * kKC * 2;           // 4 KiB: 32 token rows
-constexpr int kWStage = kMaxExperts * kKC * 2;            // 32 KiB: 256 router rows
+constexpr int kLT = 64;              // logits tile: tokens
+constexpr int kLE = 64;              // logits tile: experts
+constexpr int kLThreads = 512;       // eight waves: four 32x32 tiles x {logit, |x||w|} chains
+constexpr int kLStages = 8;          // chunks in LDS (seven loaded ahead)
+constexpr int kLStage = (kLT + kLE) * kKC * 2;  // 16 KiB
 
 // 16-byte piece `c` (0..7) of staged 128-byte row r: swizzled so that the MFMA operand
 // reads (16 rows, same piece) hit distinct banks
 __device__ __forceinline__ int roff(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
-struct RouteSmem {
-  union {
-    struct {                          // logits phase
-      uint8_t w[kWStages][kWStage];
-      uint8_t x[kXStages][kXStage];
-    } st;
-    struct {                          // selection and re-ranking phase
-      float l[kRouteTokens][kMaxExperts];  // fp32 logit (+bias)
-      float r[kRouteTokens][kMaxExperts];  // its error radius
-      WaveSel ws[kRouteThreads / kWave];
-    } sel;
+// Logits and error radii of a 64-token x 64-expert tile.  For each 64-k chunk the 64
+// token rows and 64 router rows go global -> LDS with direct-to-LDS loads (8 rows x 128
+// bytes per instruction, kLStages-1 chunks ahead).  Wave w < 4 multiplies token tile w&1
+// with expert tile (w>>1)&1; wave w+4 does the same over sign-cleared operands, giving
+// sum |x w| for the error radius (two waves per SIMD, so each hides the other's LDS
+// latency).  H must be a multiple of 128.  Each 128-k partial is a fresh MFMA chain added to the running fp32 total,
+// so a product passes through at most kKP/16 + 15 roundings in its partial and H/kKP in
+// the total.
+__global__ __launch_bounds__(kLThreads) void k_route_logits(RouteArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t st[kLStages][kLStage];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int H = a.H, E = a.E, T = a.T;
+  const int t0 = blockIdx.x * kLT, e0 = blockIdx.y * kLE;
+  const int m = lane & 31, hf = lane >> 5;
+  const int tile = wv & 3, tt = tile & 1, et = tile >> 1;
+  const bool absw = wv >= 4;
+  // wave wv loads token rows 8wv..8wv+7 and router rows 8wv..8wv+7 of the tile (one
+  // instruction each); lane L -> row base + L/8, physical piece L%8 holding logical piece
+  // (L%8) ^ f(row).  Rows past the end repeat the last one.
+  const int lr = 8 * wv + (lane >> 3);
+  const int piece = (lane & 7) ^ ((lr >> 1) & 7);
+  const uint32_t xoff = (uint32_t)min(t0 + lr, T - 1) * (uint32_t)H * 2u + 16u * (uint32_t)piece;
+  const uint32_t woff = (uint32_t)min(e0 + lr, E - 1) * (uint32_t)H * 2u + 16u * (uint32_t)piece;
+  const int nch = H / kKC;
+  // Workgroups walk the k chunks from different starting points (even, so the 128-k
+  // partials keep their pairs): rows are 2*H bytes apart, so workgroups in step would
+  // all address the same offset within their rows at once.
+  const int rot = 2 * ((blockIdx.x + 3 * blockIdx.y) % (nch / 2));
+  auto issue = [&](int c) {
+    const uint32_t base = lds_addr(&st[c % kLStages][0]) + (uint32_t)wv * 1024u;
+    const uint32_t kc = (uint32_t)((c + rot) % nch);
+    dma16(a.x, xoff + 128u * kc, base);
+    dma16(a.wr16, woff + 128u * kc, base + (uint32_t)(kLT * 128));
   };
+  f32x16 tot = {};
+  for (int c = 0; c < kLStages - 1 && c < nch; ++c) issue(c);
+  // one chunk: wait for its loads, publish them, issue the loads of chunk c+kLStages-1,
+  // read all four slices' fragments
+  auto stage_in = [&](int c, u32x4 (&av)[kKC / 16], u32x4 (&bv)[kKC / 16]) {
+    // chunk c is complete once only the loads of chunks c+1 .. (last issued) remain
+    vm_wait_dyn(2 * (min(c + kLStages - 2, nch - 1) - c));
+    __syncthreads();  // chunk c visible to every wave; chunk c-1's stage is free
+    if (c + kLStages - 1 < nch) issue(c + kLStages - 1);
+    const uint8_t *xs = &st[c % kLStages][0];
+    const uint8_t *ws = xs + kLT * 128;
+#pragma unroll
+    for (int j = 0; j < kKC / 16; ++j) {
+      av[j] = *(const u32x4 *)(xs + roff(32 * tt + m, 2 * j + hf));
+      bv[j] = *(const u32x4 *)(ws + roff(32 * et + m, 2 * j + hf));
+    }
+  };
+  // the same loop for both kinds of wave, the |.| waves clearing the sign bits first;
+  // each pair of chunks (128 k) is two fresh MFMA chains (even and odd slices) added to
+  // the running total
+  auto run = [&](auto abs_tag) {
+    constexpr bool kAbs = decltype(abs_tag)::value;
+    const u32x4 msk = {0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu};
+    auto op = [&](const u32x4 &v) { return __builtin_bit_cast(bf16x8, kAbs ? (u32x4)(v & msk) : v); };
+    for (int c = 0; c < nch; c += 2) {
+      u32x4 av[kKC / 16], bv[kKC / 16];
+      stage_in(c, av, bv);
+      f32x16 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op(av[0]), op(bv[0]), (f32x16){}, 0, 0, 0);
+      f32x16 acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op(av[1]), op(bv[1]), (f32x16){}, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op(av[2]), op(bv[2]), acc, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op(av[3]), op(bv[3]), acc1, 0, 0, 0);
+      stage_in(c + 1, av, bv);
+#pragma unroll
+      for (int j = 0; j < kKC / 16; ++j) {
+        f32x16 &ac = (j & 1) ? acc1 : acc;
+        ac = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op(av[j]), op(bv[j]), ac, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) tot[j] += acc[j] + acc1[j];
+    }
+  };
+  if (absw)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
+  // the abs waves hand sum |x w| to the logit waves through LDS
+  __syncthreads();
+  float *ab = (float *)&st[0][0] + tile * (64 * 16);
+  if (absw) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) ab[j * 64 + lane] = tot[j];
+  }
+  __syncthreads();
+  if (absw) return;
+  // Error radius of the fp32 logit: a product passes through at most kKP/16 + 15
+  // roundings in its partial's MFMA chain and H/kKP in the running total; doubled for
+  // margin, plus the bias addition, the sequential binary64 reference's own error and
+  // product underflow.
+  const float c32 = 2.0f * (float)(kKP / 16 + 15 + H / kKP) + 4.0f;
+  const int e = e0 + 32 * et + m;
+  if (e < E) {
+    const float bb = a.bias ? a.bias[e] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int t = t0 + 32 * tt + 8 * (j >> 2) + 4 * hf + (j & 3);
+      if (t < T) {
+        const float l = tot[j] + bb;
+        const float sab = ab[j * 64 + lane];
+        a.lg[(size_t)t * E + e] = l;
+        a.rd[(size_t)t * E + e] = c32 * kU32 * sab * 1.01f + 2.0f * kU32 * fabsf(l) + 1e-12f * sab + 1e-30f;
+      }
+    }
+  }
+}
+
+struct RouteSmem {
+  float l[kRouteTokens][kMaxExperts];  // fp32 logit (+bias)
+  float r[kRouteTokens][kMaxExperts];  // its error radius
+  WaveSel ws[kRouteThreads / kWave];
 };
 
 // One workgroup per 32 tokens.
-//  1. logits: for each 64-k chunk, the 32 token rows and all router rows go global ->
-//     LDS with direct-to-LDS loads (8 rows x 128 bytes per instruction); token rows are
-//     loaded eleven chunks ahead, router rows (shared by every workgroup, so L2 hits)
-//     two ahead; wave w multiplies its 32 experts with the 32 tokens.  Each 128-k partial is
-//     a fresh MFMA chain added to the running fp32 total, so a product passes through at
-//     most kKP/16 + 15 roundings in its partial and H/kKP in the total.  A second MFMA
-//     chain over sign-cleared operands gives sum |x w| for the error radius.
+//  1. fp32 logits and radii of its tokens from the workspace (or, for a float32 router,
+//     none: every expert is re-ranked in binary64).
 //  2. fp32 selection, sixteen lanes per token, certified against the radii.
 //  3. tokens the certificate does not settle are re-ranked by one wave each, in parallel.
 __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
@@ -67,8 +166,8 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
   __shared__ int s_list[kRouteTokens];
   __shared__ int s_nflag;
   __shared__ uint32_t s_mask[kMaxExperts];
-  auto &s_l = sm.sel.l;
-  auto &s_r = sm.sel.r;
+  auto &s_l = sm.l;
+  auto &s_r = sm.r;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = a.H, E = a.E, k = a.k;
@@ -79,105 +178,29 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
   if (tid == 0) s_nflag = 0;
 
   if (a.wr16) {
-    const int m = lane & 31, hf = lane >> 5;
-    const int nct = (E + 31) / 32;
-    const bool active = wv < nct;
-    // loads of one chunk: waves 0..3 each bring 8 token rows, every wave brings its own
-    // 32 router rows (4 instructions of 8 rows); lane L -> row base + L/8, physical piece
-    // L%8 holding logical piece (L%8) ^ f(row)
-    const int xr = 8 * wv + (lane >> 3);
-    const uint32_t xoff0 =
-        (uint32_t)(t0 + min(xr, nt - 1)) * (uint32_t)H * 2u + 16u * (uint32_t)((lane & 7) ^ ((xr >> 1) & 7));
-    uint32_t woff0[4];
+    // sixteen loads of each array in flight per thread (one batch for E = 256)
+    constexpr int kB = 16;
+    for (int i0 = tid; i0 < kRouteTokens * E; i0 += kRouteThreads * kB) {
+      float lv[kB], rv[kB];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = 32 * wv + 8 * u + (lane >> 3);
-      woff0[u] = (uint32_t)min(e, E - 1) * (uint32_t)H * 2u + 16u * (uint32_t)((lane & 7) ^ ((e >> 1) & 7));
-    }
-    auto issue_x = [&](int c) {
-      if (wv < 4) dma16(a.x, xoff0 + 128u * (uint32_t)c, lds_addr(&sm.st.x[c % kXStages][0]) + (uint32_t)wv * 1024u);
-    };
-    auto issue_w = [&](int c) {
-      const uint32_t base = lds_addr(&sm.st.w[c % kWStages][0]);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) dma16(a.wr16, woff0[u] + 128u * (uint32_t)c, base + (uint32_t)(4 * wv + u) * 1024u);
-    };
-    const int nch = H / kKC;
-    f32x16 tot = {}, acc = {}, aab = {};
-    const u32x4 msk = {0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu};
-    f32x16 acc1 = {}, aab1 = {};
-    auto compute = [&](int c) {
-      const uint8_t *xs = &sm.st.x[c % kXStages][0];
-      const uint8_t *ws = &sm.st.w[c % kWStages][0];
-      if ((c & 1) == 0) {
-        acc = (f32x16){};
-        acc1 = (f32x16){};
-      }
-      // all four slices' fragments first, then two independent chains per quantity
-      u32x4 av[kKC / 16], bv[kKC / 16];
-#pragma unroll
-      for (int j = 0; j < kKC / 16; ++j) {
-        av[j] = *(const u32x4 *)(xs + roff(m, 2 * j + hf));
-        bv[j] = *(const u32x4 *)(ws + roff(32 * wv + m, 2 * j + hf));
+      for (int u = 0; u < kB; ++u) {
+        const int i = min(i0 + u * kRouteThreads, kRouteTokens * E - 1);
+        const int m = i / E, e = i - m * E;
+        const size_t o = (size_t)(t0 + min(m, nt - 1)) * E + e;
+        lv[u] = a.lg[o];
+        rv[u] = a.rd[o];
       }
 #pragma unroll
-      for (int j = 0; j < kKC / 16; ++j) {
-        f32x16 &ac = (j & 1) ? acc1 : acc;
-        f32x16 &ab = (j & 1) ? aab1 : aab;
-        ac = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[j]), __builtin_bit_cast(bf16x8, bv[j]),
-                                                     ac, 0, 0, 0);
-        ab = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, (u32x4)(av[j] & msk)),
-                                                     __builtin_bit_cast(bf16x8, (u32x4)(bv[j] & msk)), ab, 0, 0, 0);
-      }
-      if (c & 1) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) tot[j] += acc[j] + acc1[j];
-      }
-    };
-    // prologue: token rows of chunks 0..kXStages-2, router rows of chunks 0..kWStages-2.
-    // Step c issues the token rows of chunk c+kXStages-1 and then the router rows of
-    // chunk c+kWStages-1; chunk c's loads are complete once only the loads issued at
-    // step c-1 and later remain.
-    for (int c = 0; c < kXStages - 1 && c < nch; ++c) issue_x(c);
-    for (int c = 0; c < kWStages - 1 && c < nch; ++c) issue_w(c);
-    int last_step = 0;  // loads issued by the previous step
-    for (int c = 0; c < nch; ++c) {
-      vm_wait_dyn(c == 0 ? 0 : last_step);
-      __syncthreads();  // chunk c visible to every wave; chunk c-1's stages are free
-      last_step = 0;
-      if (c + kXStages - 1 < nch) {
-        issue_x(c + kXStages - 1);
-        last_step += wv < 4 ? 1 : 0;
-      }
-      if (c + kWStages - 1 < nch) {
-        issue_w(c + kWStages - 1);
-        last_step += 4;
-      }
-      if (active) compute(c);
-    }
-    __syncthreads();  // every wave is past its last stage read before the logits reuse it
-    if (active) {
-      // Error radius of the fp32 logit: a product passes through at most kKP/16 + 15
-      // roundings in its partial's MFMA chain and H/kKP in the running total; doubled
-      // for margin, plus the bias addition, the sequential binary64 reference's own
-      // error and product underflow.
-      const float c32 = 2.0f * (float)(kKP / 16 + 15 + H / kKP) + 4.0f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) aab[j] += aab1[j];
-      const int e = wv * 32 + m;
-      if (e < E) {
-        const float bb = a.bias ? a.bias[e] : 0.0f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int row = 8 * (j >> 2) + 4 * hf + (j & 3);
-          const float l = tot[j] + bb;
-          s_l[row][e] = l;
-          s_r[row][e] = c32 * kU32 * aab[j] * 1.01f + 2.0f * kU32 * fabsf(l) + 1e-12f * aab[j] + 1e-30f;
+      for (int u = 0; u < kB; ++u) {
+        const int i = i0 + u * kRouteThreads;
+        if (i < kRouteTokens * E) {
+          const int m = i / E, e = i - m * E;
+          s_l[m][e] = lv[u];
+          s_r[m][e] = rv[u];
         }
       }
     }
   } else {
-    // float32 router weights: no fp32 ranking; every expert is re-ranked in binary64.
     for (int i = tid; i < kRouteTokens * kMaxExperts; i += kRouteThreads) {
       (&s_l[0][0])[i] = 0.0f;
       (&s_r[0][0])[i] = INFINITY;
@@ -277,18 +300,35 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
   // out for sure; the rest are candidates for rerank_wave.
   const int nflag = s_nflag;
   if (nflag) {
-    WaveSel &W = sm.sel.ws[wv];
+    WaveSel &W = sm.ws[wv];
     for (int f = wv; f < nflag; f += kRouteThreads / kWave) {
       const int m = s_list[f];
       const float lo = s_min_in[m], hi = s_max_out[m];
       const bool fp32_ok = a.wr16 != nullptr;
-      auto in_sel = [&](int e) {
-        bool r = false;
-        for (int j = 0; j < k; ++j) r |= s_sel[m][j] == e;
-        return r;
-      };
-      auto known_in = [&](int e) { return fp32_ok && in_sel(e) && s_l[m][e] - s_r[m][e] > hi; };
-      auto known_out = [&](int e) { return fp32_ok && !in_sel(e) && s_l[m][e] + s_r[m][e] < lo; };
+      // classify this lane's experts e = lane + 64 i up front (all LDS reads issued
+      // together): bit i of kin / kout
+      int sel[kMaxTopK];
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) sel[j] = j < k ? s_sel[m][j] : -1;
+      float lv[kMaxExperts / kWave], rv[kMaxExperts / kWave];
+#pragma unroll
+      for (int i = 0; i < kMaxExperts / kWave; ++i) {
+        const int e = lane + kWave * i;
+        lv[i] = e < E ? s_l[m][e] : 0.0f;
+        rv[i] = e < E ? s_r[m][e] : 0.0f;
+      }
+      uint32_t kin = 0, kout = 0;
+#pragma unroll
+      for (int i = 0; i < kMaxExperts / kWave; ++i) {
+        const int e = lane + kWave * i;
+        bool chosen = false;
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j) chosen |= sel[j] == e;
+        kin |= (fp32_ok && chosen && lv[i] - rv[i] > hi) ? (1u << i) : 0u;
+        kout |= (fp32_ok && !chosen && lv[i] + rv[i] < lo) ? (1u << i) : 0u;
+      }
+      auto known_in = [&](int e) { return ((kin >> (e / kWave)) & 1u) != 0u; };
+      auto known_out = [&](int e) { return ((kout >> (e / kWave)) & 1u) != 0u; };
       auto l32 = [&](int e) { return s_l[m][e]; };
       const size_t o = (size_t)(t0 + m) * k;
       rerank_wave(W, known_in, known_out, l32, E, k, a.x + (size_t)(t0 + m) * H, a.wr16, a.wr32, a.bias, H, lane,
@@ -320,6 +360,11 @@ __global__ void k_ctrl_init(Ctrl *c, uint32_t *clear, int n_words) {
 }  // namespace
 
 hipError_t launch_route(const RouteArgs &a, hipStream_t s) {
+  if (a.wr16) {
+    hipLaunchKernelGGL(k_route_logits, dim3((a.T + kLT - 1) / kLT, (a.E + kLE - 1) / kLE), dim3(kLThreads), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int nb = (a.T + kRouteTokens - 1) / kRouteTokens;
   hipLaunchKernelGGL(k_route, dim3(nb), dim3(kRouteThreads), 0, s, a);
   return hipGetLastError();

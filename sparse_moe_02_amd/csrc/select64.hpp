@@ -12,27 +12,34 @@ namespace {
 
 constexpr double kU64 = 1.1102230246251565404e-16;   // 2^-53
 
-// Binary64 dot product of x with one router row, by one wave.  Lane `lane` takes the
-// 8-element chunks c = lane + 64 i (ascending i) and sums its exact products
-// sequentially; a butterfly over the wave gives every lane the same total.  Also
-// returns sum |x_h w_h|.  Each product passes through at most seq + 6 roundings with
-// seq = 8*ceil(H/512).
-__device__ void wave_dot64(const uint16_t *x, const uint16_t *w16, const float *w32, int H,
-                           int lane, double &l, double &a) {
-  double s = 0.0, sa = 0.0;
-  // four chunks' loads in flight before their products are summed (in ascending order)
+// Binary64 dot products of x with up to G router rows (rows past n are skipped), by one
+// wave; the token row is read once and the loads of all G rows are in flight together.
+// For each row, lane `lane` takes the 8-element chunks c = lane + 64 i (ascending i) and
+// sums its exact products sequentially; a butterfly over the wave gives every lane the
+// same total.  Also returns sum |x_h w_h|.  Each product passes through at most seq + 6
+// roundings with seq = 8*ceil(H/512).
+template <int G>
+__device__ void wave_dot64_n(const uint16_t *x, const uint16_t *const *w16, const float *const *w32, int n, int H,
+                             int lane, double *l, double *a) {
+  double s[G], sa[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) s[g] = sa[g] = 0.0;
   for (int c0 = lane; c0 < H / 8; c0 += 4 * kWave) {
-    uint4 xv[4], wa[4], wb[4];
+    uint4 xv[4], wa[G][4], wb[G][4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int c = c0 + u * kWave;
       const int cc = c < H / 8 ? c : lane;
       xv[u] = *(const uint4 *)(x + 8 * cc);
-      if (w16) {
-        wa[u] = *(const uint4 *)(w16 + 8 * cc);
-      } else {
-        wa[u] = *(const uint4 *)(w32 + 8 * cc);
-        wb[u] = *(const uint4 *)(w32 + 8 * cc + 4);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        if (g >= n) break;
+        if (w16) {
+          wa[g][u] = *(const uint4 *)(w16[g] + 8 * cc);
+        } else {
+          wa[g][u] = *(const uint4 *)(w32[g] + 8 * cc);
+          wb[g][u] = *(const uint4 *)(w32[g] + 8 * cc + 4);
+        }
       }
     }
 #pragma unroll
@@ -40,26 +47,35 @@ __device__ void wave_dot64(const uint16_t *x, const uint16_t *w16, const float *
       if (c0 + u * kWave >= H / 8) break;
       const float xf[8] = {bf16_lo(xv[u].x), bf16_hi(xv[u].x), bf16_lo(xv[u].y), bf16_hi(xv[u].y),
                            bf16_lo(xv[u].z), bf16_hi(xv[u].z), bf16_lo(xv[u].w), bf16_hi(xv[u].w)};
-      float wf[8];
-      if (w16) {
-        wf[0] = bf16_lo(wa[u].x); wf[1] = bf16_hi(wa[u].x); wf[2] = bf16_lo(wa[u].y); wf[3] = bf16_hi(wa[u].y);
-        wf[4] = bf16_lo(wa[u].z); wf[5] = bf16_hi(wa[u].z); wf[6] = bf16_lo(wa[u].w); wf[7] = bf16_hi(wa[u].w);
-      } else {
-        wf[0] = __uint_as_float(wa[u].x); wf[1] = __uint_as_float(wa[u].y);
-        wf[2] = __uint_as_float(wa[u].z); wf[3] = __uint_as_float(wa[u].w);
-        wf[4] = __uint_as_float(wb[u].x); wf[5] = __uint_as_float(wb[u].y);
-        wf[6] = __uint_as_float(wb[u].z); wf[7] = __uint_as_float(wb[u].w);
-      }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const double p = (double)xf[i] * (double)wf[i];  // exact
-        s += p;
-        sa += fabs(p);
+      for (int g = 0; g < G; ++g) {
+        if (g >= n) break;
+        float wf[8];
+        if (w16) {
+          wf[0] = bf16_lo(wa[g][u].x); wf[1] = bf16_hi(wa[g][u].x); wf[2] = bf16_lo(wa[g][u].y);
+          wf[3] = bf16_hi(wa[g][u].y); wf[4] = bf16_lo(wa[g][u].z); wf[5] = bf16_hi(wa[g][u].z);
+          wf[6] = bf16_lo(wa[g][u].w); wf[7] = bf16_hi(wa[g][u].w);
+        } else {
+          wf[0] = __uint_as_float(wa[g][u].x); wf[1] = __uint_as_float(wa[g][u].y);
+          wf[2] = __uint_as_float(wa[g][u].z); wf[3] = __uint_as_float(wa[g][u].w);
+          wf[4] = __uint_as_float(wb[g][u].x); wf[5] = __uint_as_float(wb[g][u].y);
+          wf[6] = __uint_as_float(wb[g][u].z); wf[7] = __uint_as_float(wb[g][u].w);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const double p = (double)xf[i] * (double)wf[i];  // exact
+          s[g] += p;
+          sa[g] += fabs(p);
+        }
       }
     }
   }
-  l = wave_sum_f64(s);
-  a = wave_sum_f64(sa);
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    if (g >= n) break;
+    l[g] = wave_sum_f64(s[g]);
+    a[g] = wave_sum_f64(sa[g]);
+  }
 }
 
 // Error radius of a binary64 logit (plus bias) summed in any order with at most `depth`
@@ -70,7 +86,7 @@ __device__ __forceinline__ double radius64(double lb, double a, int H, int depth
   return ((double)depth + 2.0 + (double)H) * kU64 * a * 1.001 + 4.0 * kU64 * fabs(lb) + 1e-300;
 }
 
-// Additions on any path of wave_dot64's sum.
+// Additions on any path of wave_dot64_n's sum.
 __device__ __forceinline__ int wave_dot64_depth(int H) { return 8 * ((H + 511) / 512) + 6; }
 
 // Sequential ascending-h binary64 logit: the same arithmetic as the plain definition.
@@ -256,16 +272,36 @@ __device__ void rerank_wave(WaveSel &W, KnownIn known_in, KnownOut known_out, Fp
     n_c += __popcll(bc);
   }
   n_in = min(n_in, k);
-  // 2. binary64 logits of the candidates, one wave-wide dot product each
-  for (int c = 0; c < n_c; ++c) {
-    const int e = W.cand[c];
-    double l, ab;
-    wave_dot64(xrow, wr16 ? wr16 + (size_t)e * H : nullptr, wr32 ? wr32 + (size_t)e * H : nullptr, H, lane, l, ab);
-    if (bias) l += (double)bias[e];
-    if (lane == 0) {
-      W.v[c] = l;
-      W.rad[c] = __double2float_ru(radius64(l, ab, H, wave_dot64_depth(H)));
+  // 2. binary64 logits of the candidates, wave-wide dot products, kG rows at a time
+  constexpr int kG = 4;
+  for (int c0 = 0; c0 < n_c; c0 += kG) {
+    const int ng = min(kG, n_c - c0);
+    const uint16_t *r16[kG];
+    const float *r32[kG];
+#pragma unroll
+    for (int g = 0; g < kG; ++g) {
+      const int e = W.cand[c0 + min(g, ng - 1)];
+      r16[g] = wr16 ? wr16 + (size_t)e * H : nullptr;
+      r32[g] = wr32 ? wr32 + (size_t)e * H : nullptr;
     }
+    double l[kG], ab[kG];
+    if (wr16)
+      wave_dot64_n<kG>(xrow, r16, nullptr, ng, H, lane, l, ab);
+    else
+      wave_dot64_n<kG / 2>(xrow, nullptr, r32, min(ng, kG / 2), H, lane, l, ab);
+    const int done = wr16 ? ng : min(ng, kG / 2);
+#pragma unroll
+    for (int g = 0; g < kG; ++g) {
+      if (g >= done) break;
+      const int e = W.cand[c0 + g];
+      double lv = l[g];
+      if (bias) lv += (double)bias[e];
+      if (lane == 0) {
+        W.v[c0 + g] = lv;
+        W.rad[c0 + g] = __double2float_ru(radius64(lv, ab[g], H, wave_dot64_depth(H)));
+      }
+    }
+    if (!wr16) c0 -= kG - done;  // float32 rows go two at a time
   }
   wave_sync();
   // 3. membership among the candidates for the r remaining places
