@@ -53,7 +53,7 @@ void layout(moe_plan_s &p) {
     return at;
   };
   p.off_ctrl = take(sizeof(Ctrl));
-  p.off_tokmask = take(nblk * E * 4);
+  p.off_tokmask = take(nblk * kMaxExperts * 4);
   p.off_lg = take(C * E * 4);
   p.off_rd = take(C * E * 4);
   p.off_ids = take(C * k * 4);

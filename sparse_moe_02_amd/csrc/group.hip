@@ -12,7 +12,9 @@
 // expert, which every token visits.
 //
 // One workgroup per 256 tokens; each rereads every mask (popcounts are cheap), so no
-// workgroup waits for another.
+// workgroup waits for another.  Every global read the workgroup needs (all masks, and the
+// ids and gates of its own tokens) is issued before the first is used, so the kernel
+// pays one memory latency.
 //
 // Block map: an expert with n rows is split into ceil(n/160) M-blocks of balanced height
 // (section "Prefill > Match tile size to expert load": the tile height follows the
@@ -28,50 +30,81 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kSubs = 8;                                 // router workgroups per group workgroup
 constexpr int kTokensPerBlock = kSubs * kRouteTokens;   // 256
-constexpr int kParts = kThreads / kMaxExperts;          // 4 threads per expert column
+constexpr int kQuads = kMaxExperts / 4;                 // four experts per 16-byte mask load
+constexpr int kParts = kThreads / kQuads;               // 16 threads per four-expert column
 
 // Workgroup g handles tokens [256 g, 256 g + 256) = router workgroups 8g .. 8g+7.  Every
 // workgroup reads all bit masks to get the expert totals (hence the offsets) and the
 // count of earlier tokens per expert; workgroup 0 also writes the offsets and the block
 // map and resets the work queues.
+constexpr int kScat = (kTokensPerBlock * (kMaxTopK + 1) + kThreads - 1) / kThreads;  // scatter items per thread
+constexpr int kBatch = 8;                               // 16-byte mask loads in flight per thread
+
 __global__ __launch_bounds__(kThreads) void k_group(GroupArgs a) {
   __shared__ int s_tot[kParts][kMaxExperts];
   __shared__ int s_pre[kParts][kMaxExperts];
+  static_assert(sizeof(int) * kParts * kMaxExperts * 2 <= 32768, "count tables");
   __shared__ int s_off[kMaxExperts + 2];
   __shared__ int s_cnt[kMaxExperts + 1];
-  __shared__ uint32_t s_msk[kSubs][kMaxExperts];
+  __shared__ __attribute__((aligned(16))) uint32_t s_msk[kSubs][kMaxExperts];
   __shared__ int s_base[kSubs][kMaxExperts];
   __shared__ int s_cls[6], s_clsoff[6], s_clspos[6];
   const int tid = threadIdx.x;
   const int T = a.T, E = a.E, k = a.k;
   const int nblk = (T + kRouteTokens - 1) / kRouteTokens;
   const int sb0 = blockIdx.x * kSubs;
+  const int t0 = blockIdx.x * kTokensPerBlock;
   const uint32_t *__restrict__ mask = a.tokmask;
 
-  // 1. per expert: total count, and count over router workgroups before sb0
+  // 0. the expert ids and gates this thread scatters in step 3 (loads issued now)
+  int sc_e[kScat];
+  float sc_g[kScat];
+#pragma unroll
+  for (int u = 0; u < kScat; ++u) {
+    const int i = tid + u * kThreads;
+    const int lt = i / (k + 1), j = i - lt * (k + 1);
+    const int t = t0 + lt;
+    const bool ld = lt < kTokensPerBlock && t < T && j < k;
+    sc_e[u] = ld ? a.ids[(size_t)t * k + j] : -1;
+    sc_g[u] = ld ? a.gates[(size_t)t * k + j] : 1.0f;
+  }
+
+  // 1. per expert: total count, and count over router workgroups before sb0; the masks
+  // of this workgroup's own router workgroups are kept for the ranks.  Thread (q, part)
+  // reads experts 4q..4q+3 of router workgroups part, part+16, ... (rows are 256 words,
+  // zero past E).
   {
-    const int e = tid % kMaxExperts, part = tid / kMaxExperts;
-    int tot = 0, pre = 0;
-    if (e < E) {
-      // batches of kBatch independent loads in flight per thread
-      constexpr int kBatch = 16;
-      for (int b0 = part; b0 < nblk; b0 += kParts * kBatch) {
-        uint32_t mv[kBatch];
+    const int q = tid % kQuads, part = tid / kQuads;
+    int tot[4] = {0, 0, 0, 0}, pre[4] = {0, 0, 0, 0};
+    for (int b0 = part; b0 < nblk; b0 += kParts * kBatch) {
+      uint4 mv[kBatch];
 #pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
-          const int b = b0 + kParts * i;
-          mv[i] = b < nblk ? mask[(size_t)b * E + e] : 0u;
-        }
+      for (int i = 0; i < kBatch; ++i) {
+        const int b = b0 + kParts * i;
+        mv[i] = b < nblk ? *(const uint4 *)(mask + (size_t)b * kMaxExperts + 4 * q) : make_uint4(0, 0, 0, 0);
+      }
 #pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
-          const int c = __popc(mv[i]);
-          tot += c;
-          pre += b0 + kParts * i < sb0 ? c : 0;
+      for (int i = 0; i < kBatch; ++i) {
+        const int b = b0 + kParts * i;
+        const uint32_t w[4] = {mv[i].x, mv[i].y, mv[i].z, mv[i].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int n = __popc(w[c]);
+          tot[c] += n;
+          pre[c] += b < sb0 ? n : 0;
         }
+        if (b >= sb0 && b < sb0 + kSubs) *(uint4 *)&s_msk[b - sb0][4 * q] = mv[i];
       }
     }
-    s_tot[part][e] = tot;
-    s_pre[part][e] = pre;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      s_tot[part][4 * q + c] = tot[c];
+      s_pre[part][4 * q + c] = pre[c];
+    }
+  }
+  for (int i = tid; i < kSubs * kMaxExperts; i += kThreads) {
+    const int j = i / kMaxExperts;
+    if (sb0 + j >= nblk) s_msk[j][i % kMaxExperts] = 0u;
   }
   if (tid < 6) {
     s_cls[tid] = 0;
@@ -105,11 +138,6 @@ __global__ __launch_bounds__(kThreads) void k_group(GroupArgs a) {
     }
     if (tid == kWave - 1) s_off[E + 1] = incl;
   }
-  // masks of this workgroup's router workgroups
-  for (int i = tid; i < kSubs * kMaxExperts; i += kThreads) {
-    const int j = i / kMaxExperts, e = i % kMaxExperts;
-    s_msk[j][e] = (e < E && sb0 + j < nblk) ? mask[(size_t)(sb0 + j) * E + e] : 0u;
-  }
   __syncthreads();
   if (tid < E) {
     int run = s_off[tid];
@@ -122,21 +150,22 @@ __global__ __launch_bounds__(kThreads) void k_group(GroupArgs a) {
   __syncthreads();
 
   // 3. scatter: grouped row of every (token, chosen expert) and of the shared slot
-  const int t0 = blockIdx.x * kTokensPerBlock;
-  for (int i = tid; i < kTokensPerBlock * (k + 1); i += kThreads) {
+#pragma unroll
+  for (int u = 0; u < kScat; ++u) {
+    const int i = tid + u * kThreads;
     const int lt = i / (k + 1), j = i - lt * (k + 1);
     const int t = t0 + lt;
-    if (t >= T) continue;
+    if (lt >= kTokensPerBlock || t >= T) continue;
     int pos;
     float g;
     if (j < k) {
-      const int e = a.ids[(size_t)t * k + j];
+      const int e = sc_e[u];
       if ((unsigned)e >= (unsigned)E) continue;  // cannot happen for router output
       const int sj = lt / kRouteTokens;
       const uint32_t below = (1u << (lt % kRouteTokens)) - 1u;
       pos = s_base[sj][e] + __popc(s_msk[sj][e] & below);
       if (pos < s_off[e] || pos >= s_off[e + 1]) continue;
-      g = a.gates[(size_t)t * k + j];
+      g = sc_g[u];
     } else {
       pos = s_off[E] + t;
       g = 1.0f;

@@ -45,7 +45,7 @@ struct RouteArgs {
   int T, H, E, k;
   int32_t *ids;           // [T][k] ascending
   float *gates;           // [T][k]
-  uint32_t *tokmask;      // [ceil(T/32)][E] bit m: token 32*blk+m chose e
+  uint32_t *tokmask;      // [ceil(T/32)][256] bit m: token 32*blk+m chose e (0 for e >= E)
   float *lg, *rd;         // [T][E] fp32 logits (+bias) and their error radii (bf16 router)
   Ctrl *ctrl;
   int32_t *dbg_ids;       // optional [T][k] (chunk-offset)

@@ -346,7 +346,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
     atomicOr(&s_mask[s_sel[m][r]], 1u << m);
   }
   __syncthreads();
-  for (int e = tid; e < E; e += kRouteThreads) a.tokmask[(size_t)blockIdx.x * E + e] = s_mask[e];
+  for (int e = tid; e < kMaxExperts; e += kRouteThreads) a.tokmask[(size_t)blockIdx.x * kMaxExperts + e] = e < E ? s_mask[e] : 0u;
   if (tid == 0 && nflag) atomicAdd(&a.ctrl->n_refined, nflag);
 }
 
