@@ -70,6 +70,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-layers", type=int, default=40)
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replayed decode sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -205,6 +206,26 @@ def main():
                                      "traffic": profiled_traffic("k_decode"), "traffic_unit": "bytes per launch",
                                      "algorithmic_bytes_per_launch": layer_bytes}
         result["decode_algorithmic_bytes_per_layer"] = layer_bytes
+
+    if n_dec and not args.no_graph:
+        # the same 40 decode calls captured once in a HIP graph and replayed (their launch
+        # arguments do not change between calls), as a serving loop would run them
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for li in range(n_dec):
+                dec_layers[li].decode(dec_x[li], dec_out[li])
+        for _ in range(max(args.warmup, 1)):
+            graph.replay()
+        gmarks = B.HipEvents(K + 1)
+        torch.cuda.synchronize()
+        gmarks.record(0, stream)
+        for s in range(K):
+            graph.replay()
+            gmarks.record(s + 1, stream)
+        torch.cuda.synchronize()
+        g_ms = np.array([gmarks.elapsed_ms(s, s + 1) for s in range(K)])
+        result["decode_us_per_layer_graph"] = round(float(np.median(g_ms)) * 1e3 / n_dec, 3)
+        del graph
 
     if not args.no_cpu_baseline:
         import oracle

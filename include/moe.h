@@ -180,7 +180,11 @@ moe_status moe_forward_prefill(moe_plan_t plan, const void *x, int64_t T, void *
  * each other inside the launch (section "Decode > Keep every decode step on the
  * GPU"); requires E <= 256.  If an internal wait ever exceeded its poll budget, the
  * control word at byte offset 88 of the workspace (int32) becomes non-zero (the output of
- * that call is then invalid); moe_workspace_init clears it. */
+ * that call is then invalid); moe_workspace_init clears it.  The hand-off records are
+ * tagged with a per-call number kept in the workspace (bytes 92..99), so the launch
+ * arguments depend only on (plan, x, out, workspace, dbg): a sequence of decode calls may
+ * be captured once in a HIP graph and replayed, also interleaved with direct calls on the
+ * same workspace, as long as the calls on one workspace stay ordered on one stream. */
 moe_status moe_forward_decode(moe_plan_t plan, const void *x, void *out, void *workspace,
                               size_t workspace_bytes, hipStream_t stream,
                               const moe_debug_out *dbg);

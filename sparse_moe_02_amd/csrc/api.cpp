@@ -6,7 +6,6 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
-#include <atomic>
 #include <cstring>
 #include <new>
 
@@ -91,17 +90,6 @@ moe_status check_ws(const moe_plan_s *p, void *ws, size_t bytes) {
 bool overlap(const void *a, size_t na, const void *b, size_t nb) {
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
   return x < y + nb && y < x + na;
-}
-
-// Tag of one decode call's hand-off records.  Process-wide and increasing, so a call
-// never accepts a record left in its workspace by an earlier call (records are cleared
-// to tag 0 by moe_workspace_init; 0 is never issued).
-std::atomic<uint32_t> g_epoch{0};
-
-uint32_t next_epoch() {
-  uint32_t e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
-  while (e == 0) e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
-  return e;
 }
 
 hipError_t rec(const moe_debug_out *dbg, int i, hipStream_t s) {
@@ -315,7 +303,6 @@ moe_status moe_forward_decode(moe_plan_t p, const void *x, void *out, void *ws, 
   a.E = c.n_experts;
   a.k = c.top_k;
   a.I = c.inter;
-  a.epoch = next_epoch();
   a.lrec = at<uint64_t>(ws, p->off_lrec);
   a.hrec = at<uint64_t>(ws, p->off_hrec);
   a.ctrl = at<Ctrl>(ws, p->off_ctrl);

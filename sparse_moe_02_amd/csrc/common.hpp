@@ -53,6 +53,32 @@ __device__ __forceinline__ void dequant8_bf16(uint32_t w, float s, float b, uint
   }
 }
 
+// The same eight weights through fp16 "magic" operands: for each code pair (2j, 2j+1),
+// one byte permute and one and-or build a dword whose low half is the fp16 1024 + c_2j
+// and whose high half is the fp16 1024 + 16 c_2j+1 (exact), and a mixed-precision fma
+// maps each half to s c + b in fp32: the low half with (s, b - 1024 s), the high half
+// with (s/16, b - 64 s) -- the DeqPair below.  20 instructions per word instead of 23.
+struct DeqPair {
+  float s_lo, b_lo, s_hi, b_hi;
+  uint32_t nib;  // 0x00f0000f held in a vector register, so the mask-and-or is one v_and_or_b32
+};
+__device__ __forceinline__ DeqPair deq_pair(float s, float b) {
+  uint32_t nib;
+  asm("v_mov_b32 %0, 0x00f0000f" : "=v"(nib));
+  return DeqPair{s, __builtin_fmaf(-1024.0f, s, b), 0.0625f * s, __builtin_fmaf(-64.0f, s, b), nib};
+}
+__device__ __forceinline__ void dequant8_bf16_m(uint32_t w, const DeqPair &p, uint32_t out[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // byte j of w to bytes 0 and 2 (selector bytes j, j+4 of the {w, w} pair)
+    const uint32_t sel = (uint32_t)j | ((uint32_t)j << 16) | 0x0c000c00u;
+    const uint32_t x = (__builtin_amdgcn_perm(w, w, sel) & p.nib) | 0x64006400u;
+    const float lo = __builtin_fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(x & 0xffffu)), p.s_lo, p.b_lo);
+    const float hi = __builtin_fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16)), p.s_hi, p.b_hi);
+    out[j] = pack_bf16x2(lo, hi);
+  }
+}
+
 // ---------------------------------------------------------------- direct-to-LDS loads
 
 // 16 bytes per lane from gbase + voff into LDS: lane i's bytes land at lds + 16 i (lds is

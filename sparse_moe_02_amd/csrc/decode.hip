@@ -14,8 +14,12 @@
 // One launch covers the chain.  Workgroups hand results to each other as tagged
 // records: an 8-byte word holding a 32-bit value and the call's 32-bit epoch, written
 // with one device-scope store and read with device-scope loads, so a reader accepts a
-// value exactly when its tag is this call's epoch; there are no counters and no atomic
-// read-modify-writes (those serialise on one address).
+// value exactly when its tag is this call's epoch; no wait uses a counter or an atomic
+// read-modify-write (those serialise on one address).  The epoch lives in the
+// workspace: every workgroup reads the last call's epoch at its start and uses the next
+// one; the last workgroup to finish (one ticket per workgroup) stores it back.  The
+// launch arguments are therefore the same for every call, so a sequence of calls can be
+// captured once in a HIP graph and replayed.
 //   1. workgroup b computes the binary64 logits of experts b, b+G, ... and publishes
 //      each as three records (the two halves of the logit and its error radius);
 //   2. every workgroup that needs the routing reads all E logits and selects the top k
@@ -51,6 +55,9 @@ constexpr int kDnUnits = 5;             // (row, slot) units per 16-lane group p
 constexpr int kDnSlots = 10;            // slots per down round: 8 rows x 10 = 16 groups x 5
 constexpr int kHStage = 5120;           // h floats staged in LDS per down round
 constexpr int kSpins = 1 << 20;         // polls before a wait gives up (about a second)
+
+// This call's record tag (set by thread 0 at the start of k_decode).
+__shared__ uint32_t s_epoch;
 
 __device__ __forceinline__ QMat expert_mat(const QMat &routed, const QMat &shared, int e, int E, int N, int K) {
   if (e == E) return shared;
@@ -144,7 +151,7 @@ __device__ void read_logit(const DecodeArgs &a, int e, double &v, double &r) {
   const uint64_t *rec = a.lrec + 3 * (size_t)e;
   for (int i = 0;; ++i) {
     const uint64_t r0 = ld_agent(&rec[0]), r1 = ld_agent(&rec[1]), r2 = ld_agent(&rec[2]);
-    if (tag_of(r0) == a.epoch && tag_of(r1) == a.epoch && tag_of(r2) == a.epoch) {
+    if (tag_of(r0) == s_epoch && tag_of(r1) == s_epoch && tag_of(r2) == s_epoch) {
       v = __longlong_as_double((long long)(((uint64_t)(uint32_t)r1 << 32) | (uint32_t)r0));
       r = (double)__uint_as_float((uint32_t)r2);
       return;
@@ -410,7 +417,7 @@ __device__ __forceinline__ void gu_task(const DecodeArgs &a, const DecShared &sh
     if (lane == r) hv = gs / (1.0f + __expf(-gs)) * us;
   }
   const size_t row = (size_t)j * I + r0;
-  if (lane < kGuRows) st_agent(&a.hrec[row + lane], tagged(a.epoch, __float_as_uint(hv)));
+  if (lane < kGuRows) st_agent(&a.hrec[row + lane], tagged(s_epoch, __float_as_uint(hv)));
 }
 
 // ------------------------------------------------------------------ down
@@ -454,13 +461,13 @@ __device__ __forceinline__ void stage_h(const DecodeArgs &a, DecShared &sh, int 
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int t = t0 + u * kDecThreads;
-      rv[u] = t < n ? ld_agent(&rec[t]) : tagged(a.epoch, 0u);
+      rv[u] = t < n ? ld_agent(&rec[t]) : tagged(s_epoch, 0u);
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int t = t0 + u * kDecThreads;
       if (t >= n) continue;
-      for (int i = 0; tag_of(rv[u]) != a.epoch; ++i) {
+      for (int i = 0; tag_of(rv[u]) != s_epoch; ++i) {
         if (i == kSpins) {
           st_agent(&a.ctrl->d_err, 1);
           break;
@@ -544,6 +551,11 @@ __device__ __forceinline__ void dn_task(const DecodeArgs &a, DecShared &sh, int 
 __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
   __shared__ DecShared sh;
   const int b = blockIdx.x, G = gridDim.x, tid = threadIdx.x;
+  if (tid == 0) {
+    uint32_t ep = ld_agent(&a.ctrl->d_epoch) + 1u;
+    s_epoch = ep ? ep : 1u;
+  }
+  __syncthreads();
   const int E = a.E, k = a.k;
   const int n_gu = (k + 1) * (a.I / kGuTask), n_dn = a.H / kDnRows;
   const int first_shared = k * (a.I / kGuTask);  // gate/up tasks from here on are the shared expert's
@@ -561,9 +573,9 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
       const uint64_t lb = (uint64_t)__double_as_longlong(l);
       const float rad = __double2float_ru(radius64(l, ab, a.H, router_depth(a.H)));
       uint64_t *rec = a.lrec + 3 * (size_t)e;
-      st_agent(&rec[0], tagged(a.epoch, (uint32_t)lb));
-      st_agent(&rec[1], tagged(a.epoch, (uint32_t)(lb >> 32)));
-      st_agent(&rec[2], tagged(a.epoch, __float_as_uint(rad)));
+      st_agent(&rec[0], tagged(s_epoch, (uint32_t)lb));
+      st_agent(&rec[1], tagged(s_epoch, (uint32_t)(lb >> 32)));
+      st_agent(&rec[2], tagged(s_epoch, __float_as_uint(rad)));
     }
   }
 
@@ -591,6 +603,14 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
   for (int d = b; d < n_dn; d += G) {
     dn_task(a, sh, d, dl, dn_pre);
     dn_pre = false;
+  }
+
+  // the last workgroup to finish publishes this call's epoch for the next call (every
+  // workgroup read the old one before taking its ticket)
+  __syncthreads();
+  if (tid == 0 && ticket(&a.ctrl->d_done) == G - 1) {
+    st_agent(&a.ctrl->d_done, 0);
+    st_agent(&a.ctrl->d_epoch, s_epoch);
   }
 }
 

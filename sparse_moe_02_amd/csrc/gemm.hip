@@ -164,10 +164,12 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
     const uint8_t *bb = st + kAStage;
     const uint16_t *sp = (const uint16_t *)(st + kAStage + kBStage);
     float sc[2], bi[2];
+    DeqPair dp[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       sc[i] = fp16_to_f32(sp[s_lane[i]]);
       bi[i] = fp16_to_f32(sp[kSStage / 4 + s_lane[i]]);
+      dp[i] = deq_pair(sc[i], bi[i]);
     }
     auto afrag = [&](int t, int j) {
       return *(const u32x4 *)(st + t * 32 * kRowBytes + a_lane + ((a_c0 ^ j) << 4));
@@ -186,9 +188,9 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
     uint32_t d0[4], d1[4];
 #pragma unroll
     for (int t = 0; t < MT; ++t) av[0][t] = afrag(t, 0);
-    dequant8_bf16(word(0, 0), sc[0], bi[0], d0);
+    dequant8_bf16_m(word(0, 0), dp[0], d0);
     uint32_t q1 = word(1, 0), q0 = word(0, 1);
-    constexpr int kV = (23 + MT - 1) / MT;  // dequant VALU instructions per MFMA
+    constexpr int kV = (20 + MT - 1) / MT;  // dequant VALU instructions per MFMA
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int c = j & 1, nx = c ^ 1;
@@ -200,7 +202,7 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
       }
       if (j < 6) n0 = word(0, j + 2);
       __builtin_amdgcn_sched_barrier(0);
-      dequant8_bf16(q1, sc[1], bi[1], d1);
+      dequant8_bf16_m(q1, dp[1], d1);
 #pragma unroll
       for (int t = 0; t < MT; ++t) acc[t][0] = mfma(d0, av[c][t], acc[t][0]);
 #pragma unroll
@@ -209,7 +211,7 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
         __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (j < 7) dequant8_bf16(q0, sc[0], bi[0], d0);
+      if (j < 7) dequant8_bf16_m(q0, dp[0], d0);
 #pragma unroll
       for (int t = 0; t < MT; ++t) acc[t][1] = mfma(d1, av[c][t], acc[t][1]);
       if (j < 7) {

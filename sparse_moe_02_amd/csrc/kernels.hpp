@@ -32,7 +32,9 @@ struct Ctrl {
   int q_down[kXcds];
   int pad2[2];
   int d_err;             // decode: a wait ran out of polls (sticky; cleared by workspace init)
-  int pad[41];
+  uint32_t d_epoch;      // decode: tag of the last finished call's records (0 after init)
+  int d_done;            // decode: workgroups of the running call that have finished
+  int pad[39];
 };
 static_assert(sizeof(Ctrl) == 256, "control block is one 256-byte slot");
 static_assert(__builtin_offsetof(Ctrl, d_err) == 88, "documented offset of the decode error word");
@@ -89,7 +91,6 @@ struct DecodeArgs {
   QMat gate, up, down;      // routed stacked
   QMat s_gate, s_up, s_down;
   int H, E, k, I;
-  uint32_t epoch;           // tag of this call's records: nonzero, new for every call
   uint64_t *lrec;           // [E][3] tagged records: low and high word of the binary64 logit, radius
   uint64_t *hrec;           // [(k+1)*I] tagged h values
   Ctrl *ctrl;

@@ -140,6 +140,50 @@ def test_decode_back_to_back_same_workspace():
     m.close()
 
 
+def test_decode_graph_replay():
+    """Three decode calls captured once in a HIP graph (their launch arguments do not
+    change between calls: the record tag lives in the workspace) and replayed several
+    times, with direct calls on the same workspace and host syncs between the replays:
+    every replay bitwise equal to the direct result, in tolerance, no wait out of polls."""
+    import torch
+
+    from sparse_moe_02_amd.layer import MoeLayer, bf16_bits, bf16_tensor
+
+    L = synth.make_layer(1, 5)
+    xs = [synth.make_x(1, 5)[0], synth.make_x(1, 6)[0]]
+    refs = []
+    for x in xs:
+        r = oracle.route(x[None], L.router_w, None, 8)
+        refs.append(oracle.experts(x[None], L, r["ids"], r["gates"]))
+    m = MoeLayer(L, top_k=8, max_chunk_tokens=1)
+    xd = [bf16_tensor(x, "cuda:0") for x in xs]
+    direct = [bf16_bits(m.decode(xd[i])) for i in range(2)]
+    torch.cuda.synchronize()
+    outs = [torch.empty_like(xd[0]) for _ in range(3)]
+    g = torch.cuda.CUDAGraph()
+    say("[graph] capturing three decode calls")
+    with torch.cuda.graph(g):
+        for i in range(3):
+            m.decode(xd[i % 2], out=outs[i])
+    for rep in range(4):
+        for o in outs:
+            o.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(3):
+            assert np.array_equal(bf16_bits(outs[i]), direct[i % 2]), f"replay {rep} call {i}"
+        # direct calls on the same workspace between replays
+        mid = bf16_bits(m.decode(xd[(rep + 1) % 2]))
+        torch.cuda.synchronize()
+        assert np.array_equal(mid, direct[(rep + 1) % 2]), f"direct call after replay {rep}"
+    for i in range(2):
+        assert rel_err(to_f64(direct[i])[None], refs[i]) <= TOL
+    assert m.decode_error() == 0
+    say("[graph] 4 replays x 3 calls bitwise equal to direct calls")
+    del g
+    m.close()
+
+
 def test_long_prompt_128k_chunked():
     sh = synth.shape_of(4)
     L = synth.make_layer(4)
