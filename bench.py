@@ -71,6 +71,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-layers", type=int, default=40)
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replayed decode sweep")
+    ap.add_argument("--no-long-prompt", action="store_true", help="skip the 131072-token chunked prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -206,6 +207,33 @@ def main():
                                      "traffic": profiled_traffic("k_decode"), "traffic_unit": "bytes per launch",
                                      "algorithmic_bytes_per_launch": layer_bytes}
         result["decode_algorithmic_bytes_per_layer"] = layer_bytes
+
+    if not args.no_long_prompt:
+        # long prompt (131072 tokens, the same layer) through the chunk driver: one bounded
+        # workspace (fixed by the 4096-token chunk), so peak temporary memory is that
+        # workspace; torch's allocator is checked for anything beyond it
+        shl = synth.shape_of(4)
+        log(f"bench: long prompt {shl.T} tokens (drawing x)")
+        xl = bf16_tensor(synth.make_x(4), dev)
+        outl = torch.empty_like(xl)
+        pre.prefill(xl, outl)
+        torch.cuda.synchronize()
+        base_alloc = torch.cuda.memory_allocated(dev)
+        torch.cuda.reset_peak_memory_stats(dev)
+        lmarks = B.HipEvents(3)
+        lmarks.record(0, stream)
+        pre.prefill(xl, outl)
+        lmarks.record(1, stream)
+        pre.prefill(xl, outl)
+        lmarks.record(2, stream)
+        torch.cuda.synchronize()
+        l_ms = min(lmarks.elapsed_ms(0, 1), lmarks.elapsed_ms(1, 2))
+        extra = int(torch.cuda.max_memory_allocated(dev) - base_alloc)
+        result["long_prompt"] = {"tokens": shl.T, "chunk": shl.chunk, "us": round(l_ms * 1e3, 1),
+                                 "tokens_per_s": round(shl.T / (l_ms * 1e-3), 1),
+                                 "vs_4k_prefill": round(shl.T / (l_ms * 1e-3) / tok_s, 4),
+                                 "workspace_bytes": int(pre.ws_bytes), "extra_device_bytes_during_call": extra}
+        del xl, outl
 
     if n_dec and not args.no_graph:
         # the same 40 decode calls captured once in a HIP graph and replayed (their launch
