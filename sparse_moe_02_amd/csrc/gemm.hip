@@ -335,17 +335,24 @@ __device__ void gemm_persistent(const GemmArgs &a) {
 __global__ __launch_bounds__(kGemmThreads) void k_gemm_gateup(GemmArgs a) { gemm_persistent<true>(a); }
 __global__ __launch_bounds__(kGemmThreads) void k_gemm_down(GemmArgs a) { gemm_persistent<false>(a); }
 
-// Combine: out[t] = sum over the k+1 grouped rows of token t (already gate-weighted),
-// fp32 sum, bf16 result.  One workgroup per token, eight columns per thread.
-__global__ __launch_bounds__(256) void k_finalize(const uint16_t *y, const int32_t *slot_row, uint16_t *out, int H,
-                                                  int k) {
+// Combine: out[t] = sum over the NR = k+1 grouped rows of token t (already
+// gate-weighted), fp32 sum in slot order, bf16 result.  One workgroup per token, eight
+// columns per thread; the token's row indices go through LDS and all NR row loads of a
+// thread are issued before the first is summed.
+template <int NR>
+__global__ __launch_bounds__(256) void k_finalize(const uint16_t *y, const int32_t *slot_row, uint16_t *out, int H) {
+  __shared__ int s_rows[NR];
   const int t = blockIdx.x;
-  const int32_t *sr = slot_row + (size_t)t * (k + 1);
+  if ((int)threadIdx.x < NR) s_rows[threadIdx.x] = slot_row[(size_t)t * NR + threadIdx.x];
+  __syncthreads();
   for (int c = threadIdx.x; c < H / 8; c += 256) {
+    uint4 v[NR];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) v[j] = *(const uint4 *)(y + (size_t)s_rows[j] * H + 8 * c);
     float acc[8] = {};
-    for (int j = 0; j <= k; ++j) {
-      const uint4 v = *(const uint4 *)(y + (size_t)sr[j] * H + 8 * c);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         acc[2 * i] += bf16_lo(w[i]);
@@ -358,6 +365,17 @@ __global__ __launch_bounds__(256) void k_finalize(const uint16_t *y, const int32
     o.z = pack_bf16x2(acc[4], acc[5]);
     o.w = pack_bf16x2(acc[6], acc[7]);
     *(uint4 *)(out + (size_t)t * H + 8 * c) = o;
+  }
+}
+
+template <int NR>
+hipError_t launch_fin(const uint16_t *y, const int32_t *slot_row, uint16_t *out, int T, int H, int nr, hipStream_t s) {
+  if constexpr (NR > kMaxTopK + 1) {
+    return hipErrorInvalidValue;
+  } else {
+    if (nr != NR) return launch_fin<NR + 1>(y, slot_row, out, T, H, nr, s);
+    hipLaunchKernelGGL(k_finalize<NR>, dim3(T), dim3(256), 0, s, y, slot_row, out, H);
+    return hipGetLastError();
   }
 }
 
@@ -375,8 +393,7 @@ hipError_t launch_gemm_down(const GemmArgs &a, int n_blocks, hipStream_t s) {
 
 hipError_t launch_finalize(const uint16_t *y, const int32_t *slot_row, uint16_t *out, int T, int H, int k,
                            hipStream_t s) {
-  hipLaunchKernelGGL(k_finalize, dim3(T), dim3(256), 0, s, y, slot_row, out, H, k);
-  return hipGetLastError();
+  return launch_fin<2>(y, slot_row, out, T, H, k + 1, s);
 }
 
 }  // namespace moe
