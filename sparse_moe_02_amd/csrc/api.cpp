@@ -30,8 +30,6 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
-
 moe_status check_qmat(const moe_qmat &m) {
   if (!m.q || !m.scale || !m.bias) return MOE_ERR_NULL;
   if (!aligned16(m.q)) return MOE_ERR_ALIGN;
@@ -127,7 +125,7 @@ moe_status moe_plan_create(const moe_config *cfg, const moe_weights *w, moe_plan
   const moe_config &c = *cfg;
   if (c.group_size != 64) return MOE_ERR_SHAPE;
   if (c.hidden < 256 || c.hidden > 16384 || c.hidden % 256) return MOE_ERR_SHAPE;
-  if (c.inter < 128 || c.inter > 4096 || !is_pow2(c.inter)) return MOE_ERR_SHAPE;
+  if (c.inter < 128 || c.inter > 4096 || c.inter % 128) return MOE_ERR_SHAPE;
   if (c.n_experts < 1 || c.n_experts > kMaxExperts) return MOE_ERR_SHAPE;
   if (c.top_k < 1 || c.top_k > c.n_experts || c.top_k > kMaxTopK) return MOE_ERR_SHAPE;
   if (c.max_chunk_tokens < 1 || c.max_chunk_tokens > 65536) return MOE_ERR_SHAPE;

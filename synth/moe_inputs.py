@@ -62,6 +62,11 @@ CONFIGS = {
                 zipf_bias=True, weights_cfg=2, x_cfg=2),
     4: MoeShape("prefill-128k", T=131072, H=2048, E=256, k=8, I=512,
                 router_fp32=False, zipf_bias=False, weights_cfg=2),
+    # edge shapes for the parity tests (not benchmark workloads): sizes that are not
+    # multiples of the kernels' tiles, and the largest sizes the library accepts
+    10: MoeShape("odd-shape", T=37, H=768, E=40, k=6, I=384, router_fp32=False, zipf_bias=False,
+                 chunk=16),
+    11: MoeShape("max-size", T=3, H=16384, E=4, k=4, I=4096, router_fp32=False, zipf_bias=False, chunk=3),
 }
 
 

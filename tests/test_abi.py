@@ -65,7 +65,7 @@ def _weights(B, base=0x10000):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(group_size=32), 2), (dict(hidden=2000), 2), (dict(hidden=128), 2), (dict(inter=384), 2),
+    (dict(group_size=32), 2), (dict(hidden=2000), 2), (dict(hidden=128), 2), (dict(inter=320), 2),
     (dict(inter=64), 2), (dict(n_experts=257), 2), (dict(n_experts=0), 2), (dict(top_k=0), 2),
     (dict(top_k=17, n_experts=32), 2), (dict(top_k=9, n_experts=8), 2), (dict(max_chunk_tokens=0), 2),
     (dict(flags=4), 2), (dict(router_dtype=1), 3), (dict(qparam_dtype=0), 3),

@@ -214,6 +214,28 @@ def test_prefill_single_token_and_ragged_tail():
         _check_out(f"T{T}/c{chunk}", res["out"][sample], ref)
 
 
+@pytest.mark.parametrize("cfg", [10, 11])
+def test_edge_shapes_prefill_and_decode(cfg):
+    """Shapes off the benchmark's grid: H = 768, I = 384, E = 40, k = 6 over ragged
+    16-token chunks (partial M-blocks, N-blocks and logits tiles, idle waves); and the
+    largest sizes the library accepts, H = 16384 and I = 4096 (k = E = 4)."""
+    import torch
+
+    from sparse_moe_02_amd.layer import MoeLayer, bf16_bits, bf16_tensor
+
+    sh = synth.shape_of(cfg)
+    L, x = synth.make_layer(cfg), synth.make_x(cfg)
+    ref = oracle.forward(x, L, sh.k)
+    r, res = _prefill_case(L, x, sh.k, sh.chunk, sh.name)
+    _check_out(sh.name, res["out"], ref["out"])
+    m = MoeLayer(L, top_k=sh.k, max_chunk_tokens=1)
+    got = np.stack([bf16_bits(m.decode(bf16_tensor(x[t], "cuda:0"))) for t in range(min(sh.T, 4))])
+    torch.cuda.synchronize()
+    _check_out(sh.name + "/decode", to_f64(got), ref["out"][:got.shape[0]])
+    assert m.decode_error() == 0
+    m.close()
+
+
 def test_exact_and_near_ties():
     """Duplicated router rows (exact ties) and crafted near-ties below the fp32 and the
     binary64 error bounds: the lower index must win exactly as in the oracle."""
