@@ -5,6 +5,7 @@
 // between (section "Prefill > Keep expert routing on the GPU").
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 #include <new>
@@ -20,8 +21,9 @@ struct moe_plan_s {
   int n_cu;
   int dec_grid;  // workgroups of the decode launch (all resident at once)
   // workspace layout (byte offsets)
+  size_t slot_u64;  // 8-byte words per partial-sum slot of a split gate/up piece
   size_t off_ctrl, off_tokmask, off_lg, off_rd, off_ids, off_gates, off_counts, off_offsets, off_row_token,
-      off_row_gate, off_slot_row, off_mblocks, off_h, off_y, off_lrec, off_hrec, off_dend, total;
+      off_row_gate, off_slot_row, off_mblocks, off_h, off_y, off_lrec, off_hrec, off_tk, off_dend, total;
 };
 
 namespace {
@@ -62,9 +64,16 @@ void layout(moe_plan_s &p) {
   p.off_slot_row = take(rows * 4);
   p.off_mblocks = take(max_mblocks * 16);
   p.off_h = take(rows * I * 2);
-  p.off_y = take(rows * H * 2);
+  // y also holds the partial sums of split gate/up items (before the down GEMM writes y):
+  // at least kPartSlots slots, one per piece, sized for the tallest M-block of a chunk
+  const size_t mt_max = (std::min<size_t>(kBM, C) + 31) / 32;
+  p.slot_u64 = mt_max * 32 * 2 * kGateUpCols / 2;
+  const size_t nb_gu = (I + kGateUpCols - 1) / kGateUpCols;
+  const size_t part = std::min<size_t>(kMaxSplit * nb_gu * max_mblocks, kPartSlots) * p.slot_u64 * 8;
+  p.off_y = take(std::max(rows * H * 2, part));
   p.off_lrec = take(E * 3 * 8);  // decode records: cleared by moe_workspace_init
   p.off_hrec = take((k + 1) * I * 8);
+  p.off_tk = take(kMaxTailItems * 4);  // split-item tickets: zero between launches
   p.off_dend = o;
   p.total = o;
 }
@@ -256,6 +265,12 @@ moe_status moe_forward_prefill(moe_plan_t p, const void *x, int64_t T, void *out
     g1.H = (int)H;
     g1.I = c.inter;
     g1.h = at<uint16_t>(ws, p->off_h);
+    // the partial sums of split gate/up items live in y, which only the down GEMM writes
+    g1.tail_queue = &ctrl->q_tail;
+    g1.part = at<uint64_t>(ws, p->off_y);
+    g1.max_pieces = (int)std::min<size_t>((p->off_lrec - p->off_y) / (p->slot_u64 * 8), 1 << 20);
+    g1.slot_u64 = (int)p->slot_u64;
+    g1.tickets = at<int>(ws, p->off_tk);
     if (rec(d, MOE_STAGE_GATEUP, stream) != hipSuccess) return MOE_ERR_HIP;
     if (launch_gemm_gateup(g1, gemm_blocks, stream) != hipSuccess) return MOE_ERR_HIP;
 
@@ -267,6 +282,7 @@ moe_status moe_forward_prefill(moe_plan_t p, const void *x, int64_t T, void *out
     g2.w1 = QMat{};
     g2.s1 = QMat{};
     g2.y = at<uint16_t>(ws, p->off_y);
+    g2.part = nullptr;
     if (rec(d, MOE_STAGE_DOWN, stream) != hipSuccess) return MOE_ERR_HIP;
     if (launch_gemm_down(g2, gemm_blocks, stream) != hipSuccess) return MOE_ERR_HIP;
 

@@ -25,8 +25,11 @@
 // super-step s+1 are in flight while s is multiplied; the loop holds no global load
 // into registers, so the only memory wait is the explicit one at each step.
 // Work items come from eight atomic queues, one per XCD: the N-blocks of one M-block
-// run on the same XCD so its activation rows are fetched into one L2; an XCD whose
-// queue is empty takes work from the others.
+// run on the same XCD so its activation rows are fetched into one L2; a workgroup whose
+// queue is empty reads all eight counts in one round trip and takes work from the
+// fullest.  When the last round of gate/up items would leave most of the grid idle, its
+// items are split along K into pieces whose partial sums are combined by the piece that
+// finishes last.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -73,9 +76,19 @@ __device__ __forceinline__ f32x16 mfma(const uint32_t (&w)[4], const u32x4 &x, c
 // weight rows: GU (gate/up + SwiGLU, K = H): tile 0 = gate row n, tile 1 = up row n with
 // n = nb*256 + 32*wave + lane%32; down (K = I): tile i = row nb*512 + 64*wave + 32 i +
 // lane%32.  Weight slot (0..511) = 64*wave + 32*tile + lane%32.
+// A split gate/up item: this launch computes K-steps [ks0, ks1) of it as piece p of S.
+// Every piece stores its fp32 partial sums in its slot of `slots` (device-scope stores)
+// and takes a ticket; the piece that takes the last ticket reads back the S partial sums
+// and adds them in piece order, so the result does not depend on which piece finishes
+// last, and runs the epilogue.  No piece waits for another.
+struct Piece {
+  int ti;  // split item: slots [ti*S, ti*S + S) of GemmArgs::part, ticket ti; -1: whole item
+  int S, p;
+};
+
 template <int MT, bool GU>
-__device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, float *s_gate, int e, int row0,
-                          int rows, int nb) {
+__device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, float *s_gate, int *s_last, int e,
+                          int row0, int rows, int nb, int ks0, int ks1, const Piece &pc) {
   // thread index made opaque so per-lane address arithmetic is computed per item instead
   // of being hoisted out of the persistent loop (where every row-tile variant's copy
   // would hold registers for the whole kernel)
@@ -86,7 +99,6 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
   const int H = a.H, I = a.I;
   const int K = GU ? H : I;
   const int N = GU ? I : H;  // rows of each weight matrix
-  const int nss = K / 128;
   const QMat M0 = GU ? expert_mat(a.w0, a.s0, e, a.E, I, H) : expert_mat(a.w0, a.s0, e, a.E, H, I);
   const QMat M1 = GU ? expert_mat(a.w1, a.s1, e, a.E, I, H) : M0;
   auto slot_mat = [&](int slot) -> const QMat & { return (GU && ((slot >> 5) & 1)) ? M1 : M0; };
@@ -230,20 +242,76 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
   // in flight name the other.  The stage loads are issued from inline asm, so the
   // compiler adds no waits of its own for them; each wave waits for its loads, then the
   // barrier publishes every wave's.
-  issue(0, stage0);
-  for (int ss = 0; ss < nss; ss += 2) {
+  issue(ks0, stage0);
+  for (int ss = ks0; ss < ks1; ss += 2) {
     vm_wait<0>();
     __syncthreads();  // stage0 holds step ss for every wave; stage1 is free
-    if (ss + 1 < nss) issue(ss + 1, stage1);
+    if (ss + 1 < ks1) issue(ss + 1, stage1);
     if (active) compute(stage0);
-    if (ss + 1 >= nss) break;
+    if (ss + 1 >= ks1) break;
     vm_wait<0>();
     __syncthreads();  // stage1 holds step ss+1; stage0 is free
-    if (ss + 2 < nss) issue(ss + 2, stage0);
+    if (ss + 2 < ks1) issue(ss + 2, stage0);
     if (active) compute(stage1);
   }
   // every wave is past its last LDS read before the epilogue reuses stage0
   __builtin_amdgcn_s_barrier();
+  if (GU && pc.ti >= 0) {
+    // slot layout: per (wave, tile, matrix) 8 rows of 64 lanes of fp32 pairs, so each
+    // store and load instruction covers 512 contiguous bytes
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const size_t wbase = (size_t)wu * MT * 2 * 512 + ln;
+    if (active) {
+      uint64_t *mine = a.part + ((size_t)pc.ti * pc.S + pc.p) * a.slot_u64 + wbase;
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int h = 0; h < 8; ++h)
+            st_agent(mine + (t * 2 + j) * 512 + h * 64,
+                     ((uint64_t)__float_as_uint(acc[t][j][2 * h + 1]) << 32) | __float_as_uint(acc[t][j][2 * h]));
+    }
+    vm_drain();  // this thread's partial sums are stored
+    __syncthreads();
+    if (tid == 0) {
+      const int c = ticket(a.tickets + pc.ti);
+      *s_last = c == pc.S - 1;
+      if (c == pc.S - 1) st_agent(a.tickets + pc.ti, 0);  // ready for the next launch
+    }
+    __syncthreads();
+    if (!*s_last) return;
+    if (active) {
+      // one (tile, matrix) at a time: the S pieces' sums (this piece's own as stored) in
+      // flight together, then added in piece order
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          asm volatile("" ::: "memory");  // keeps the groups' loads apart (register pressure)
+          uint64_t v[kMaxSplit][8];
+#pragma unroll
+          for (int q = 0; q < kMaxSplit; ++q) {
+            // pieces past S re-read the last slot; their terms are dropped below
+            const uint64_t *src = a.part + ((size_t)pc.ti * pc.S + min(q, pc.S - 1)) * a.slot_u64 + wbase + (t * 2 + j) * 512;
+#pragma unroll
+            for (int h = 0; h < 8; ++h) v[q][h] = ld_agent(src + h * 64);
+          }
+#pragma unroll
+          for (int h = 0; h < 8; ++h) {
+            float lo = __uint_as_float((uint32_t)v[0][h]), hi = __uint_as_float((uint32_t)(v[0][h] >> 32));
+#pragma unroll
+            for (int q = 1; q < kMaxSplit; ++q) {
+              lo = q < pc.S ? lo + __uint_as_float((uint32_t)v[q][h]) : lo;
+              hi = q < pc.S ? hi + __uint_as_float((uint32_t)(v[q][h] >> 32)) : hi;
+            }
+            acc[t][j][2 * h] = lo;
+            acc[t][j][2 * h + 1] = hi;
+          }
+        }
+    }
+  }
   if (active) {
     // Epilogue, one 32-row tile at a time: the wave converts its tile to bf16 in its own
     // LDS area (GU: 32 rows x 32 h values; down: 32 rows x 64 gate-weighted outputs; rows
@@ -301,34 +369,112 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
 // Persistent grid.  Queue x serves M-blocks x, x+8, x+16, ... (all their N-blocks,
 // consecutive); workgroup b starts on queue b % 8 (its XCD under round-robin
 // dispatch) and moves on to the other queues when its own is empty.
+//
+// Gate/up: when the items fill their last round on the grid to at most half, that round
+// would leave most workgroups idle while the rest run whole items.  Those last items (the
+// M-blocks at the end of the block map, the shortest) are then split along K into S
+// pieces (S <= 4, S * items <= workgroups) taken from one more queue after the others
+// are empty, so the last round runs pieces of a fraction of an item each.
+template <bool GU>
+__device__ __forceinline__ void run_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, float *s_gate,
+                                         int *s_last, const int4 &mb, int nb, int ks0, int ks1, const Piece &pc) {
+  switch (mb.w) {
+    case 1: gemm_item<1, GU>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc); break;
+    case 2: gemm_item<2, GU>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc); break;
+    case 3: gemm_item<3, GU>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc); break;
+    case 4: gemm_item<4, GU>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc); break;
+    default: gemm_item<5, GU>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc); break;
+  }
+}
+
 template <bool GU>
 __device__ void gemm_persistent(const GemmArgs &a) {
   __shared__ __attribute__((aligned(16))) uint8_t stage0[kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t stage1[kStageBytes];
   __shared__ float s_gate[kBM];
-  __shared__ int s_item;
+  __shared__ int s_item, s_queue, s_last;
   const int NB = GU ? (a.I + kGateUpCols - 1) / kGateUpCols : (a.H + kDownCols - 1) / kDownCols;
+  const int nss = (GU ? a.H : a.I) / 128;
   const int nmb = a.ctrl->n_mblocks;
-  const int x0 = blockIdx.x % kXcds;
-  for (int d = 0; d < kXcds; ++d) {
-    const int x = (x0 + d) % kXcds;
-    const int n_items = NB * ((nmb - x + kXcds - 1) / kXcds);
-    for (;;) {
-      if (threadIdx.x == 0) s_item = atomicAdd(&a.queue[x], 1);
-      __syncthreads();
-      const int item = __builtin_amdgcn_readfirstlane(s_item);  // uniform: keeps item state scalar
-      __syncthreads();
-      if (item >= n_items) break;
-      const int4 mb = a.mblocks[x + kXcds * (item / NB)];
-      const int nb = item % NB;
-      switch (mb.w) {
-        case 1: gemm_item<1, GU>(a, stage0, stage1, s_gate, mb.x, mb.y, mb.z, nb); break;
-        case 2: gemm_item<2, GU>(a, stage0, stage1, s_gate, mb.x, mb.y, mb.z, nb); break;
-        case 3: gemm_item<3, GU>(a, stage0, stage1, s_gate, mb.x, mb.y, mb.z, nb); break;
-        case 4: gemm_item<4, GU>(a, stage0, stage1, s_gate, mb.x, mb.y, mb.z, nb); break;
-        default: gemm_item<5, GU>(a, stage0, stage1, s_gate, mb.x, mb.y, mb.z, nb); break;
+  int m_cut = nmb, S = 1, n_tail = 0;
+  if (GU && a.part) {
+    const int P = gridDim.x, R = (NB * nmb) % P;
+    if (R > 0 && 2 * R <= P) {
+      const int mt = (R + NB - 1) / NB, ti = mt * NB;
+      const int s = min(min(min(kMaxSplit, P / ti), nss), min(a.max_pieces / ti, kMaxTailItems / ti));
+      if (s >= 2) {
+        m_cut = nmb - mt;
+        S = s;
+        n_tail = ti;
       }
     }
+  }
+  auto items_of = [&](int x) { return m_cut > x ? NB * ((m_cut - x + kXcds - 1) / kXcds) : 0; };
+  int cur = blockIdx.x % kXcds;  // wave 0: queue being drained (kXcds: the tail pieces)
+  for (;;) {
+    if (threadIdx.x < 64) {
+      // Claim the next unit.  The current queue first (one atomic); once it is empty, the
+      // remaining counts of all eight queues are read in one round trip (one lane per
+      // queue, atomic adds of zero, so the values are the queues' own) and the fullest
+      // is taken; then the tail pieces.
+      const int lane = threadIdx.x;
+      int v = -1, q = -1;
+      if (cur < kXcds) {
+        int c = 0;
+        if (lane == 0) c = atomicAdd(&a.queue[cur], 1);
+        c = __shfl(c, 0);
+        if (c < items_of(cur)) v = c, q = cur;
+      }
+      while (q < 0 && cur < kXcds) {
+        int rem = 0, zero = 0;
+        asm volatile("" : "+v"(zero));  // a real read-modify-write, not turned into a load
+        if (lane < kXcds) rem = items_of(lane) - atomicAdd(&a.queue[lane], zero);
+        int best = -1, best_rem = 0;
+        for (int i = 0; i < kXcds; ++i) {
+          const int r = __shfl(rem, i);
+          if (r > best_rem) best_rem = r, best = i;
+        }
+        if (best < 0) {
+          cur = kXcds;
+          break;
+        }
+        cur = best;
+        int c = 0;
+        if (lane == 0) c = atomicAdd(&a.queue[cur], 1);
+        c = __shfl(c, 0);
+        if (c < items_of(cur)) v = c, q = cur;
+      }
+      if (q < 0 && n_tail) {
+        int c = 0;
+        if (lane == 0) c = atomicAdd(a.tail_queue, 1);
+        c = __shfl(c, 0);
+        if (c < n_tail * S) v = c, q = kXcds;
+      }
+      if (lane == 0) {
+        s_item = v;
+        s_queue = q;
+      }
+    }
+    __syncthreads();
+    const int v = __builtin_amdgcn_readfirstlane(s_item);  // uniform: keeps item state scalar
+    const int q = __builtin_amdgcn_readfirstlane(s_queue);
+    __syncthreads();
+    if (v < 0) break;
+    int4 mb;
+    int nb, ks0 = 0, ks1 = nss;
+    Piece pc{-1, 1, 0};
+    if (q < kXcds) {
+      mb = a.mblocks[q + kXcds * (v / NB)];
+      nb = v % NB;
+    } else {
+      const int ti = v / S, p = v % S;
+      mb = a.mblocks[m_cut + ti / NB];
+      nb = ti % NB;
+      ks0 = p * nss / S;
+      ks1 = (p + 1) * nss / S;
+      pc = Piece{ti, S, p};
+    }
+    run_item<GU>(a, stage0, stage1, s_gate, &s_last, mb, nb, ks0, ks1, pc);
   }
 }
 

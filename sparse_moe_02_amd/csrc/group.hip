@@ -211,6 +211,7 @@ __global__ __launch_bounds__(kThreads) void k_group(GroupArgs a) {
       a.ctrl->q_gateup[x] = 0;
       a.ctrl->q_down[x] = 0;
     }
+    a.ctrl->q_tail = 0;
     if (a.dbg_n_refined) *a.dbg_n_refined = a.ctrl->n_refined;
     a.ctrl->n_refined = 0;
   }

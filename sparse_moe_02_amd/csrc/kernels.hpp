@@ -20,6 +20,9 @@ struct QMat {
   const uint16_t *b;
 };
 
+constexpr int kMaxTailItems = 1024;  // split gate/up tail items per launch (<= workgroups / 2)
+constexpr int kMaxSplit = 4;         // pieces per split gate/up item
+constexpr int kPartSlots = 256;      // partial-sum slots provided at least (when y is smaller)
 constexpr int kXcds = 8;           // MI355X: 8 accelerator complex dies, one L2 each
 
 // Control words at the start of the workspace.
@@ -30,7 +33,8 @@ struct Ctrl {
   int pad1;
   int q_gateup[kXcds];   // grouped GEMM work queues, one per XCD (reset by the group kernel)
   int q_down[kXcds];
-  int pad2[2];
+  int q_tail;            // gate/up tail-piece queue (reset by the group kernel)
+  int pad2;
   int d_err;             // decode: a wait ran out of polls (sticky; cleared by workspace init)
   uint32_t d_epoch;      // decode: tag of the last finished call's records (0 after init)
   int d_done;            // decode: workgroups of the running call that have finished
@@ -74,6 +78,11 @@ struct GemmArgs {
   const int4 *mblocks;
   const Ctrl *ctrl;
   int *queue;               // kXcds counters
+  int *tail_queue;          // gate/up: counter of claimed tail pieces
+  uint64_t *part;           // gate/up: fp32 partial sums of split tail items (null: no split)
+  int *tickets;             // gate/up: pieces finished per split tail item (zero between launches)
+  int max_pieces;           // partial-sum slots that fit in `part`
+  int slot_u64;             // 8-byte words per slot: 32 rows x 2 x kGateUpCols fp32 per MT
   const int32_t *row_token;
   const float *row_gate;
   QMat w0, w1;              // routed stacked (gate, up) or (down, -)

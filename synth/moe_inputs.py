@@ -67,6 +67,10 @@ CONFIGS = {
     10: MoeShape("odd-shape", T=37, H=768, E=40, k=6, I=384, router_fp32=False, zipf_bias=False,
                  chunk=16),
     11: MoeShape("max-size", T=3, H=16384, E=4, k=4, I=4096, router_fp32=False, zipf_bias=False, chunk=3),
+    # gate/up items whose last round is split along K (into 2 and into 3 pieces, the
+    # latter over 10 K-steps, so the pieces are uneven)
+    12: MoeShape("split-2", T=1024, H=768, E=40, k=6, I=384, router_fp32=False, zipf_bias=False, chunk=1024),
+    13: MoeShape("split-3", T=1024, H=1280, E=32, k=4, I=512, router_fp32=False, zipf_bias=False, chunk=1024),
 }
 
 

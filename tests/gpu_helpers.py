@@ -76,3 +76,25 @@ def check_routing_prefill(res, ref_ids, ref_gates, x_len, E, k, chunk, group_of_
         rt = res["row_token"][c * chunk * (k + 1): c * chunk * (k + 1) + n]
         assert np.array_equal(rt, g["row_token"]), f"row_token differs in chunk {c}"
     return gerr
+
+
+def gateup_split(counts, T, H, I, E, k, chunk, n_cu):
+    """The grouped GEMM's rule for splitting its last round of gate/up items along K, run
+    on the host from one chunk's expert counts: returns (pieces per split item, split
+    items).  An expert with n rows makes ceil(n / 160) M-blocks; items = M-blocks x
+    ceil(I / 256); the last round is split when it fills at most half of the n_cu
+    workgroups, into S = min(4, n_cu // items_in_round, K-steps, slots // items) pieces."""
+    nmb = sum(-(-int(n) // 160) for n in counts if n)
+    nb = -(-I // 256)
+    nss = H // 128
+    r = (nb * nmb) % n_cu
+    if r == 0 or 2 * r > n_cu:
+        return 1, 0
+    ti = -(-r // nb) * nb
+    mt_max = (min(160, chunk) + 31) // 32
+    slot = mt_max * 32 * 2 * 256 // 2
+    rows = chunk * (k + 1)
+    part = min(4 * nb * (rows // 160 + E + 2), 256) * slot * 8
+    max_pieces = max(rows * H * 2, part) // (slot * 8)
+    s = min(4, n_cu // ti, nss, max_pieces // ti, 1024 // ti)
+    return (s, ti) if s >= 2 else (1, 0)

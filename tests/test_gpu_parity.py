@@ -7,7 +7,7 @@ for bit; gates within 2e-5; outputs within max|gpu - oracle| / max|oracle| <= 2e
 import numpy as np
 import pytest
 
-from gpu_helpers import (TOL, check_routing_prefill, ensure_lib, oracle, rel_err, run_prefill, say, synth,
+from gpu_helpers import (TOL, check_routing_prefill, ensure_lib, gateup_split, oracle, rel_err, run_prefill, say, synth,
                          to_f64, token_rel_err)
 
 pytestmark = pytest.mark.gpu
@@ -69,8 +69,13 @@ def test_tiny_decode_each_token():
 
 
 def test_prefill_uniform_4k():
+    import torch
+
     L, x = synth.make_layer(2), synth.make_x(2)
     r, res = _prefill_case(L, x, 8, 4096, "uniform-4k")
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    s, ti = gateup_split(res["counts"][0], 4096, 2048, 512, 256, 8, 4096, n_cu)
+    say(f"[uniform-4k] {ti} gate/up items split into {s} pieces")
     say("[uniform-4k] oracle experts")
     ref = oracle.experts(x, L, r["ids"], r["gates"])
     _check_out("uniform-4k", res["out"], ref)
@@ -234,6 +239,34 @@ def test_edge_shapes_prefill_and_decode(cfg):
     _check_out(sh.name + "/decode", to_f64(got), ref["out"][:got.shape[0]])
     assert m.decode_error() == 0
     m.close()
+
+
+@pytest.mark.parametrize("cfg,pieces", [(12, 2), (13, 3)])
+def test_split_gateup_tail(cfg, pieces):
+    """The last round of gate/up items split along K (2 pieces over 6 K-steps; 3 uneven
+    pieces over 10): parity with the oracle, and bitwise the same output on a second run
+    (the partial sums are added in piece order whichever piece finishes last)."""
+    import torch
+
+    from sparse_moe_02_amd.layer import MoeLayer, bf16_bits, bf16_tensor
+
+    sh = synth.shape_of(cfg)
+    L, x = synth.make_layer(cfg), synth.make_x(cfg)
+    r, res = _prefill_case(L, x, sh.k, sh.chunk, sh.name)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    s, ti = gateup_split(res["counts"][0], sh.T, sh.H, sh.I, sh.E, sh.k, sh.chunk, n_cu)
+    say(f"[{sh.name}] {n_cu} CUs: {ti} gate/up items split into {s} pieces")
+    if n_cu == 256:
+        assert s == pieces
+    ref = oracle.experts(x, L, r["ids"], r["gates"])
+    _check_out(sh.name, res["out"], ref)
+    m = MoeLayer(L, top_k=sh.k, max_chunk_tokens=sh.chunk)
+    xd = bf16_tensor(x, "cuda:0")
+    a = bf16_bits(m.prefill(xd))
+    b = bf16_bits(m.prefill(xd))
+    torch.cuda.synchronize()
+    m.close()
+    assert np.array_equal(a, b), "prefill output differs between two runs"
 
 
 def test_exact_and_near_ties():
