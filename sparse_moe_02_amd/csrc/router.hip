@@ -27,26 +27,27 @@ constexpr float kU32 = 5.9604644775390625e-8f;       // 2^-24
 // ---------------------------------------------------------------------------- prefill
 
 constexpr int kRouteThreads = 512;   // selection: 8 waves, four tokens each
-constexpr int kKC = 64;              // k per chunk (one LDS stage)
-constexpr int kKP = 128;             // k per fresh fp32 partial sum (two chunks)
+constexpr int kKC = 128;             // k per chunk (one LDS stage, one fresh fp32 partial sum)
+constexpr int kKP = 128;             // k per fresh fp32 partial sum
 constexpr int kLT = 64;              // logits tile: tokens
 constexpr int kLE = 64;              // logits tile: experts
 constexpr int kLThreads = 512;       // eight waves: four 32x32 tiles x {logit, |x||w|} chains
-constexpr int kLStages = 8;          // chunks in LDS (seven loaded ahead)
-constexpr int kLStage = (kLT + kLE) * kKC * 2;  // 16 KiB
+constexpr int kLStages = 4;          // chunks in LDS (three loaded ahead)
+constexpr int kLStage = (kLT + kLE) * kKC * 2;  // 32 KiB: two 64-k halves of x rows, then of router rows
+constexpr int kLHalf = (kLT + kLE) * 128;       // one 64-k half: 64 token rows, then 64 router rows
 
 // 16-byte piece `c` (0..7) of staged 128-byte row r: swizzled so that the MFMA operand
 // reads (16 rows, same piece) hit distinct banks
 __device__ __forceinline__ int roff(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
-// Logits and error radii of a 64-token x 64-expert tile.  For each 64-k chunk the 64
-// token rows and 64 router rows go global -> LDS with direct-to-LDS loads (8 rows x 128
-// bytes per instruction, kLStages-1 chunks ahead).  Wave w < 4 multiplies token tile w&1
-// with expert tile (w>>1)&1; wave w+4 does the same over sign-cleared operands, giving
-// sum |x w| for the error radius (two waves per SIMD, so each hides the other's LDS
-// latency).  H must be a multiple of 128.  Each 128-k partial is a fresh MFMA chain added to the running fp32 total,
-// so a product passes through at most kKP/16 + 15 roundings in its partial and H/kKP in
-// the total.
+// Logits and error radii of a 64-token x 64-expert tile.  For each 128-k chunk the 64
+// token rows and 64 router rows go global -> LDS with direct-to-LDS loads (two 64-k
+// halves of 8 rows x 128 bytes per wave and operand), kLStages-1 chunks ahead.  Wave
+// w < 4 multiplies token tile w&1 with expert tile (w>>1)&1; wave w+4 does the same over
+// sign-cleared operands, giving sum |x w| for the error radius (two waves per SIMD, so
+// each hides the other's LDS latency).  H must be a multiple of 128.  Each chunk is two
+// fresh MFMA chains (even and odd slices) added to the running fp32 total, so a product
+// passes through at most kKP/16 + 15 roundings in its partial and H/kKP in the total.
 __global__ __launch_bounds__(kLThreads) void k_route_logits(RouteArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t st[kLStages][kLStage];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -63,15 +64,19 @@ __global__ __launch_bounds__(kLThreads) void k_route_logits(RouteArgs a) {
   const uint32_t xoff = (uint32_t)min(t0 + lr, T - 1) * (uint32_t)H * 2u + 16u * (uint32_t)piece;
   const uint32_t woff = (uint32_t)min(e0 + lr, E - 1) * (uint32_t)H * 2u + 16u * (uint32_t)piece;
   const int nch = H / kKC;
-  // Workgroups walk the k chunks from different starting points (even, so the 128-k
-  // partials keep their pairs): rows are 2*H bytes apart, so workgroups in step would
-  // all address the same offset within their rows at once.
-  const int rot = 2 * ((blockIdx.x + 3 * blockIdx.y) % (nch / 2));
+  // Workgroups walk the k chunks from different starting points: rows are 2*H bytes
+  // apart, so workgroups in step would all address the same offset within their rows.
+  // The workgroups of one token block (same XCD) keep the same start, so each chunk of
+  // its rows is fetched into L2 once for all of them.
+  const int rot = blockIdx.x % nch;
   auto issue = [&](int c) {
     const uint32_t base = lds_addr(&st[c % kLStages][0]) + (uint32_t)wv * 1024u;
     const uint32_t kc = (uint32_t)((c + rot) % nch);
-    dma16(a.x, xoff + 128u * kc, base);
-    dma16(a.wr16, woff + 128u * kc, base + (uint32_t)(kLT * 128));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      dma16(a.x, xoff + 256u * kc + 128u * h, base + h * kLHalf);
+      dma16(a.wr16, woff + 256u * kc + 128u * h, base + h * kLHalf + (uint32_t)(kLT * 128));
+    }
   };
   f32x16 tot = {};
   for (int c = 0; c < kLStages - 1 && c < nch; ++c) issue(c);
@@ -79,34 +84,31 @@ __global__ __launch_bounds__(kLThreads) void k_route_logits(RouteArgs a) {
   // read all four slices' fragments
   auto stage_in = [&](int c, u32x4 (&av)[kKC / 16], u32x4 (&bv)[kKC / 16]) {
     // chunk c is complete once only the loads of chunks c+1 .. (last issued) remain
-    vm_wait_dyn(2 * (min(c + kLStages - 2, nch - 1) - c));
+    vm_wait_dyn(4 * (min(c + kLStages - 2, nch - 1) - c));
     __syncthreads();  // chunk c visible to every wave; chunk c-1's stage is free
     if (c + kLStages - 1 < nch) issue(c + kLStages - 1);
-    const uint8_t *xs = &st[c % kLStages][0];
-    const uint8_t *ws = xs + kLT * 128;
 #pragma unroll
     for (int j = 0; j < kKC / 16; ++j) {
-      av[j] = *(const u32x4 *)(xs + roff(32 * tt + m, 2 * j + hf));
-      bv[j] = *(const u32x4 *)(ws + roff(32 * et + m, 2 * j + hf));
+      const uint8_t *xs = &st[c % kLStages][0] + (j >> 2) * kLHalf;
+      const uint8_t *ws = xs + kLT * 128;
+      av[j] = *(const u32x4 *)(xs + roff(32 * tt + m, 2 * (j & 3) + hf));
+      bv[j] = *(const u32x4 *)(ws + roff(32 * et + m, 2 * (j & 3) + hf));
     }
   };
   // the same loop for both kinds of wave, the |.| waves clearing the sign bits first;
-  // each pair of chunks (128 k) is two fresh MFMA chains (even and odd slices) added to
-  // the running total
+  // each chunk (128 k) is two fresh MFMA chains (even and odd slices) added to the
+  // running total
   auto run = [&](auto abs_tag) {
     constexpr bool kAbs = decltype(abs_tag)::value;
     const u32x4 msk = {0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu};
     auto op = [&](const u32x4 &v) { return __builtin_bit_cast(bf16x8, kAbs ? (u32x4)(v & msk) : v); };
-    for (int c = 0; c < nch; c += 2) {
+    for (int c = 0; c < nch; ++c) {
       u32x4 av[kKC / 16], bv[kKC / 16];
       stage_in(c, av, bv);
       f32x16 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op(av[0]), op(bv[0]), (f32x16){}, 0, 0, 0);
       f32x16 acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op(av[1]), op(bv[1]), (f32x16){}, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op(av[2]), op(bv[2]), acc, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op(av[3]), op(bv[3]), acc1, 0, 0, 0);
-      stage_in(c + 1, av, bv);
 #pragma unroll
-      for (int j = 0; j < kKC / 16; ++j) {
+      for (int j = 2; j < kKC / 16; ++j) {
         f32x16 &ac = (j & 1) ? acc1 : acc;
         ac = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op(av[j]), op(bv[j]), ac, 0, 0, 0);
       }
