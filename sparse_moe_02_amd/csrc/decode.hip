@@ -23,9 +23,10 @@
 //   1. workgroup b computes the binary64 logits of experts b, b+G, ... and publishes
 //      each as three records (the two halves of the logit and its error radius);
 //   2. every workgroup that needs the routing reads all E logits and selects the top k
-//      itself (same values, same arithmetic, same result): a threshold from each wave's
-//      q-th largest logit leaves a few candidates, ranked exactly, then certified
-//      against the radii; undecided experts are summed sequentially in binary64;
+//      itself (same values, same arithmetic, same result): one wave takes all E keys
+//      (four per lane) through k rounds of a wave maximum and certifies the choice
+//      against the radii; only when that fails do the four waves re-rank (exact ranks
+//      of the candidates, undecided experts summed sequentially in binary64);
 //   3. gate/up task g (16 rows of one expert slot) runs on workgroup g mod G and
 //      publishes h as records; tasks of the shared expert run before the routing is
 //      known; a workgroup's first down task has its weight loads issued together with
@@ -96,6 +97,7 @@ struct DecShared {
   double red[2][4];
   int ids[kMaxTopK];
   float gates[kMaxTopK];
+  int fast;  // select_topk: the one-wave selection was certified
   float unit[kDnRows * kDnSlots];
   __attribute__((aligned(16))) float h[kHStage];
 };
@@ -232,12 +234,114 @@ __device__ __forceinline__ uint32_t logit_key(double v, int e) {
   return (ord & 0xffffff00u) | (uint32_t)(255 - e);
 }
 
+// Top-k of the E logits by one wave (four experts per lane): the keys of select_topk,
+// k rounds of a wave maximum, the same certificate (every chosen logit minus its radius
+// above every other logit plus its radius); ids ascending and softmax gates into sh.ids,
+// sh.gates.  The lane's twelve records are loaded together and re-polled together.
+// Returns false, having written nothing, when the certificate fails.
+__device__ bool select_topk_wave(const DecodeArgs &a, DecShared &sh, bool write_debug) {
+  constexpr int NV = kMaxExperts / kWave;
+  const int lane = threadIdx.x & 63, E = a.E, k = a.k;
+  double v[NV], r[NV];
+  bool valid[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) valid[i] = lane + kWave * i < E;
+  uint64_t rec[NV][3];
+  for (int it = 0;; ++it) {
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int j = 0; j < 3; ++j) rec[i][j] = valid[i] ? ld_agent(&a.lrec[3 * (size_t)(lane + kWave * i) + j]) : 0u;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int j = 0; j < 3; ++j) ok &= !valid[i] || tag_of(rec[i][j]) == s_epoch;
+    if (__ballot(!ok) == 0ull) break;
+    if (it == kSpins) {  // as read_logit: flag the error, missing logits count as -inf
+      st_agent(&a.ctrl->d_err, 1);
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        if (valid[i] && (tag_of(rec[i][0]) != s_epoch || tag_of(rec[i][1]) != s_epoch || tag_of(rec[i][2]) != s_epoch))
+          rec[i][0] = 0u, rec[i][1] = (uint64_t)0xfff00000u, rec[i][2] = 0u;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  uint32_t key[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    v[i] = valid[i] ? __longlong_as_double((long long)(((uint64_t)(uint32_t)rec[i][1] << 32) | (uint32_t)rec[i][0]))
+                    : -INFINITY;
+    r[i] = valid[i] ? (double)__uint_as_float((uint32_t)rec[i][2]) : 0.0;
+    key[i] = valid[i] ? logit_key(v[i], lane + kWave * i) : 0u;
+  }
+  uint32_t chosen = 0;
+  for (int rr = 0; rr < k; ++rr) {
+    uint32_t best = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) best = max(best, key[i]);
+    best = wave_max_u32(best);
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (key[i] == best && best != 0u) key[i] = 0u, chosen |= 1u << i;
+  }
+  double mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    if (!valid[i]) continue;
+    if ((chosen >> i) & 1u)
+      mn = fmin(mn, v[i] - r[i]);
+    else
+      mx = fmax(mx, v[i] + r[i]);
+  }
+  wave_minmax_f64(mn, mx);
+  if (!(mn > mx)) return false;  // false for NaN or an infinite radius as well
+  // softmax of the chosen logits (as fp32), ids ascending
+  float gmax = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    if ((chosen >> i) & 1u) gmax = fmaxf(gmax, (float)v[i]);
+  gmax = wave_max(gmax);
+  float ex[NV], part = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    ex[i] = ((chosen >> i) & 1u) ? __expf((float)v[i] - gmax) : 0.0f;
+    part += ex[i];
+  }
+  const float den = wave_sum(part);
+  int below = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const bool ch = (chosen >> i) & 1u;
+    const uint64_t bal = __ballot(ch);
+    const int pos = below + __popcll(bal & ((1ull << lane) - 1ull));
+    if (ch && pos < kMaxTopK) {
+      const int e = lane + kWave * i;
+      const float g = ex[i] / den;
+      sh.ids[pos] = e;
+      sh.gates[pos] = g;
+      if (write_debug && a.dbg_ids) a.dbg_ids[pos] = e;
+      if (write_debug && a.dbg_gates) a.dbg_gates[pos] = g;
+    }
+    below += __popcll(bal);
+  }
+  return true;
+}
+
 // Top-k of the E logits of this call (value descending, index ascending) into sh.ids
-// (ascending) and sh.gates.  One expert per thread (E <= 256): each wave takes its top k
+// (ascending) and sh.gates: select_topk_wave, or when its certificate fails the
+// four-wave path below.  One expert per thread (E <= 256): each wave takes its top k
 // by k rounds of a wave maximum; a chosen candidate is one of the 4k whose rank among
 // them is below k.  The choice is certified against the binary64 error radii; experts
 // closer than their radii are re-ranked by resolve64.
 __device__ void select_topk(const DecodeArgs &a, DecShared &sh, bool write_debug) {
+  if (threadIdx.x < kWave) {
+    const bool ok = select_topk_wave(a, sh, write_debug);
+    if (threadIdx.x == 0) sh.fast = ok;
+  }
+  __syncthreads();
+  if (sh.fast) return;  // uniform
   Sel64 &S = sh.S;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, E = a.E, k = a.k;
   const bool mine = tid < E;
