@@ -301,6 +301,24 @@ def test_exact_and_near_ties():
     assert res["n_refined"][0] > 0
     lg = r["logits"]
     assert np.any(lg[:, 200] == lg[:, 17]) and 0 < abs(lg[0, e8] - lg[0, e9]) < 1e-5
+    # decode of the same tokens: token 1's tie is below the binary64 radii, so the
+    # one-wave certificate fails and the exact re-rank decides; tokens that choose a
+    # duplicated expert have exact ties at the boundary or inside the top k
+    import torch
+
+    from sparse_moe_02_amd.layer import MoeLayer, bf16_tensor
+
+    dup = [t for t in range(256) if {17, 99} & set(r["ids"][t].tolist())][:6]
+    tokens = [0, 1] + dup
+    m = MoeLayer(L2, top_k=8, max_chunk_tokens=1)
+    for t in tokens:
+        _, d = m.decode(bf16_tensor(x[t], "cuda:0"), debug=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(d["topk_ids"].cpu().numpy()[0], r["ids"][t]), f"decode ids of token {t}"
+        assert np.max(np.abs(d["gates"].cpu().numpy()[0] - r["gates"][t])) <= 2e-5
+    assert m.decode_error() == 0
+    say(f"[ties] decode ids exact on tokens {tokens}")
+    m.close()
 
 
 def test_bias_dominance_and_all_experts():
