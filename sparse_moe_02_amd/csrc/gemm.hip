@@ -86,9 +86,13 @@ struct Piece {
   int S, p;
 };
 
+// `claim` (wave-uniform; null: none) is the queue counter the next work item will be
+// taken from: wave 0 takes the ticket once the item's last multiply is done, so the
+// atomic's round trip overlaps the epilogue, and leaves the value in *s_pend when the
+// item ends.
 template <int MT, bool GU>
 __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, float *s_gate, int *s_last, int e,
-                          int row0, int rows, int nb, int ks0, int ks1, const Piece &pc) {
+                          int row0, int rows, int nb, int ks0, int ks1, const Piece &pc, int *claim, int *s_pend) {
   // thread index made opaque so per-lane address arithmetic is computed per item instead
   // of being hoisted out of the persistent loop (where every row-tile variant's copy
   // would hold registers for the whole kernel)
@@ -256,6 +260,8 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
   }
   // every wave is past its last LDS read before the epilogue reuses stage0
   __builtin_amdgcn_s_barrier();
+  int pend = 0;
+  if (tid == 0 && claim) pend = atomicAdd(claim, 1);
   if (GU && pc.ti >= 0) {
     // slot layout: per (wave, tile, matrix) 8 rows of 64 lanes of fp32 pairs, so each
     // store and load instruction covers 512 contiguous bytes
@@ -273,7 +279,8 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
             st_agent(mine + (t * 2 + j) * 512 + h * 64,
                      ((uint64_t)__float_as_uint(acc[t][j][2 * h + 1]) << 32) | __float_as_uint(acc[t][j][2 * h]));
     }
-    vm_drain();  // this thread's partial sums are stored
+    vm_drain();  // this thread's partial sums are stored (and the claim has returned)
+    if (tid == 0) *s_pend = pend;
     __syncthreads();
     if (tid == 0) {
       const int c = ticket(a.tickets + pc.ti);
@@ -364,6 +371,7 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
       __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next tile overwrites
     }
   }
+  if (tid == 0 && !(GU && pc.ti >= 0)) *s_pend = pend;
 }
 
 // Persistent grid.  Queue x serves M-blocks x, x+8, x+16, ... (all their N-blocks,
@@ -377,13 +385,14 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
 // are empty, so the last round runs pieces of a fraction of an item each.
 template <bool GU>
 __device__ __forceinline__ void run_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, float *s_gate,
-                                         int *s_last, const int4 &mb, int nb, int ks0, int ks1, const Piece &pc) {
+                                         int *s_last, const int4 &mb, int nb, int ks0, int ks1, const Piece &pc,
+                                         int *claim, int *s_pend) {
   switch (mb.w) {
-    case 1: gemm_item<1, GU>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc); break;
-    case 2: gemm_item<2, GU>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc); break;
-    case 3: gemm_item<3, GU>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc); break;
-    case 4: gemm_item<4, GU>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc); break;
-    default: gemm_item<5, GU>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc); break;
+    case 1: gemm_item<1, GU>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc, claim, s_pend); break;
+    case 2: gemm_item<2, GU>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc, claim, s_pend); break;
+    case 3: gemm_item<3, GU>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc, claim, s_pend); break;
+    case 4: gemm_item<4, GU>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc, claim, s_pend); break;
+    default: gemm_item<5, GU>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc, claim, s_pend); break;
   }
 }
 
@@ -392,7 +401,7 @@ __device__ void gemm_persistent(const GemmArgs &a) {
   __shared__ __attribute__((aligned(16))) uint8_t stage0[kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t stage1[kStageBytes];
   __shared__ float s_gate[kBM];
-  __shared__ int s_item, s_queue, s_last;
+  __shared__ int s_item, s_queue, s_last, s_pend;
   const int NB = GU ? (a.I + kGateUpCols - 1) / kGateUpCols : (a.H + kDownCols - 1) / kDownCols;
   const int nss = (GU ? a.H : a.I) / 128;
   const int nmb = a.ctrl->n_mblocks;
@@ -411,6 +420,7 @@ __device__ void gemm_persistent(const GemmArgs &a) {
   }
   auto items_of = [&](int x) { return m_cut > x ? NB * ((m_cut - x + kXcds - 1) / kXcds) : 0; };
   int cur = blockIdx.x % kXcds;  // wave 0: queue being drained (kXcds: the tail pieces)
+  int pq = -1;                    // wave 0: queue of the ticket in s_pend (-1: none)
   for (;;) {
     if (threadIdx.x < 64) {
       // Claim the next unit.  The current queue first (one atomic); once it is empty, the
@@ -421,7 +431,8 @@ __device__ void gemm_persistent(const GemmArgs &a) {
       int v = -1, q = -1;
       if (cur < kXcds) {
         int c = 0;
-        if (lane == 0) c = atomicAdd(&a.queue[cur], 1);
+        if (lane == 0) c = pq == cur ? s_pend : atomicAdd(&a.queue[cur], 1);
+        pq = -1;
         c = __shfl(c, 0);
         if (c < items_of(cur)) v = c, q = cur;
       }
@@ -446,7 +457,8 @@ __device__ void gemm_persistent(const GemmArgs &a) {
       }
       if (q < 0 && n_tail) {
         int c = 0;
-        if (lane == 0) c = atomicAdd(a.tail_queue, 1);
+        if (lane == 0) c = pq == kXcds ? s_pend : atomicAdd(a.tail_queue, 1);
+        pq = -1;
         c = __shfl(c, 0);
         if (c < n_tail * S) v = c, q = kXcds;
       }
@@ -474,7 +486,12 @@ __device__ void gemm_persistent(const GemmArgs &a) {
       ks1 = (p + 1) * nss / S;
       pc = Piece{ti, S, p};
     }
-    run_item<GU>(a, stage0, stage1, s_gate, &s_last, mb, nb, ks0, ks1, pc);
+    // the item takes the next ticket from the queue this one came from (the tail
+    // pieces' queue for a piece)
+    int *claim = q < kXcds ? &a.queue[q] : a.tail_queue;
+    run_item<GU>(a, stage0, stage1, s_gate, &s_last, mb, nb, ks0, ks1, pc, claim, &s_pend);
+    cur = q;
+    pq = q;
   }
 }
 
