@@ -402,6 +402,11 @@ __device__ void gemm_persistent(const GemmArgs &a) {
   __shared__ __attribute__((aligned(16))) uint8_t stage1[kStageBytes];
   __shared__ float s_gate[kBM];
   __shared__ int s_item, s_queue, s_last, s_pend;
+  // down: the first kMbCache block-map entries, copied once per launch, so an item finds
+  // its entry without a round trip to memory (down runs about twice as many items per
+  // workgroup as gate/up, which measured no better with the copy)
+  constexpr int kMbCache = GU ? 1 : 384;
+  __shared__ int4 s_mbc[kMbCache];
   const int NB = GU ? (a.I + kGateUpCols - 1) / kGateUpCols : (a.H + kDownCols - 1) / kDownCols;
   const int nss = (GU ? a.H : a.I) / 128;
   const int nmb = a.ctrl->n_mblocks;
@@ -420,6 +425,13 @@ __device__ void gemm_persistent(const GemmArgs &a) {
   }
   auto items_of = [&](int x) { return m_cut > x ? NB * ((m_cut - x + kXcds - 1) / kXcds) : 0; };
   int cur = blockIdx.x % kXcds;  // wave 0: queue being drained (kXcds: the tail pieces)
+  if (!GU)
+    for (int i = threadIdx.x; i < min(nmb, kMbCache); i += blockDim.x) s_mbc[i] = a.mblocks[i];
+  auto mblock = [&](int i) {  // after a barrier; wave-uniform, kept in scalar registers
+    const int4 m = !GU && i < kMbCache ? s_mbc[i] : a.mblocks[i];
+    return make_int4(__builtin_amdgcn_readfirstlane(m.x), __builtin_amdgcn_readfirstlane(m.y),
+                     __builtin_amdgcn_readfirstlane(m.z), __builtin_amdgcn_readfirstlane(m.w));
+  };
   int pq = -1;                    // wave 0: queue of the ticket in s_pend (-1: none)
   for (;;) {
     if (threadIdx.x < 64) {
@@ -476,11 +488,11 @@ __device__ void gemm_persistent(const GemmArgs &a) {
     int nb, ks0 = 0, ks1 = nss;
     Piece pc{-1, 1, 0};
     if (q < kXcds) {
-      mb = a.mblocks[q + kXcds * (v / NB)];
+      mb = mblock(q + kXcds * (v / NB));
       nb = v % NB;
     } else {
       const int ti = v / S, p = v % S;
-      mb = a.mblocks[m_cut + ti / NB];
+      mb = mblock(m_cut + ti / NB);
       nb = ti % NB;
       ks0 = p * nss / S;
       ks1 = (p + 1) * nss / S;
