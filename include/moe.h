@@ -48,7 +48,7 @@
  *     failed launch returns MOE_ERR_HIP (hipGetLastError() is left for the
  *     caller).  No C++ exception crosses this interface.
  *   - x and out must not alias.  x, out, router weight and code arrays must be
- *     16-byte aligned, scale/bias arrays 4-byte aligned, the workspace 256-byte aligned.
+ *     16-byte aligned, scale/bias arrays 8-byte aligned, the workspace 256-byte aligned.
  *
  * Layouts (row-major):
  *   x, out           bf16 [T][H]
@@ -56,7 +56,12 @@
  *   router bias      float32 [E], or NULL
  *   quantised W[N][K]  q: uint32 [N][K/8]; element k of row n is the 4-bit code
  *                    in bits 4*(k%8) of q[n][k/8] (low nibble first);
- *                    scale, bias: fp16 [N][K/64]; w = scale*code + bias.
+ *                    w = scale*code + bias with one fp16 scale and bias per row
+ *                    n and group g = k/64, stored in 16-row tiles: the pair of
+ *                    (n, g) is element ((n/16)*(K/64) + g)*16 + n%16 of the
+ *                    scale and of the bias array (moe_pack_qparams converts
+ *                    row-major [N][K/64] arrays).  A tile holds 64 B per group
+ *                    pair, so a 128-k step of 16 rows reads one run of 64 B.
  *   routed experts   stacked: gate, up [E][I][H]; down [E][H][I] (q, scale
  *                    and bias each stacked on the leading axis)
  *   shared expert    gate, up [I][H]; down [H][I]
@@ -83,7 +88,7 @@ typedef enum {
   MOE_ERR_TOKENS = 6,    /* T < 1 (prefill) */
   MOE_ERR_DEVICE = 7,    /* current device is not gfx950, or device query failed */
   MOE_ERR_HIP = 8,       /* a kernel launch failed */
-  MOE_ERR_ALIAS = 9,     /* x and out overlap */
+  MOE_ERR_ALIAS = 9,     /* x and out (or a pack's src and dst) overlap */
   MOE_ERR_ALLOC = 10     /* host allocation failed */
 } moe_status;
 
@@ -107,8 +112,8 @@ typedef struct {               /* (host) */
 
 typedef struct {               /* (host struct of device pointers) */
   const uint32_t *q;           /* [N][K/8] codes */
-  const void *scale;           /* fp16 [N][K/64] */
-  const void *bias;            /* fp16 [N][K/64] */
+  const void *scale;           /* fp16, N*K/64 values in 16-row tiles */
+  const void *bias;            /* fp16, same layout */
 } moe_qmat;
 
 typedef struct {               /* (host struct of device pointers) */
@@ -188,6 +193,18 @@ moe_status moe_forward_prefill(moe_plan_t plan, const void *x, int64_t T, void *
 moe_status moe_forward_decode(moe_plan_t plan, const void *x, void *out, void *workspace,
                               size_t workspace_bytes, hipStream_t stream,
                               const moe_debug_out *dbg);
+
+/* Weight preparation: rewrite an fp16 array of one value per (row, group of 64)
+ * from row-major src [rows][k/64] into the 16-row tile layout the quantised
+ * matrices use (element (n, g) to ((n/16)*(k/64) + g)*16 + n%16) in dst (enqueued
+ * on stream).  rows: a multiple of 16 (a stack of experts' matrices may be packed
+ * in one call: every N here is a multiple of 16, so tiles never straddle two
+ * experts); k: a positive multiple of 64.  src and dst are device arrays of
+ * rows*k/64 fp16, 4-byte aligned, and must not overlap.  MOE_ERR_NULL,
+ * MOE_ERR_SHAPE (rows < 16 or not a multiple of 16, k not a positive multiple of
+ * 64), MOE_ERR_ALIGN, MOE_ERR_ALIAS (overlap) or MOE_ERR_HIP. */
+moe_status moe_pack_qparams(const void *src, void *dst, int64_t rows, int32_t k,
+                            hipStream_t stream);
 
 const char *moe_status_string(moe_status s);
 

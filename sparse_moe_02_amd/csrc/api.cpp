@@ -35,7 +35,7 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 moe_status check_qmat(const moe_qmat &m) {
   if (!m.q || !m.scale || !m.bias) return MOE_ERR_NULL;
   if (!aligned16(m.q)) return MOE_ERR_ALIGN;
-  if (((uintptr_t)m.scale & 3u) || ((uintptr_t)m.bias & 3u)) return MOE_ERR_ALIGN;
+  if (((uintptr_t)m.scale & 7u) || ((uintptr_t)m.bias & 7u)) return MOE_ERR_ALIGN;
   return MOE_OK;
 }
 
@@ -114,18 +114,31 @@ const char *moe_status_string(moe_status s) {
     case MOE_ERR_NULL: return "a required pointer is NULL";
     case MOE_ERR_SHAPE: return "unsupported shape or flags";
     case MOE_ERR_DTYPE: return "unsupported dtype";
-    case MOE_ERR_ALIGN: return "pointer not aligned (16 B; workspace 256 B)";
+    case MOE_ERR_ALIGN: return "pointer not aligned (16 B; scale/bias 8 B; workspace 256 B)";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_TOKENS: return "token count out of range";
     case MOE_ERR_DEVICE: return "current device is not gfx950 or cannot be queried";
     case MOE_ERR_HIP: return "HIP launch failed";
-    case MOE_ERR_ALIAS: return "x and out overlap";
+    case MOE_ERR_ALIAS: return "input and output arrays overlap";
     case MOE_ERR_ALLOC: return "host allocation failed";
   }
   return "unknown status";
 }
 
 const char *moe_version(void) { return "moe-mi355x gfx950 1"; }
+
+moe_status moe_pack_qparams(const void *src, void *dst, int64_t rows, int32_t k, hipStream_t stream) {
+  if (!src || !dst) return MOE_ERR_NULL;
+  if (rows < 16 || rows % 16 != 0 || k < 64 || k % 64 != 0) return MOE_ERR_SHAPE;
+  if (((uintptr_t)src & 3u) || ((uintptr_t)dst & 3u)) return MOE_ERR_ALIGN;
+  const uintptr_t bytes = (uintptr_t)rows * (uintptr_t)(k / 64) * 2u;
+  const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+  if (s0 < d0 + bytes && d0 < s0 + bytes) return MOE_ERR_ALIAS;
+  if (moe::launch_pack_qparams(static_cast<const uint16_t *>(src), static_cast<uint16_t *>(dst), rows, k / 64,
+                               stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
 
 moe_status moe_plan_create(const moe_config *cfg, const moe_weights *w, moe_plan_t *plan,
                            size_t *workspace_bytes) {

@@ -34,6 +34,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)(pac
 
 __device__ __forceinline__ float fp16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
+// Scale and bias arrays (G groups of 64 per row) are stored in tiles of kQpRows rows:
+// the tile's values of one group are contiguous, groups follow each other.
+constexpr int kQpRows = 16;
+__device__ __forceinline__ size_t qp_index(size_t n, int g, int G) {
+  return ((n / kQpRows) * (size_t)G + (size_t)g) * kQpRows + (n % kQpRows);
+}
+
 // 4-bit code i (0..7) of a packed word as float.
 __device__ __forceinline__ float code_f(uint32_t w, int i) { return (float)((w >> (4 * i)) & 0xfu); }
 

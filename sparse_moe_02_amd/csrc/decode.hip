@@ -51,6 +51,7 @@ namespace {
 constexpr int kDecThreads = 256;        // four waves
 constexpr int kGuRows = 4;              // gate/up rows per wave in one task
 constexpr int kGuTask = 4 * kGuRows;    // rows of one gate/up task
+static_assert(kGuRows == 4 && kGuTask % 4 == 0 && kQpRows % 4 == 0, "a wave reads its rows' scale/bias of one group as one 8-byte run");
 constexpr int kDnRows = 8;              // output rows of one down task
 constexpr int kDnUnits = 5;             // (row, slot) units per 16-lane group per round
 constexpr int kDnSlots = 10;            // slots per down round: 8 rows x 10 = 16 groups x 5
@@ -434,7 +435,7 @@ __device__ void select_topk(const DecodeArgs &a, DecShared &sh, bool write_debug
 // 32-element chunk c = lane + 64 p of the H-long rows.
 struct GuLoad {
   uint4 wg[kGuRows], wu[kGuRows];
-  uint32_t sg[kGuRows], bg[kGuRows], su[kGuRows], bu[kGuRows];
+  uint2 sg, bg, su, bu;  // fp16 scale/bias of rows r0..r0+3: row r in half r%2 of word r/2
   uint4 x[4];
   bool ok;
 };
@@ -449,11 +450,13 @@ __device__ __forceinline__ void gu_issue(const DecodeArgs &a, const QMat &Gm, co
     const size_t row = (size_t)(r0 + r);
     L.wg[r] = *(const uint4 *)(Gm.q + row * (H / 8) + 4 * cc);
     L.wu[r] = *(const uint4 *)(Um.q + row * (H / 8) + 4 * cc);
-    L.sg[r] = Gm.s[row * (H / 64) + cc / 2];
-    L.bg[r] = Gm.b[row * (H / 64) + cc / 2];
-    L.su[r] = Um.s[row * (H / 64) + cc / 2];
-    L.bu[r] = Um.b[row * (H / 64) + cc / 2];
   }
+  // r0 is a multiple of 4, so the four rows' values of one group are adjacent (8 bytes)
+  const size_t qi = qp_index((size_t)r0, cc / 2, H / 64);
+  L.sg = *(const uint2 *)(Gm.s + qi);
+  L.bg = *(const uint2 *)(Gm.b + qi);
+  L.su = *(const uint2 *)(Um.s + qi);
+  L.bu = *(const uint2 *)(Um.b + qi);
 #pragma unroll
   for (int q = 0; q < 4; ++q) L.x[q] = *(const uint4 *)(a.x + 32 * cc + 8 * q);
 }
@@ -475,8 +478,9 @@ __device__ __forceinline__ void gu_accumulate(const GuLoad &L, float (&ag)[kGuRo
   for (int i = 0; i < 32; ++i) xs += xf[i];
 #pragma unroll
   for (int r = 0; r < kGuRows; ++r) {
-    ag[r] += fp16_to_f32((uint16_t)L.sg[r]) * dot_codes32(L.wg[r], xf) + fp16_to_f32((uint16_t)L.bg[r]) * xs;
-    au[r] += fp16_to_f32((uint16_t)L.su[r]) * dot_codes32(L.wu[r], xf) + fp16_to_f32((uint16_t)L.bu[r]) * xs;
+    auto half = [&](uint2 v) { return fp16_to_f32((uint16_t)(((r >> 1) ? v.y : v.x) >> (16 * (r & 1)))); };
+    ag[r] += half(L.sg) * dot_codes32(L.wg[r], xf) + half(L.bg) * xs;
+    au[r] += half(L.su) * dot_codes32(L.wu[r], xf) + half(L.bu) * xs;
   }
 }
 
@@ -547,8 +551,9 @@ __device__ __forceinline__ void dn_issue(const DecodeArgs &a, const DecShared &s
     const QMat D = expert_mat(a.down, a.s_down, e, a.E, a.H, I);
     const size_t n = (size_t)(n0 + r);
     L.w[m] = *(const uint4 *)(D.q + n * (I / 8) + 4 * cc);
-    L.s[m] = D.s[n * (I / 64) + cc / 2];
-    L.b[m] = D.b[n * (I / 64) + cc / 2];
+    const size_t qi = qp_index(n, cc / 2, I / 64);
+    L.s[m] = D.s[qi];
+    L.b[m] = D.b[qi];
   }
 }
 

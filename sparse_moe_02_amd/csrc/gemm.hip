@@ -11,7 +11,7 @@
 // the down epilogue (the k+1 rows of a token are summed by a short gather kernel).
 //
 // MI355X mapping.  A work item is (M-block of one expert, N-block).  Eight waves (two
-// per SIMD) split the N-block; each wave covers all rows of the M-block (1..4 tiles of
+// per SIMD) split the N-block; each wave covers all rows of the M-block (1..5 tiles of
 // 32), so a weight element is dequantised once per work item, and each wave interleaves
 // its dequant VALU work between its own MFMAs (k-slice software pipeline).  For a 128-wide K super-step, lane l of a
 // wave owns weight row n = l%32 and the 64 consecutive k of half h = l/32: exactly eight
@@ -38,10 +38,10 @@ namespace moe {
 namespace {
 
 constexpr int kRowBytes = 256;                 // 128 bf16 per staged activation row
-constexpr int kAStage = kBM * kRowBytes;       // 32 KiB: up to 128 activation rows
+constexpr int kAStage = kBM * kRowBytes;       // 40 KiB: up to 160 activation rows
 constexpr int kBStage = 512 * 64;              // 32 KiB: 512 weight rows x 64 B (128 codes)
-constexpr int kSStage = 2 * 512 * 4;           // 4 KiB: scales then biases, 2 fp16 per row
-constexpr int kStageBytes = kAStage + kBStage + kSStage;  // 68 KiB
+constexpr int kSStage = 2 * 512 * 4;           // 4 KiB: scales then biases, 2 groups per row
+constexpr int kStageBytes = kAStage + kBStage + kSStage;  // 76 KiB
 
 template <int N>
 __device__ __forceinline__ void vm_wait() {
@@ -135,19 +135,25 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
     bbase[i] = (const char *)slot_mat(16 * v).q;
     boff[i] = 4u * ((uint32_t)slot_row(slot) * (uint32_t)(K / 8) + 4u * (uint32_t)((lane & 3) ^ ((slot >> 2) & 3)));
   }
-  // S: 16 wave-loads of 256 B (64 slots x 2 fp16): v < 8 scales, v >= 8 biases.  Wave-load
-  // v covers tile t = (v >> 2) & 1 of the wave pair m = v & 3, so its rows come from one
-  // matrix: lane l takes slot 64 (2m + l/32) + 32 t + l%32.  Wave wu takes v = wu + 8i.
+  // S: 16 wave-loads of 256 B (64 slots x 2 groups): v < 8 scales, v >= 8 biases.
+  // Wave-load v covers tile t = (v >> 2) & 1 of the wave pair m = v & 3, so its rows come
+  // from one matrix.  Lane l takes the two rows 2(l%32), 2(l%32)+1 of those 64 (slot
+  // 64 (2m + r/32) + 32 t + r%32 for r = 2(l%32)) in group 2ss + l/32: in the 16-row
+  // tile layout the two values are adjacent, and the 16 lanes of one tile read the step's
+  // 64-byte run.  In LDS, fp16 index 128 v + 64 (l/32) + r holds row r's group.  Wave wu
+  // takes v = wu + 8i.
   const char *sbase[2];
   uint32_t soff[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int v = wu + 8 * i;
     const int t = (v >> 2) & 1, m = v & 3;
-    const int slot = 64 * (2 * m + (lane >> 5)) + 32 * t + (lane & 31);
+    const int r64 = 2 * (lane & 31);
+    const int slot = 64 * (2 * m + (r64 >> 5)) + 32 * t + (r64 & 31);
     const QMat &M = slot_mat(32 * t);
     sbase[i] = (const char *)((v >> 3) ? M.b : M.s);
-    soff[i] = 2u * (uint32_t)slot_row(slot) * (uint32_t)(K / 64);
+    const uint32_t n = (uint32_t)min(slot_row(slot), N - 2);
+    soff[i] = 2u * (uint32_t)qp_index(n, lane >> 5, K / 64);
   }
   auto issue = [&](int ss, uint8_t *st) {
     const uint32_t l = lds_addr(st);
@@ -156,7 +162,7 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma16(bbase[i] + ss * 64, boff[i], l + kAStage + (wu + 8 * i) * 1024);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma4(sbase[i] + ss * 4, soff[i], l + kAStage + kBStage + (wu + 8 * i) * 256);
+    for (int i = 0; i < 2; ++i) dma4(sbase[i] + ss * (4 * kQpRows), soff[i], l + kAStage + kBStage + (wu + 8 * i) * 256);
   };
   if (!GU && tid < MT * 32) s_gate[tid] = a.row_gate[row0 + min(tid, rows - 1)];  // read by the epilogue
   f32x16 acc[MT][2];
@@ -174,7 +180,7 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     b_lane[i] = (64 * wu + 32 * i + (lane & 31));
-    s_lane[i] = 128 * ((i << 2) | (wu >> 1)) + 2 * (32 * (wu & 1) + (lane & 31)) + hf;
+    s_lane[i] = 128 * ((i << 2) | (wu >> 1)) + 64 * hf + 32 * (wu & 1) + (lane & 31);
   }
   auto compute = [&](const uint8_t *st) {
     const uint8_t *bb = st + kAStage;

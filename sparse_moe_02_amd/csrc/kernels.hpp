@@ -117,5 +117,6 @@ hipError_t launch_finalize(const uint16_t *y, const int32_t *slot_row, uint16_t 
 int decode_grid(const DecodeArgs &a, int n_cu);  // workgroups of the decode launch
 hipError_t launch_decode(const DecodeArgs &a, int grid, hipStream_t s);
 hipError_t launch_ctrl_init(Ctrl *c, void *clear, size_t clear_bytes, hipStream_t s);
+hipError_t launch_pack_qparams(const uint16_t *src, uint16_t *dst, int64_t rows, int G, hipStream_t s);
 
 }  // namespace moe

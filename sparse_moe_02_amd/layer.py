@@ -26,9 +26,11 @@ def _dev(a: np.ndarray, device) -> torch.Tensor:
 class MoeLayer:
     """One MoE layer on one GPU.
 
-    ``weights`` holds numpy arrays with the library's layouts: ``router_w`` [E][H]
-    (uint16 bf16 bits or float32), ``router_b`` [E] float32 or None, and
-    ``{gate,up,down}_{q,s,b}`` stacked over E+1 experts (the shared expert last).
+    ``weights`` holds numpy arrays: ``router_w`` [E][H] (uint16 bf16 bits or float32),
+    ``router_b`` [E] float32 or None, and ``{gate,up,down}_{q,s,b}`` stacked over E+1
+    experts (the shared expert last), scale and bias row-major [E+1][N][K/64].  Those
+    two are rewritten on the device into the library's 16-row tile layout
+    (``moe_pack_qparams``).
     """
 
     def __init__(self, weights, top_k: int, max_chunk_tokens: int = 4096, device: str = "cuda:0"):
@@ -41,6 +43,8 @@ class MoeLayer:
                      "down_q", "down_s", "down_b"):
             a = getattr(weights, name)
             self.t[name] = None if a is None else _dev(a, self.device)
+            if name in ("gate_s", "gate_b", "up_s", "up_b", "down_s", "down_b"):
+                self.t[name] = self._tiled(self.t[name])
         fp32_router = weights.router_w.dtype == np.float32
         self.cfg = B.moe_config(hidden=self.H, inter=self.I, n_experts=self.E, top_k=top_k, group_size=64,
                                 router_dtype=B.MOE_FP32 if fp32_router else B.MOE_BF16,
@@ -55,6 +59,13 @@ class MoeLayer:
         self.plan, self.ws_bytes = B.moe_plan_create(self.cfg, self.w)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
         B.moe_workspace_init(self.plan, self.ws.data_ptr(), self.ws_bytes, self.stream())
+
+    def _tiled(self, rm: torch.Tensor) -> torch.Tensor:
+        """fp16 bits [E+1][N][G] row-major -> the same values in 16-row tiles."""
+        out = torch.empty_like(rm)
+        rows, G = rm.shape[0] * rm.shape[1], rm.shape[2]
+        B.moe_pack_qparams(rm.data_ptr(), out.data_ptr(), rows, 64 * G, self.stream())
+        return out
 
     def stream(self) -> int:
         return torch.cuda.current_stream(self.device).cuda_stream

@@ -110,6 +110,21 @@ def test_forwards_reject_null_plan(B):
     assert L.moe_workspace_init(None, 0x3000, 1 << 20, None) == 1
 
 
+def test_pack_qparams_host_validation(B):
+    # every case is rejected on the host, before anything is enqueued
+    L = B.lib()
+    assert L.moe_pack_qparams(None, 0x200000, 16, 64, None) == 1
+    assert L.moe_pack_qparams(0x100000, None, 16, 64, None) == 1
+    for rows, k in ((0, 64), (8, 64), (24, 64), (16, 0), (16, 32), (16, 96), (-16, 64)):
+        assert L.moe_pack_qparams(0x100000, 0x200000, rows, k, None) == 2, (rows, k)
+    assert L.moe_pack_qparams(0x100002, 0x200000, 16, 64, None) == 4
+    assert L.moe_pack_qparams(0x100000, 0x200006, 16, 64, None) == 4
+    # 32 rows x 2 groups = 128 bytes: destinations starting inside the source overlap it
+    assert L.moe_pack_qparams(0x100000, 0x100040, 32, 128, None) == 9
+    assert L.moe_pack_qparams(0x100040, 0x100000, 32, 128, None) == 9
+    assert L.moe_pack_qparams(0x100000, 0x100000, 32, 128, None) == 9
+
+
 def test_product_path_fails_loudly_without_library(B, monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(B, "_lib", None)

@@ -372,3 +372,28 @@ def test_abi_errors_on_device():
     assert ei.value.status == 6
     torch.cuda.synchronize()
     m.close()
+
+
+def test_pack_qparams_tile_layout():
+    # moe_pack_qparams against the layout's definition: element (n, g) of a row-major
+    # [rows][G] array goes to ((n/16) G + g) 16 + n%16; bit for bit, every value.
+    import torch
+
+    from sparse_moe_02_amd import binding as B
+
+    rng = np.random.default_rng(11)
+    s = torch.cuda.current_stream().cuda_stream
+    for rows, k in ((16, 64), (48, 256), (257 * 16, 512), (2 * 512, 2048)):
+        G = k // 64
+        say(f"pack rows={rows} k={k}")
+        a = rng.integers(0, 1 << 16, size=(rows, G), dtype=np.uint16)
+        want = np.empty(rows * G, dtype=np.uint16)
+        for n in range(0, rows, 16):  # the definition, one tile at a time
+            for g in range(G):
+                base = ((n // 16) * G + g) * 16
+                want[base:base + 16] = a[n:n + 16, g]
+        src = torch.from_numpy(a.view(np.int16)).to("cuda:0")
+        dst = torch.full((rows * G,), -1, dtype=torch.int16, device="cuda:0")
+        B.moe_pack_qparams(src.data_ptr(), dst.data_ptr(), rows, k, s)
+        torch.cuda.synchronize()
+        assert np.array_equal(dst.cpu().numpy().view(np.uint16), want), (rows, k)
