@@ -54,8 +54,11 @@
  *   x, out           bf16 [T][H]
  *   router weight    [E][H], bf16 (MOE_BF16) or float32 (MOE_FP32)
  *   router bias      float32 [E], or NULL
- *   quantised W[N][K]  q: uint32 [N][K/8]; element k of row n is the 4-bit code
- *                    in bits 4*(k%8) of q[n][k/8] (low nibble first);
+ *   quantised W[N][K]  q: uint32 words in tiles of 16 rows x 128 k: element k of
+ *                    row n is the 4-bit code in bits 4*(k%8) (low nibble first) of
+ *                    word ((n/16)*(K/128) + k/128)*256 + (n%16)*16 + (k%128)/8, so a
+ *                    128-k step of 16 rows is one run of 1 KB (moe_pack_codes
+ *                    converts row-major [N][K/8] words);
  *                    w = scale*code + bias with one fp16 scale and bias per row
  *                    n and group g = k/64, stored in 16-row tiles: the pair of
  *                    (n, g) is element ((n/16)*(K/64) + g)*16 + n%16 of the
@@ -111,7 +114,7 @@ typedef struct {               /* (host) */
 } moe_config;
 
 typedef struct {               /* (host struct of device pointers) */
-  const uint32_t *q;           /* [N][K/8] codes */
+  const uint32_t *q;           /* N*K/8 code words in 16 x 128 tiles */
   const void *scale;           /* fp16, N*K/64 values in 16-row tiles */
   const void *bias;            /* fp16, same layout */
 } moe_qmat;
@@ -205,6 +208,16 @@ moe_status moe_forward_decode(moe_plan_t plan, const void *x, void *out, void *w
  * 64), MOE_ERR_ALIGN, MOE_ERR_ALIAS (overlap) or MOE_ERR_HIP. */
 moe_status moe_pack_qparams(const void *src, void *dst, int64_t rows, int32_t k,
                             hipStream_t stream);
+
+/* Weight preparation: rewrite row-major 4-bit code words src [rows][k/8] (element k
+ * of row n in bits 4*(k%8) of word k/8) into the tile layout of the quantised
+ * matrices (word w of row n to ((n/16)*(k/128) + w/16)*256 + (n%16)*16 + w%16) in dst
+ * (enqueued on stream).  rows: a multiple of 16 (a stack of experts' matrices may be
+ * packed in one call); k: a positive multiple of 128.  src and dst are device arrays
+ * of rows*k/8 uint32, 16-byte aligned, and must not overlap.  MOE_ERR_NULL,
+ * MOE_ERR_SHAPE, MOE_ERR_ALIGN, MOE_ERR_ALIAS or MOE_ERR_HIP. */
+moe_status moe_pack_codes(const uint32_t *src, uint32_t *dst, int64_t rows, int32_t k,
+                          hipStream_t stream);
 
 const char *moe_status_string(moe_status s);
 

@@ -29,7 +29,7 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_
                 9: "MOE_ERR_ALIAS", 10: "MOE_ERR_ALLOC"}
 
 EXPORTED = ("moe_plan_create", "moe_plan_destroy", "moe_workspace_init", "moe_forward_prefill",
-            "moe_forward_decode", "moe_pack_qparams", "moe_status_string", "moe_version")
+            "moe_forward_decode", "moe_pack_qparams", "moe_pack_codes", "moe_status_string", "moe_version")
 
 
 class moe_config(ctypes.Structure):
@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
             L.moe_forward_decode.argtypes = [P, P, P, P, SZ, P, ctypes.POINTER(moe_debug_out)]
             L.moe_pack_qparams.restype = ctypes.c_int
             L.moe_pack_qparams.argtypes = [P, P, I64, ctypes.c_int32, P]
+            L.moe_pack_codes.restype = ctypes.c_int
+            L.moe_pack_codes.argtypes = [P, P, I64, ctypes.c_int32, P]
             L.moe_status_string.restype = ctypes.c_char_p
             L.moe_status_string.argtypes = [ctypes.c_int]
             L.moe_version.restype = ctypes.c_char_p
@@ -147,6 +149,10 @@ def moe_forward_decode(plan, x_ptr: int, out_ptr: int, ws_ptr: int, ws_bytes: in
 
 def moe_pack_qparams(src_ptr: int, dst_ptr: int, rows: int, k: int, stream: int) -> None:
     _check("moe_pack_qparams", lib().moe_pack_qparams(src_ptr, dst_ptr, rows, k, stream))
+
+
+def moe_pack_codes(src_ptr: int, dst_ptr: int, rows: int, k: int, stream: int) -> None:
+    _check("moe_pack_codes", lib().moe_pack_codes(src_ptr, dst_ptr, rows, k, stream))
 
 
 # ---------------------------------------------------------------- HIP events (timing)

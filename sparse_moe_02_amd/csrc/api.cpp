@@ -127,6 +127,17 @@ const char *moe_status_string(moe_status s) {
 
 const char *moe_version(void) { return "moe-mi355x gfx950 1"; }
 
+moe_status moe_pack_codes(const uint32_t *src, uint32_t *dst, int64_t rows, int32_t k, hipStream_t stream) {
+  if (!src || !dst) return MOE_ERR_NULL;
+  if (rows < 16 || rows % 16 != 0 || k < 128 || k % 128 != 0) return MOE_ERR_SHAPE;
+  if (!aligned16(src) || !aligned16(dst)) return MOE_ERR_ALIGN;
+  const uintptr_t bytes = (uintptr_t)rows * (uintptr_t)(k / 8) * 4u;
+  const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+  if (s0 < d0 + bytes && d0 < s0 + bytes) return MOE_ERR_ALIAS;
+  if (moe::launch_pack_codes(src, dst, rows, k, stream) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
 moe_status moe_pack_qparams(const void *src, void *dst, int64_t rows, int32_t k, hipStream_t stream) {
   if (!src || !dst) return MOE_ERR_NULL;
   if (rows < 16 || rows % 16 != 0 || k < 64 || k % 64 != 0) return MOE_ERR_SHAPE;

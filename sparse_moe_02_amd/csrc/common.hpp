@@ -37,6 +37,11 @@ __device__ __forceinline__ float fp16_to_f32(uint16_t h) { return (float)__built
 // Scale and bias arrays (G groups of 64 per row) are stored in tiles of kQpRows rows:
 // the tile's values of one group are contiguous, groups follow each other.
 constexpr int kQpRows = 16;
+// Code words are stored in tiles of 16 rows x 128 k (16 words per row per tile): word w
+// of row n (K/8 words per row) is at code_index(n, w, K).
+__device__ __forceinline__ size_t code_index(size_t n, int w, int K) {
+  return ((n >> 4) * (size_t)(K / 128) + (size_t)(w >> 4)) * 256u + (n & 15u) * 16u + (size_t)(w & 15);
+}
 __device__ __forceinline__ size_t qp_index(size_t n, int g, int G) {
   return ((n / kQpRows) * (size_t)G + (size_t)g) * kQpRows + (n % kQpRows);
 }

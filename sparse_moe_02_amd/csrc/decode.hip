@@ -448,8 +448,9 @@ __device__ __forceinline__ void gu_issue(const DecodeArgs &a, const QMat &Gm, co
 #pragma unroll
   for (int r = 0; r < kGuRows; ++r) {
     const size_t row = (size_t)(r0 + r);
-    L.wg[r] = *(const uint4 *)(Gm.q + row * (H / 8) + 4 * cc);
-    L.wu[r] = *(const uint4 *)(Um.q + row * (H / 8) + 4 * cc);
+    const size_t ci = code_index(row, 4 * cc, H);
+    L.wg[r] = *(const uint4 *)(Gm.q + ci);
+    L.wu[r] = *(const uint4 *)(Um.q + ci);
   }
   // r0 is a multiple of 4, so the four rows' values of one group are adjacent (8 bytes)
   const size_t qi = qp_index((size_t)r0, cc / 2, H / 64);
@@ -550,7 +551,7 @@ __device__ __forceinline__ void dn_issue(const DecodeArgs &a, const DecShared &s
     const int e = slot < k ? sh.ids[slot] : a.E;
     const QMat D = expert_mat(a.down, a.s_down, e, a.E, a.H, I);
     const size_t n = (size_t)(n0 + r);
-    L.w[m] = *(const uint4 *)(D.q + n * (I / 8) + 4 * cc);
+    L.w[m] = *(const uint4 *)(D.q + code_index(n, 4 * cc, I));
     const size_t qi = qp_index(n, cc / 2, I / 64);
     L.s[m] = D.s[qi];
     L.b[m] = D.b[qi];

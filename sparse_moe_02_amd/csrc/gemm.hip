@@ -125,7 +125,10 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
     const uint32_t row_elem = GU ? (uint32_t)a.row_token[rr] * (uint32_t)H : (uint32_t)rr * (uint32_t)I;
     aoff[i] = 2u * (row_elem + 8u * (uint32_t)((lane & 15) ^ (r & 15)));
   }
-  // B: 32 wave-loads of 1 KiB (16 slots x 64 B); wave takes v = wu + 8i, i < 4
+  // B: 32 wave-loads of 1 KiB (16 slots x 64 B); wave takes v = wu + 8i, i < 4.  The 16
+  // slots of a wave-load are 16 consecutive weight rows starting at a multiple of 16, so
+  // in the tiled code layout each wave-load reads one contiguous KiB (the next step's is
+  // the next KiB of the tile row).
   const char *bbase[4];
   uint32_t boff[4];
 #pragma unroll
@@ -133,7 +136,7 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
     const int v = wu + 8 * i;
     const int slot = 16 * v + (lane >> 2);
     bbase[i] = (const char *)slot_mat(16 * v).q;
-    boff[i] = 4u * ((uint32_t)slot_row(slot) * (uint32_t)(K / 8) + 4u * (uint32_t)((lane & 3) ^ ((slot >> 2) & 3)));
+    boff[i] = 4u * (uint32_t)code_index((size_t)slot_row(slot), 4 * ((lane & 3) ^ ((slot >> 2) & 3)), K);
   }
   // S: 16 wave-loads of 256 B (64 slots x 2 groups): v < 8 scales, v >= 8 biases.
   // Wave-load v covers tile t = (v >> 2) & 1 of the wave pair m = v & 3, so its rows come
@@ -160,7 +163,7 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
 #pragma unroll
     for (int i = 0; i < MT; ++i) dma16(abase + ss * 256, aoff[i], l + (wu + 8 * i) * 1024);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(bbase[i] + ss * 64, boff[i], l + kAStage + (wu + 8 * i) * 1024);
+    for (int i = 0; i < 4; ++i) dma16(bbase[i] + ss * 1024, boff[i], l + kAStage + (wu + 8 * i) * 1024);
 #pragma unroll
     for (int i = 0; i < 2; ++i) dma4(sbase[i] + ss * (4 * kQpRows), soff[i], l + kAStage + kBStage + (wu + 8 * i) * 256);
   };

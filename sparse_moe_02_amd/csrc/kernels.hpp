@@ -118,5 +118,6 @@ int decode_grid(const DecodeArgs &a, int n_cu);  // workgroups of the decode lau
 hipError_t launch_decode(const DecodeArgs &a, int grid, hipStream_t s);
 hipError_t launch_ctrl_init(Ctrl *c, void *clear, size_t clear_bytes, hipStream_t s);
 hipError_t launch_pack_qparams(const uint16_t *src, uint16_t *dst, int64_t rows, int G, hipStream_t s);
+hipError_t launch_pack_codes(const uint32_t *src, uint32_t *dst, int64_t rows, int K, hipStream_t s);
 
 }  // namespace moe

@@ -28,9 +28,9 @@ class MoeLayer:
 
     ``weights`` holds numpy arrays: ``router_w`` [E][H] (uint16 bf16 bits or float32),
     ``router_b`` [E] float32 or None, and ``{gate,up,down}_{q,s,b}`` stacked over E+1
-    experts (the shared expert last), scale and bias row-major [E+1][N][K/64].  Those
-    two are rewritten on the device into the library's 16-row tile layout
-    (``moe_pack_qparams``).
+    experts (the shared expert last), codes row-major [E+1][N][K/8] and scale and bias
+    row-major [E+1][N][K/64].  All three are rewritten on the device into the library's
+    tile layouts (``moe_pack_codes``, ``moe_pack_qparams``).
     """
 
     def __init__(self, weights, top_k: int, max_chunk_tokens: int = 4096, device: str = "cuda:0"):
@@ -45,6 +45,8 @@ class MoeLayer:
             self.t[name] = None if a is None else _dev(a, self.device)
             if name in ("gate_s", "gate_b", "up_s", "up_b", "down_s", "down_b"):
                 self.t[name] = self._tiled(self.t[name])
+            elif name in ("gate_q", "up_q", "down_q"):
+                self.t[name] = self._tiled_codes(self.t[name])
         fp32_router = weights.router_w.dtype == np.float32
         self.cfg = B.moe_config(hidden=self.H, inter=self.I, n_experts=self.E, top_k=top_k, group_size=64,
                                 router_dtype=B.MOE_FP32 if fp32_router else B.MOE_BF16,
@@ -65,6 +67,12 @@ class MoeLayer:
         out = torch.empty_like(rm)
         rows, G = rm.shape[0] * rm.shape[1], rm.shape[2]
         B.moe_pack_qparams(rm.data_ptr(), out.data_ptr(), rows, 64 * G, self.stream())
+        return out
+
+    def _tiled_codes(self, rm: torch.Tensor) -> torch.Tensor:
+        """uint32 codes [E+1][N][K/8] row-major -> the same words in 16 x 128 tiles."""
+        out = torch.empty_like(rm)
+        B.moe_pack_codes(rm.data_ptr(), out.data_ptr(), rm.shape[0] * rm.shape[1], 8 * rm.shape[2], self.stream())
         return out
 
     def stream(self) -> int:

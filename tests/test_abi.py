@@ -125,6 +125,19 @@ def test_pack_qparams_host_validation(B):
     assert L.moe_pack_qparams(0x100000, 0x100000, 32, 128, None) == 9
 
 
+def test_pack_codes_host_validation(B):
+    L = B.lib()
+    assert L.moe_pack_codes(None, 0x200000, 16, 128, None) == 1
+    assert L.moe_pack_codes(0x100000, None, 16, 128, None) == 1
+    for rows, k in ((0, 128), (8, 128), (24, 128), (16, 0), (16, 64), (16, 192), (-16, 128)):
+        assert L.moe_pack_codes(0x100000, 0x200000, rows, k, None) == 2, (rows, k)
+    assert L.moe_pack_codes(0x100008, 0x200000, 16, 128, None) == 4
+    assert L.moe_pack_codes(0x100000, 0x200004, 16, 128, None) == 4
+    # 16 rows x 16 words = 1 KiB
+    assert L.moe_pack_codes(0x100000, 0x100200, 16, 128, None) == 9
+    assert L.moe_pack_codes(0x100200, 0x100000, 16, 128, None) == 9
+
+
 def test_product_path_fails_loudly_without_library(B, monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(B, "_lib", None)

@@ -397,3 +397,28 @@ def test_pack_qparams_tile_layout():
         B.moe_pack_qparams(src.data_ptr(), dst.data_ptr(), rows, k, s)
         torch.cuda.synchronize()
         assert np.array_equal(dst.cpu().numpy().view(np.uint16), want), (rows, k)
+
+
+def test_pack_codes_tile_layout():
+    # moe_pack_codes against the layout's definition: word w of row n of a row-major
+    # [rows][k/8] array goes to ((n/16)(k/128) + w/16) 256 + (n%16) 16 + w%16.
+    import torch
+
+    from sparse_moe_02_amd import binding as B
+
+    rng = np.random.default_rng(12)
+    s = torch.cuda.current_stream().cuda_stream
+    for rows, k in ((16, 128), (48, 384), (257 * 16, 512), (2 * 512, 2048)):
+        KW = k // 8
+        say(f"pack codes rows={rows} k={k}")
+        a = rng.integers(0, 1 << 32, size=(rows, KW), dtype=np.uint32)
+        want = np.empty(rows * KW, dtype=np.uint32)
+        for n in range(rows):  # the definition, one row at a time
+            for w0 in range(0, KW, 16):
+                base = ((n // 16) * (k // 128) + w0 // 16) * 256 + (n % 16) * 16
+                want[base:base + 16] = a[n, w0:w0 + 16]
+        src = torch.from_numpy(a.view(np.int32)).to("cuda:0")
+        dst = torch.full((rows * KW,), -1, dtype=torch.int32, device="cuda:0")
+        B.moe_pack_codes(src.data_ptr(), dst.data_ptr(), rows, k, s)
+        torch.cuda.synchronize()
+        assert np.array_equal(dst.cpu().numpy().view(np.uint32), want), (rows, k)
