@@ -50,7 +50,7 @@
  *   - x and out must not alias.  x, out, router weight and code arrays must be
  *     16-byte aligned, scale/bias arrays 8-byte aligned, the workspace 256-byte aligned.
  *
- * Layouts (row-major):
+ * Layouts (row-major unless stated):
  *   x, out           bf16 [T][H]
  *   router weight    [E][H], bf16 (MOE_BF16) or float32 (MOE_FP32)
  *   router bias      float32 [E], or NULL
