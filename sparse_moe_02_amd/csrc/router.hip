@@ -179,7 +179,31 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
   for (int e = tid; e < kMaxExperts; e += kRouteThreads) s_mask[e] = 0;
   if (tid == 0) s_nflag = 0;
 
-  if (a.wr16) {
+  if (a.wr16 && E % 4 == 0) {
+    // 16-byte loads: four of each array in flight per thread (one batch for E = 256)
+    constexpr int kB = 4;
+    const int E4 = E / 4;
+    for (int i0 = tid; i0 < kRouteTokens * E4; i0 += kRouteThreads * kB) {
+      float4 lv[kB], rv[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int i = min(i0 + u * kRouteThreads, kRouteTokens * E4 - 1);
+        const int m = i / E4, e4 = i - m * E4;
+        const size_t o = (size_t)(t0 + min(m, nt - 1)) * E + 4 * e4;
+        lv[u] = *(const float4 *)(a.lg + o);
+        rv[u] = *(const float4 *)(a.rd + o);
+      }
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int i = i0 + u * kRouteThreads;
+        if (i < kRouteTokens * E4) {
+          const int m = i / E4, e4 = i - m * E4;
+          *(float4 *)&s_l[m][4 * e4] = lv[u];
+          *(float4 *)&s_r[m][4 * e4] = rv[u];
+        }
+      }
+    }
+  } else if (a.wr16) {
     // sixteen loads of each array in flight per thread (one batch for E = 256)
     constexpr int kB = 16;
     for (int i0 = tid; i0 < kRouteTokens * E; i0 += kRouteThreads * kB) {
