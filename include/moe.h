@@ -92,13 +92,42 @@ typedef enum {
   MOE_ERR_DEVICE = 7,    /* current device is not gfx950, or device query failed */
   MOE_ERR_HIP = 8,       /* a kernel launch failed */
   MOE_ERR_ALIAS = 9,     /* x and out (or a pack's src and dst) overlap */
-  MOE_ERR_ALLOC = 10     /* host allocation failed */
+  MOE_ERR_ALLOC = 10,    /* host allocation failed */
+  MOE_ERR_WAIT = 11      /* moe_workspace_check: an internal decode wait ran out of polls
+                            since the workspace was initialised; outputs of the decode
+                            calls since then are not valid */
 } moe_status;
 
 typedef enum { MOE_BF16 = 0, MOE_FP16 = 1, MOE_FP32 = 2 } moe_dtype;
 
-/* Flags (moe_config.flags). */
+/* Flags (moe_config.flags).  Section "Optimization strategy" of the pages measures each
+ * optimisation against an otherwise identical configuration without it; the flags
+ * below select such configurations.  Unknown bits are rejected (MOE_ERR_SHAPE).
+ *
+ * MOE_F_FORCE_BM(rows): every M-block of the grouped GEMMs is `rows` tall (32, 64, 96,
+ *   128 or 160; the last block of an expert holds the remainder) instead of a height
+ *   picked from the expert's row count (section "Prefill > Match tile size to expert
+ *   load": the ablation fixes the tile size).  The smallest tile the grouped GEMM has is
+ *   one 32 x 32 MFMA tile, so MOE_F_FORCE_BM(32) is the fixed-small-tile configuration.
+ * MOE_F_NO_FALLBACK: prefill keeps the fp32 top-k of a token even when its error bound
+ *   does not certify it (no binary64 re-rank).  Routing may then differ from the exact
+ *   ranking; for tests and timing only.  No effect with a float32 router (ranked in
+ *   binary64 throughout) or on decode.
+ * MOE_F_SEPARATE_DEQUANT: prefill dequantises the weights of every expert that has rows
+ *   into bf16 matrices in the workspace first, and the grouped GEMMs read those (section
+ *   "Prefill > Dequantize weights during matmul": the ablation expands the 4-bit weights
+ *   into a bf16 array that the matrix kernel reads back).  The workspace grows by the
+ *   bf16 size of all E+1 experts' matrices.
+ * MOE_F_HOST_ROUTING: prefill stops after grouping each chunk, synchronises the stream
+ *   on the host, reads the block-map length and launches the grouped GEMMs with exactly
+ *   one workgroup per work item (section "Prefill > Keep expert routing on the GPU": the
+ *   ablation lets the CPU inspect the routing before the next launch).  The forward then
+ *   blocks the host; the stream must not be under graph capture. */
 #define MOE_F_NONE 0u
+#define MOE_F_FORCE_BM(rows) ((uint32_t)((rows) / 32) & 0xfu)
+#define MOE_F_NO_FALLBACK (1u << 4)
+#define MOE_F_SEPARATE_DEQUANT (1u << 5)
+#define MOE_F_HOST_ROUTING (1u << 6)
 
 typedef struct {               /* (host) */
   int32_t hidden;              /* H: multiple of 256, <= 16384 */
@@ -163,6 +192,10 @@ typedef struct {
   int32_t *row_token;          /* [n_chunks * max_chunk_tokens * (k+1)] */
   int32_t *n_refined;          /* [n_chunks] */
   hipEvent_t *events;          /* (host) */
+  float *logits32;             /* [T][E] prefill, bf16 router only: the fp32 logits (+ bias)
+                                  that the selection ranks first (left untouched otherwise) */
+  float *radii32;              /* [T][E] prefill, bf16 router only: the certified bound on
+                                  |logits32 - exact logit| used by that ranking */
 } moe_debug_out;
 
 /* Validate cfg and w (host checks only: no device work, no device memory) and
@@ -178,6 +211,13 @@ void moe_plan_destroy(moe_plan_t plan);
 moe_status moe_workspace_init(moe_plan_t plan, void *workspace, size_t workspace_bytes,
                               hipStream_t stream);
 
+/* Read the workspace's decode error word (enqueued on stream, then the host waits for
+ * stream): MOE_OK if every decode call on this workspace since moe_workspace_init
+ * completed its internal hand-offs, MOE_ERR_WAIT if a wait ran out of polls (the word
+ * stays set until moe_workspace_init), MOE_ERR_HIP if the copy failed.  Blocks the host. */
+moe_status moe_workspace_check(moe_plan_t plan, const void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
 /* Prefill: x, out bf16 [T][H]; T >= 1.  Tokens are processed in chunks of at
  * most max_chunk_tokens with one workspace. */
 moe_status moe_forward_prefill(moe_plan_t plan, const void *x, int64_t T, void *out,
@@ -192,7 +232,10 @@ moe_status moe_forward_prefill(moe_plan_t plan, const void *x, int64_t T, void *
  * tagged with a per-call number kept in the workspace (bytes 92..99), so the launch
  * arguments depend only on (plan, x, out, workspace, dbg): a sequence of decode calls may
  * be captured once in a HIP graph and replayed, also interleaved with direct calls on the
- * same workspace, as long as the calls on one workspace stay ordered on one stream. */
+ * same workspace, as long as the calls on one workspace stay ordered on one stream.
+ * Workgroups of the launch wait for each other, so the launch must have the GPU to
+ * itself: a concurrent kernel that occupies compute units can delay the waits until they
+ * run out of polls (check with moe_workspace_check). */
 moe_status moe_forward_decode(moe_plan_t plan, const void *x, void *out, void *workspace,
                               size_t workspace_bytes, hipStream_t stream,
                               const moe_debug_out *dbg);

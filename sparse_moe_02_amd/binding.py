@@ -26,10 +26,24 @@ CTRL_DECODE_ERR_OFFSET = 88  # byte offset of the decode wait-failure word in th
 
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE", 4: "MOE_ERR_ALIGN",
                 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_TOKENS", 7: "MOE_ERR_DEVICE", 8: "MOE_ERR_HIP",
-                9: "MOE_ERR_ALIAS", 10: "MOE_ERR_ALLOC"}
+                9: "MOE_ERR_ALIAS", 10: "MOE_ERR_ALLOC", 11: "MOE_ERR_WAIT"}
+MOE_ERR_WAIT = 11
 
-EXPORTED = ("moe_plan_create", "moe_plan_destroy", "moe_workspace_init", "moe_forward_prefill",
-            "moe_forward_decode", "moe_pack_qparams", "moe_pack_codes", "moe_status_string", "moe_version")
+# moe_config.flags (include/moe.h)
+MOE_F_NONE = 0
+
+
+def MOE_F_FORCE_BM(rows: int) -> int:
+    return (rows // 32) & 0xF
+
+
+MOE_F_NO_FALLBACK = 1 << 4
+MOE_F_SEPARATE_DEQUANT = 1 << 5
+MOE_F_HOST_ROUTING = 1 << 6
+
+EXPORTED = ("moe_plan_create", "moe_plan_destroy", "moe_workspace_init", "moe_workspace_check",
+            "moe_forward_prefill", "moe_forward_decode", "moe_pack_qparams", "moe_pack_codes",
+            "moe_status_string", "moe_version")
 
 
 class moe_config(ctypes.Structure):
@@ -52,7 +66,7 @@ class moe_weights(ctypes.Structure):
 class moe_debug_out(ctypes.Structure):
     _fields_ = [("topk_ids", ctypes.c_void_p), ("gates", ctypes.c_void_p), ("counts", ctypes.c_void_p),
                 ("offsets", ctypes.c_void_p), ("row_token", ctypes.c_void_p), ("n_refined", ctypes.c_void_p),
-                ("events", ctypes.c_void_p)]
+                ("events", ctypes.c_void_p), ("logits32", ctypes.c_void_p), ("radii32", ctypes.c_void_p)]
 
 
 class MoeError(RuntimeError):
@@ -82,6 +96,8 @@ def lib() -> ctypes.CDLL:
             L.moe_plan_destroy.argtypes = [P]
             L.moe_workspace_init.restype = ctypes.c_int
             L.moe_workspace_init.argtypes = [P, P, SZ, P]
+            L.moe_workspace_check.restype = ctypes.c_int
+            L.moe_workspace_check.argtypes = [P, P, SZ, P]
             L.moe_forward_prefill.restype = ctypes.c_int
             L.moe_forward_prefill.argtypes = [P, P, I64, P, P, SZ, P, ctypes.POINTER(moe_debug_out)]
             L.moe_forward_decode.restype = ctypes.c_int
@@ -133,6 +149,14 @@ def moe_plan_destroy(plan) -> None:
 
 def moe_workspace_init(plan, ws_ptr: int, ws_bytes: int, stream: int) -> None:
     _check("moe_workspace_init", lib().moe_workspace_init(plan, ws_ptr, ws_bytes, stream))
+
+
+def moe_workspace_check(plan, ws_ptr: int, ws_bytes: int, stream: int) -> int:
+    """MOE_OK or MOE_ERR_WAIT (returned, not raised); raises on other statuses."""
+    st = lib().moe_workspace_check(plan, ws_ptr, ws_bytes, stream)
+    if st not in (MOE_OK, MOE_ERR_WAIT):
+        raise MoeError("moe_workspace_check", st)
+    return st
 
 
 def moe_forward_prefill(plan, x_ptr: int, T: int, out_ptr: int, ws_ptr: int, ws_bytes: int, stream: int,

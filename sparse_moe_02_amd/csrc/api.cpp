@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstddef>
 #include <cstdint>
 #include <cstring>
 #include <new>
@@ -30,6 +31,11 @@ namespace {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// M-block height forced by MOE_F_FORCE_BM (0: chosen from each expert's row count)
+int forced_rows(uint32_t flags) { return 32 * (int)(flags & 0xfu); }
+
+constexpr uint32_t kKnownFlags = 0xfu | MOE_F_NO_FALLBACK | MOE_F_HOST_ROUTING;
+
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 moe_status check_qmat(const moe_qmat &m) {
@@ -44,7 +50,8 @@ void layout(moe_plan_s &p) {
   const size_t H = p.cfg.hidden, I = p.cfg.inter;
   const size_t nblk = (C + kRouteTokens - 1) / kRouteTokens;
   const size_t rows = C * (k + 1);
-  const size_t max_mblocks = rows / kBM + E + 2;
+  const size_t bm = forced_rows(p.cfg.flags) ? (size_t)forced_rows(p.cfg.flags) : (size_t)kBM;
+  const size_t max_mblocks = rows / bm + E + 2;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -121,6 +128,7 @@ const char *moe_status_string(moe_status s) {
     case MOE_ERR_HIP: return "HIP launch failed";
     case MOE_ERR_ALIAS: return "input and output arrays overlap";
     case MOE_ERR_ALLOC: return "host allocation failed";
+    case MOE_ERR_WAIT: return "a decode wait ran out of polls; decode outputs since the workspace init are invalid";
   }
   return "unknown status";
 }
@@ -162,7 +170,7 @@ moe_status moe_plan_create(const moe_config *cfg, const moe_weights *w, moe_plan
   if (c.n_experts < 1 || c.n_experts > kMaxExperts) return MOE_ERR_SHAPE;
   if (c.top_k < 1 || c.top_k > c.n_experts || c.top_k > kMaxTopK) return MOE_ERR_SHAPE;
   if (c.max_chunk_tokens < 1 || c.max_chunk_tokens > 65536) return MOE_ERR_SHAPE;
-  if (c.flags != 0) return MOE_ERR_SHAPE;
+  if ((c.flags & ~kKnownFlags) != 0 || forced_rows(c.flags) > kBM) return MOE_ERR_SHAPE;
   if (c.router_dtype != MOE_BF16 && c.router_dtype != MOE_FP32) return MOE_ERR_DTYPE;
   if (c.qparam_dtype != MOE_FP16) return MOE_ERR_DTYPE;
   if (!w->router_w) return MOE_ERR_NULL;
@@ -207,6 +215,18 @@ moe_status moe_workspace_init(moe_plan_t p, void *ws, size_t bytes, hipStream_t 
              : MOE_ERR_HIP;
 }
 
+moe_status moe_workspace_check(moe_plan_t p, const void *ws, size_t bytes, hipStream_t stream) {
+  if (!p) return MOE_ERR_NULL;
+  const moe_status st = check_ws(p, const_cast<void *>(ws), bytes);
+  if (st != MOE_OK) return st;
+  int32_t word = 0;
+  if (hipMemcpyAsync(&word, static_cast<const char *>(ws) + p->off_ctrl + offsetof(Ctrl, d_err), sizeof(word),
+                     hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  return word ? MOE_ERR_WAIT : MOE_OK;
+}
+
 moe_status moe_forward_prefill(moe_plan_t p, const void *x, int64_t T, void *out, void *ws, size_t bytes,
                                hipStream_t stream, const moe_debug_out *dbg) {
   if (!p || !x || !out) return MOE_ERR_NULL;
@@ -244,12 +264,22 @@ moe_status moe_forward_prefill(moe_plan_t p, const void *x, int64_t T, void *out
     ra.lg = at<float>(ws, p->off_lg);
     ra.rd = at<float>(ws, p->off_rd);
     ra.ctrl = ctrl;
+    ra.no_fallback = (c.flags & MOE_F_NO_FALLBACK) != 0;
     if (dbg) {
       ra.dbg_ids = dbg->topk_ids ? dbg->topk_ids + (size_t)c0 * k : nullptr;
       ra.dbg_gates = dbg->gates ? dbg->gates + (size_t)c0 * k : nullptr;
     }
     if (rec(d, MOE_STAGE_ROUTE, stream) != hipSuccess) return MOE_ERR_HIP;
     if (launch_route(ra, stream) != hipSuccess) return MOE_ERR_HIP;
+    if (dbg && !fp32_router) {
+      const size_t n = (size_t)Tc * E * sizeof(float);
+      if (dbg->logits32 &&
+          hipMemcpyAsync(dbg->logits32 + (size_t)c0 * E, ra.lg, n, hipMemcpyDeviceToDevice, stream) != hipSuccess)
+        return MOE_ERR_HIP;
+      if (dbg->radii32 &&
+          hipMemcpyAsync(dbg->radii32 + (size_t)c0 * E, ra.rd, n, hipMemcpyDeviceToDevice, stream) != hipSuccess)
+        return MOE_ERR_HIP;
+    }
 
     GroupArgs ga{};
     ga.ids = ra.ids;
@@ -265,6 +295,7 @@ moe_status moe_forward_prefill(moe_plan_t p, const void *x, int64_t T, void *out
     ga.slot_row = at<int32_t>(ws, p->off_slot_row);
     ga.mblocks = at<int4>(ws, p->off_mblocks);
     ga.ctrl = ctrl;
+    ga.force_rows = forced_rows(c.flags);
     if (dbg) {
       ga.dbg_counts = dbg->counts ? dbg->counts + (size_t)ci * (E + 1) : nullptr;
       ga.dbg_offsets = dbg->offsets ? dbg->offsets + (size_t)ci * (E + 2) : nullptr;
@@ -273,6 +304,19 @@ moe_status moe_forward_prefill(moe_plan_t p, const void *x, int64_t T, void *out
     }
     if (rec(d, MOE_STAGE_GROUP, stream) != hipSuccess) return MOE_ERR_HIP;
     if (launch_group(ga, stream) != hipSuccess) return MOE_ERR_HIP;
+
+    // persistent grid of one workgroup per CU; with MOE_F_HOST_ROUTING the host waits for
+    // the block map and launches one workgroup per work item instead
+    int grid_gu = gemm_blocks, grid_dn = gemm_blocks;
+    if (c.flags & MOE_F_HOST_ROUTING) {
+      int nmb = 0;
+      if (hipMemcpyAsync(&nmb, &ctrl->n_mblocks, sizeof(nmb), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+          hipStreamSynchronize(stream) != hipSuccess)
+        return MOE_ERR_HIP;
+      const int nb_gu = (c.inter + kGateUpCols - 1) / kGateUpCols, nb_dn = (c.hidden + kDownCols - 1) / kDownCols;
+      grid_gu = std::max(1, nmb * nb_gu);
+      grid_dn = std::max(1, nmb * nb_dn);
+    }
 
     GemmArgs g1{};
     g1.x = xc;
@@ -296,7 +340,7 @@ moe_status moe_forward_prefill(moe_plan_t p, const void *x, int64_t T, void *out
     g1.slot_u64 = (int)p->slot_u64;
     g1.tickets = at<int>(ws, p->off_tk);
     if (rec(d, MOE_STAGE_GATEUP, stream) != hipSuccess) return MOE_ERR_HIP;
-    if (launch_gemm_gateup(g1, gemm_blocks, stream) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_gemm_gateup(g1, grid_gu, stream) != hipSuccess) return MOE_ERR_HIP;
 
     GemmArgs g2 = g1;
     g2.x = g1.h;
@@ -308,7 +352,7 @@ moe_status moe_forward_prefill(moe_plan_t p, const void *x, int64_t T, void *out
     g2.y = at<uint16_t>(ws, p->off_y);
     g2.part = nullptr;
     if (rec(d, MOE_STAGE_DOWN, stream) != hipSuccess) return MOE_ERR_HIP;
-    if (launch_gemm_down(g2, gemm_blocks, stream) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_gemm_down(g2, grid_dn, stream) != hipSuccess) return MOE_ERR_HIP;
 
     if (rec(d, MOE_STAGE_FINAL, stream) != hipSuccess) return MOE_ERR_HIP;
     if (launch_finalize(g2.y, ga.slot_row, oc, Tc, (int)H, (int)k, stream) != hipSuccess) return MOE_ERR_HIP;

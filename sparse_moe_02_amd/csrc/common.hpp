@@ -46,30 +46,17 @@ __device__ __forceinline__ size_t qp_index(size_t n, int g, int G) {
   return ((n / kQpRows) * (size_t)G + (size_t)g) * kQpRows + (n % kQpRows);
 }
 
-// 4-bit code i (0..7) of a packed word as float.
-__device__ __forceinline__ float code_f(uint32_t w, int i) { return (float)((w >> (4 * i)) & 0xfu); }
-
-// Dequantise the 8 codes of one word with one (scale, bias) and pack to 4 bf16x2 words
-// (element order k, k+1, ... low half first): w = scale*code + bias in fp32, then RNE.
-__device__ __forceinline__ void dequant8_bf16(uint32_t w, float s, float b, uint32_t out[4]) {
-  uint32_t lo = w & 0x0f0f0f0fu;         // codes 0,2,4,6 in bytes 0..3
-  uint32_t hi = (w >> 4) & 0x0f0f0f0fu;  // codes 1,3,5,7
-  // keep the byte layout opaque so each code converts with one v_cvt_f32_ubyteN
-  // (otherwise the extraction is re-derived from w with an extra shift/bfe per code)
-  asm("" : "+v"(lo), "+v"(hi));
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float c0 = (float)((lo >> (8 * j)) & 0xffu);
-    const float c1 = (float)((hi >> (8 * j)) & 0xffu);
-    out[j] = pack_bf16x2(__builtin_fmaf(s, c0, b), __builtin_fmaf(s, c1, b));
-  }
-}
-
-// The same eight weights through fp16 "magic" operands: for each code pair (2j, 2j+1),
-// one byte permute and one and-or build a dword whose low half is the fp16 1024 + c_2j
-// and whose high half is the fp16 1024 + 16 c_2j+1 (exact), and a mixed-precision fma
-// maps each half to s c + b in fp32: the low half with (s, b - 1024 s), the high half
-// with (s/16, b - 64 s) -- the DeqPair below.  20 instructions per word instead of 23.
+// Dequantise the 8 codes of one packed word with one (scale, bias) and pack the eight
+// weights to 4 bf16x2 words (element order k, k+1, ... low half first): w = s*code + b
+// in fp32, then rounded to nearest even.  The int4 -> float step is the fp16 "magic
+// number" conversion published by Kim et al., "Who Says Elephants Can't Run: Bringing
+// Large Scale MoE Models into Cloud Scale Production" (arXiv 2211.10017): OR-ing a 4-bit
+// code into the mantissa of the fp16 number 1024 gives exactly 1024 + code.  Here, for
+// each code pair (2j, 2j+1), one byte permute and one and-or build a dword whose low
+// half is the fp16 1024 + c_2j and whose high half is the fp16 1024 + 16 c_2j+1 (both
+// exact), and a mixed-precision fma maps each half to s c + b in fp32: the low half
+// with (s, b - 1024 s), the high half with (s/16, b - 64 s) -- the DeqPair below.  20
+// VALU instructions per word.
 struct DeqPair {
   float s_lo, b_lo, s_hi, b_hi;
   uint32_t nib;  // 0x00f0000f held in a vector register, so the mask-and-or is one v_and_or_b32
@@ -189,12 +176,6 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-__device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) v = fminf(v, __shfl_xor(v, o));
-  return v;
-}
-
 // Cross-workgroup hand-off without cache maintenance: agent-scope relaxed atomic
 // stores/loads are coherent across XCDs; draining vmcnt after the data stores orders
 // them before a following relaxed ticket update.
@@ -209,16 +190,6 @@ __device__ __forceinline__ T ld_agent(const T *p) {
 __device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0xF70); }  // vmcnt(0)
 __device__ __forceinline__ int ticket(int *p) {
   return __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Block until *flag reaches `target` (device-scope acquire), giving up after
-// `spins` polls; returns false on timeout.
-__device__ __forceinline__ bool wait_at_least(const int *flag, int target, int spins) {
-  for (int i = 0; i < spins; ++i) {
-    if (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) >= target) return true;
-    __builtin_amdgcn_s_sleep(2);
-  }
-  return false;
 }
 
 }  // namespace moe

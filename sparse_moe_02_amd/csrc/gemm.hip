@@ -115,14 +115,17 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
   const bool active = wcol0 < N;
 
   // --- this wave's share of each stage's loads: wave-uniform bases + 32-bit offsets
-  // A: MT*8 wave-loads of 1 KiB (4 rows each); wave takes v = wu + 8i, i < MT
-  const char *abase = (const char *)a.x;
+  // A: MT*8 wave-loads of 1 KiB (4 rows each); wave takes v = wu + 8i, i < MT.  The
+  // per-lane offsets stay below 2^31 bytes: a token row (gate/up) is at most 65535 x
+  // 16384 x 2 bytes in; the h rows (down) are addressed from the M-block's first row,
+  // which goes into the 64-bit base, so the offset is at most 159 x 4096 x 2 bytes.
+  const char *abase = GU ? (const char *)a.x : (const char *)a.x + (size_t)row0 * I * 2;
   uint32_t aoff[MT];
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
     const int r = 4 * (wu + 8 * i) + (lane >> 4);
-    const int rr = row0 + min(r, rows - 1);
-    const uint32_t row_elem = GU ? (uint32_t)a.row_token[rr] * (uint32_t)H : (uint32_t)rr * (uint32_t)I;
+    const int rl = min(r, rows - 1);
+    const uint32_t row_elem = GU ? (uint32_t)a.row_token[row0 + rl] * (uint32_t)H : (uint32_t)rl * (uint32_t)I;
     aoff[i] = 2u * (row_elem + 8u * (uint32_t)((lane & 15) ^ (r & 15)));
   }
   // B: 32 wave-loads of 1 KiB (16 slots x 64 B); wave takes v = wu + 8i, i < 4.  The 16

@@ -49,7 +49,8 @@ __global__ __launch_bounds__(kThreads) void k_group(GroupArgs a) {
   __shared__ int s_cnt[kMaxExperts + 1];
   __shared__ __attribute__((aligned(16))) uint32_t s_msk[kSubs][kMaxExperts];
   __shared__ int s_base[kSubs][kMaxExperts];
-  __shared__ int s_cls[6], s_clsoff[6], s_clspos[6];
+  __shared__ int s_cls[6], s_clsoff[6];
+  __shared__ int s_pc[kBM / 32 + 1][kMaxExperts + 1];  // per class, per expert: M-blocks (then their scan)
   const int tid = threadIdx.x;
   const int T = a.T, E = a.E, k = a.k;
   const int nblk = (T + kRouteTokens - 1) / kRouteTokens;
@@ -109,7 +110,6 @@ __global__ __launch_bounds__(kThreads) void k_group(GroupArgs a) {
   }
   if (tid < 6) {
     s_cls[tid] = 0;
-    s_clspos[tid] = 0;
   }
   __syncthreads();
   if (tid < E) {
@@ -187,23 +187,64 @@ __global__ __launch_bounds__(kThreads) void k_group(GroupArgs a) {
     if (a.dbg_offsets) a.dbg_offsets[e] = s_off[e];
   }
 
-  // 4. block map: balanced M-blocks per expert, ordered tallest class first
+  // 4. block map: balanced M-blocks per expert, ordered tallest class first.  With a
+  // forced height F: floor(n/F) blocks of F rows and one block of the remainder.  Inside
+  // a height class the blocks follow in expert order (a prefix scan over the experts'
+  // block counts of that class, not an atomic), so the map, and with it the items the
+  // gate/up GEMM splits along K, is the same on every run.
+  constexpr int kCls = kBM / 32;
   int nmb = 0, q = 0, rem = 0;
+  const int F = a.force_rows;
+  for (int i = tid; i < (kCls + 1) * (kMaxExperts + 1); i += kThreads) (&s_pc[0][0])[i] = 0;
+  __syncthreads();
   if (tid <= E) {
     const int n = s_cnt[tid];
-    nmb = (n + kBM - 1) / kBM;
-    if (nmb) {
-      q = n / nmb;
-      rem = n % nmb;
-      // rem blocks of q+1 rows, nmb-rem blocks of q rows
-      if (rem) atomicAdd(&s_cls[(q + 1 + 31) / 32], rem);
-      if (nmb - rem) atomicAdd(&s_cls[(q + 31) / 32], nmb - rem);
+    if (F) {
+      nmb = (n + F - 1) / F;
+      if (nmb) {
+        q = F;
+        rem = n - (nmb - 1) * F;  // rows of the last block (1..F)
+        if (nmb > 1) s_pc[F / 32][tid] += nmb - 1;
+        s_pc[(rem + 31) / 32][tid] += 1;
+      }
+    } else {
+      nmb = (n + kBM - 1) / kBM;
+      if (nmb) {
+        q = n / nmb;
+        rem = n % nmb;
+        // rem blocks of q+1 rows, nmb-rem blocks of q rows
+        if (rem) s_pc[(q + 1 + 31) / 32][tid] += rem;
+        if (nmb - rem) s_pc[(q + 31) / 32][tid] += nmb - rem;
+      }
     }
+  }
+  __syncthreads();
+  // exclusive scan of each class's per-expert counts (wave c-1 takes class c); the total
+  // goes to s_cls[c]
+  if (tid < kCls * kWave) {
+    const int c = tid / kWave + 1, lane = tid % kWave;
+    const int per = (E + 1 + kWave - 1) / kWave;
+    const int lo = lane * per, hi = min(lo + per, E + 1);
+    int sum = 0;
+    for (int e = lo; e < hi; ++e) sum += s_pc[c][e];
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    int run = incl - sum;
+    for (int e = lo; e < hi; ++e) {
+      const int v = s_pc[c][e];
+      s_pc[c][e] = run;
+      run += v;
+    }
+    if (lane == kWave - 1) s_cls[c] = incl;
   }
   __syncthreads();
   if (tid == 0) {
     int run = 0;
-    for (int c = kBM / 32; c >= 1; --c) {
+    for (int c = kCls; c >= 1; --c) {
       s_clsoff[c] = run;
       run += s_cls[c];
     }
@@ -219,10 +260,15 @@ __global__ __launch_bounds__(kThreads) void k_group(GroupArgs a) {
   __syncthreads();
   if (tid <= E && nmb) {
     int row = s_off[tid];
+    int seen[kCls + 1] = {};  // this expert's blocks placed so far, per class
     for (int i = 0; i < nmb; ++i) {
-      const int rows = q + (i < rem ? 1 : 0);
+      const int rows = F ? (i + 1 < nmb ? F : rem) : q + (i < rem ? 1 : 0);
       const int cls = (rows + 31) / 32;
-      const int slot = s_clsoff[cls] + atomicAdd(&s_clspos[cls], 1);
+      int pos = 0;
+#pragma unroll
+      for (int c = 1; c <= kCls; ++c)
+        if (c == cls) pos = seen[c]++;
+      const int slot = s_clsoff[cls] + s_pc[cls][tid] + pos;
       a.mblocks[slot] = make_int4(tid, row, rows, cls);
       row += rows;
     }

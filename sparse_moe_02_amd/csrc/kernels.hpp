@@ -56,6 +56,7 @@ struct RouteArgs {
   Ctrl *ctrl;
   int32_t *dbg_ids;       // optional [T][k] (chunk-offset)
   float *dbg_gates;
+  bool no_fallback;       // keep uncertified fp32 selections (MOE_F_NO_FALLBACK)
 };
 
 struct GroupArgs {
@@ -71,6 +72,7 @@ struct GroupArgs {
   int4 *mblocks;          // {expert, row0, rows, mt}
   Ctrl *ctrl;
   int32_t *dbg_counts, *dbg_offsets, *dbg_row_token, *dbg_n_refined;
+  int force_rows;         // 0: M-block heights from the expert's row count; else fixed height
 };
 
 struct GemmArgs {

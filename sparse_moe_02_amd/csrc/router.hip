@@ -294,7 +294,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
       s_min_in[m] = mn;
       s_max_out[m] = mx;
     }
-    if (m < nt && cert) {
+    if (m < nt && (cert || (a.no_fallback && a.wr16))) {
       // gates: softmax of the chosen logits (lane q < k holds choice q; choice 0 is the
       // largest); ids in ascending order
       const float top = __shfl(my_l, lane & ~15);

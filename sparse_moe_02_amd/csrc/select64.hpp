@@ -125,8 +125,6 @@ struct Sel64 {
   int cand[kMaxExperts];     // candidate -> expert
   int state[kMaxExperts];
   int chosen[kMaxExperts];   // per expert: 1 if selected
-  int list[kMaxTopK];
-  float ex[kMaxTopK];
   int n, nin;
 };
 
@@ -160,53 +158,6 @@ __device__ void resolve64(Sel64 &S, int r, const uint16_t *x, const uint16_t *w1
         rank += (S.v[j] > S.v[c]) || (S.v[j] == S.v[c] && S.cand[j] < e);
     if (rank < rr) S.chosen[e] = 1;
     S.gl[e] = S.v[c];
-  }
-  __syncthreads();
-}
-
-// Compact the chosen experts into ascending S.list and write ids/gates (softmax of S.gl
-// over them; AGENT: with device-coherent stores).  Experts are gathered unordered, then
-// each of the k entries finds its rank among the k.
-template <bool AGENT = false>
-__device__ void emit_selection(Sel64 &S, int E, int k, int32_t *ids, float *gates, int32_t *dbg_ids,
-                               float *dbg_gates, int tid, int nthr) {
-  if (tid == 0) S.nin = 0;
-  if (tid < kMaxTopK) S.list[tid] = 0;
-  __syncthreads();
-  for (int e = tid; e < E; e += nthr)
-    if (S.chosen[e]) {
-      const int at = atomicAdd(&S.nin, 1);
-      if (at < kMaxTopK) S.cand[at] = e;
-    }
-  __syncthreads();
-  const int n = min(S.nin, k);
-  if (tid < n) {
-    const int e = S.cand[tid];
-    int pos = 0;
-    for (int j = 0; j < n; ++j) pos += S.cand[j] < e;
-    S.list[pos] = e;
-  }
-  __syncthreads();
-  if (tid < k) {  // each chosen expert's exponential once
-    double mx = -INFINITY;
-    for (int j = 0; j < k; ++j) mx = fmax(mx, S.gl[S.list[j]]);
-    S.ex[tid] = __expf((float)(S.gl[S.list[tid]] - mx));
-  }
-  __syncthreads();
-  if (tid < k) {
-    float den = 0.f;
-    for (int j = 0; j < k; ++j) den += S.ex[j];
-    const int e = S.list[tid];
-    const float g = S.ex[tid] / den;
-    if (AGENT) {  // read by other workgroups of the same launch
-      st_agent(&ids[tid], e);
-      st_agent(&gates[tid], g);
-    } else {
-      ids[tid] = e;
-      gates[tid] = g;
-    }
-    if (dbg_ids) dbg_ids[tid] = e;
-    if (dbg_gates) dbg_gates[tid] = g;
   }
   __syncthreads();
 }

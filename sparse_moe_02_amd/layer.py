@@ -33,7 +33,8 @@ class MoeLayer:
     tile layouts (``moe_pack_codes``, ``moe_pack_qparams``).
     """
 
-    def __init__(self, weights, top_k: int, max_chunk_tokens: int = 4096, device: str = "cuda:0"):
+    def __init__(self, weights, top_k: int, max_chunk_tokens: int = 4096, device: str = "cuda:0",
+                 flags: int = 0):
         self.device = torch.device(device)
         E1, I, H8 = weights.gate_q.shape
         self.E, self.I, self.H, self.k = E1 - 1, I, H8 * 8, top_k
@@ -50,7 +51,7 @@ class MoeLayer:
         fp32_router = weights.router_w.dtype == np.float32
         self.cfg = B.moe_config(hidden=self.H, inter=self.I, n_experts=self.E, top_k=top_k, group_size=64,
                                 router_dtype=B.MOE_FP32 if fp32_router else B.MOE_BF16,
-                                qparam_dtype=B.MOE_FP16, max_chunk_tokens=max_chunk_tokens, flags=0)
+                                qparam_dtype=B.MOE_FP16, max_chunk_tokens=max_chunk_tokens, flags=flags)
         self.w = B.moe_weights()
         self.w.router_w = self.t["router_w"].data_ptr()
         self.w.router_bias = self.t["router_b"].data_ptr() if self.t["router_b"] is not None else None
@@ -91,11 +92,17 @@ class MoeLayer:
 
     # ------------------------------------------------------------------ forwards
 
-    def _debug(self, T: int, decode: bool, events):
+    def _debug(self, T: int, decode: bool, events, outputs: bool = True, logits: bool = False):
+        """The debug struct (and the tensors it points at).  outputs=False: events only."""
         nch = 1 if decode else (T + self.chunk - 1) // self.chunk
-        d = {"topk_ids": torch.empty((T, self.k), dtype=torch.int32, device=self.device),
-             "gates": torch.empty((T, self.k), dtype=torch.float32, device=self.device)}
-        if not decode:
+        d = {}
+        if outputs:
+            d["topk_ids"] = torch.empty((T, self.k), dtype=torch.int32, device=self.device)
+            d["gates"] = torch.empty((T, self.k), dtype=torch.float32, device=self.device)
+        if outputs and logits and not decode:
+            d["logits32"] = torch.empty((T, self.E), dtype=torch.float32, device=self.device)
+            d["radii32"] = torch.empty((T, self.E), dtype=torch.float32, device=self.device)
+        if outputs and not decode:
             d["counts"] = torch.empty((nch, self.E + 1), dtype=torch.int32, device=self.device)
             d["offsets"] = torch.empty((nch, self.E + 2), dtype=torch.int32, device=self.device)
             d["row_token"] = torch.full((nch * self.chunk * (self.k + 1),), -1, dtype=torch.int32,
@@ -108,13 +115,15 @@ class MoeLayer:
             s.events = events.ptr
         return s, d
 
-    def prefill(self, x: torch.Tensor, out: torch.Tensor | None = None, debug: bool = False, events=None):
-        """x: bf16 [T][H] on the device.  Returns out (and the debug tensors)."""
+    def prefill(self, x: torch.Tensor, out: torch.Tensor | None = None, debug: bool = False, events=None,
+                logits: bool = False):
+        """x: bf16 [T][H] on the device.  Returns out (and the debug tensors when debug).
+        events alone (debug False) records the stage events and writes no debug output."""
         assert x.dtype == torch.bfloat16 and x.is_contiguous() and x.shape[1] == self.H
         T = x.shape[0]
         if out is None:
             out = torch.empty_like(x)
-        dbg, d = self._debug(T, False, events) if (debug or events is not None) else (None, None)
+        dbg, d = self._debug(T, False, events, debug, logits) if (debug or events is not None) else (None, None)
         B.moe_forward_prefill(self.plan, x.data_ptr(), T, out.data_ptr(), self.ws.data_ptr(), self.ws_bytes,
                               self.stream(), dbg)
         return (out, d) if debug else out
@@ -124,17 +133,15 @@ class MoeLayer:
         assert x.dtype == torch.bfloat16 and x.is_contiguous() and x.numel() == self.H
         if out is None:
             out = torch.empty_like(x)
-        dbg, d = self._debug(1, True, events) if (debug or events is not None) else (None, None)
+        dbg, d = self._debug(1, True, events, debug) if (debug or events is not None) else (None, None)
         B.moe_forward_decode(self.plan, x.data_ptr(), out.data_ptr(), self.ws.data_ptr(), self.ws_bytes,
                              self.stream(), dbg)
         return (out, d) if debug else out
 
     def decode_error(self) -> int:
-        """The decode kernel's wait-failure word (0 = every call so far completed its
-        internal hand-offs); synchronises the device."""
-        torch.cuda.synchronize()
-        o = B.CTRL_DECODE_ERR_OFFSET
-        return int(self.ws[o:o + 4].cpu().view(torch.int32).item())
+        """moe_workspace_check: 0 (MOE_OK) if every decode call so far completed its internal
+        hand-offs, else MOE_ERR_WAIT; waits for the stream."""
+        return B.moe_workspace_check(self.plan, self.ws.data_ptr(), self.ws_bytes, self.stream())
 
 
 def bf16_tensor(bits: np.ndarray, device) -> torch.Tensor:

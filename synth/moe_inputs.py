@@ -71,6 +71,9 @@ CONFIGS = {
     # latter over 10 K-steps, so the pieces are uneven)
     12: MoeShape("split-2", T=1024, H=768, E=40, k=6, I=384, router_fp32=False, zipf_bias=False, chunk=1024),
     13: MoeShape("split-3", T=1024, H=1280, E=32, k=4, I=512, router_fp32=False, zipf_bias=False, chunk=1024),
+    # a bf16 router whose expert count is not a multiple of 4 (scalar logit reads in the
+    # selection, a partial 64-expert logits tile), over ragged 24-token chunks
+    14: MoeShape("e42-bf16", T=50, H=512, E=42, k=6, I=256, router_fp32=False, zipf_bias=False, chunk=24),
 }
 
 

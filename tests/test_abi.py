@@ -68,12 +68,40 @@ def _weights(B, base=0x10000):
     (dict(group_size=32), 2), (dict(hidden=2000), 2), (dict(hidden=128), 2), (dict(inter=320), 2),
     (dict(inter=64), 2), (dict(n_experts=257), 2), (dict(n_experts=0), 2), (dict(top_k=0), 2),
     (dict(top_k=17, n_experts=32), 2), (dict(top_k=9, n_experts=8), 2), (dict(max_chunk_tokens=0), 2),
-    (dict(flags=4), 2), (dict(router_dtype=1), 3), (dict(qparam_dtype=0), 3),
+    (dict(flags=6), 2), (dict(flags=7), 2), (dict(flags=1 << 7), 2), (dict(flags=1 << 31), 2),
+    (dict(router_dtype=1), 3), (dict(qparam_dtype=0), 3),
 ])
 def test_plan_rejects_bad_config(B, kw, status):
     with pytest.raises(B.MoeError) as ei:
         B.moe_plan_create(_cfg(B, **kw), _weights(B))
     assert ei.value.status == status
+
+
+@pytest.mark.parametrize("kw", [
+    dict(flags=1), dict(flags=5), dict(flags=16), dict(flags=64), dict(flags=5 | 16 | 64),
+    # the largest accepted chunk with the largest intermediate size and top-k: a down GEMM
+    # M-block's h rows lie up to 65536 x 17 x 4096 x 2 bytes (> 2^32) into the workspace
+    dict(max_chunk_tokens=65536, top_k=16, inter=4096, n_experts=32),
+    dict(max_chunk_tokens=65536, hidden=16384),
+])
+def test_plan_accepts_valid_flags_and_sizes(B, kw):
+    # host validation passes; on a machine without a gfx950 the device query then fails
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_plan_create(_cfg(B, **kw), _weights(B))
+    assert ei.value.status == 7
+
+
+def test_flag_values_match_header(B):
+    hdr = open(os.path.join(ROOT, "include", "moe.h")).read()
+    for name in ("MOE_F_NO_FALLBACK", "MOE_F_SEPARATE_DEQUANT", "MOE_F_HOST_ROUTING"):
+        m = re.search(r"#define " + name + r" \(1u << (\d+)\)", hdr)
+        assert m and getattr(B, name) == 1 << int(m.group(1)), name
+    assert re.search(r"#define MOE_F_FORCE_BM\(rows\) \(\(uint32_t\)\(\(rows\) / 32\) & 0xfu\)", hdr)
+    assert [B.MOE_F_FORCE_BM(r) for r in (32, 64, 96, 128, 160)] == [1, 2, 3, 4, 5]
+    assert re.search(r"MOE_ERR_WAIT = 11", hdr) and B.MOE_ERR_WAIT == 11
 
 
 def test_plan_rejects_null_and_misaligned_weights(B):
@@ -108,6 +136,7 @@ def test_forwards_reject_null_plan(B):
     assert L.moe_forward_prefill(None, 0x1000, 1, 0x2000, 0x3000, 1 << 20, None, None) == 1
     assert L.moe_forward_decode(None, 0x1000, 0x2000, 0x3000, 1 << 20, None, None) == 1
     assert L.moe_workspace_init(None, 0x3000, 1 << 20, None) == 1
+    assert L.moe_workspace_check(None, 0x3000, 1 << 20, None) == 1
 
 
 def test_pack_qparams_host_validation(B):
