@@ -214,7 +214,9 @@ moe_status moe_workspace_init(moe_plan_t plan, void *workspace, size_t workspace
 /* Read the workspace's decode error word (enqueued on stream, then the host waits for
  * stream): MOE_OK if every decode call on this workspace since moe_workspace_init
  * completed its internal hand-offs, MOE_ERR_WAIT if a wait ran out of polls (the word
- * stays set until moe_workspace_init), MOE_ERR_HIP if the copy failed.  Blocks the host. */
+ * stays set until moe_workspace_init), MOE_ERR_HIP if the copy failed.  Blocks the host.
+ * workspace NULL: the array of moe_forward_decode_static on the current device (the
+ * word stays set for the life of the process). */
 moe_status moe_workspace_check(moe_plan_t plan, const void *workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
@@ -239,6 +241,21 @@ moe_status moe_forward_prefill(moe_plan_t plan, const void *x, int64_t T, void *
 moe_status moe_forward_decode(moe_plan_t plan, const void *x, void *out, void *workspace,
                               size_t workspace_bytes, hipStream_t stream,
                               const moe_debug_out *dbg);
+
+/* Decode without a caller workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same computation and result as moe_forward_decode, with the control block and
+ * hand-off records in a device array inside the library (1 MiB per device, held until
+ * the process ends) instead of a workspace.  Allocates nothing: no hipMalloc, no
+ * hipFree, no allocating library call.  The first call on a device enqueues a kernel on
+ * `stream` that clears the array.  MOE_ERR_WORKSPACE if the plan's decode records do not
+ * fit the array ((256 + E*24, rounded up to 256) + (k+1)*I*8 bytes > 1 MiB; never for
+ * sizes moe_plan_create accepts today).  Every call on a GPU shares that GPU's array:
+ * calls that may overlap on one GPU (different streams, different threads) race and
+ * must be ordered by the caller.  moe_workspace_check(plan, NULL, 0, stream) reads this
+ * array's error word.  Other errors as moe_forward_decode. */
+moe_status moe_forward_decode_static(moe_plan_t plan, const void *x, void *out, hipStream_t stream,
+                                     const moe_debug_out *dbg);
 
 /* Weight preparation: rewrite an fp16 array of one value per (row, group of 64)
  * from row-major src [rows][k/64] into the 16-row tile layout the quantised

@@ -9,6 +9,7 @@
 #include <cstddef>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "../../include/moe.h"
@@ -109,6 +110,83 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb) {
 hipError_t rec(const moe_debug_out *dbg, int i, hipStream_t s) {
   if (dbg && dbg->events) return hipEventRecord(dbg->events[i], s);
   return hipSuccess;
+}
+
+// One decode launch over the given control block and hand-off records.
+moe_status decode_launch(const moe_plan_s *p, const void *x, void *out, Ctrl *ctrl, uint64_t *lrec, uint64_t *hrec,
+                         hipStream_t stream, const moe_debug_out *dbg) {
+  const moe_config &c = p->cfg;
+  DecodeArgs a{};
+  a.x = static_cast<const uint16_t *>(x);
+  const bool fp32_router = c.router_dtype == MOE_FP32;
+  a.wr16 = fp32_router ? nullptr : static_cast<const uint16_t *>(p->w.router_w);
+  a.wr32 = fp32_router ? static_cast<const float *>(p->w.router_w) : nullptr;
+  a.bias = p->w.router_bias;
+  a.gate = qm(p->w.gate);
+  a.up = qm(p->w.up);
+  a.down = qm(p->w.down);
+  a.s_gate = qm(p->w.s_gate);
+  a.s_up = qm(p->w.s_up);
+  a.s_down = qm(p->w.s_down);
+  a.H = c.hidden;
+  a.E = c.n_experts;
+  a.k = c.top_k;
+  a.I = c.inter;
+  a.lrec = lrec;
+  a.hrec = hrec;
+  a.ctrl = ctrl;
+  a.out = static_cast<uint16_t *>(out);
+  if (dbg) {
+    a.dbg_ids = dbg->topk_ids;
+    a.dbg_gates = dbg->gates;
+  }
+  if (rec(dbg, MOE_DSTAGE_LAYER, stream) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_decode(a, p->dec_grid, stream) != hipSuccess) return MOE_ERR_HIP;
+  if (rec(dbg, MOE_DECODE_STAGES, stream) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+// ------------------------------------------------------------ static decode scratch
+// moe_forward_decode_static keeps the decode's control block and hand-off records in
+// this file-scope device array instead of a caller workspace: [0, 256) the control
+// block, [kStaticLrec, ...) the logit records (E x 3 words), then the h records
+// ((k+1) x I words).  Each device holds its own copy; host code uses only the address
+// hipGetSymbolAddress returns for the current device (the array's name is a host-side
+// stand-in).  The first call on a device clears the control block and the records with
+// a kernel on the caller's stream; later calls rely on the decode protocol itself (the
+// last workgroup of a call re-arms the completion count and publishes the call's tag).
+constexpr size_t kStaticLrec = 256;
+size_t static_hrec_offset(const moe_config &c) { return align256(kStaticLrec + (size_t)c.n_experts * 3 * 8); }
+size_t static_decode_bytes(const moe_config &c) {
+  return static_hrec_offset(c) + (size_t)(c.top_k + 1) * c.inter * 8;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_static_mu;
+char *g_static_ptr[kMaxDevices];
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+
+// Address of this device's scratch (set up on the first call on the device).
+moe_status static_scratch(hipStream_t stream, char **base) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (!g_static_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MOE_ERR_HIP;
+    char *b = static_cast<char *>(ptr);
+    if (launch_ctrl_init(reinterpret_cast<Ctrl *>(b), b + kStaticLrec, kStaticScratchBytes - kStaticLrec, stream) !=
+        hipSuccess)
+      return MOE_ERR_HIP;
+    g_static_ptr[dev] = b;
+  }
+  *base = g_static_ptr[dev];
+  return MOE_OK;
 }
 
 }  // namespace
@@ -217,11 +295,19 @@ moe_status moe_workspace_init(moe_plan_t p, void *ws, size_t bytes, hipStream_t 
 
 moe_status moe_workspace_check(moe_plan_t p, const void *ws, size_t bytes, hipStream_t stream) {
   if (!p) return MOE_ERR_NULL;
-  const moe_status st = check_ws(p, const_cast<void *>(ws), bytes);
-  if (st != MOE_OK) return st;
+  const char *ctrl = nullptr;
+  if (ws) {
+    const moe_status st = check_ws(p, const_cast<void *>(ws), bytes);
+    if (st != MOE_OK) return st;
+    ctrl = static_cast<const char *>(ws) + p->off_ctrl;
+  } else {  // the static scratch of moe_forward_decode_static on the current device
+    char *b = nullptr;
+    const moe_status st = static_scratch(stream, &b);
+    if (st != MOE_OK) return st;
+    ctrl = b;
+  }
   int32_t word = 0;
-  if (hipMemcpyAsync(&word, static_cast<const char *>(ws) + p->off_ctrl + offsetof(Ctrl, d_err), sizeof(word),
-                     hipMemcpyDeviceToHost, stream) != hipSuccess ||
+  if (hipMemcpyAsync(&word, ctrl + offsetof(Ctrl, d_err), sizeof(word), hipMemcpyDeviceToHost, stream) != hipSuccess ||
       hipStreamSynchronize(stream) != hipSuccess)
     return MOE_ERR_HIP;
   return word ? MOE_ERR_WAIT : MOE_OK;
@@ -369,34 +455,22 @@ moe_status moe_forward_decode(moe_plan_t p, const void *x, void *out, void *ws, 
   if (st != MOE_OK) return st;
   const moe_config &c = p->cfg;
   if (overlap(x, (size_t)c.hidden * 2, out, (size_t)c.hidden * 2)) return MOE_ERR_ALIAS;
-  DecodeArgs a{};
-  a.x = static_cast<const uint16_t *>(x);
-  const bool fp32_router = c.router_dtype == MOE_FP32;
-  a.wr16 = fp32_router ? nullptr : static_cast<const uint16_t *>(p->w.router_w);
-  a.wr32 = fp32_router ? static_cast<const float *>(p->w.router_w) : nullptr;
-  a.bias = p->w.router_bias;
-  a.gate = qm(p->w.gate);
-  a.up = qm(p->w.up);
-  a.down = qm(p->w.down);
-  a.s_gate = qm(p->w.s_gate);
-  a.s_up = qm(p->w.s_up);
-  a.s_down = qm(p->w.s_down);
-  a.H = c.hidden;
-  a.E = c.n_experts;
-  a.k = c.top_k;
-  a.I = c.inter;
-  a.lrec = at<uint64_t>(ws, p->off_lrec);
-  a.hrec = at<uint64_t>(ws, p->off_hrec);
-  a.ctrl = at<Ctrl>(ws, p->off_ctrl);
-  a.out = static_cast<uint16_t *>(out);
-  if (dbg) {
-    a.dbg_ids = dbg->topk_ids;
-    a.dbg_gates = dbg->gates;
-  }
-  if (rec(dbg, MOE_DSTAGE_LAYER, stream) != hipSuccess) return MOE_ERR_HIP;
-  if (launch_decode(a, p->dec_grid, stream) != hipSuccess) return MOE_ERR_HIP;
-  if (rec(dbg, MOE_DECODE_STAGES, stream) != hipSuccess) return MOE_ERR_HIP;
-  return MOE_OK;
+  return decode_launch(p, x, out, at<Ctrl>(ws, p->off_ctrl), at<uint64_t>(ws, p->off_lrec),
+                       at<uint64_t>(ws, p->off_hrec), stream, dbg);
+}
+
+moe_status moe_forward_decode_static(moe_plan_t p, const void *x, void *out, hipStream_t stream,
+                                     const moe_debug_out *dbg) {
+  if (!p || !x || !out) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(out)) return MOE_ERR_ALIGN;
+  const moe_config &c = p->cfg;
+  if (overlap(x, (size_t)c.hidden * 2, out, (size_t)c.hidden * 2)) return MOE_ERR_ALIAS;
+  if (static_decode_bytes(c) > kStaticScratchBytes) return MOE_ERR_WORKSPACE;
+  char *base = nullptr;
+  const moe_status st = static_scratch(stream, &base);
+  if (st != MOE_OK) return st;
+  return decode_launch(p, x, out, reinterpret_cast<Ctrl *>(base), reinterpret_cast<uint64_t *>(base + kStaticLrec),
+                       reinterpret_cast<uint64_t *>(base + static_hrec_offset(c)), stream, dbg);
 }
 
 }  // extern "C"

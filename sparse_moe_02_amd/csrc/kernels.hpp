@@ -23,6 +23,7 @@ struct QMat {
 constexpr int kMaxTailItems = 1024;  // split gate/up tail items per launch (<= workgroups / 2)
 constexpr int kMaxSplit = 4;         // pieces per split gate/up item
 constexpr int kPartSlots = 256;      // partial-sum slots provided at least (when y is smaller)
+constexpr size_t kStaticScratchBytes = size_t(1) << 20;  // moe_forward_decode_static's device array
 constexpr int kXcds = 8;           // MI355X: 8 accelerator complex dies, one L2 each
 
 // Control words at the start of the workspace.
