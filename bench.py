@@ -7,8 +7,9 @@ not from cache).  Inputs are resident in HBM before timing starts.
 
 Prints one JSON line: value = prefill tokens/s; also decode microseconds per layer, the
 per-stage times from HIP events recorded by the library on its stream, roofline figures
-for the dominant kernel of each form, and the oracle's CPU throughput on the same
-workload.
+for the dominant kernel of each form (against the datasheet peaks and against ceilings
+measured in the same run), the skewed-routing prefill, the 128K chunked prompt, and the
+oracle's CPU throughput on the same workload.
 """
 
 from __future__ import annotations
@@ -64,6 +65,108 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def pct(a, q):
+    return float(np.percentile(np.asarray(a), q))
+
+
+def mblock_rows(counts, force_rows=0, bm=160):
+    """The grouped GEMMs' M-blocks for one chunk's expert counts (the block-map rule of the
+    grouping kernel): balanced blocks of at most `bm` rows, or blocks of `force_rows` and one
+    remainder block.  Returns (rows of every block, MFMA tile rows of every block)."""
+    rows = []
+    for n in (int(c) for c in counts):
+        if n == 0:
+            continue
+        if force_rows:
+            nmb = -(-n // force_rows)
+            rows += [force_rows] * (nmb - 1) + [n - (nmb - 1) * force_rows]
+        else:
+            nmb = -(-n // bm)
+            q, rem = divmod(n, nmb)
+            rows += [q + 1] * rem + [q] * (nmb - rem)
+    rows = np.array(rows)
+    return rows, 32 * ((rows + 31) // 32)
+
+
+def time_events(fn, reps, stream, B):
+    """Run fn() reps times with HIP events between runs on `stream`; per-run ms."""
+    import torch
+
+    ev = B.HipEvents(reps + 1)
+    torch.cuda.synchronize()
+    ev.record(0, stream)
+    for i in range(reps):
+        fn()
+        ev.record(i + 1, stream)
+    torch.cuda.synchronize()
+    return np.array([ev.elapsed_ms(i, i + 1) for i in range(reps)])
+
+
+def ceilings(dev, stream, B, dec_layers, dec_x, H, I, k):
+    """Measured reference points: HBM read stream, MFMA loop, launch cost, and the decode
+    step's nine-expert weight stream with the experts already known (with and without the
+    dequant arithmetic)."""
+    import torch
+
+    from sparse_moe_02_amd import probes
+
+    out = {}
+    sink = torch.zeros(1 << 16, dtype=torch.float32, device=dev)
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    for grid in (2048, 4096):
+        probes.read_stream(buf.data_ptr(), nbytes, sink.data_ptr(), grid, stream)
+    ms = time_events(lambda: probes.read_stream(buf.data_ptr(), nbytes, sink.data_ptr(), 4096, stream), 5, stream, B)
+    out["hbm_read_GBs"] = round(nbytes / (float(np.min(ms)) * 1e-3) / 1e9, 1)
+    del buf
+    iters, grid = 4000, 1024  # 4 waves per workgroup: 4 waves per SIMD
+    flop = grid * 4 * iters * 4 * (2 * 32 * 32 * 16)
+    probes.mfma(100, sink.data_ptr(), grid, stream)
+    ms = time_events(lambda: probes.mfma(iters, sink.data_ptr(), grid, stream), 3, stream, B)
+    out["mfma_bf16_TFLOPs"] = round(flop / (float(np.min(ms)) * 1e-3) / 1e12, 1)
+
+    def graph_of(fn, n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        return g
+
+    n = 40
+    g1 = graph_of(lambda: probes.empty(1, 64, torch.cuda.current_stream().cuda_stream), n)
+    ms = time_events(g1.replay, 10, stream, B)
+    out["empty_kernel_graph_us"] = round(float(np.median(ms)) * 1e3 / n, 3)
+    g2 = graph_of(lambda: probes.empty(288, 256, torch.cuda.current_stream().cuda_stream), n)
+    ms = time_events(g2.replay, 10, stream, B)
+    out["empty_kernel_288x256_graph_us"] = round(float(np.median(ms)) * 1e3 / n, 3)
+    del g1, g2
+    if dec_layers:
+        # the experts each decode layer's token chose, from one debug call per layer
+        mats = []
+        for m, x in zip(dec_layers, dec_x):
+            _, d = m.decode(x, debug=True)
+            ids = d["topk_ids"].cpu().numpy()[0].tolist() + [m.E]
+            p = []
+            for e in ids:
+                for name in ("gate", "up", "down"):
+                    for part in ("_q", "_s", "_b"):
+                        p.append(m.t[name + part][e].data_ptr())
+            mats.append(p)
+        for arith in (True, False):
+            def sweep(arith=arith):
+                s = torch.cuda.current_stream().cuda_stream
+                for p, x in zip(mats, dec_x):
+                    probes.expert_stream(p, x.data_ptr(), H, I, arith, sink.data_ptr(), 1024, s)
+            g = graph_of(sweep, 1)
+            ms = time_events(g.replay, 10, stream, B)
+            key = "expert_stream_us" if arith else "expert_stream_no_arith_us"
+            out[key] = round(float(np.median(ms)) * 1e3 / len(mats), 3)
+            del g
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -72,6 +175,8 @@ def main():
     ap.add_argument("--decode-layers", type=int, default=40)
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replayed decode sweep")
     ap.add_argument("--no-long-prompt", action="store_true", help="skip the 131072-token chunked prefill")
+    ap.add_argument("--no-skewed", action="store_true", help="skip the skewed-routing prefill")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the measured ceilings")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -104,7 +209,7 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "copies": 5}), flush=True)
         return
-    sh2, sh1 = synth.shape_of(2), synth.shape_of(1)
+    sh2 = synth.shape_of(2)
     T, H, I, E, k = sh2.T, sh2.H, sh2.I, sh2.E, sh2.k
 
     log("bench: drawing the prefill layer")
@@ -128,6 +233,7 @@ def main():
     stream = torch.cuda.current_stream().cuda_stream
 
     def step(ev_pre=None, ev_dec=None):
+        # events only (no debug outputs): the timed prefill writes nothing but its output
         pre.prefill(xp, outp, events=ev_pre)
         for li in range(n_dec):
             dec_layers[li].decode(dec_x[li], dec_out[li], events=ev_dec[li] if ev_dec else None)
@@ -151,8 +257,9 @@ def main():
 
     step_ms = [marks.elapsed_ms(s, s + 1) for s in range(K)]
     pre_ms = np.array([e.elapsed_ms(0, B.MOE_PREFILL_STAGES) for e in ev_pre])
-    stage_ms = {name: float(np.mean([e.elapsed_ms(i, i + 1) for e in ev_pre]))
-                for i, name in enumerate(B.PREFILL_STAGE_NAMES)}
+    stage_all = {name: np.array([e.elapsed_ms(i, i + 1) for e in ev_pre])
+                 for i, name in enumerate(B.PREFILL_STAGE_NAMES)}
+    stage_ms = {name: float(np.median(v)) for name, v in stage_all.items()}
     prefill_ms = float(np.median(pre_ms))
     tok_s = T / (prefill_ms * 1e-3)
 
@@ -161,6 +268,7 @@ def main():
     down_flop = 2.0 * H * I * rows
     router_flop = 2.0 * T * E * H
     gu_ms = stage_ms["gateup"]
+    gu_tflops = gateup_flop / (gu_ms * 1e-3) / 1e12
     result = {
         "metric": METRIC,
         "value": round(tok_s, 1),
@@ -178,19 +286,27 @@ def main():
                    "tokens": T, "hidden": H, "experts": E, "top_k": k, "shared_experts": 1, "inter": I,
                    "weights": "int4 affine group-64, fp16 scale/bias", "decode_layers": n_dec},
         "prefill_us": round(prefill_ms * 1e3, 2),
+        "prefill_us_p10_p90": [round(pct(pre_ms, 10) * 1e3, 2), round(pct(pre_ms, 90) * 1e3, 2)],
         "prefill_stage_us": {n: round(v * 1e3, 2) for n, v in stage_ms.items()},
         "prefill_tflops": round((gateup_flop + down_flop + router_flop) / (prefill_ms * 1e-3) / 1e12, 1),
         "roofline": {"kernel": "gemm_gateup (grouped GEMM gate/up + SwiGLU)", "bound": "mfma",
-                     "achieved": round(gateup_flop / (gu_ms * 1e-3) / 1e12, 1), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(gateup_flop / (gu_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "achieved": round(gu_tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": profiled_traffic("k_gemm_gateup"), "traffic_unit": "bytes per launch",
-                     "algorithmic_flop_per_launch": gateup_flop},
+                     "algorithmic_flop_per_launch": gateup_flop,
+                     "us_p10_p90": [round(pct(stage_all["gateup"], 10) * 1e3, 2),
+                                    round(pct(stage_all["gateup"], 90) * 1e3, 2)]},
+        "down_roofline": {"kernel": "gemm_down (grouped GEMM down + gate)", "bound": "mfma",
+                          "achieved": round(down_flop / (stage_ms["down"] * 1e-3) / 1e12, 1),
+                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(down_flop / (stage_ms["down"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                          "algorithmic_flop_per_launch": down_flop},
         "step_ms_events": round(float(np.mean(step_ms)), 4),
     }
     if n_dec:
-        dec_stage = {name: float(np.mean([e.elapsed_ms(i, i + 1) for es in ev_dec for e in es]))
+        dec_stage = {name: float(np.median([e.elapsed_ms(i, i + 1) for es in ev_dec for e in es]))
                      for i, name in enumerate(B.DECODE_STAGE_NAMES)}
-        dec_layer_ms = float(np.mean([e.elapsed_ms(0, B.MOE_DECODE_STAGES) for es in ev_dec for e in es]))
+        dec_layer_ms = float(np.median([e.elapsed_ms(0, B.MOE_DECODE_STAGES) for es in ev_dec for e in es]))
         sweep_ms = np.array([m - p for m, p in zip(step_ms, pre_ms)])
         us_layer = float(np.median(sweep_ms)) * 1e3 / n_dec
         qmat_gu = I * H // 2 + 2 * 2 * I * (H // 64)
@@ -212,6 +328,47 @@ def main():
 
     if n_dec:
         result["decode_roofline"] = decode_roofline(dec_stage["layer"] * 1e3, "HIP events around each call")
+
+    if not args.no_skewed:
+        # the skewed workload: the same weights and tokens, router bias with Zipf(1.2)
+        # popularity (hot experts of 1000+ rows, about 150 empty)
+        log("bench: skewed-routing prefill")
+        Ls = synth.make_layer(3)
+        sk = MoeLayer(Ls, top_k=k, max_chunk_tokens=T, device=dev)
+        del Ls
+        _, dsk = sk.prefill(xp, outp, debug=True)
+        torch.cuda.synchronize()
+        cnt_s = dsk["counts"].cpu().numpy()[0]
+        _, dun = pre.prefill(xp, outp, debug=True)
+        torch.cuda.synchronize()
+        cnt_u = dun["counts"].cpu().numpy()[0]
+        ev_s = [B.HipEvents(B.MOE_PREFILL_STAGES + 1) for _ in range(K)]
+        for _ in range(args.warmup):
+            sk.prefill(xp, outp)
+        for s in range(K):
+            sk.prefill(xp, outp, events=ev_s[s])
+        torch.cuda.synchronize()
+        sk_ms = np.array([e.elapsed_ms(0, B.MOE_PREFILL_STAGES) for e in ev_s])
+        sk_stage = {name: round(float(np.median([e.elapsed_ms(i, i + 1) for e in ev_s])) * 1e3, 2)
+                    for i, name in enumerate(B.PREFILL_STAGE_NAMES)}
+
+        def row_eff(c):
+            r, tr = mblock_rows(c)
+            return round(float(r.sum() / tr.sum()), 4), int(r.size)
+
+        eff_s, nmb_s = row_eff(cnt_s)
+        eff_u, nmb_u = row_eff(cnt_u)
+        sk_us = float(np.median(sk_ms)) * 1e3
+        result["skewed_prefill"] = {
+            "tokens": T, "us": round(sk_us, 2),
+            "us_p10_p90": [round(pct(sk_ms, 10) * 1e3, 2), round(pct(sk_ms, 90) * 1e3, 2)],
+            "tokens_per_s": round(T / (sk_us * 1e-6), 1), "vs_uniform": round(prefill_ms * 1e3 / sk_us, 4),
+            "stage_us": sk_stage, "max_expert_rows": int(cnt_s[:E].max()), "empty_experts": int((cnt_s[:E] == 0).sum()),
+            "mfma_row_efficiency": eff_s, "mblocks": nmb_s,
+            "uniform_mfma_row_efficiency": eff_u, "uniform_mblocks": nmb_u,
+            "gateup_frac": round(gateup_flop / (sk_stage["gateup"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        sk.close()
+        del sk, dsk, dun
 
     if not args.no_long_prompt:
         # long prompt (131072 tokens, the same layer) through the chunk driver: one bounded
@@ -249,19 +406,58 @@ def main():
                 dec_layers[li].decode(dec_x[li], dec_out[li])
         for _ in range(max(args.warmup, 1)):
             graph.replay()
-        gmarks = B.HipEvents(K + 1)
-        torch.cuda.synchronize()
-        gmarks.record(0, stream)
-        for s in range(K):
-            graph.replay()
-            gmarks.record(s + 1, stream)
-        torch.cuda.synchronize()
-        g_ms = np.array([gmarks.elapsed_ms(s, s + 1) for s in range(K)])
+        g_ms = time_events(graph.replay, K, stream, B)
         result["decode_us_per_layer_graph"] = round(float(np.median(g_ms)) * 1e3 / n_dec, 3)
+        result["decode_us_per_layer_graph_p10_p90"] = [round(pct(g_ms, 10) * 1e3 / n_dec, 3),
+                                                       round(pct(g_ms, 90) * 1e3 / n_dec, 3)]
         # back-to-back launches: the per-launch time the kernel trace reports
         result["decode_roofline"] = decode_roofline(result["decode_us_per_layer_graph"],
                                                     f"graph replay of {n_dec} calls, HIP events on the stream")
         del graph
+
+    if n_dec and not args.no_graph:
+        # small-batch decode (T rows per call, e.g. a speculative decoder's verification
+        # batch): the same 40 weight sets, T rows each, captured once and replayed; the
+        # bytes a call must read are the union of the rows' experts (each read once)
+        qmat_gu = I * H // 2 + 2 * 2 * I * (H // 64)
+        qmat_dn = H * I // 2 + 2 * 2 * H * (I // 64)
+        expert_bytes = 2 * qmat_gu + qmat_dn
+        batch = {}
+        for Tb in (2, 4, 8):
+            xb = [torch.stack([dec_x[(li + j) % n_dec] for j in range(Tb)]) for li in range(n_dec)]
+            ob = [torch.empty_like(v) for v in xb]
+            union = []
+            for li in range(n_dec):
+                _, d = dec_layers[li].decode_batch(xb[li], ob[li], debug=True)
+                union.append(len(set(d["topk_ids"].cpu().numpy().ravel().tolist())) + 1)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for li in range(n_dec):
+                    dec_layers[li].decode_batch(xb[li], ob[li])
+            g.replay()
+            b_ms = time_events(g.replay, K, stream, B)
+            us = float(np.median(b_ms)) * 1e3 / n_dec
+            nbytes = float(np.mean(union)) * expert_bytes + E * H * 2 + 2 * Tb * H * 2
+            batch[str(Tb)] = {"us_per_call": round(us, 3), "us_per_row": round(us / Tb, 3),
+                              "active_experts": round(float(np.mean(union)), 2),
+                              "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+            del g, xb, ob
+        result["decode_batch"] = batch
+
+    if not args.no_ceilings:
+        log("bench: measured ceilings")
+        c = ceilings(dev, stream, B, dec_layers, dec_x, H, I, k)
+        result["ceilings"] = c
+        result["roofline"]["frac_vs_measured"] = round(gu_tflops / c["mfma_bf16_TFLOPs"], 4)
+        result["roofline"]["measured_peak"] = c["mfma_bf16_TFLOPs"]
+        if "decode_roofline" in result:
+            dr = result["decode_roofline"]
+            dr["frac_vs_measured"] = round(dr["achieved"] / c["hbm_read_GBs"], 4)
+            dr["measured_peak"] = c["hbm_read_GBs"]
+            if "expert_stream_us" in c:
+                # the single-phase stream of the same bytes, routing given: the floor this
+                # dependency chain (router -> selection -> gate/up -> down) sits above
+                dr["vs_expert_stream"] = round(c["expert_stream_us"] / result["decode_us_per_layer_graph"], 4)
 
     if not args.no_cpu_baseline:
         import oracle

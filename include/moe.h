@@ -242,15 +242,27 @@ moe_status moe_forward_decode(moe_plan_t plan, const void *x, void *out, void *w
                               size_t workspace_bytes, hipStream_t stream,
                               const moe_debug_out *dbg);
 
+/* Decode of a small batch: T rows (1 <= T <= 8, e.g. the draft tokens a speculative
+ * decoder verifies at once; section "Limits of further optimization": batches of 2-5
+ * rows are an inefficient shape for one-row kernels and read experts again).  x, out
+ * bf16 [T][H].  Same layer, routing and numerics per row as moe_forward_decode (which
+ * is this call with T = 1), in one launch that reads each active expert's weights once
+ * -- the union of the rows' experts -- and applies them to every row that chose the
+ * expert.  debug topk_ids / gates are [T][k].  MOE_ERR_TOKENS if T is out of range;
+ * other errors and the graph-capture property as moe_forward_decode. */
+moe_status moe_forward_decode_batch(moe_plan_t plan, const void *x, int32_t T, void *out, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream, const moe_debug_out *dbg);
+
 /* Decode without a caller workspace, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation):
  * the same computation and result as moe_forward_decode, with the control block and
- * hand-off records in a device array inside the library (1 MiB per device, held until
- * the process ends) instead of a workspace.  Allocates nothing: no hipMalloc, no
- * hipFree, no allocating library call.  The first call on a device enqueues a kernel on
- * `stream` that clears the array.  MOE_ERR_WORKSPACE if the plan's decode records do not
- * fit the array ((256 + E*24, rounded up to 256) + (k+1)*I*8 bytes > 1 MiB; never for
- * sizes moe_plan_create accepts today).  Every call on a GPU shares that GPU's array:
+ * the decode's records, intermediate values and counters in a device array inside the
+ * library (2 MiB per device, held until the process ends) instead of a workspace.
+ * Allocates nothing: no hipMalloc, no hipFree, no allocating library call.  The first
+ * call on a device enqueues a kernel on `stream` that clears the array.
+ * MOE_ERR_WORKSPACE if the plan's one-token decode records (24E + 8(k+1)I bytes, plus
+ * alignment and 2.3 KB of counters) do not fit the array (never for sizes
+ * moe_plan_create accepts today: at most 0.57 MB).  Every call on a GPU shares that GPU's array:
  * calls that may overlap on one GPU (different streams, different threads) race and
  * must be ordered by the caller.  moe_workspace_check(plan, NULL, 0, stream) reads this
  * array's error word.  Other errors as moe_forward_decode. */

@@ -16,6 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_mi355x.so")
 ROOT_INCLUDE = os.path.join(os.path.dirname(HERE), "include")
+PROBES_SRC = os.path.join(HERE, "probes", "probes.hip")
+PROBES_LIB = os.path.join(HERE, "probes", "libmoe_probes.so")
 
 ARCH = "gfx950"
 # packed-fp32 instructions are disabled: plain fp32 code only
@@ -46,16 +48,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 8) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, sources()))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     r = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(jobs: int = 8) -> str:
+    """The layer's library, then the benchmark's probe library (a separate .so)."""
+    os.makedirs(BUILD, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(_compile, sources() + [PROBES_SRC]))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], PROBES_LIB)
     return LIB
 
 

@@ -42,7 +42,8 @@ MOE_F_SEPARATE_DEQUANT = 1 << 5
 MOE_F_HOST_ROUTING = 1 << 6
 
 EXPORTED = ("moe_plan_create", "moe_plan_destroy", "moe_workspace_init", "moe_workspace_check",
-            "moe_forward_prefill", "moe_forward_decode", "moe_forward_decode_static", "moe_pack_qparams",
+            "moe_forward_prefill", "moe_forward_decode", "moe_forward_decode_batch", "moe_forward_decode_static",
+            "moe_pack_qparams",
             "moe_pack_codes", "moe_status_string", "moe_version")
 
 
@@ -102,6 +103,8 @@ def lib() -> ctypes.CDLL:
             L.moe_forward_prefill.argtypes = [P, P, I64, P, P, SZ, P, ctypes.POINTER(moe_debug_out)]
             L.moe_forward_decode.restype = ctypes.c_int
             L.moe_forward_decode.argtypes = [P, P, P, P, SZ, P, ctypes.POINTER(moe_debug_out)]
+            L.moe_forward_decode_batch.restype = ctypes.c_int
+            L.moe_forward_decode_batch.argtypes = [P, P, ctypes.c_int32, P, P, SZ, P, ctypes.POINTER(moe_debug_out)]
             L.moe_forward_decode_static.restype = ctypes.c_int
             L.moe_forward_decode_static.argtypes = [P, P, P, P, ctypes.POINTER(moe_debug_out)]
             L.moe_pack_qparams.restype = ctypes.c_int
@@ -171,6 +174,13 @@ def moe_forward_decode(plan, x_ptr: int, out_ptr: int, ws_ptr: int, ws_bytes: in
                        dbg: moe_debug_out | None = None) -> None:
     _check("moe_forward_decode", lib().moe_forward_decode(plan, x_ptr, out_ptr, ws_ptr, ws_bytes, stream,
                                                           ctypes.byref(dbg) if dbg is not None else None))
+
+
+def moe_forward_decode_batch(plan, x_ptr: int, T: int, out_ptr: int, ws_ptr: int, ws_bytes: int, stream: int,
+                             dbg: moe_debug_out | None = None) -> None:
+    _check("moe_forward_decode_batch", lib().moe_forward_decode_batch(plan, x_ptr, T, out_ptr, ws_ptr, ws_bytes,
+                                                                      stream,
+                                                                      ctypes.byref(dbg) if dbg is not None else None))
 
 
 def moe_forward_decode_static(plan, x_ptr: int, out_ptr: int, stream: int, dbg: moe_debug_out | None = None) -> None:

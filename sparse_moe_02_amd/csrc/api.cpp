@@ -21,11 +21,14 @@ struct moe_plan_s {
   moe_config cfg;
   moe_weights w;
   int n_cu;
-  int dec_grid;  // workgroups of the decode launch (all resident at once)
+  int dec_cap[4];  // batch-decode workgroups that fit at once, for up to 2, 2, 4, 8 tokens
+  int dec1_cap;    // the same for the one-token kernel
+  DecodeLayout dec;         // decode regions inside the workspace (up to 8 tokens), from off_dec
+  DecodeLayout dec_static;  // the same for one token, inside the static scratch (after 256 B)
   // workspace layout (byte offsets)
   size_t slot_u64;  // 8-byte words per partial-sum slot of a split gate/up piece
   size_t off_ctrl, off_tokmask, off_lg, off_rd, off_ids, off_gates, off_counts, off_offsets, off_row_token,
-      off_row_gate, off_slot_row, off_mblocks, off_h, off_y, off_lrec, off_hrec, off_tk, off_dend, total;
+      off_row_gate, off_slot_row, off_mblocks, off_h, off_y, off_dec, off_tk, off_dend, total;
 };
 
 namespace {
@@ -79,9 +82,12 @@ void layout(moe_plan_s &p) {
   const size_t nb_gu = (I + kGateUpCols - 1) / kGateUpCols;
   const size_t part = std::min<size_t>(kMaxSplit * nb_gu * max_mblocks, kPartSlots) * p.slot_u64 * 8;
   p.off_y = take(std::max(rows * H * 2, part));
-  p.off_lrec = take(E * 3 * 8);  // decode records: cleared by moe_workspace_init
-  p.off_hrec = take((k + 1) * I * 8);
-  p.off_tk = take(kMaxTailItems * 4);  // split-item tickets: zero between launches
+  // decode records and counters (cleared by moe_workspace_init), then the split-item
+  // tickets of the gate/up GEMM (zero between launches)
+  p.dec = decode_layout((int)H, (int)E, (int)k, (int)I, kMaxDecodeT);
+  p.dec_static = decode_layout((int)H, (int)E, (int)k, (int)I, 1);
+  p.off_dec = take(p.dec.total);
+  p.off_tk = take(kMaxTailItems * 4);
   p.off_dend = o;
   p.total = o;
 }
@@ -112,9 +118,10 @@ hipError_t rec(const moe_debug_out *dbg, int i, hipStream_t s) {
   return hipSuccess;
 }
 
-// One decode launch over the given control block and hand-off records.
-moe_status decode_launch(const moe_plan_s *p, const void *x, void *out, Ctrl *ctrl, uint64_t *lrec, uint64_t *hrec,
-                         hipStream_t stream, const moe_debug_out *dbg) {
+// One decode launch of T tokens over the given control block and decode regions (L:
+// offsets from `base`).
+moe_status decode_launch(const moe_plan_s *p, const void *x, int T, void *out, Ctrl *ctrl, char *base,
+                         const DecodeLayout &L, hipStream_t stream, const moe_debug_out *dbg) {
   const moe_config &c = p->cfg;
   DecodeArgs a{};
   a.x = static_cast<const uint16_t *>(x);
@@ -132,34 +139,39 @@ moe_status decode_launch(const moe_plan_s *p, const void *x, void *out, Ctrl *ct
   a.E = c.n_experts;
   a.k = c.top_k;
   a.I = c.inter;
-  a.lrec = lrec;
-  a.hrec = hrec;
+  a.T = T;
+  a.lrec = reinterpret_cast<uint64_t *>(base + L.lrec);
+  a.srec = reinterpret_cast<uint64_t *>(base + L.srec);
+  a.hflag = reinterpret_cast<uint64_t *>(base + L.hflag);
+  a.hval = reinterpret_cast<float *>(base + L.hval);
+  a.hrec1 = reinterpret_cast<uint64_t *>(base + L.hrec1);
+  a.part = reinterpret_cast<float *>(base + L.part);
+  a.rbctr = reinterpret_cast<int *>(base + L.rbctr);
+  a.endctr = reinterpret_cast<int *>(base + L.endctr);
   a.ctrl = ctrl;
   a.out = static_cast<uint16_t *>(out);
   if (dbg) {
     a.dbg_ids = dbg->topk_ids;
     a.dbg_gates = dbg->gates;
   }
+  const int cap = p->dec_cap[T <= 1 ? 0 : T <= 2 ? 1 : T <= 4 ? 2 : 3];
   if (rec(dbg, MOE_DSTAGE_LAYER, stream) != hipSuccess) return MOE_ERR_HIP;
-  if (launch_decode(a, p->dec_grid, stream) != hipSuccess) return MOE_ERR_HIP;
+  const hipError_t e = T == 1 ? launch_decode1(a, decode1_grid(a, p->dec1_cap), stream)
+                              : launch_decode(a, decode_grid(a, cap), stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
   if (rec(dbg, MOE_DECODE_STAGES, stream) != hipSuccess) return MOE_ERR_HIP;
   return MOE_OK;
 }
 
 // ------------------------------------------------------------ static decode scratch
-// moe_forward_decode_static keeps the decode's control block and hand-off records in
-// this file-scope device array instead of a caller workspace: [0, 256) the control
-// block, [kStaticLrec, ...) the logit records (E x 3 words), then the h records
-// ((k+1) x I words).  Each device holds its own copy; host code uses only the address
-// hipGetSymbolAddress returns for the current device (the array's name is a host-side
-// stand-in).  The first call on a device clears the control block and the records with
-// a kernel on the caller's stream; later calls rely on the decode protocol itself (the
-// last workgroup of a call re-arms the completion count and publishes the call's tag).
-constexpr size_t kStaticLrec = 256;
-size_t static_hrec_offset(const moe_config &c) { return align256(kStaticLrec + (size_t)c.n_experts * 3 * 8); }
-size_t static_decode_bytes(const moe_config &c) {
-  return static_hrec_offset(c) + (size_t)(c.top_k + 1) * c.inter * 8;
-}
+// moe_forward_decode_static keeps the decode's control block and its records, h values,
+// partial outputs and counters in this file-scope device array instead of a caller
+// workspace: [0, 256) the control block, then the one-token decode regions.  Each device
+// holds its own copy; host code uses only the address hipGetSymbolAddress returns for the
+// current device (the array's name is a host-side stand-in).  The first call on a device
+// clears the array with a kernel on the caller's stream; later calls rely on the decode
+// protocol itself (tags per call; the last arriver of every counter resets it).
+constexpr size_t kStaticDec = 256;
 
 constexpr int kMaxDevices = 64;
 std::mutex g_static_mu;
@@ -180,7 +192,7 @@ moe_status static_scratch(hipStream_t stream, char **base) {
     void *ptr = nullptr;
     if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MOE_ERR_HIP;
     char *b = static_cast<char *>(ptr);
-    if (launch_ctrl_init(reinterpret_cast<Ctrl *>(b), b + kStaticLrec, kStaticScratchBytes - kStaticLrec, stream) !=
+    if (launch_ctrl_init(reinterpret_cast<Ctrl *>(b), b + kStaticDec, kStaticScratchBytes - kStaticDec, stream) !=
         hipSuccess)
       return MOE_ERR_HIP;
     g_static_ptr[dev] = b;
@@ -267,14 +279,8 @@ moe_status moe_plan_create(const moe_config *cfg, const moe_weights *w, moe_plan
   p->cfg = c;
   p->w = *w;
   p->n_cu = prop.multiProcessorCount;
-  {
-    DecodeArgs da{};
-    da.H = c.hidden;
-    da.E = c.n_experts;
-    da.k = c.top_k;
-    da.I = c.inter;
-    p->dec_grid = decode_grid(da, p->n_cu);
-  }
+  for (int v = 0; v < 4; ++v) p->dec_cap[v] = decode_capacity(1 << v, p->n_cu);
+  p->dec1_cap = decode1_capacity(p->n_cu);
   layout(*p);
   if (workspace_bytes) *workspace_bytes = p->total;
   *plan = p;
@@ -287,7 +293,7 @@ moe_status moe_workspace_init(moe_plan_t p, void *ws, size_t bytes, hipStream_t 
   if (!p) return MOE_ERR_NULL;
   const moe_status st = check_ws(p, ws, bytes);
   if (st != MOE_OK) return st;
-  return launch_ctrl_init(at<Ctrl>(ws, p->off_ctrl), at<char>(ws, p->off_lrec), p->off_dend - p->off_lrec, stream) ==
+  return launch_ctrl_init(at<Ctrl>(ws, p->off_ctrl), at<char>(ws, p->off_dec), p->off_dend - p->off_dec, stream) ==
                  hipSuccess
              ? MOE_OK
              : MOE_ERR_HIP;
@@ -422,7 +428,7 @@ moe_status moe_forward_prefill(moe_plan_t p, const void *x, int64_t T, void *out
     // the partial sums of split gate/up items live in y, which only the down GEMM writes
     g1.tail_queue = &ctrl->q_tail;
     g1.part = at<uint64_t>(ws, p->off_y);
-    g1.max_pieces = (int)std::min<size_t>((p->off_lrec - p->off_y) / (p->slot_u64 * 8), 1 << 20);
+    g1.max_pieces = (int)std::min<size_t>((p->off_dec - p->off_y) / (p->slot_u64 * 8), 1 << 20);
     g1.slot_u64 = (int)p->slot_u64;
     g1.tickets = at<int>(ws, p->off_tk);
     if (rec(d, MOE_STAGE_GATEUP, stream) != hipSuccess) return MOE_ERR_HIP;
@@ -449,14 +455,20 @@ moe_status moe_forward_prefill(moe_plan_t p, const void *x, int64_t T, void *out
 
 moe_status moe_forward_decode(moe_plan_t p, const void *x, void *out, void *ws, size_t bytes, hipStream_t stream,
                               const moe_debug_out *dbg) {
+  return moe_forward_decode_batch(p, x, 1, out, ws, bytes, stream, dbg);
+}
+
+moe_status moe_forward_decode_batch(moe_plan_t p, const void *x, int32_t T, void *out, void *ws, size_t bytes,
+                                    hipStream_t stream, const moe_debug_out *dbg) {
   if (!p || !x || !out) return MOE_ERR_NULL;
+  if (T < 1 || T > kMaxDecodeT) return MOE_ERR_TOKENS;
   if (!aligned16(x) || !aligned16(out)) return MOE_ERR_ALIGN;
   moe_status st = check_ws(p, ws, bytes);
   if (st != MOE_OK) return st;
   const moe_config &c = p->cfg;
-  if (overlap(x, (size_t)c.hidden * 2, out, (size_t)c.hidden * 2)) return MOE_ERR_ALIAS;
-  return decode_launch(p, x, out, at<Ctrl>(ws, p->off_ctrl), at<uint64_t>(ws, p->off_lrec),
-                       at<uint64_t>(ws, p->off_hrec), stream, dbg);
+  const size_t n = (size_t)T * c.hidden * 2;
+  if (overlap(x, n, out, n)) return MOE_ERR_ALIAS;
+  return decode_launch(p, x, T, out, at<Ctrl>(ws, p->off_ctrl), at<char>(ws, p->off_dec), p->dec, stream, dbg);
 }
 
 moe_status moe_forward_decode_static(moe_plan_t p, const void *x, void *out, hipStream_t stream,
@@ -465,12 +477,11 @@ moe_status moe_forward_decode_static(moe_plan_t p, const void *x, void *out, hip
   if (!aligned16(x) || !aligned16(out)) return MOE_ERR_ALIGN;
   const moe_config &c = p->cfg;
   if (overlap(x, (size_t)c.hidden * 2, out, (size_t)c.hidden * 2)) return MOE_ERR_ALIAS;
-  if (static_decode_bytes(c) > kStaticScratchBytes) return MOE_ERR_WORKSPACE;
+  if (kStaticDec + p->dec_static.total > kStaticScratchBytes) return MOE_ERR_WORKSPACE;
   char *base = nullptr;
   const moe_status st = static_scratch(stream, &base);
   if (st != MOE_OK) return st;
-  return decode_launch(p, x, out, reinterpret_cast<Ctrl *>(base), reinterpret_cast<uint64_t *>(base + kStaticLrec),
-                       reinterpret_cast<uint64_t *>(base + static_hrec_offset(c)), stream, dbg);
+  return decode_launch(p, x, 1, out, reinterpret_cast<Ctrl *>(base), base + kStaticDec, p->dec_static, stream, dbg);
 }
 
 }  // extern "C"

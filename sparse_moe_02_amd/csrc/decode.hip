@@ -1,46 +1,61 @@
-// Decode form (one token) in a single launch: router logits, top-k selection, the
-// gate/up GEMVs with SwiGLU and the down GEMVs with the gate-weighted combine.
+// Decode form for a batch of T = 2..8 tokens in a single launch: router logits, top-k
+// selection, the gate/up GEMVs with SwiGLU and the down GEMVs with the gate-weighted
+// combine.  (One token runs the kernel of decode1.hip.)
 //
 // "Optimizing on-device inference for Apple Silicon", section "Decode > Optimize the
 // one-row weight path": a group of lanes shares one output row, each lane reading a
 // different part of the packed weight row.  Section "Decode > Reduce intermediate and
 // state traffic": the two input projections and the gated activation are one step; the
 // output projection, the routing weights and the shared expert's result are another.
-// Section "Decode > Keep every decode step on the GPU": the token's whole layer runs
-// without the host.
+// Section "Decode > Keep every decode step on the GPU": the whole layer runs without the
+// host.  Section "Limits of further optimization": verification batches of a few rows
+// are an inefficient shape for one-row kernels and read experts again; here a batch of
+// T <= 8 rows reads each active expert once (the union of the tokens' experts) and
+// applies it to every token that chose it.
 //
 // Batch-1 decode moves every active weight byte once, so the layer is bound by HBM reads
 // and by the latency of its dependency chain (logits -> selection -> gate/up -> down).
-// One launch covers the chain.  Workgroups hand results to each other as tagged
-// records: an 8-byte word holding a 32-bit value and the call's 32-bit epoch, written
-// with one device-scope store and read with device-scope loads, so a reader accepts a
-// value exactly when its tag is this call's epoch; no wait uses a counter or an atomic
-// read-modify-write (those serialise on one address).  The epoch lives in the
-// workspace: every workgroup reads the last call's epoch at its start and uses the next
-// one; the last workgroup to finish (one ticket per workgroup) stores it back.  The
-// launch arguments are therefore the same for every call, so a sequence of calls can be
-// captured once in a HIP graph and replayed.
-//   1. workgroup b computes the binary64 logits of experts b, b+G, ... and publishes
-//      each as three records (the two halves of the logit and its error radius);
-//   2. every workgroup that needs the routing reads all E logits and selects the top k
-//      itself (same values, same arithmetic, same result): one wave takes all E keys
-//      (four per lane) through k rounds of a wave maximum and certifies the choice
-//      against the radii; only when that fails do the four waves re-rank (exact ranks
-//      of the candidates, undecided experts summed sequentially in binary64);
-//   3. gate/up task g (16 rows of one expert slot) runs on workgroup g mod G and
-//      publishes h as records; tasks of the shared expert run before the routing is
-//      known; a workgroup's first down task has its weight loads issued together with
-//      its routed gate/up loads;
-//   4. down task d (8 output rows, every slot) reads the h records into LDS (all loads
-//      in flight at once, re-reading only records not yet published) and sums
-//      gate * (W_down h) in slot order.
+// One launch covers the chain.  Workgroups hand results to each other as tagged records
+// (an 8-byte word holding a 32-bit value and the call's 32-bit tag, written with one
+// device-scope store and read with device-scope loads, so a reader accepts a value
+// exactly when its tag is this call's) or as plain device-scope stores followed by a
+// tagged flag once they have completed.  The tag lives in the workspace: every
+// workgroup reads the last call's tag at its start and uses the next one; the last
+// workgroup to finish (two-level tickets on counters 256 bytes apart) stores it back.
+// The launch arguments are therefore the same for every call, so a sequence of calls can
+// be captured once in a HIP graph and replayed.
+//   1. the shared expert's gate/up tasks need no routing and run first;
+//   2. router: the first ceil(E/4) workgroups compute one expert's binary64 logit per
+//      wave for every token and publish it with its error radius;
+//   3. workgroup t (t < T) selects token t's top k (one wave, certified against the
+//      radii; the four-wave exact path when the certificate fails) and publishes the
+//      chosen experts (ascending) and their softmax gates;
+//   4. every workgroup with routed work reads the T selections and forms the list of
+//      active experts: the shared one first, then the chosen ones in ascending order,
+//      each with the set of tokens that use it;
+//   5. gate/up task (active expert, 16 rows) dequantises its rows once and multiplies
+//      them with every token of the expert; h goes out with device-scope stores and a
+//      tagged flag per task;
+//   6. down task (active expert, 64 output rows) waits for the expert's gate/up flags,
+//      stages h as bf16 in LDS, and writes gate * (W_down h) per token; each (token, row
+//      block) counts its k+1 arrivals and the last one sums the k+1 slots in slot order
+//      (routed experts ascending, then the shared one) and writes the bf16 output.
 // Every workgroup of the grid is resident at once (the grid is capped by the occupancy
 // of this kernel), so each wait ends; a wait that exceeds its poll budget sets an error
-// word instead of hanging.  The dot products use the packed codes directly:
-//     sum_k v_k (s q_k + b) = s * sum_k v_k q_k + b * sum_k v_k   (per group of 64).
-#include <type_traits>
+// word instead of hanging.
+//
+// GEMV arithmetic: the dot product of a weight row with v uses the codes directly,
+//     sum_k v_k (s q_k + b) = s * sum_k v_k (128 + q_k) + (b - 128 s) * sum_k v_k
+// per group of 64: each 4-bit code becomes the exact bf16 number 128 + q by placing it in
+// the low mantissa bits of 128 (0x4300), and v_dot2_f32_bf16 multiplies code pairs with
+// bf16 activation pairs (x is bf16; h is rounded to bf16 when staged).
+#include <algorithm>
 
 #include "common.hpp"
+
+// Every fused multiply-add below is written out, so the arithmetic of a row is the same
+// in every template instance (the output of a row does not depend on the batch size).
+#pragma clang fp contract(off)
 #include "kernels.hpp"
 #include "select64.hpp"
 
@@ -48,15 +63,13 @@ namespace moe {
 
 namespace {
 
-constexpr int kDecThreads = 256;        // four waves
-constexpr int kGuRows = 4;              // gate/up rows per wave in one task
-constexpr int kGuTask = 4 * kGuRows;    // rows of one gate/up task
-static_assert(kGuRows == 4 && kGuTask % 4 == 0 && kQpRows % 4 == 0, "a wave reads its rows' scale/bias of one group as one 8-byte run");
-constexpr int kDnRows = 8;              // output rows of one down task
-constexpr int kDnUnits = 5;             // (row, slot) units per 16-lane group per round
-constexpr int kDnSlots = 10;            // slots per down round: 8 rows x 10 = 16 groups x 5
-constexpr int kHStage = 5120;           // h floats staged in LDS per down round
-constexpr int kSpins = 1 << 20;         // polls before a wait gives up (about a second)
+constexpr int kDecThreads = 256;      // four waves
+constexpr int kHbWords = 8192;        // LDS words of staged h (bf16 pairs) per down round
+constexpr int kSpins = 1 << 20;       // polls before a wait gives up (about a second)
+constexpr int kActMax = kMaxDecodeT * kMaxTopK + 1;
+constexpr int kSrecRep = 16;          // copies of the selection records
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 
 // This call's record tag (set by thread 0 at the start of k_decode).
 __shared__ uint32_t s_epoch;
@@ -70,25 +83,38 @@ __device__ __forceinline__ QMat expert_mat(const QMat &routed, const QMat &share
   return m;
 }
 
-// sum_i v[i] * code_i over the 32 codes of four packed words
-__device__ __forceinline__ float dot_codes32(const uint4 &w, const float (&v)[32]) {
-  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-  float s = 0.f;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    uint32_t lo = ws[q] & 0x0f0f0f0fu, hi = (ws[q] >> 4) & 0x0f0f0f0fu;
-    asm("" : "+v"(lo), "+v"(hi));  // one v_cvt_f32_ubyteN per code
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      s = __builtin_fmaf(v[8 * q + 2 * j], (float)((lo >> (8 * j)) & 0xffu), s);
-      s = __builtin_fmaf(v[8 * q + 2 * j + 1], (float)((hi >> (8 * j)) & 0xffu), s);
-    }
-  }
-  return s;
-}
-
 __device__ __forceinline__ uint64_t tagged(uint32_t epoch, uint32_t v) { return ((uint64_t)epoch << 32) | v; }
 __device__ __forceinline__ uint32_t tag_of(uint64_t r) { return (uint32_t)(r >> 32); }
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// The eight 4-bit codes of a word as four bf16 pairs holding 128 + code (exact): codes
+// 2j, 2j+1 are byte j of the low and of the high nibbles.
+__device__ __forceinline__ void codes_bf16(uint32_t w, uint32_t *o) {
+  const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t sel = (uint32_t)j | 0x0c00u | ((uint32_t)(4 + j) << 16) | 0x0c000000u;
+    o[j] = __builtin_amdgcn_perm(hi, lo, sel) | 0x43004300u;
+  }
+}
+
+// sum over 32 elements of (128 + q) v with the codes of a 16-byte chunk converted by
+// codes_bf16 (16 words) and v as 16 bf16 pairs
+__device__ __forceinline__ float dot32(const uint32_t (&o)[16], const uint32_t *v) {
+  float d = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) d = dot2(o[i], v[i], d);
+  return d;
+}
+__device__ __forceinline__ float sum32(const uint32_t *v) {
+  float d = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) d = dot2(0x3f803f80u, v[i], d);  // pairs of 1.0
+  return d;
+}
 
 struct DecShared {
   Sel64 S;
@@ -96,62 +122,105 @@ struct DecShared {
   int wcnt[kDecThreads / kWave];
   float wf[kDecThreads / kWave];
   double red[2][4];
-  int ids[kMaxTopK];
-  float gates[kMaxTopK];
-  int fast;  // select_topk: the one-wave selection was certified
-  float unit[kDnRows * kDnSlots];
-  __attribute__((aligned(16))) float h[kHStage];
+  int fast;                                      // the one-wave selection was certified
+  int ids[kMaxDecodeT][kMaxTopK];                // every token's experts, ascending
+  float gates[kMaxDecodeT][kMaxTopK];
+  uint32_t emask[kMaxExperts + 1];               // tokens that chose each expert
+  int act_e[kActMax];                            // active experts: shared first, then ascending
+  uint32_t act_m[kActMax];                       // their token masks
+  int n_act;
+  int arrive[kMaxDecodeT];                       // this workgroup completed (token, row block)
+  __attribute__((aligned(16))) uint32_t hb[kHbWords];  // staged h, bf16 pairs
 };
 
 // ------------------------------------------------------------------ router (binary64)
 
-// Additions on any path of router_logit's sum: 8 per 2048 elements per lane, a 6-level
-// butterfly, 3 across the four waves.
-__device__ __forceinline__ int router_depth(int H) { return 8 * ((H + 2047) / 2048) + 9; }
+// Additions on any path of router_wave's sum: H/64 per lane, a 6-level butterfly.
+__device__ __forceinline__ int router_depth(int H) { return H / 64 + 6; }
 
-// Binary64 logit of expert e (exact products, summed lane-sequentially, then over the
-// wave, then over the four waves in order) and sum |x w|, in every thread.
-__device__ void router_logit(const DecodeArgs &a, DecShared &sh, int e, double &l, double &ab) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, H = a.H;
-  double s = 0.0, sa = 0.0;
-  for (int c = tid; c < H / 8; c += kDecThreads) {
-    const uint4 xv = *(const uint4 *)(a.x + 8 * c);
-    const float xf[8] = {bf16_lo(xv.x), bf16_hi(xv.x), bf16_lo(xv.y), bf16_hi(xv.y),
-                         bf16_lo(xv.z), bf16_hi(xv.z), bf16_lo(xv.w), bf16_hi(xv.w)};
-    float wf[8];
-    if (a.wr16) {
-      const uint4 wv4 = *(const uint4 *)(a.wr16 + (size_t)e * H + 8 * c);
-      wf[0] = bf16_lo(wv4.x); wf[1] = bf16_hi(wv4.x); wf[2] = bf16_lo(wv4.y); wf[3] = bf16_hi(wv4.y);
-      wf[4] = bf16_lo(wv4.z); wf[5] = bf16_hi(wv4.z); wf[6] = bf16_lo(wv4.w); wf[7] = bf16_hi(wv4.w);
-    } else {
-      const float4 w0 = *(const float4 *)(a.wr32 + (size_t)e * H + 8 * c);
-      const float4 w1 = *(const float4 *)(a.wr32 + (size_t)e * H + 8 * c + 4);
-      wf[0] = w0.x; wf[1] = w0.y; wf[2] = w0.z; wf[3] = w0.w;
-      wf[4] = w1.x; wf[5] = w1.y; wf[6] = w1.z; wf[7] = w1.w;
+// Binary64 logits of expert e for every token, by one wave: lane takes the 8-element
+// chunks c = lane + 64 i of the router row (read once) and sums the exact products of
+// each token sequentially; a butterfly gives every lane the totals.  The loads of four
+// chunks of the row (and of the first token) are issued before any is used.  Lane 0
+// publishes (t, e)'s three records: the two halves of the logit (+ bias) and its error
+// radius.
+template <int TT>
+__device__ void router_wave(const DecodeArgs &a, int e) {
+  const int lane = threadIdx.x & 63, H = a.H, E = a.E, T = a.T;
+  constexpr int B4 = 4;
+  double s[TT], sa[TT];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) s[t] = sa[t] = 0.0;
+  for (int c0 = lane; c0 < H / 8; c0 += B4 * kWave) {
+    uint4 w0[B4], w1[B4], xv[B4];
+#pragma unroll
+    for (int u = 0; u < B4; ++u) {
+      const int c = c0 + u * kWave;
+      const int cc = c < H / 8 ? c : lane;  // past the row: a valid chunk, skipped below
+      if (a.wr16) {
+        w0[u] = *(const uint4 *)(a.wr16 + (size_t)e * H + 8 * cc);
+      } else {
+        w0[u] = *(const uint4 *)(a.wr32 + (size_t)e * H + 8 * cc);
+        w1[u] = *(const uint4 *)(a.wr32 + (size_t)e * H + 8 * cc + 4);
+      }
+      xv[u] = *(const uint4 *)(a.x + 8 * cc);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const double p = (double)xf[i] * (double)wf[i];  // exact
-      s += p;
-      sa += fabs(p);
+    for (int t = 0; t < TT; ++t) {
+      if (t >= T) break;
+      if (t > 0) {
+#pragma unroll
+        for (int u = 0; u < B4; ++u) {
+          const int c = c0 + u * kWave;
+          xv[u] = *(const uint4 *)(a.x + (size_t)t * H + 8 * (c < H / 8 ? c : lane));
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < B4; ++u) {
+        if (c0 + u * kWave >= H / 8) break;
+        float wf[8];
+        if (a.wr16) {
+          wf[0] = bf16_lo(w0[u].x); wf[1] = bf16_hi(w0[u].x); wf[2] = bf16_lo(w0[u].y); wf[3] = bf16_hi(w0[u].y);
+          wf[4] = bf16_lo(w0[u].z); wf[5] = bf16_hi(w0[u].z); wf[6] = bf16_lo(w0[u].w); wf[7] = bf16_hi(w0[u].w);
+        } else {
+          wf[0] = __uint_as_float(w0[u].x); wf[1] = __uint_as_float(w0[u].y);
+          wf[2] = __uint_as_float(w0[u].z); wf[3] = __uint_as_float(w0[u].w);
+          wf[4] = __uint_as_float(w1[u].x); wf[5] = __uint_as_float(w1[u].y);
+          wf[6] = __uint_as_float(w1[u].z); wf[7] = __uint_as_float(w1[u].w);
+        }
+        const float xf[8] = {bf16_lo(xv[u].x), bf16_hi(xv[u].x), bf16_lo(xv[u].y), bf16_hi(xv[u].y),
+                             bf16_lo(xv[u].z), bf16_hi(xv[u].z), bf16_lo(xv[u].w), bf16_hi(xv[u].w)};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const double p = (double)xf[i] * (double)wf[i];  // exact
+          s[t] += p;
+          sa[t] += fabs(p);
+        }
+      }
     }
   }
-  s = wave_sum_f64(s);
-  sa = wave_sum_f64(sa);
-  if (lane == 0) {
-    sh.red[0][wv] = s;
-    sh.red[1][wv] = sa;
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+    if (t >= T) break;
+    double l = wave_sum_f64(s[t]);
+    const double ab = wave_sum_f64(sa[t]);
+    if (a.bias) l += (double)a.bias[e];
+    if (lane == 0) {
+      const uint64_t lb = (uint64_t)__double_as_longlong(l);
+      const float rad = __double2float_ru(radius64(l, ab, H, router_depth(H)));
+      uint64_t *rec = a.lrec + 3 * ((size_t)t * E + e);
+      st_agent(&rec[0], tagged(s_epoch, (uint32_t)lb));
+      st_agent(&rec[1], tagged(s_epoch, (uint32_t)(lb >> 32)));
+      st_agent(&rec[2], tagged(s_epoch, __float_as_uint(rad)));
+    }
   }
-  __syncthreads();
-  l = ((sh.red[0][0] + sh.red[0][1]) + sh.red[0][2]) + sh.red[0][3];
-  ab = ((sh.red[1][0] + sh.red[1][1]) + sh.red[1][2]) + sh.red[1][3];
-  if (a.bias) l += (double)a.bias[e];
-  __syncthreads();
 }
 
-// Wait for expert e's three logit records of this call.
-__device__ void read_logit(const DecodeArgs &a, int e, double &v, double &r) {
-  const uint64_t *rec = a.lrec + 3 * (size_t)e;
+// ------------------------------------------------------------------ selection
+
+// Wait for expert e's three logit records of token t.
+__device__ void read_logit(const DecodeArgs &a, int t, int e, double &v, double &r) {
+  const uint64_t *rec = a.lrec + 3 * ((size_t)t * a.E + e);
   for (int i = 0;; ++i) {
     const uint64_t r0 = ld_agent(&rec[0]), r1 = ld_agent(&rec[1]), r2 = ld_agent(&rec[2]);
     if (tag_of(r0) == s_epoch && tag_of(r1) == s_epoch && tag_of(r2) == s_epoch) {
@@ -169,28 +238,8 @@ __device__ void read_logit(const DecodeArgs &a, int e, double &v, double &r) {
   }
 }
 
-__device__ double block_min_f64(double v, DecShared &sh) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) v = fmin(v, __shfl_xor(v, o));
-  if ((threadIdx.x & 63) == 0) sh.red[0][threadIdx.x >> 6] = v;
-  __syncthreads();
-  v = fmin(fmin(sh.red[0][0], sh.red[0][1]), fmin(sh.red[0][2], sh.red[0][3]));
-  __syncthreads();
-  return v;
-}
-
-__device__ double block_max_f64(double v, DecShared &sh) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) v = fmax(v, __shfl_xor(v, o));
-  if ((threadIdx.x & 63) == 0) sh.red[0][threadIdx.x >> 6] = v;
-  __syncthreads();
-  v = fmax(fmax(sh.red[0][0], sh.red[0][1]), fmax(sh.red[0][2], sh.red[0][3]));
-  __syncthreads();
-  return v;
-}
-
-// DPP row maxima / minima (16 lanes), then the four row results through scalar registers:
-// the wave-wide result in every lane.
+// DPP row maxima, then the four row results through scalar registers: the wave-wide
+// result in every lane.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
@@ -235,25 +284,26 @@ __device__ __forceinline__ uint32_t logit_key(double v, int e) {
   return (ord & 0xffffff00u) | (uint32_t)(255 - e);
 }
 
-// Top-k of the E logits by one wave (four experts per lane): the keys of select_topk,
-// k rounds of a wave maximum, the same certificate (every chosen logit minus its radius
-// above every other logit plus its radius); ids ascending and softmax gates into sh.ids,
-// sh.gates.  The lane's twelve records are loaded together and re-polled together.
+// Top-k of token t's E logits by one wave (four experts per lane): k rounds of a wave
+// maximum over the keys, then the certificate (every chosen logit minus its radius above
+// every other logit plus its radius).  Ids ascending and softmax gates into sh.ids[t],
+// sh.gates[t].  The lane's twelve records are loaded together and re-polled together.
 // Returns false, having written nothing, when the certificate fails.
-__device__ bool select_topk_wave(const DecodeArgs &a, DecShared &sh, bool write_debug) {
+__device__ bool select_topk_wave(const DecodeArgs &a, DecShared &sh, int t) {
   constexpr int NV = kMaxExperts / kWave;
   const int lane = threadIdx.x & 63, E = a.E, k = a.k;
   double v[NV], r[NV];
   bool valid[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) valid[i] = lane + kWave * i < E;
+  const uint64_t *base = a.lrec + 3 * (size_t)t * E;
   uint64_t rec[NV][3];
   for (int it = 0;; ++it) {
     bool ok = true;
 #pragma unroll
     for (int i = 0; i < NV; ++i)
 #pragma unroll
-      for (int j = 0; j < 3; ++j) rec[i][j] = valid[i] ? ld_agent(&a.lrec[3 * (size_t)(lane + kWave * i) + j]) : 0u;
+      for (int j = 0; j < 3; ++j) rec[i][j] = valid[i] ? ld_agent(&base[3 * (size_t)(lane + kWave * i) + j]) : 0u;
 #pragma unroll
     for (int i = 0; i < NV; ++i)
 #pragma unroll
@@ -318,27 +368,23 @@ __device__ bool select_topk_wave(const DecodeArgs &a, DecShared &sh, bool write_
     const uint64_t bal = __ballot(ch);
     const int pos = below + __popcll(bal & ((1ull << lane) - 1ull));
     if (ch && pos < kMaxTopK) {
-      const int e = lane + kWave * i;
-      const float g = ex[i] / den;
-      sh.ids[pos] = e;
-      sh.gates[pos] = g;
-      if (write_debug && a.dbg_ids) a.dbg_ids[pos] = e;
-      if (write_debug && a.dbg_gates) a.dbg_gates[pos] = g;
+      sh.ids[t][pos] = lane + kWave * i;
+      sh.gates[t][pos] = ex[i] / den;
     }
     below += __popcll(bal);
   }
   return true;
 }
 
-// Top-k of the E logits of this call (value descending, index ascending) into sh.ids
-// (ascending) and sh.gates: select_topk_wave, or when its certificate fails the
-// four-wave path below.  One expert per thread (E <= 256): each wave takes its top k
-// by k rounds of a wave maximum; a chosen candidate is one of the 4k whose rank among
-// them is below k.  The choice is certified against the binary64 error radii; experts
-// closer than their radii are re-ranked by resolve64.
-__device__ void select_topk(const DecodeArgs &a, DecShared &sh, bool write_debug) {
+// Top-k of token t (value descending, index ascending) into sh.ids[t] (ascending) and
+// sh.gates[t]: select_topk_wave, or when its certificate fails the four-wave path below.
+// One expert per thread (E <= 256): each wave takes its top k by k rounds of a wave
+// maximum; a chosen candidate is one of the 4k whose rank among them is below k.  The
+// choice is certified against the binary64 error radii; experts closer than their radii
+// are re-ranked by resolve64.
+__device__ void select_topk(const DecodeArgs &a, DecShared &sh, int t) {
   if (threadIdx.x < kWave) {
-    const bool ok = select_topk_wave(a, sh, write_debug);
+    const bool ok = select_topk_wave(a, sh, t);
     if (threadIdx.x == 0) sh.fast = ok;
   }
   __syncthreads();
@@ -348,7 +394,7 @@ __device__ void select_topk(const DecodeArgs &a, DecShared &sh, bool write_debug
   const bool mine = tid < E;
   double v = -INFINITY, r = 0.0;
   if (mine) {
-    read_logit(a, tid, v, r);
+    read_logit(a, t, tid, v, r);
     S.gl[tid] = v;
   }
   uint32_t key = mine ? logit_key(v, tid) : 0u;
@@ -391,7 +437,7 @@ __device__ void select_topk(const DecodeArgs &a, DecShared &sh, bool write_debug
       S.rad[c] = r;
     }
     const int nin1 = __syncthreads_count(sure_in);
-    resolve64(S, k - nin1, a.x, a.wr16, a.wr32, a.bias, a.H, tid, kDecThreads);
+    resolve64(S, k - nin1, a.x + (size_t)t * a.H, a.wr16, a.wr32, a.bias, a.H, tid, kDecThreads);
   }
   // ids ascending (rank of each chosen expert = chosen experts below it) and softmax
   // gates of the chosen logits
@@ -418,328 +464,497 @@ __device__ void select_topk(const DecodeArgs &a, DecShared &sh, bool write_debug
   __syncthreads();
   const float den = (sh.wf[0] + sh.wf[1]) + (sh.wf[2] + sh.wf[3]);
   if (ch && below < kMaxTopK) {
-    const float g = ex / den;
-    sh.ids[below] = tid;
-    sh.gates[below] = g;
-    if (write_debug && a.dbg_ids) a.dbg_ids[below] = tid;
-    if (write_debug && a.dbg_gates) a.dbg_gates[below] = g;
+    sh.ids[t][below] = tid;
+    sh.gates[t][below] = ex / den;
   }
   __syncthreads();
-  if (tid < k) sh.ids[tid] = min(max(sh.ids[tid], 0), E - 1);  // keep reads in bounds even after a failed wait
+  if (tid < k) sh.ids[t][tid] = min(max(sh.ids[t][tid], 0), E - 1);  // keep reads in bounds even after a failed wait
   __syncthreads();
+}
+
+// Every token's selection from the selectors' records into sh.ids / sh.gates, then the
+// list of active experts (shared first, then ascending) with their token masks.
+__device__ void read_routing(const DecodeArgs &a, DecShared &sh, int rep) {
+  const int tid = threadIdx.x, T = a.T, E = a.E, k = a.k;
+  if (tid < kWave) {
+    const int n = T * 2 * k;  // <= 256
+    uint64_t rec[4];
+    for (int it = 0;; ++it) {
+      bool ok = true;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = tid + kWave * i;
+        rec[i] = j < n ? ld_agent(&a.srec[(size_t)rep * n + j]) : tagged(s_epoch, 0u);
+        ok &= tag_of(rec[i]) == s_epoch;
+      }
+      if (__ballot(!ok) == 0ull) break;
+      if (it == kSpins) {
+        st_agent(&a.ctrl->d_err, 1);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = tid + kWave * i;
+      if (j >= n) continue;
+      const int t = j / (2 * k), q = j - t * 2 * k;
+      if (q < k)
+        sh.ids[t][q] = min(max((int)(uint32_t)rec[i], 0), E - 1);  // in bounds even after a failed wait
+      else
+        sh.gates[t][q - k] = __uint_as_float((uint32_t)rec[i]);
+    }
+  }
+  for (int e = tid; e <= E; e += kDecThreads) sh.emask[e] = e == E ? (1u << T) - 1u : 0u;
+  __syncthreads();
+  if (tid < T * k) atomicOr(&sh.emask[sh.ids[tid / k][tid % k]], 1u << (tid / k));
+  __syncthreads();
+  if (tid < kWave) {
+    int n = 1;
+    if (tid == 0) {
+      sh.act_e[0] = E;
+      sh.act_m[0] = sh.emask[E];
+    }
+    for (int e0 = 0; e0 < E; e0 += kWave) {
+      const int e = e0 + tid;
+      const bool on = e < E && sh.emask[e] != 0u;
+      const uint64_t bal = __ballot(on);
+      if (on) {
+        const int p = n + __popcll(bal & ((1ull << tid) - 1ull));
+        sh.act_e[p] = e;
+        sh.act_m[p] = sh.emask[e];
+      }
+      n += __popcll(bal);
+    }
+    if (tid == 0) sh.n_act = n;
+  }
+  __syncthreads();
+}
+
+// index of the n-th set bit of m (n < popcount(m))
+__device__ __forceinline__ int nth_bit(uint32_t m, int n) {
+  for (int i = 0; i < n; ++i) m &= m - 1u;
+  return __ffs((int)m) - 1;
+}
+
+// slot of expert u in token t's selection (k for the shared expert)
+__device__ __forceinline__ int slot_of(const DecodeArgs &a, const DecShared &sh, int t, int u) {
+  if (u == a.E) return a.k;
+  int j = 0;
+  for (int q = 0; q < a.k; ++q) j = sh.ids[t][q] == u ? q : j;
+  return j;
 }
 
 // ------------------------------------------------------------------ gate/up
 
-// One round of a gate/up task for the calling wave: rows r0..r0+3 of slot j, the
-// 32-element chunk c = lane + 64 p of the H-long rows.
-struct GuLoad {
-  uint4 wg[kGuRows], wu[kGuRows];
-  uint2 sg, bg, su, bu;  // fp16 scale/bias of rows r0..r0+3: row r in half r%2 of word r/2
-  uint4 x[4];
-  bool ok;
-};
-
-__device__ __forceinline__ void gu_issue(const DecodeArgs &a, const QMat &Gm, const QMat &Um, int r0, int c,
-                                         GuLoad &L) {
-  const int H = a.H;
-  L.ok = c < H / 32;
-  const int cc = L.ok ? c : 0;
-#pragma unroll
-  for (int r = 0; r < kGuRows; ++r) {
-    const size_t row = (size_t)(r0 + r);
-    const size_t ci = code_index(row, 4 * cc, H);
-    L.wg[r] = *(const uint4 *)(Gm.q + ci);
-    L.wu[r] = *(const uint4 *)(Um.q + ci);
-  }
-  // r0 is a multiple of 4, so the four rows' values of one group are adjacent (8 bytes)
-  const size_t qi = qp_index((size_t)r0, cc / 2, H / 64);
-  L.sg = *(const uint2 *)(Gm.s + qi);
-  L.bg = *(const uint2 *)(Gm.b + qi);
-  L.su = *(const uint2 *)(Um.s + qi);
-  L.bu = *(const uint2 *)(Um.b + qi);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) L.x[q] = *(const uint4 *)(a.x + 32 * cc + 8 * q);
-}
-
-__device__ __forceinline__ void gu_accumulate(const GuLoad &L, float (&ag)[kGuRows], float (&au)[kGuRows]) {
-  if (!L.ok) return;
-  float xf[32];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t xw[4] = {L.x[q].x, L.x[q].y, L.x[q].z, L.x[q].w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      xf[8 * q + 2 * i] = bf16_lo(xw[i]);
-      xf[8 * q + 2 * i + 1] = bf16_hi(xw[i]);
-    }
-  }
-  float xs = 0.f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) xs += xf[i];
-#pragma unroll
-  for (int r = 0; r < kGuRows; ++r) {
-    auto half = [&](uint2 v) { return fp16_to_f32((uint16_t)(((r >> 1) ? v.y : v.x) >> (16 * (r & 1)))); };
-    ag[r] += half(L.sg) * dot_codes32(L.wg[r], xf) + half(L.bg) * xs;
-    au[r] += half(L.su) * dot_codes32(L.wu[r], xf) + half(L.bu) * xs;
-  }
-}
-
-__device__ __forceinline__ int gu_expert(const DecodeArgs &a, const DecShared &sh, int j) {
-  return j < a.k ? sh.ids[j] : a.E;
-}
-
-__device__ __forceinline__ void gu_start(const DecodeArgs &a, const DecShared &sh, int g, GuLoad &L) {
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int tpe = a.I / kGuTask;
-  const int j = g / tpe, r0 = (g - j * tpe) * kGuTask + kGuRows * wv;
-  const int e = gu_expert(a, sh, j);
-  gu_issue(a, expert_mat(a.gate, a.s_gate, e, a.E, a.I, a.H), expert_mat(a.up, a.s_up, e, a.E, a.I, a.H), r0,
-           lane, L);
-}
-
-// Gate/up task g: slot j = g / (I/16), rows i0 .. i0+15 (wave w: i0+4w .. i0+4w+3).
-// `first` holds the already-issued first round.  Publishes this wave's 4 h records.
-__device__ __forceinline__ void gu_task(const DecodeArgs &a, const DecShared &sh, int g, const GuLoad &first) {
+// Gate/up task: rows rb*16 .. rb*16+15 of active expert `act` (expert u, tokens tm);
+// wave w takes rows rb*16 + 4w .. rb*16 + 4w + 3; lane takes the 32-element chunks
+// c = lane + 64 i.  The loads of all four rows of a chunk are issued before any is used;
+// each row's codes are converted once and multiplied with every token.  h of (t, slot,
+// row) goes out with device-scope stores; after all four waves' stores have completed,
+// the task's tagged flag.
+template <int TT>
+__device__ void gu_task(const DecodeArgs &a, DecShared &sh, int act, int u, uint32_t tm, int rb) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int I = a.I, H = a.H;
-  const int tpe = I / kGuTask;
-  const int j = g / tpe, r0 = (g - j * tpe) * kGuTask + kGuRows * wv;
-  float ag[kGuRows] = {}, au[kGuRows] = {};
-  gu_accumulate(first, ag, au);
-  const int np = (H / 32 + kWave - 1) / kWave;
-  if (np > 1) {
-    const int e = gu_expert(a, sh, j);
-    const QMat Gm = expert_mat(a.gate, a.s_gate, e, a.E, I, H);
-    const QMat Um = expert_mat(a.up, a.s_up, e, a.E, I, H);
-    for (int p = 1; p < np; ++p) {
-      GuLoad L;
-      gu_issue(a, Gm, Um, r0, lane + kWave * p, L);
-      gu_accumulate(L, ag, au);
+  const int H = a.H, I = a.I, E = a.E, k = a.k;
+  const QMat Gm = expert_mat(a.gate, a.s_gate, u, E, I, H), Um = expert_mat(a.up, a.s_up, u, E, I, H);
+  const int r0 = rb * kDecGuTask + 4 * wv;  // rows r0 .. r0+3 (r0 a multiple of 4)
+  float acc[TT][4][2];
+#pragma unroll
+  for (int t = 0; t < TT; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[t][r][0] = acc[t][r][1] = 0.f;
+  for (int c = lane; c < H / 32; c += kWave) {
+    uint4 cw[2][4];
+    uint32_t sv[2][2], bv[2][2];  // per matrix and row pair: fp16 scale / bias of the two rows
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const QMat &M = m ? Um : Gm;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) cw[m][r] = *(const uint4 *)(M.q + code_index((size_t)(r0 + r), 4 * c, H));
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const size_t qi = qp_index((size_t)(r0 + 2 * pp), c / 2, H / 64);
+        sv[m][pp] = *(const uint32_t *)(M.s + qi);
+        bv[m][pp] = *(const uint32_t *)(M.b + qi);
+      }
+    }
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      uint32_t o[2][2][16];
+      float s[2][2], b2[2][2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const uint4 &w = cw[m][2 * pp + r];
+          codes_bf16(w.x, &o[m][r][0]);
+          codes_bf16(w.y, &o[m][r][4]);
+          codes_bf16(w.z, &o[m][r][8]);
+          codes_bf16(w.w, &o[m][r][12]);
+          s[m][r] = fp16_to_f32((uint16_t)(sv[m][pp] >> (16 * r)));
+          b2[m][r] = __builtin_fmaf(-128.0f, s[m][r], fp16_to_f32((uint16_t)(bv[m][pp] >> (16 * r))));
+        }
+#pragma unroll
+      for (int t = 0; t < TT; ++t) {
+        if (!((tm >> t) & 1u)) continue;
+        uint32_t xw[16];
+        const uint4 *xp = (const uint4 *)(a.x + (size_t)t * H + 32 * c);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint4 xq = xp[v];
+          xw[4 * v] = xq.x; xw[4 * v + 1] = xq.y; xw[4 * v + 2] = xq.z; xw[4 * v + 3] = xq.w;
+        }
+        const float xs = sum32(xw);
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int r = 0; r < 2; ++r)
+            acc[t][2 * pp + r][m] =
+                __builtin_fmaf(s[m][r], dot32(o[m][r], xw), __builtin_fmaf(b2[m][r], xs, acc[t][2 * pp + r][m]));
+      }
     }
   }
-  float hv = 0.f;
 #pragma unroll
-  for (int r = 0; r < kGuRows; ++r) {
-    const float gs = wave_sum(ag[r]);
-    const float us = wave_sum(au[r]);
-    if (lane == r) hv = gs / (1.0f + __expf(-gs)) * us;
+  for (int t = 0; t < TT; ++t) {
+    if (!((tm >> t) & 1u)) continue;
+    const int j = slot_of(a, sh, t, u);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float gs = wave_sum(acc[t][r][0]);
+      const float us = wave_sum(acc[t][r][1]);
+      const float hv = gs / (1.0f + __expf(-gs)) * us;
+      if (lane == r) st_agent(&a.hval[((size_t)t * (k + 1) + j) * I + r0 + r], hv);
+    }
   }
-  const size_t row = (size_t)j * I + r0;
-  if (lane < kGuRows) st_agent(&a.hrec[row + lane], tagged(s_epoch, __float_as_uint(hv)));
+  vm_drain();  // this wave's h stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) st_agent(&a.hflag[(size_t)act * (I / kDecGuTask) + rb], tagged(s_epoch, 1u));
 }
 
 // ------------------------------------------------------------------ down
 
-// Units of a down round: u = r * nb + jj (row r of the task, slot j0 + jj).  16-lane
-// group q (lane/16 + 4*wave) takes u = q + 16 m; lane cl = lane % 16 takes the
-// 32-element chunk c = cl + 16 p of the I-long rows.
-struct DnLoad {
-  uint4 w[kDnUnits];
-  uint32_t s[kDnUnits], b[kDnUnits];
+// Down task: output rows n0 = rb*64 .. n0+63 of active expert `act` (expert u, tokens tm).
+// Waits for the expert's I/16 gate/up flags, stages each token's h as bf16 pairs in LDS
+// (in rounds when they do not fit), then 16-lane group q of wave w takes rows
+// n0 + 16w + 4i + q (i < 4), lane cl = lane%16 the 32-element chunks c = cl + 16p.  Writes
+// gate * y per (token, slot, row) and counts the (token, row block) arrivals; the
+// workgroup that completes a (token, row block) sums its k+1 slots in slot order.
+// The weights of one chunk c of a down task (the lane's four rows), in plain words (a union
+// vector type kept across calls here is not split into registers).  The first chunk
+// (c = lane % 16) of a workgroup's first down task is loaded before the expert's h is
+// ready.
+struct DnPre {
+  uint32_t w[4][4];     // code words
+  uint32_t s[4], b[4];  // fp16 bits
 };
 
-__device__ __forceinline__ void dn_issue(const DecodeArgs &a, const DecShared &sh, int n0, int j0, int nb, int c,
-                                         DnLoad &L) {
-  const int I = a.I, k = a.k, q = (threadIdx.x >> 4);
-  const int cc = c < I / 32 ? c : 0;
+__device__ __forceinline__ void dn_load(const DecodeArgs &a, int u, int rb, int c, DnPre &P) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, q = lane >> 4;
+  const int H = a.H, I = a.I;
+  if (c >= I / 32) return;  // no such chunk for this lane (I = 128, 256, 384)
+  const QMat D = expert_mat(a.down, a.s_down, u, a.E, H, I);
 #pragma unroll
-  for (int m = 0; m < kDnUnits; ++m) {
-    int u = q + 16 * m;
-    u = u < kDnRows * nb ? u : 0;  // surplus units read unit 0 (result discarded)
-    const int r = u / nb, slot = j0 + (u - r * nb);
-    const int e = slot < k ? sh.ids[slot] : a.E;
-    const QMat D = expert_mat(a.down, a.s_down, e, a.E, a.H, I);
-    const size_t n = (size_t)(n0 + r);
-    L.w[m] = *(const uint4 *)(D.q + code_index(n, 4 * cc, I));
-    const size_t qi = qp_index(n, cc / 2, I / 64);
-    L.s[m] = D.s[qi];
-    L.b[m] = D.b[qi];
+  for (int i = 0; i < 4; ++i) {
+    const size_t n = (size_t)(rb * kDecDnTask + 16 * wv + 4 * i + q);
+    const uint4 v = *(const uint4 *)(D.q + code_index(n, 4 * c, I));
+    P.w[i][0] = v.x;
+    P.w[i][1] = v.y;
+    P.w[i][2] = v.z;
+    P.w[i][3] = v.w;
+    const size_t qi = qp_index(n, c / 2, I / 64);
+    P.s[i] = D.s[qi];
+    P.b[i] = D.b[qi];
   }
 }
 
-// h of slots j0 .. j0+nb-1 into LDS from their tagged records: each thread issues the
-// loads of up to 16 records at once, then re-reads (one by one) the few whose tag is not
-// yet this call's.
-__device__ __forceinline__ void stage_h(const DecodeArgs &a, DecShared &sh, int j0, int nb) {
-  const int tid = threadIdx.x;
-  const int n = nb * a.I;
-  const uint64_t *rec = a.hrec + (size_t)j0 * a.I;
-  constexpr int kBatch = 16;
-  for (int t0 = tid; t0 < n; t0 += kDecThreads * kBatch) {
-    uint64_t rv[kBatch];
+// Down task: output rows n0 = rb*64 .. n0+63 of active expert `act` (expert u, tokens tm).
+// Waits for the expert's I/16 gate/up flags, stages each token's h as bf16 pairs in LDS
+// (in rounds when they do not fit), then 16-lane group q of wave w takes rows
+// n0 + 16w + 4i + q (i < 4), lane cl = lane%16 the 32-element chunks c = cl + 16p (the
+// first one's weights in `pre`).  Writes gate * y per (token, slot, row) and counts the
+// (token, row block) arrivals; the workgroup that completes a (token, row block) sums its
+// k+1 slots in slot order.
+template <int TT>
+__device__ __forceinline__ void dn_task(const DecodeArgs &a, DecShared &sh, int act, int u, uint32_t tm, int rb,
+                                        DnPre pre) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, q = lane >> 4, cl = lane & 15;
+  const int H = a.H, I = a.I, k = a.k;
+  const int ntb = I / kDecGuTask;
+  // 1. the expert's gate/up tasks are done
+  if (tid < kWave) {
+    const uint64_t *fl = a.hflag + (size_t)act * ntb;
+    for (int it = 0;; ++it) {
+      bool ok = true;
+      for (int i = tid; i < ntb; i += kWave) ok &= tag_of(ld_agent(&fl[i])) == s_epoch;
+      if (__ballot(!ok) == 0ull) break;
+      if (it == kSpins) {
+        st_agent(&a.ctrl->d_err, 1);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  const int n0 = rb * kDecDnTask;
+  const int nt = __popc(tm);
+  const int per_round = kHbWords / (I / 2);  // tokens whose h fits in LDS at once (>= 4)
+  for (int t0 = 0; t0 < nt; t0 += per_round) {
+    const int nb = min(per_round, nt - t0);
+    if (t0 > 0) dn_load(a, u, rb, cl, pre);
+    __syncthreads();  // the flags are seen (first round) / the previous round's reads are done
+    for (int i = tid; i < nb * (I / 2); i += kDecThreads) {
+      const int ti = i / (I / 2), w = i - ti * (I / 2);
+      const int t = nth_bit(tm, t0 + ti);
+      const float *hp = a.hval + ((size_t)t * (k + 1) + slot_of(a, sh, t, u)) * I + 2 * w;
+      sh.hb[ti * (I / 2) + w] = pack_bf16x2(ld_agent(hp), ld_agent(hp + 1));
+    }
+    __syncthreads();
+    float acc[TT][4];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int t = t0 + u * kDecThreads;
-      rv[u] = t < n ? ld_agent(&rec[t]) : tagged(s_epoch, 0u);
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[t][i] = 0.f;
+    auto chunk = [&](int c, const DnPre &W) {
+      uint32_t o[4][16];
+      float s[4], b2[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[i] = fp16_to_f32((uint16_t)W.s[i]);
+        b2[i] = __builtin_fmaf(-128.0f, s[i], fp16_to_f32((uint16_t)W.b[i]));
+#pragma unroll
+        for (int v = 0; v < 4; ++v) codes_bf16(W.w[i][v], &o[i][4 * v]);
+      }
+#pragma unroll
+      for (int ti = 0; ti < TT; ++ti) {
+        if (ti >= nb) break;
+        const uint32_t *hp = &sh.hb[ti * (I / 2) + 16 * c];
+        uint32_t hw[16];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint4 x4 = *(const uint4 *)(hp + 4 * v);
+          hw[4 * v] = x4.x; hw[4 * v + 1] = x4.y; hw[4 * v + 2] = x4.z; hw[4 * v + 3] = x4.w;
+        }
+        const float hs = sum32(hw);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[ti][i] = __builtin_fmaf(s[i], dot32(o[i], hw), __builtin_fmaf(b2[i], hs, acc[ti][i]));
+      }
+    };
+    if (cl < I / 32) chunk(cl, pre);
+    for (int c = cl + 16; c < I / 32; c += 16) {
+      DnPre L;
+      dn_load(a, u, rb, c, L);
+      chunk(c, L);
     }
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int t = t0 + u * kDecThreads;
-      if (t >= n) continue;
-      for (int i = 0; tag_of(rv[u]) != s_epoch; ++i) {
-        if (i == kSpins) {
-          st_agent(&a.ctrl->d_err, 1);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-        rv[u] = ld_agent(&rec[t]);
+    for (int ti = 0; ti < TT; ++ti) {
+      if (ti >= nb) break;
+      const int t = nth_bit(tm, t0 + ti);
+      const int j = slot_of(a, sh, t, u);
+      const float g = j < k ? sh.gates[t][j] : 1.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float y = row16_sum(acc[ti][i]);
+        const float gy = g * y;
+        if (cl == 0) st_agent(&a.part[((size_t)t * (k + 1) + j) * H + n0 + 16 * wv + 4 * i + q], gy);
       }
-      sh.h[t] = __uint_as_float((uint32_t)rv[u]);
+    }
+  }
+  vm_drain();  // this thread's partial outputs have completed
+  __syncthreads();
+  if (tid == 0) {
+    for (int i = 0; i < nt; ++i) {
+      const int t = nth_bit(tm, i);
+      int *ctr = a.rbctr + ((size_t)t * (H / kDecDnTask) + rb) * kCtrStride;
+      const int c = ticket(ctr);
+      sh.arrive[i] = c == k;  // the (k+1)-th arrival
+      if (c == k) st_agent(ctr, 0);
     }
   }
   __syncthreads();
-}
-
-__device__ __forceinline__ void dn_accumulate(const DecodeArgs &a, DecShared &sh, const DnLoad &L, int nb, int c,
-                                              float (&acc)[kDnUnits]) {
-  const int I = a.I, q = threadIdx.x >> 4;
-  if (c >= I / 32) return;
+  // the (token, row block)s this workgroup completed: sum the k+1 slots in slot order
+  for (int i = 0; i < nt; ++i) {
+    if (!sh.arrive[i]) continue;  // uniform
+    const int t = nth_bit(tm, i);
+    if (tid < kDecDnTask) {
+      const float *pp = a.part + (size_t)t * (k + 1) * H + n0 + tid;
+      float v[kMaxTopK + 1];
 #pragma unroll
-  for (int m = 0; m < kDnUnits; ++m) {
-    const int u = q + 16 * m;
-    if (u >= kDnRows * nb) continue;
-    const int jj = u % nb;
-    const float4 *hp = (const float4 *)&sh.h[jj * I + 32 * c];
-    float hv[32];
+      for (int j = 0; j <= kMaxTopK; ++j) v[j] = j <= k ? ld_agent(pp + (size_t)j * H) : 0.f;
+      float sum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float4 v = hp[i];
-      hv[4 * i] = v.x;
-      hv[4 * i + 1] = v.y;
-      hv[4 * i + 2] = v.z;
-      hv[4 * i + 3] = v.w;
+      for (int j = 0; j <= kMaxTopK; ++j) sum += j <= k ? v[j] : 0.f;
+      a.out[(size_t)t * H + n0 + tid] = f32_to_bf16(sum);
     }
-    float hs = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) hs += hv[i];
-    acc[m] += fp16_to_f32((uint16_t)L.s[m]) * dot_codes32(L.w[m], hv) + fp16_to_f32((uint16_t)L.b[m]) * hs;
   }
-}
-
-// Down task d: output rows n0 = 8d .. 8d+7 over every slot, rounds of nb slots and
-// chunk passes; `pre` (if given) is round 0's first pass, already issued.
-__device__ __forceinline__ void dn_task(const DecodeArgs &a, DecShared &sh, int d, const DnLoad &pre, bool has_pre) {
-  const int tid = threadIdx.x, q = tid >> 4, cl = tid & 15;
-  const int I = a.I, k = a.k, n0 = d * kDnRows;
-  const int nbmax = min(min(k + 1, kDnSlots), kHStage / I);
-  const int npass = (I / 32 + 15) / 16;
-  float out_acc = 0.f;  // thread t < 8: row n0 + t
-  for (int j0 = 0; j0 <= k; j0 += nbmax) {
-    const int nb = min(nbmax, k + 1 - j0);
-    stage_h(a, sh, j0, nb);
-    float acc[kDnUnits] = {};
-    for (int p = 0; p < npass; ++p) {
-      const int c = cl + 16 * p;
-      if (has_pre && j0 == 0 && p == 0) {
-        dn_accumulate(a, sh, pre, nb, c, acc);
-      } else {
-        DnLoad L;
-        dn_issue(a, sh, n0, j0, nb, c, L);
-        dn_accumulate(a, sh, L, nb, c, acc);
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < kDnUnits; ++m) {
-      const float v = row16_sum(acc[m]);
-      const int u = q + 16 * m;
-      if (cl == 0 && u < kDnRows * nb) {
-        const int slot = j0 + u % nb;
-        sh.unit[u] = (slot < k ? sh.gates[slot] : 1.0f) * v;
-      }
-    }
-    __syncthreads();
-    if (tid < kDnRows)
-      for (int jj = 0; jj < nb; ++jj) out_acc += sh.unit[tid * nb + jj];
-    __syncthreads();
-  }
-  if (tid < kDnRows) a.out[n0 + tid] = f32_to_bf16(out_acc);
 }
 
 // ------------------------------------------------------------------ the layer
 
+// Workgroups start XCD by XCD (workgroup b on the XCD b mod 8 under the round-robin
+// placement), the XCD of workgroup 0 first and the others up to a few microseconds
+// later.  Work that every other workgroup waits for -- the router and the selections --
+// goes to the workgroups b = 0 mod 8; the shared expert's gate/up tasks, which need no
+// routing, to b = 1 mod 8, the next XCD to start; the other tasks follow.  pos(b) orders
+// the workgroups by residue 1, 2, ..., 7, 0 (then by b).
+__device__ __forceinline__ int wg_pos(int b, int G) {
+  const int r = b % 8, ri = (r + 7) % 8;  // residue 1 -> 0, ..., 0 -> 7
+  int before = 0;
+  for (int j = 0; j < ri; ++j) {
+    const int rj = (j + 1) % 8;
+    before += G / 8 + (rj < G % 8 ? 1 : 0);
+  }
+  return before + b / 8;
+}
+
+template <int TT>
 __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
   __shared__ DecShared sh;
-  const int b = blockIdx.x, G = gridDim.x, tid = threadIdx.x;
+  const int b = blockIdx.x, G = gridDim.x, tid = threadIdx.x, wv = tid >> 6;
   if (tid == 0) {
     uint32_t ep = ld_agent(&a.ctrl->d_epoch) + 1u;
     s_epoch = ep ? ep : 1u;
   }
-  __syncthreads();
-  const int E = a.E, k = a.k;
-  const int n_gu = (k + 1) * (a.I / kGuTask), n_dn = a.H / kDnRows;
-  const int first_shared = k * (a.I / kGuTask);  // gate/up tasks from here on are the shared expert's
+  const int T = a.T, E = a.E, k = a.k;
+  const int ntb = a.I / kDecGuTask;       // gate/up tasks per active expert
+  const int nrb = a.H / kDecDnTask;       // down tasks per active expert
+  const int act_max = min(T * k, E) + 1;
+  const uint32_t all_tok = (1u << T) - 1u;
+  const int gpos = wg_pos(b, G);          // gate/up tasks g = gpos, gpos + G, ...
+  const int nrw = 4 * ((G + 7) / 8);      // router waves: four per workgroup b = 0 mod 8
+  const bool spread_sel = 8 * (T - 1) < G;
+  const bool selector = spread_sel ? (b % 8 == 0 && b / 8 < T) : b < T;
+  const int my_tok = spread_sel ? b / 8 : b;
 
-  // The shared expert needs no routing: issue its gate/up loads before the router work.
-  GuLoad gl;
-  const bool gu_early = b < n_gu && b >= first_shared;
-  if (gu_early) gu_start(a, sh, b, gl);
+  // the first down task's weights, if it belongs to the shared expert (known now)
+  DnPre pre;
+  const bool pre_shared = b < nrb;
+  if (pre_shared) dn_load(a, E, b, threadIdx.x & 15, pre);
+  __syncthreads();  // s_epoch
 
-  // 1. router logits, published as records
-  for (int e = b; e < E; e += G) {
-    double l, ab;
-    router_logit(a, sh, e, l, ab);
-    if (tid == 0) {
-      const uint64_t lb = (uint64_t)__double_as_longlong(l);
-      const float rad = __double2float_ru(radius64(l, ab, a.H, router_depth(a.H)));
-      uint64_t *rec = a.lrec + 3 * (size_t)e;
-      st_agent(&rec[0], tagged(s_epoch, (uint32_t)lb));
-      st_agent(&rec[1], tagged(s_epoch, (uint32_t)(lb >> 32)));
-      st_agent(&rec[2], tagged(s_epoch, __float_as_uint(rad)));
+  // 1. the shared expert (active index 0): gate/up before the routing is known
+  for (int g = gpos; g < ntb; g += G) gu_task<TT>(a, sh, 0, E, all_tok, g);
+
+  // 2. router logits, published as records
+  if (b % 8 == 0)
+    for (int e = (b / 8) * 4 + wv; e < E; e += nrw) router_wave<TT>(a, e);
+
+  // 3. selection of token my_tok, published as records (ids ascending, then gates), in
+  // kSrecRep copies so that few workgroups poll each copy
+  if (selector) {
+    const int t = my_tok;
+    select_topk(a, sh, t);
+    for (int i = tid; i < kSrecRep * 2 * k; i += kDecThreads) {
+      const int r = i / (2 * k), q = i - r * 2 * k;
+      const uint32_t v = q < k ? (uint32_t)sh.ids[t][q] : __float_as_uint(sh.gates[t][q - k]);
+      st_agent(&a.srec[((size_t)r * T + t) * 2 * k + q], tagged(s_epoch, v));
+    }
+    if (tid < k) {
+      if (a.dbg_ids) a.dbg_ids[(size_t)t * k + tid] = sh.ids[t][tid];
+      if (a.dbg_gates) a.dbg_gates[(size_t)t * k + tid] = sh.gates[t][tid];
     }
   }
 
-  if (gu_early) gu_task(a, sh, b, gl);
-
-  // 2. the selection, in every workgroup that uses it
-  int g0 = gu_early ? b + G : b;
-  const bool routed_gu = g0 < first_shared;
-  if (routed_gu || b < n_dn || b == 0) select_topk(a, sh, b == 0);
-
-  // 3. routed gate/up tasks; the first down task's loads go out with the first of them
-  DnLoad dl;
-  bool dn_pre = false;
-  const int nbmax = min(min(k + 1, kDnSlots), kHStage / a.I);
-  for (int g = g0; g < n_gu; g += G) {
-    gu_start(a, sh, g, gl);
-    if (!dn_pre && b < n_dn) {
-      dn_issue(a, sh, b * kDnRows, 0, min(nbmax, k + 1), tid & 15, dl);
-      dn_pre = true;
+  // 4. the routing, in every workgroup that may have routed work
+  int g_next = gpos;
+  while (g_next < ntb) g_next += G;
+  const bool may_gu = g_next < ntb * act_max;
+  const bool may_dn = b < nrb * act_max;
+  if (may_gu || may_dn) {
+    read_routing(a, sh, b % kSrecRep);
+    const int n_act = sh.n_act;
+    // the first down task's weights (a routed expert's) go out with the gate/up loads
+    if (!pre_shared && b < nrb * n_act) dn_load(a, sh.act_e[b / nrb], b % nrb, threadIdx.x & 15, pre);
+    // 5. routed gate/up tasks
+    for (int g = g_next; g < ntb * n_act; g += G) {
+      const int act = g / ntb;
+      gu_task<TT>(a, sh, act, sh.act_e[act], sh.act_m[act], g - act * ntb);
     }
-    gu_task(a, sh, g, gl);
+    // 6. down tasks
+    for (int d = b; d < nrb * n_act; d += G) {
+      const int act = d / nrb;
+      if (d != b) dn_load(a, sh.act_e[act], d - act * nrb, threadIdx.x & 15, pre);
+      dn_task<TT>(a, sh, act, sh.act_e[act], sh.act_m[act], d - act * nrb, pre);
+    }
   }
 
-  // 4. down tasks
-  for (int d = b; d < n_dn; d += G) {
-    dn_task(a, sh, d, dl, dn_pre);
-    dn_pre = false;
-  }
-
-  // the last workgroup to finish publishes this call's epoch for the next call (every
-  // workgroup read the old one before taking its ticket)
+  // 7. the last workgroup to finish publishes this call's tag for the next call (every
+  // workgroup read the old one before taking its ticket): eight group counters, then one
   __syncthreads();
-  if (tid == 0 && ticket(&a.ctrl->d_done) == G - 1) {
-    st_agent(&a.ctrl->d_done, 0);
-    st_agent(&a.ctrl->d_epoch, s_epoch);
+  if (tid == 0) {
+    const int grp = b % 8, n_g = G / 8 + (grp < G % 8 ? 1 : 0);
+    int *cg = a.endctr + (1 + grp) * kCtrStride;
+    if (ticket(cg) == n_g - 1) {
+      st_agent(cg, 0);
+      if (ticket(a.endctr) == min(G, 8) - 1) {
+        st_agent(a.endctr, 0);
+        st_agent(&a.ctrl->d_epoch, s_epoch);
+      }
+    }
   }
+}
+
+template <int TT>
+int capacity_of(int n_cu) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode<TT>, kDecThreads, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  return per_cu * n_cu;
 }
 
 }  // namespace
 
-int decode_grid(const DecodeArgs &a, int n_cu) {
-  const int n_gu = (a.k + 1) * (a.I / kGuTask), n_dn = a.H / kDnRows;
-  int want = a.E;
-  want = want > n_gu ? want : n_gu;
-  want = want > n_dn ? want : n_dn;
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode, kDecThreads, 0) != hipSuccess || per_cu < 1)
-    per_cu = 1;
-  const int cap = per_cu * n_cu;
-  return want < cap ? want : cap;
+DecodeLayout decode_layout(int H, int E, int k, int I, int t_max) {
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  DecodeLayout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = al(o + bytes);
+    return at;
+  };
+  const size_t T = (size_t)t_max, K1 = (size_t)k + 1;
+  if (t_max <= 1) {  // the one-token kernel: logit and h records and the end counters only
+    L.lrec = take((size_t)E * 3 * 8);
+    L.hrec1 = take(K1 * I * 8);
+    L.endctr = take(9 * kCtrStride * 4);
+    L.total = o;
+    return L;
+  }
+  L.lrec = take(T * E * 3 * 8);
+  L.srec = take(kSrecRep * T * 2 * k * 8);
+  L.hflag = take((std::min<size_t>(T * k, E) + 1) * (I / kDecGuTask) * 8);
+  L.hval = take(T * K1 * I * 4);
+  L.hrec1 = take(K1 * I * 8);
+  L.part = take(T * K1 * H * 4);
+  L.rbctr = take(T * (H / kDecDnTask) * kCtrStride * 4);
+  L.endctr = take(9 * kCtrStride * 4);
+  L.total = o;
+  return L;
+}
+
+int decode_capacity(int t_max, int n_cu) {
+  if (t_max <= 2) return capacity_of<2>(n_cu);
+  if (t_max <= 4) return capacity_of<4>(n_cu);
+  return capacity_of<8>(n_cu);
+}
+
+int decode_grid(const DecodeArgs &a, int capacity) {
+  const int act_max = std::min(a.T * a.k, a.E) + 1;
+  int want = (a.E + 3) / 4;
+  want = std::max(want, act_max * (a.I / kDecGuTask));
+  want = std::max(want, act_max * (a.H / kDecDnTask));
+  want = std::max(want, a.T);
+  return std::min(want, capacity);
 }
 
 hipError_t launch_decode(const DecodeArgs &a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(k_decode, dim3(grid), dim3(kDecThreads), 0, s, a);
+  if (a.T <= 2)
+    hipLaunchKernelGGL(k_decode<2>, dim3(grid), dim3(kDecThreads), 0, s, a);
+  else if (a.T <= 4)
+    hipLaunchKernelGGL(k_decode<4>, dim3(grid), dim3(kDecThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_decode<8>, dim3(grid), dim3(kDecThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -1,0 +1,740 @@
+// Decode form for one token in a single launch: router logits, top-k selection, the
+// gate/up GEMVs with SwiGLU and the down GEMVs with the gate-weighted combine.  (Batches
+// of 2..8 tokens run the union-of-experts kernel in decode.hip.)
+//
+// "Optimizing on-device inference for Apple Silicon", section "Decode > Optimize the
+// one-row weight path": a group of lanes shares one output row, each lane reading a
+// different part of the packed weight row.  Section "Decode > Reduce intermediate and
+// state traffic": the two input projections and the gated activation are one step; the
+// output projection, the routing weights and the shared expert's result are another.
+// Section "Decode > Keep every decode step on the GPU": the token's whole layer runs
+// without the host.
+//
+// Batch-1 decode moves every active weight byte once, so the layer is bound by HBM reads
+// and by the latency of its dependency chain (logits -> selection -> gate/up -> down).
+// One launch covers the chain.  Workgroups hand results to each other as tagged
+// records: an 8-byte word holding a 32-bit value and the call's 32-bit epoch, written
+// with one device-scope store and read with device-scope loads, so a reader accepts a
+// value exactly when its tag is this call's epoch; no wait uses a counter or an atomic
+// read-modify-write (those serialise on one address).  The epoch lives in the
+// workspace: every workgroup reads the last call's epoch at its start and uses the next
+// one; the last workgroup to finish stores it back (two-level tickets: eight group
+// counters, then one, each on its own 256-byte line -- one counter for every workgroup
+// measured about 3 us per launch).  The launch arguments are therefore the same for
+// every call, so a sequence of calls can be captured once in a HIP graph and replayed.
+#include <type_traits>
+
+#include "common.hpp"
+#include "kernels.hpp"
+#include "select64.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kDecThreads = 256;        // four waves
+constexpr int kGuRows = 4;              // gate/up rows per wave in one task
+constexpr int kGuTask = 4 * kGuRows;    // rows of one gate/up task
+static_assert(kGuRows == 4 && kGuTask % 4 == 0 && kQpRows % 4 == 0, "a wave reads its rows' scale/bias of one group as one 8-byte run");
+constexpr int kDnRows = 8;              // output rows of one down task
+constexpr int kDnUnits = 5;             // (row, slot) units per 16-lane group per round
+constexpr int kDnSlots = 10;            // slots per down round: 8 rows x 10 = 16 groups x 5
+constexpr int kHStage = 5120;           // h floats staged in LDS per down round
+constexpr int kSpins = 1 << 20;         // polls before a wait gives up (about a second)
+
+// This call's record tag (set by thread 0 at the start of k_decode).
+__shared__ uint32_t s_epoch;
+
+__device__ __forceinline__ QMat expert_mat(const QMat &routed, const QMat &shared, int e, int E, int N, int K) {
+  if (e == E) return shared;
+  QMat m;
+  m.q = routed.q + (size_t)e * N * (K / 8);
+  m.s = routed.s + (size_t)e * N * (K / 64);
+  m.b = routed.b + (size_t)e * N * (K / 64);
+  return m;
+}
+
+// sum_i v[i] * code_i over the 32 codes of four packed words
+__device__ __forceinline__ float dot_codes32(const uint4 &w, const float (&v)[32]) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  float s = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t lo = ws[q] & 0x0f0f0f0fu, hi = (ws[q] >> 4) & 0x0f0f0f0fu;
+    asm("" : "+v"(lo), "+v"(hi));  // one v_cvt_f32_ubyteN per code
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s = __builtin_fmaf(v[8 * q + 2 * j], (float)((lo >> (8 * j)) & 0xffu), s);
+      s = __builtin_fmaf(v[8 * q + 2 * j + 1], (float)((hi >> (8 * j)) & 0xffu), s);
+    }
+  }
+  return s;
+}
+
+__device__ __forceinline__ uint64_t tagged(uint32_t epoch, uint32_t v) { return ((uint64_t)epoch << 32) | v; }
+__device__ __forceinline__ uint32_t tag_of(uint64_t r) { return (uint32_t)(r >> 32); }
+
+struct DecShared {
+  Sel64 S;
+  uint32_t cand[kDecThreads / kWave][kMaxTopK];  // each wave's top-k keys
+  int wcnt[kDecThreads / kWave];
+  float wf[kDecThreads / kWave];
+  double red[2][4];
+  int ids[kMaxTopK];
+  float gates[kMaxTopK];
+  int fast;  // select_topk: the one-wave selection was certified
+  float unit[kDnRows * kDnSlots];
+  __attribute__((aligned(16))) float h[kHStage];
+};
+
+// ------------------------------------------------------------------ router (binary64)
+
+// Additions on any path of router_logit's sum: 8 per 2048 elements per lane, a 6-level
+// butterfly, 3 across the four waves.
+__device__ __forceinline__ int router_depth(int H) { return 8 * ((H + 2047) / 2048) + 9; }
+
+// Binary64 logit of expert e (exact products, summed lane-sequentially, then over the
+// wave, then over the four waves in order) and sum |x w|, in every thread.
+__device__ void router_logit(const DecodeArgs &a, DecShared &sh, int e, double &l, double &ab) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, H = a.H;
+  double s = 0.0, sa = 0.0;
+  for (int c = tid; c < H / 8; c += kDecThreads) {
+    const uint4 xv = *(const uint4 *)(a.x + 8 * c);
+    const float xf[8] = {bf16_lo(xv.x), bf16_hi(xv.x), bf16_lo(xv.y), bf16_hi(xv.y),
+                         bf16_lo(xv.z), bf16_hi(xv.z), bf16_lo(xv.w), bf16_hi(xv.w)};
+    float wf[8];
+    if (a.wr16) {
+      const uint4 wv4 = *(const uint4 *)(a.wr16 + (size_t)e * H + 8 * c);
+      wf[0] = bf16_lo(wv4.x); wf[1] = bf16_hi(wv4.x); wf[2] = bf16_lo(wv4.y); wf[3] = bf16_hi(wv4.y);
+      wf[4] = bf16_lo(wv4.z); wf[5] = bf16_hi(wv4.z); wf[6] = bf16_lo(wv4.w); wf[7] = bf16_hi(wv4.w);
+    } else {
+      const float4 w0 = *(const float4 *)(a.wr32 + (size_t)e * H + 8 * c);
+      const float4 w1 = *(const float4 *)(a.wr32 + (size_t)e * H + 8 * c + 4);
+      wf[0] = w0.x; wf[1] = w0.y; wf[2] = w0.z; wf[3] = w0.w;
+      wf[4] = w1.x; wf[5] = w1.y; wf[6] = w1.z; wf[7] = w1.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const double p = (double)xf[i] * (double)wf[i];  // exact
+      s += p;
+      sa += fabs(p);
+    }
+  }
+  s = wave_sum_f64(s);
+  sa = wave_sum_f64(sa);
+  if (lane == 0) {
+    sh.red[0][wv] = s;
+    sh.red[1][wv] = sa;
+  }
+  __syncthreads();
+  l = ((sh.red[0][0] + sh.red[0][1]) + sh.red[0][2]) + sh.red[0][3];
+  ab = ((sh.red[1][0] + sh.red[1][1]) + sh.red[1][2]) + sh.red[1][3];
+  if (a.bias) l += (double)a.bias[e];
+  __syncthreads();
+}
+
+// Wait for expert e's three logit records of this call.
+__device__ void read_logit(const DecodeArgs &a, int e, double &v, double &r) {
+  const uint64_t *rec = a.lrec + 3 * (size_t)e;
+  for (int i = 0;; ++i) {
+    const uint64_t r0 = ld_agent(&rec[0]), r1 = ld_agent(&rec[1]), r2 = ld_agent(&rec[2]);
+    if (tag_of(r0) == s_epoch && tag_of(r1) == s_epoch && tag_of(r2) == s_epoch) {
+      v = __longlong_as_double((long long)(((uint64_t)(uint32_t)r1 << 32) | (uint32_t)r0));
+      r = (double)__uint_as_float((uint32_t)r2);
+      return;
+    }
+    if (i == kSpins) {
+      st_agent(&a.ctrl->d_err, 1);
+      v = -INFINITY;
+      r = 0.0;
+      return;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+__device__ double block_min_f64(double v, DecShared &sh) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) v = fmin(v, __shfl_xor(v, o));
+  if ((threadIdx.x & 63) == 0) sh.red[0][threadIdx.x >> 6] = v;
+  __syncthreads();
+  v = fmin(fmin(sh.red[0][0], sh.red[0][1]), fmin(sh.red[0][2], sh.red[0][3]));
+  __syncthreads();
+  return v;
+}
+
+__device__ double block_max_f64(double v, DecShared &sh) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) v = fmax(v, __shfl_xor(v, o));
+  if ((threadIdx.x & 63) == 0) sh.red[0][threadIdx.x >> 6] = v;
+  __syncthreads();
+  v = fmax(fmax(sh.red[0][0], sh.red[0][1]), fmax(sh.red[0][2], sh.red[0][3]));
+  __syncthreads();
+  return v;
+}
+
+// DPP row maxima / minima (16 lanes), then the four row results through scalar registers:
+// the wave-wide result in every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, false));  // row_ror:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false));  // row_ror:8
+  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+  return max(a, b);
+}
+
+template <int C>
+__device__ __forceinline__ double dpp_d(double x) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, C, 0xf, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), C, 0xf, 0xf, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ double readlane_d(double x, int l) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// wave minimum of mn and maximum of mx together
+__device__ __forceinline__ void wave_minmax_f64(double &mn, double &mx) {
+  mn = fmin(mn, dpp_d<0xB1>(mn)); mx = fmax(mx, dpp_d<0xB1>(mx));
+  mn = fmin(mn, dpp_d<0x4E>(mn)); mx = fmax(mx, dpp_d<0x4E>(mx));
+  mn = fmin(mn, dpp_d<0x124>(mn)); mx = fmax(mx, dpp_d<0x124>(mx));
+  mn = fmin(mn, dpp_d<0x128>(mn)); mx = fmax(mx, dpp_d<0x128>(mx));
+  mn = fmin(fmin(readlane_d(mn, 0), readlane_d(mn, 16)), fmin(readlane_d(mn, 32), readlane_d(mn, 48)));
+  mx = fmax(fmax(readlane_d(mx, 0), readlane_d(mx, 16)), fmax(readlane_d(mx, 32), readlane_d(mx, 48)));
+}
+
+// Order-preserving 32-bit key of a logit of expert e: the fp32 value's ordered bits with
+// the low 8 replaced by the complemented index, so the largest key is the largest logit,
+// ties (and logits equal in their top 24 bits) to the lower index.  The truncation only
+// changes the choice between logits much closer than 2^-15 relative; the certificate
+// below, on the binary64 values and radii, catches any such choice.
+__device__ __forceinline__ uint32_t logit_key(double v, int e) {
+  const uint32_t b = __float_as_uint((float)v);
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return (ord & 0xffffff00u) | (uint32_t)(255 - e);
+}
+
+// Top-k of the E logits by one wave (four experts per lane): the keys of select_topk,
+// k rounds of a wave maximum, the same certificate (every chosen logit minus its radius
+// above every other logit plus its radius); ids ascending and softmax gates into sh.ids,
+// sh.gates.  The lane's twelve records are loaded together and re-polled together.
+// Returns false, having written nothing, when the certificate fails.
+__device__ bool select_topk_wave(const DecodeArgs &a, DecShared &sh, bool write_debug) {
+  constexpr int NV = kMaxExperts / kWave;
+  const int lane = threadIdx.x & 63, E = a.E, k = a.k;
+  double v[NV], r[NV];
+  bool valid[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) valid[i] = lane + kWave * i < E;
+  uint64_t rec[NV][3];
+  for (int it = 0;; ++it) {
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int j = 0; j < 3; ++j) rec[i][j] = valid[i] ? ld_agent(&a.lrec[3 * (size_t)(lane + kWave * i) + j]) : 0u;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int j = 0; j < 3; ++j) ok &= !valid[i] || tag_of(rec[i][j]) == s_epoch;
+    if (__ballot(!ok) == 0ull) break;
+    if (it == kSpins) {  // as read_logit: flag the error, missing logits count as -inf
+      st_agent(&a.ctrl->d_err, 1);
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        if (valid[i] && (tag_of(rec[i][0]) != s_epoch || tag_of(rec[i][1]) != s_epoch || tag_of(rec[i][2]) != s_epoch))
+          rec[i][0] = 0u, rec[i][1] = (uint64_t)0xfff00000u, rec[i][2] = 0u;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  uint32_t key[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    v[i] = valid[i] ? __longlong_as_double((long long)(((uint64_t)(uint32_t)rec[i][1] << 32) | (uint32_t)rec[i][0]))
+                    : -INFINITY;
+    r[i] = valid[i] ? (double)__uint_as_float((uint32_t)rec[i][2]) : 0.0;
+    key[i] = valid[i] ? logit_key(v[i], lane + kWave * i) : 0u;
+  }
+  uint32_t chosen = 0;
+  for (int rr = 0; rr < k; ++rr) {
+    uint32_t best = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) best = max(best, key[i]);
+    best = wave_max_u32(best);
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (key[i] == best && best != 0u) key[i] = 0u, chosen |= 1u << i;
+  }
+  double mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    if (!valid[i]) continue;
+    if ((chosen >> i) & 1u)
+      mn = fmin(mn, v[i] - r[i]);
+    else
+      mx = fmax(mx, v[i] + r[i]);
+  }
+  wave_minmax_f64(mn, mx);
+  if (!(mn > mx)) return false;  // false for NaN or an infinite radius as well
+  // softmax of the chosen logits (as fp32), ids ascending
+  float gmax = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    if ((chosen >> i) & 1u) gmax = fmaxf(gmax, (float)v[i]);
+  gmax = wave_max(gmax);
+  float ex[NV], part = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    ex[i] = ((chosen >> i) & 1u) ? __expf((float)v[i] - gmax) : 0.0f;
+    part += ex[i];
+  }
+  const float den = wave_sum(part);
+  int below = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const bool ch = (chosen >> i) & 1u;
+    const uint64_t bal = __ballot(ch);
+    const int pos = below + __popcll(bal & ((1ull << lane) - 1ull));
+    if (ch && pos < kMaxTopK) {
+      const int e = lane + kWave * i;
+      const float g = ex[i] / den;
+      sh.ids[pos] = e;
+      sh.gates[pos] = g;
+      if (write_debug && a.dbg_ids) a.dbg_ids[pos] = e;
+      if (write_debug && a.dbg_gates) a.dbg_gates[pos] = g;
+    }
+    below += __popcll(bal);
+  }
+  return true;
+}
+
+// Top-k of the E logits of this call (value descending, index ascending) into sh.ids
+// (ascending) and sh.gates: select_topk_wave, or when its certificate fails the
+// four-wave path below.  One expert per thread (E <= 256): each wave takes its top k
+// by k rounds of a wave maximum; a chosen candidate is one of the 4k whose rank among
+// them is below k.  The choice is certified against the binary64 error radii; experts
+// closer than their radii are re-ranked by resolve64.
+__device__ void select_topk(const DecodeArgs &a, DecShared &sh, bool write_debug) {
+  if (threadIdx.x < kWave) {
+    const bool ok = select_topk_wave(a, sh, write_debug);
+    if (threadIdx.x == 0) sh.fast = ok;
+  }
+  __syncthreads();
+  if (sh.fast) return;  // uniform
+  Sel64 &S = sh.S;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, E = a.E, k = a.k;
+  const bool mine = tid < E;
+  double v = -INFINITY, r = 0.0;
+  if (mine) {
+    read_logit(a, tid, v, r);
+    S.gl[tid] = v;
+  }
+  uint32_t key = mine ? logit_key(v, tid) : 0u;
+  const uint32_t key0 = key;
+  for (int rr = 0; rr < k; ++rr) {
+    const uint32_t best = wave_max_u32(key);
+    key = key == best ? 0u : key;
+    if (lane == 0) sh.cand[wv][rr] = best;
+  }
+  __syncthreads();
+  {
+    // rank of my key among the 4k wave candidates (keys are distinct)
+    int rank = 0;
+    for (int w2 = 0; w2 < kDecThreads / kWave; ++w2)
+      for (int rr = 0; rr < k; ++rr) rank += sh.cand[w2][rr] > key0 ? 1 : 0;
+    S.chosen[tid] = (mine && key == 0u && rank < k) ? 1 : 0;  // key cleared: one of my wave's k
+  }
+  __syncthreads();
+  const bool sel = mine && S.chosen[tid];
+  // certification: every chosen logit minus its radius above every other plus its radius
+  double mn = sel ? v - r : INFINITY, mx = (mine && !sel) ? v + r : -INFINITY;
+  wave_minmax_f64(mn, mx);
+  if (lane == 0) {
+    sh.red[0][wv] = mn;
+    sh.red[1][wv] = mx;
+  }
+  __syncthreads();
+  mn = fmin(fmin(sh.red[0][0], sh.red[0][1]), fmin(sh.red[0][2], sh.red[0][3]));
+  mx = fmax(fmax(sh.red[1][0], sh.red[1][1]), fmax(sh.red[1][2], sh.red[1][3]));
+  const bool sure_in = sel && v - r > mx;
+  const bool sure_out = mine && !sel && v + r < mn;
+  if (!__syncthreads_and(!mine || sure_in || sure_out)) {
+    if (mine) S.chosen[tid] = sure_in ? 1 : 0;
+    if (tid == 0) S.n = 0;
+    __syncthreads();
+    if (mine && !sure_in && !sure_out) {
+      const int c = atomicAdd(&S.n, 1);
+      S.cand[c] = tid;
+      S.v[c] = v;
+      S.rad[c] = r;
+    }
+    const int nin1 = __syncthreads_count(sure_in);
+    resolve64(S, k - nin1, a.x, a.wr16, a.wr32, a.bias, a.H, tid, kDecThreads);
+  }
+  // ids ascending (rank of each chosen expert = chosen experts below it) and softmax
+  // gates of the chosen logits
+  const bool ch = mine && S.chosen[tid];
+  const float gl = ch ? (float)S.gl[tid] : -INFINITY;
+  const uint64_t bal = __ballot(ch);
+  const uint32_t gb = __float_as_uint(gl);
+  const uint32_t wo = wave_max_u32((gb & 0x80000000u) ? ~gb : (gb | 0x80000000u));  // ordered bits
+  if (lane == 0) {
+    sh.wcnt[wv] = __popcll(bal);
+    sh.wf[wv] = __uint_as_float((wo & 0x80000000u) ? (wo & 0x7fffffffu) : ~wo);
+  }
+  __syncthreads();
+  int below = __popcll(bal & ((1ull << lane) - 1ull));
+  float gmax = -INFINITY;
+  for (int w2 = 0; w2 < kDecThreads / kWave; ++w2) {
+    below += w2 < wv ? sh.wcnt[w2] : 0;
+    gmax = fmaxf(gmax, sh.wf[w2]);
+  }
+  const float ex = ch ? __expf(gl - gmax) : 0.0f;
+  const float ws = wave_sum(ex);
+  __syncthreads();  // every thread has read sh.wf / sh.wcnt
+  if (lane == 0) sh.wf[wv] = ws;
+  __syncthreads();
+  const float den = (sh.wf[0] + sh.wf[1]) + (sh.wf[2] + sh.wf[3]);
+  if (ch && below < kMaxTopK) {
+    const float g = ex / den;
+    sh.ids[below] = tid;
+    sh.gates[below] = g;
+    if (write_debug && a.dbg_ids) a.dbg_ids[below] = tid;
+    if (write_debug && a.dbg_gates) a.dbg_gates[below] = g;
+  }
+  __syncthreads();
+  if (tid < k) sh.ids[tid] = min(max(sh.ids[tid], 0), E - 1);  // keep reads in bounds even after a failed wait
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------ gate/up
+
+// One round of a gate/up task for the calling wave: rows r0..r0+3 of slot j, the
+// 32-element chunk c = lane + 64 p of the H-long rows.
+struct GuLoad {
+  uint4 wg[kGuRows], wu[kGuRows];
+  uint2 sg, bg, su, bu;  // fp16 scale/bias of rows r0..r0+3: row r in half r%2 of word r/2
+  uint4 x[4];
+  bool ok;
+};
+
+__device__ __forceinline__ void gu_issue(const DecodeArgs &a, const QMat &Gm, const QMat &Um, int r0, int c,
+                                         GuLoad &L) {
+  const int H = a.H;
+  L.ok = c < H / 32;
+  const int cc = L.ok ? c : 0;
+#pragma unroll
+  for (int r = 0; r < kGuRows; ++r) {
+    const size_t row = (size_t)(r0 + r);
+    const size_t ci = code_index(row, 4 * cc, H);
+    L.wg[r] = *(const uint4 *)(Gm.q + ci);
+    L.wu[r] = *(const uint4 *)(Um.q + ci);
+  }
+  // r0 is a multiple of 4, so the four rows' values of one group are adjacent (8 bytes)
+  const size_t qi = qp_index((size_t)r0, cc / 2, H / 64);
+  L.sg = *(const uint2 *)(Gm.s + qi);
+  L.bg = *(const uint2 *)(Gm.b + qi);
+  L.su = *(const uint2 *)(Um.s + qi);
+  L.bu = *(const uint2 *)(Um.b + qi);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) L.x[q] = *(const uint4 *)(a.x + 32 * cc + 8 * q);
+}
+
+__device__ __forceinline__ void gu_accumulate(const GuLoad &L, float (&ag)[kGuRows], float (&au)[kGuRows]) {
+  if (!L.ok) return;
+  float xf[32];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t xw[4] = {L.x[q].x, L.x[q].y, L.x[q].z, L.x[q].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xf[8 * q + 2 * i] = bf16_lo(xw[i]);
+      xf[8 * q + 2 * i + 1] = bf16_hi(xw[i]);
+    }
+  }
+  float xs = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) xs += xf[i];
+#pragma unroll
+  for (int r = 0; r < kGuRows; ++r) {
+    auto half = [&](uint2 v) { return fp16_to_f32((uint16_t)(((r >> 1) ? v.y : v.x) >> (16 * (r & 1)))); };
+    ag[r] += half(L.sg) * dot_codes32(L.wg[r], xf) + half(L.bg) * xs;
+    au[r] += half(L.su) * dot_codes32(L.wu[r], xf) + half(L.bu) * xs;
+  }
+}
+
+__device__ __forceinline__ int gu_expert(const DecodeArgs &a, const DecShared &sh, int j) {
+  return j < a.k ? sh.ids[j] : a.E;
+}
+
+__device__ __forceinline__ void gu_start(const DecodeArgs &a, const DecShared &sh, int g, GuLoad &L) {
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tpe = a.I / kGuTask;
+  const int j = g / tpe, r0 = (g - j * tpe) * kGuTask + kGuRows * wv;
+  const int e = gu_expert(a, sh, j);
+  gu_issue(a, expert_mat(a.gate, a.s_gate, e, a.E, a.I, a.H), expert_mat(a.up, a.s_up, e, a.E, a.I, a.H), r0,
+           lane, L);
+}
+
+// Gate/up task g: slot j = g / (I/16), rows i0 .. i0+15 (wave w: i0+4w .. i0+4w+3).
+// `first` holds the already-issued first round.  Publishes this wave's 4 h records.
+__device__ __forceinline__ void gu_task(const DecodeArgs &a, const DecShared &sh, int g, const GuLoad &first) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int I = a.I, H = a.H;
+  const int tpe = I / kGuTask;
+  const int j = g / tpe, r0 = (g - j * tpe) * kGuTask + kGuRows * wv;
+  float ag[kGuRows] = {}, au[kGuRows] = {};
+  gu_accumulate(first, ag, au);
+  const int np = (H / 32 + kWave - 1) / kWave;
+  if (np > 1) {
+    const int e = gu_expert(a, sh, j);
+    const QMat Gm = expert_mat(a.gate, a.s_gate, e, a.E, I, H);
+    const QMat Um = expert_mat(a.up, a.s_up, e, a.E, I, H);
+    for (int p = 1; p < np; ++p) {
+      GuLoad L;
+      gu_issue(a, Gm, Um, r0, lane + kWave * p, L);
+      gu_accumulate(L, ag, au);
+    }
+  }
+  float hv = 0.f;
+#pragma unroll
+  for (int r = 0; r < kGuRows; ++r) {
+    const float gs = wave_sum(ag[r]);
+    const float us = wave_sum(au[r]);
+    if (lane == r) hv = gs / (1.0f + __expf(-gs)) * us;
+  }
+  const size_t row = (size_t)j * I + r0;
+  if (lane < kGuRows) st_agent(&a.hrec1[row + lane], tagged(s_epoch, __float_as_uint(hv)));
+}
+
+// ------------------------------------------------------------------ down
+
+// Units of a down round: u = r * nb + jj (row r of the task, slot j0 + jj).  16-lane
+// group q (lane/16 + 4*wave) takes u = q + 16 m; lane cl = lane % 16 takes the
+// 32-element chunk c = cl + 16 p of the I-long rows.
+struct DnLoad {
+  uint4 w[kDnUnits];
+  uint32_t s[kDnUnits], b[kDnUnits];
+};
+
+__device__ __forceinline__ void dn_issue(const DecodeArgs &a, const DecShared &sh, int n0, int j0, int nb, int c,
+                                         DnLoad &L) {
+  const int I = a.I, k = a.k, q = (threadIdx.x >> 4);
+  const int cc = c < I / 32 ? c : 0;
+#pragma unroll
+  for (int m = 0; m < kDnUnits; ++m) {
+    int u = q + 16 * m;
+    u = u < kDnRows * nb ? u : 0;  // surplus units read unit 0 (result discarded)
+    const int r = u / nb, slot = j0 + (u - r * nb);
+    const int e = slot < k ? sh.ids[slot] : a.E;
+    const QMat D = expert_mat(a.down, a.s_down, e, a.E, a.H, I);
+    const size_t n = (size_t)(n0 + r);
+    L.w[m] = *(const uint4 *)(D.q + code_index(n, 4 * cc, I));
+    const size_t qi = qp_index(n, cc / 2, I / 64);
+    L.s[m] = D.s[qi];
+    L.b[m] = D.b[qi];
+  }
+}
+
+// h of slots j0 .. j0+nb-1 into LDS from their tagged records: each thread issues the
+// loads of up to 16 records at once, then re-reads (one by one) the few whose tag is not
+// yet this call's.
+__device__ __forceinline__ void stage_h(const DecodeArgs &a, DecShared &sh, int j0, int nb) {
+  const int tid = threadIdx.x;
+  const int n = nb * a.I;
+  const uint64_t *rec = a.hrec1 + (size_t)j0 * a.I;
+  constexpr int kBatch = 16;
+  for (int t0 = tid; t0 < n; t0 += kDecThreads * kBatch) {
+    uint64_t rv[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int t = t0 + u * kDecThreads;
+      rv[u] = t < n ? ld_agent(&rec[t]) : tagged(s_epoch, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int t = t0 + u * kDecThreads;
+      if (t >= n) continue;
+      for (int i = 0; tag_of(rv[u]) != s_epoch; ++i) {
+        if (i == kSpins) {
+          st_agent(&a.ctrl->d_err, 1);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        rv[u] = ld_agent(&rec[t]);
+      }
+      sh.h[t] = __uint_as_float((uint32_t)rv[u]);
+    }
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void dn_accumulate(const DecodeArgs &a, DecShared &sh, const DnLoad &L, int nb, int c,
+                                              float (&acc)[kDnUnits]) {
+  const int I = a.I, q = threadIdx.x >> 4;
+  if (c >= I / 32) return;
+#pragma unroll
+  for (int m = 0; m < kDnUnits; ++m) {
+    const int u = q + 16 * m;
+    if (u >= kDnRows * nb) continue;
+    const int jj = u % nb;
+    const float4 *hp = (const float4 *)&sh.h[jj * I + 32 * c];
+    float hv[32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 v = hp[i];
+      hv[4 * i] = v.x;
+      hv[4 * i + 1] = v.y;
+      hv[4 * i + 2] = v.z;
+      hv[4 * i + 3] = v.w;
+    }
+    float hs = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) hs += hv[i];
+    acc[m] += fp16_to_f32((uint16_t)L.s[m]) * dot_codes32(L.w[m], hv) + fp16_to_f32((uint16_t)L.b[m]) * hs;
+  }
+}
+
+// Down task d: output rows n0 = 8d .. 8d+7 over every slot, rounds of nb slots and
+// chunk passes; `pre` (if given) is round 0's first pass, already issued.
+__device__ __forceinline__ void dn_task(const DecodeArgs &a, DecShared &sh, int d, const DnLoad &pre, bool has_pre) {
+  const int tid = threadIdx.x, q = tid >> 4, cl = tid & 15;
+  const int I = a.I, k = a.k, n0 = d * kDnRows;
+  const int nbmax = min(min(k + 1, kDnSlots), kHStage / I);
+  const int npass = (I / 32 + 15) / 16;
+  float out_acc = 0.f;  // thread t < 8: row n0 + t
+  for (int j0 = 0; j0 <= k; j0 += nbmax) {
+    const int nb = min(nbmax, k + 1 - j0);
+    stage_h(a, sh, j0, nb);
+    float acc[kDnUnits] = {};
+    for (int p = 0; p < npass; ++p) {
+      const int c = cl + 16 * p;
+      if (has_pre && j0 == 0 && p == 0) {
+        dn_accumulate(a, sh, pre, nb, c, acc);
+      } else {
+        DnLoad L;
+        dn_issue(a, sh, n0, j0, nb, c, L);
+        dn_accumulate(a, sh, L, nb, c, acc);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < kDnUnits; ++m) {
+      const float v = row16_sum(acc[m]);
+      const int u = q + 16 * m;
+      if (cl == 0 && u < kDnRows * nb) {
+        const int slot = j0 + u % nb;
+        sh.unit[u] = (slot < k ? sh.gates[slot] : 1.0f) * v;
+      }
+    }
+    __syncthreads();
+    if (tid < kDnRows)
+      for (int jj = 0; jj < nb; ++jj) out_acc += sh.unit[tid * nb + jj];
+    __syncthreads();
+  }
+  if (tid < kDnRows) a.out[n0 + tid] = f32_to_bf16(out_acc);
+}
+
+// ------------------------------------------------------------------ the layer
+
+__global__ __launch_bounds__(kDecThreads) void k_decode1(DecodeArgs a) {
+  __shared__ DecShared sh;
+  const int b = blockIdx.x, G = gridDim.x, tid = threadIdx.x;
+  if (tid == 0) {
+    uint32_t ep = ld_agent(&a.ctrl->d_epoch) + 1u;
+    s_epoch = ep ? ep : 1u;
+  }
+  __syncthreads();
+  const int E = a.E, k = a.k;
+  const int n_gu = (k + 1) * (a.I / kGuTask), n_dn = a.H / kDnRows;
+  const int first_shared = k * (a.I / kGuTask);  // gate/up tasks from here on are the shared expert's
+
+  // The shared expert needs no routing: issue its gate/up loads before the router work.
+  GuLoad gl;
+  const bool gu_early = b < n_gu && b >= first_shared;
+  if (gu_early) gu_start(a, sh, b, gl);
+
+  // 1. router logits, published as records
+  for (int e = b; e < E; e += G) {
+    double l, ab;
+    router_logit(a, sh, e, l, ab);
+    if (tid == 0) {
+      const uint64_t lb = (uint64_t)__double_as_longlong(l);
+      const float rad = __double2float_ru(radius64(l, ab, a.H, router_depth(a.H)));
+      uint64_t *rec = a.lrec + 3 * (size_t)e;
+      st_agent(&rec[0], tagged(s_epoch, (uint32_t)lb));
+      st_agent(&rec[1], tagged(s_epoch, (uint32_t)(lb >> 32)));
+      st_agent(&rec[2], tagged(s_epoch, __float_as_uint(rad)));
+    }
+  }
+
+  if (gu_early) gu_task(a, sh, b, gl);
+
+  // 2. the selection, in every workgroup that uses it
+  int g0 = gu_early ? b + G : b;
+  const bool routed_gu = g0 < first_shared;
+  if (routed_gu || b < n_dn || b == 0) select_topk(a, sh, b == 0);
+
+  // 3. routed gate/up tasks; the first down task's loads go out with the first of them
+  DnLoad dl;
+  bool dn_pre = false;
+  const int nbmax = min(min(k + 1, kDnSlots), kHStage / a.I);
+  for (int g = g0; g < n_gu; g += G) {
+    gu_start(a, sh, g, gl);
+    if (!dn_pre && b < n_dn) {
+      dn_issue(a, sh, b * kDnRows, 0, min(nbmax, k + 1), tid & 15, dl);
+      dn_pre = true;
+    }
+    gu_task(a, sh, g, gl);
+  }
+
+  // 4. down tasks
+  for (int d = b; d < n_dn; d += G) {
+    dn_task(a, sh, d, dl, dn_pre);
+    dn_pre = false;
+  }
+
+  // the last workgroup to finish publishes this call's epoch for the next call (every
+  // workgroup read the old one before taking its ticket)
+  __syncthreads();
+  if (tid == 0) {
+    const int grp = b % 8, n_g = G / 8 + (grp < G % 8 ? 1 : 0);
+    int *cg = a.endctr + (1 + grp) * kCtrStride;
+    if (ticket(cg) == n_g - 1) {
+      st_agent(cg, 0);
+      if (ticket(a.endctr) == min(G, 8) - 1) {
+        st_agent(a.endctr, 0);
+        st_agent(&a.ctrl->d_epoch, s_epoch);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+int decode1_capacity(int n_cu) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode1, kDecThreads, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  return per_cu * n_cu;
+}
+
+int decode1_grid(const DecodeArgs &a, int capacity) {
+  const int n_gu = (a.k + 1) * (a.I / kGuTask), n_dn = a.H / kDnRows;
+  int want = a.E;
+  want = want > n_gu ? want : n_gu;
+  want = want > n_dn ? want : n_dn;
+  return want < capacity ? want : capacity;
+}
+
+hipError_t launch_decode1(const DecodeArgs &a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(k_decode1, dim3(grid), dim3(kDecThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -23,7 +23,7 @@ struct QMat {
 constexpr int kMaxTailItems = 1024;  // split gate/up tail items per launch (<= workgroups / 2)
 constexpr int kMaxSplit = 4;         // pieces per split gate/up item
 constexpr int kPartSlots = 256;      // partial-sum slots provided at least (when y is smaller)
-constexpr size_t kStaticScratchBytes = size_t(1) << 20;  // moe_forward_decode_static's device array
+constexpr size_t kStaticScratchBytes = size_t(2) << 20;  // moe_forward_decode_static's device array
 constexpr int kXcds = 8;           // MI355X: 8 accelerator complex dies, one L2 each
 
 // Control words at the start of the workspace.
@@ -95,21 +95,40 @@ struct GemmArgs {
   uint16_t *y;              // down output, gate-weighted, per grouped row [rows][H]
 };
 
+constexpr int kMaxDecodeT = 8;     // tokens of one decode call (a verification batch)
+constexpr int kDecGuTask = 16;     // rows of one decode gate/up task
+constexpr int kDecDnTask = 64;     // output rows of one decode down task
+constexpr int kCtrStride = 64;     // ints between two completion counters (256 bytes)
+
 struct DecodeArgs {
-  const uint16_t *x;        // [H]
+  const uint16_t *x;        // [T][H]
   const uint16_t *wr16;
   const float *wr32;
   const float *bias;
   QMat gate, up, down;      // routed stacked
   QMat s_gate, s_up, s_down;
-  int H, E, k, I;
-  uint64_t *lrec;           // [E][3] tagged records: low and high word of the binary64 logit, radius
-  uint64_t *hrec;           // [(k+1)*I] tagged h values
+  int H, E, k, I, T;
+  uint64_t *lrec;           // [T][E][3] tagged records: low and high word of the binary64 logit, radius
+  uint64_t *srec;           // [T][2k] tagged records: the chosen experts (ascending), then their gates
+  uint64_t *hflag;          // [min(T*k, E) + 1][I/16] tagged: gate/up task (active expert, row block) done
+  float *hval;              // [T][k+1][I] h of every (token, slot); slot k = shared expert
+  uint64_t *hrec1;          // one-token kernel: [(k+1)*I] tagged h values
+  float *part;              // [T][k+1][H] gate-weighted down output of every (token, slot)
+  int *rbctr;               // [T][H/64] arrivals per (token, row block), kCtrStride ints apart
+  int *endctr;              // [9] end-of-call arrivals (8 groups + 1), kCtrStride ints apart
   Ctrl *ctrl;
-  uint16_t *out;            // [H]
-  int32_t *dbg_ids;
+  uint16_t *out;            // [T][H]
+  int32_t *dbg_ids;         // [T][k]
   float *dbg_gates;
 };
+
+// Decode workspace regions, in bytes, for T <= t_max tokens (offsets from a 256-byte
+// aligned base; each region 256-byte aligned).  t_max = 1: only the regions of the
+// one-token kernel (lrec, hrec1, endctr; the other offsets are 0 and unused).
+struct DecodeLayout {
+  size_t lrec, srec, hflag, hval, hrec1, part, rbctr, endctr, total;
+};
+DecodeLayout decode_layout(int H, int E, int k, int I, int t_max);
 
 hipError_t launch_route(const RouteArgs &a, hipStream_t s);
 hipError_t launch_group(const GroupArgs &a, hipStream_t s);
@@ -117,8 +136,15 @@ hipError_t launch_gemm_gateup(const GemmArgs &a, int n_blocks, hipStream_t s);
 hipError_t launch_gemm_down(const GemmArgs &a, int n_blocks, hipStream_t s);
 hipError_t launch_finalize(const uint16_t *y, const int32_t *slot_row, uint16_t *out, int T, int H, int k,
                            hipStream_t s);
-int decode_grid(const DecodeArgs &a, int n_cu);  // workgroups of the decode launch
+// Workgroups that may be resident at once for the decode kernel of up to t_max tokens
+// (all of its workgroups wait for each other, so its grid never exceeds this).
+int decode_capacity(int t_max, int n_cu);
+int decode_grid(const DecodeArgs &a, int capacity);  // workgroups of one decode launch
 hipError_t launch_decode(const DecodeArgs &a, int grid, hipStream_t s);
+// The one-token kernel (decode1.hip): logits, selection and h as tagged records.
+int decode1_capacity(int n_cu);
+int decode1_grid(const DecodeArgs &a, int capacity);
+hipError_t launch_decode1(const DecodeArgs &a, int grid, hipStream_t s);
 hipError_t launch_ctrl_init(Ctrl *c, void *clear, size_t clear_bytes, hipStream_t s);
 hipError_t launch_pack_qparams(const uint16_t *src, uint16_t *dst, int64_t rows, int G, hipStream_t s);
 hipError_t launch_pack_codes(const uint32_t *src, uint32_t *dst, int64_t rows, int K, hipStream_t s);

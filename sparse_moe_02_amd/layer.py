@@ -138,6 +138,17 @@ class MoeLayer:
                              self.stream(), dbg)
         return (out, d) if debug else out
 
+    def decode_batch(self, x: torch.Tensor, out: torch.Tensor | None = None, debug: bool = False, events=None):
+        """x: bf16 [T][H] on the device, 1 <= T <= 8 (one launch for the T rows)."""
+        assert x.dtype == torch.bfloat16 and x.is_contiguous() and x.dim() == 2 and x.shape[1] == self.H
+        T = x.shape[0]
+        if out is None:
+            out = torch.empty_like(x)
+        dbg, d = self._debug(T, True, events, debug) if (debug or events is not None) else (None, None)
+        B.moe_forward_decode_batch(self.plan, x.data_ptr(), T, out.data_ptr(), self.ws.data_ptr(), self.ws_bytes,
+                                   self.stream(), dbg)
+        return (out, d) if debug else out
+
     def decode_error(self) -> int:
         """moe_workspace_check: 0 (MOE_OK) if every decode call so far completed its internal
         hand-offs, else MOE_ERR_WAIT; waits for the stream."""

@@ -383,6 +383,52 @@ def test_decode_with_router_bias():
     m.close()
 
 
+@pytest.mark.parametrize("cfg,layer_i,Ts", [(1, 9, (2, 3, 5, 8)), (3, 0, (8,)), (0, 0, (8,)), (14, 0, (7,)),
+                                             (11, 0, (3,))])
+def test_decode_batch(cfg, layer_i, Ts):
+    """moe_forward_decode_batch (T rows, one launch, each active expert read once): ids of
+    every row bit-exact against the oracle, gates close, outputs in tolerance, and every
+    row bitwise equal to the same row in a two-row batch (the per-row arithmetic does not
+    depend on the batch).
+    Shapes: the benchmark layer, its skewed-bias variant, the tiny layer (E = 16, k = 2),
+    E = 42 bf16 router, and the largest sizes (I = 4096: h staged in two LDS rounds)."""
+    import torch
+
+    from sparse_moe_02_amd.layer import MoeLayer, bf16_bits, bf16_tensor
+
+    sh = synth.shape_of(cfg)
+    L = synth.make_layer(cfg, layer_i)
+    xall = synth.make_x(cfg, layer_i, rows=slice(0, min(sh.T, 8))) if sh.T >= 8 else None
+    if xall is None:  # shapes with fewer tokens: tile them
+        x0 = synth.make_x(cfg, layer_i)
+        xall = np.concatenate([x0] * (8 // x0.shape[0] + 1))[:8]
+    m = MoeLayer(L, top_k=sh.k, max_chunk_tokens=1)
+    # row t alone in a two-row batch (with row (t+1) % 8 beside it)
+    single = [bf16_bits(m.decode_batch(bf16_tensor(xall[[t, (t + 1) % 8]], "cuda:0")))[0] for t in range(8)]
+    for T in Ts:
+        x = xall[:T]
+        say(f"[{sh.name}/batch] T={T}")
+        out, d = m.decode_batch(bf16_tensor(x, "cuda:0"), debug=True)
+        torch.cuda.synchronize()
+        r = oracle.route(x, L.router_w, L.router_b, sh.k)
+        assert np.array_equal(d["topk_ids"].cpu().numpy(), r["ids"]), f"T={T}: ids differ"
+        assert np.max(np.abs(d["gates"].cpu().numpy() - r["gates"])) <= GATE_TOL
+        got = bf16_bits(out)
+        for t in range(T):
+            assert np.array_equal(got[t], single[t]), f"T={T}: row {t} differs from the same row in a 2-row batch"
+        ref = oracle.experts(x, L, r["ids"], r["gates"])
+        _check_out(f"{sh.name}/batch{T}", to_f64(got), ref)
+    # a batch of one repeated row: every row the same; and close to the one-token decode
+    xr = np.repeat(xall[:1], 4, axis=0)
+    got = bf16_bits(m.decode_batch(bf16_tensor(xr, "cuda:0")))
+    one = bf16_bits(m.decode(bf16_tensor(xall[0], "cuda:0")))
+    torch.cuda.synchronize()
+    assert all(np.array_equal(got[t], single[0]) for t in range(4))
+    assert rel_err(to_f64(got[:1]), to_f64(one[None])) <= TOL
+    assert m.decode_error() == 0
+    m.close()
+
+
 @pytest.mark.parametrize("flags,name", [(1, "force-bm32"), (5, "force-bm160"), (64, "host-routing")])
 def test_prefill_flag_variants(flags, name):
     """The ablation configurations reach the same result: fixed 32- and 160-row M-blocks
