@@ -55,13 +55,13 @@ def lib() -> ctypes.CDLL:
             L.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
             L.oracle_max_threads.restype = ctypes.c_int
             L.oracle_dequant.restype = None
-            L.oracle_dequant.argtypes = [P, P, P, I64, I64, P]
+            L.oracle_dequant.argtypes = [P, P, P, I64, I64, ctypes.c_int, P]
             L.oracle_route.restype = ctypes.c_int
             L.oracle_route.argtypes = [P, I64, I64, I64, I64, P, ctypes.c_int, P, P, P, P, P]
             L.oracle_group.restype = ctypes.c_int
             L.oracle_group.argtypes = [P, I64, I64, I64, P, P, P, P]
             L.oracle_experts.restype = ctypes.c_int
-            L.oracle_experts.argtypes = [P, I64, I64, I64, I64, I64, P, P] + [P] * 9 + [P]
+            L.oracle_experts.argtypes = [P, I64, I64, I64, I64, I64, P, P] + [P] * 9 + [ctypes.c_int, P, P]
             _lib = L
     return _lib
 
@@ -86,15 +86,26 @@ def bf16_to_double(bits: int) -> float:
     return lib().oracle_bf16_to_double(int(bits))
 
 
+def _qparam_bits(a):
+    """Scale/bias arrays: float16 values, or bf16 bit patterns as uint16.  Returns
+    (uint16 bits, is_bf16)."""
+    if a.dtype == np.float16:
+        return _c(a, np.float16).view(np.uint16), False
+    assert a.dtype == np.uint16, "scale/bias: float16 values or bf16 bits (uint16)"
+    return _c(a, np.uint16), True
+
+
 def dequant(q, scale, bias) -> np.ndarray:
-    """Dequantise one matrix: q uint32 [N][K/8], scale/bias float16 [N][K/64] -> float64 [N][K]."""
+    """Dequantise one matrix: q uint32 [N][K/8], scale/bias [N][K/64] (float16, or bf16 bits
+    as uint16) -> float64 [N][K]."""
     q = _c(q, np.uint32)
-    s = _c(scale, np.float16).view(np.uint16)
-    b = _c(bias, np.float16).view(np.uint16)
+    s, sbf = _qparam_bits(scale)
+    b, bbf = _qparam_bits(bias)
+    assert sbf == bbf
     N, K = q.shape[0], q.shape[1] * 8
     assert s.shape == (N, K // 64) and b.shape == (N, K // 64)
     w = np.empty((N, K), np.float64)
-    lib().oracle_dequant(_p(q), _p(s), _p(b), N, K, _p(w))
+    lib().oracle_dequant(_p(q), _p(s), _p(b), N, K, int(sbf), _p(w))
     return w
 
 
@@ -141,13 +152,20 @@ def experts(x_bits, layer, ids, gates) -> np.ndarray:
     k = ids.shape[1]
     E = layer.gate_q.shape[0] - 1
     I = layer.gate_q.shape[1]
-    arrs = []
+    arrs, kinds = [], set()
     for nm in ("gate", "up", "down"):
         arrs.append(_c(getattr(layer, nm + "_q"), np.uint32))
-        arrs.append(_c(getattr(layer, nm + "_s"), np.float16).view(np.uint16))
-        arrs.append(_c(getattr(layer, nm + "_b"), np.float16).view(np.uint16))
+        for part in ("_s", "_b"):
+            bits, is_bf = _qparam_bits(getattr(layer, nm + part))
+            arrs.append(bits)
+            kinds.add(is_bf)
+    assert len(kinds) == 1, "all scale/bias arrays of a layer share one dtype"
+    sg = getattr(layer, "shared_gate", None)
+    sg = None if sg is None else _c(sg, np.uint16)
+    assert sg is None or sg.shape == (H,)
     out = np.empty((T, H), np.float64)
-    rc = lib().oracle_experts(_p(x), T, H, I, E, k, _p(ids), _p(gates), *[_p(a) for a in arrs], _p(out))
+    rc = lib().oracle_experts(_p(x), T, H, I, E, k, _p(ids), _p(gates), *[_p(a) for a in arrs], int(kinds.pop()),
+                              _p(sg), _p(out))
     if rc != 0:
         raise ValueError(f"oracle_experts failed ({rc})")
     return out

@@ -31,7 +31,13 @@
  *   - activation: SwiGLU, h = silu(gate) * up with silu(a) = a / (1 + exp(-a));
  *   - the shared expert is added with weight 1;
  *   - quantised layout: W[N][K], code of element k in bits 4*(k%8) of word
- *     q[n][k/8]; scale/bias are IEEE binary16, one pair per 64 consecutive k.
+ *     q[n][k/8]; one scale/bias pair per 64 consecutive k, IEEE binary16 or
+ *     bfloat16 (the pages' checkpoint stores them as bf16; the same section);
+ *   - the shared expert's output is added with weight 1, or, when a gate vector
+ *     w_sg [H] (bf16) is given, with weight sigmoid(x_t . w_sg) (section
+ *     "Decode > Reduce intermediate and state traffic" fuses the shared
+ *     expert's result into the output projection; a learned scalar gate on it
+ *     is the optional form).
  *
  * Shapes: T tokens, H hidden, E routed experts, k chosen per token, I the
  * intermediate size.  Expert matrices are stacked over E+1 experts with the
@@ -78,16 +84,21 @@ static inline int code_at(const uint32_t *row_words, int64_t k) {
   return (int)((row_words[k >> 3] >> (4 * (k & 7))) & 0xfu);
 }
 
-/* w[n][k] = scale[n][k/64] * code(n,k) + bias[n][k/64], exact in binary64. */
+static double qparam_to_double(uint16_t v, int qbf16) {
+  return qbf16 ? oracle_bf16_to_double(v) : oracle_fp16_to_double(v);
+}
+
+/* w[n][k] = scale[n][k/64] * code(n,k) + bias[n][k/64], exact in binary64.  scale and
+ * bias are binary16 bit patterns (qbf16 == 0) or bfloat16 ones (qbf16 != 0). */
 void oracle_dequant(const uint32_t *q, const uint16_t *scale, const uint16_t *bias,
-                    int64_t N, int64_t K, double *w) {
+                    int64_t N, int64_t K, int qbf16, double *w) {
   const int64_t G = K / 64;
 #pragma omp parallel for schedule(static)
   for (int64_t n = 0; n < N; ++n) {
     const uint32_t *qr = q + n * (K / 8);
     for (int64_t g = 0; g < G; ++g) {
-      const double s = oracle_fp16_to_double(scale[n * G + g]);
-      const double b = oracle_fp16_to_double(bias[n * G + g]);
+      const double s = qparam_to_double(scale[n * G + g], qbf16);
+      const double b = qparam_to_double(bias[n * G + g], qbf16);
       for (int64_t k = g * 64; k < g * 64 + 64; ++k) w[n * K + k] = s * (double)code_at(qr, k) + b;
     }
   }
@@ -198,8 +209,10 @@ int oracle_group(const int32_t *ids, int64_t T, int64_t E, int64_t k, int32_t *c
 }
 
 /* Experts and combine:
- *   out[t] = sum_{j<k} gates[t][j] * FFN_{ids[t][j]}(x_t) + FFN_E(x_t)
+ *   out[t] = sum_{j<k} gates[t][j] * FFN_{ids[t][j]}(x_t) + c_t * FFN_E(x_t)
  *   FFN_e(v) = Wd_e * (silu(Wg_e v) .* (Wu_e v))
+ *   c_t = 1, or sigmoid(sum_h x[t][h] * w_sg[h]) (ascending h, binary64) when
+ *   shared_gate (bf16 [H]) is not NULL
  * Contributions are added to out[t] in ascending expert index, shared last.
  *   gate_q/up_q [E+1][I][H/8], gate_s/.. [E+1][I][H/64]
  *   down_q [E+1][H][I/8], down_s/.. [E+1][H][I/64]
@@ -208,7 +221,8 @@ int oracle_experts(const uint16_t *x, int64_t T, int64_t H, int64_t I, int64_t E
                    const int32_t *ids, const double *gates, const uint32_t *gate_q,
                    const uint16_t *gate_s, const uint16_t *gate_b, const uint32_t *up_q,
                    const uint16_t *up_s, const uint16_t *up_b, const uint32_t *down_q,
-                   const uint16_t *down_s, const uint16_t *down_b, double *out) {
+                   const uint16_t *down_s, const uint16_t *down_b, int qbf16,
+                   const uint16_t *shared_gate, double *out) {
   if (T < 0 || H <= 0 || I <= 0 || H % 64 || I % 64 || E <= 0 || k <= 0 || k > E) return -1;
   double *wg = (double *)malloc(sizeof(double) * I * H);
   double *wu = (double *)malloc(sizeof(double) * I * H);
@@ -226,6 +240,12 @@ int oracle_experts(const uint16_t *x, int64_t T, int64_t H, int64_t I, int64_t E
       if (e == E) {
         tok[n] = t;
         g[n] = 1.0;
+        if (shared_gate) {
+          double z = 0.0;
+          for (int64_t h = 0; h < H; ++h)
+            z += oracle_bf16_to_double(x[t * H + h]) * oracle_bf16_to_double(shared_gate[h]);
+          g[n] = 1.0 / (1.0 + exp(-z));
+        }
         ++n;
         continue;
       }
@@ -237,9 +257,10 @@ int oracle_experts(const uint16_t *x, int64_t T, int64_t H, int64_t I, int64_t E
         }
     }
     if (n == 0) continue;
-    oracle_dequant(gate_q + e * I * (H / 8), gate_s + e * I * (H / 64), gate_b + e * I * (H / 64), I, H, wg);
-    oracle_dequant(up_q + e * I * (H / 8), up_s + e * I * (H / 64), up_b + e * I * (H / 64), I, H, wu);
-    oracle_dequant(down_q + e * H * (I / 8), down_s + e * H * (I / 64), down_b + e * H * (I / 64), H, I, wd);
+    oracle_dequant(gate_q + e * I * (H / 8), gate_s + e * I * (H / 64), gate_b + e * I * (H / 64), I, H, qbf16, wg);
+    oracle_dequant(up_q + e * I * (H / 8), up_s + e * I * (H / 64), up_b + e * I * (H / 64), I, H, qbf16, wu);
+    oracle_dequant(down_q + e * H * (I / 8), down_s + e * H * (I / 64), down_b + e * H * (I / 64), H, I, qbf16,
+                   wd);
 #pragma omp parallel
     {
       double *xd = (double *)malloc(sizeof(double) * H);

@@ -28,6 +28,7 @@ TID_ROUTER_W = 0
 TID_ROUTER_B = 1
 TID_X = 2
 TID_EXPERT0 = 3  # expert e, matrix m (0 gate, 1 up, 2 down) -> 3 + 3*e + m
+TID_SHARED_GATE = 1 << 20
 
 X_BLOCK_ROWS = 4096
 
@@ -43,6 +44,8 @@ class MoeShape:
     router_fp32: bool  # router weight stored as float32 (else bf16)
     zipf_bias: bool   # add the skewed per-expert router bias
     layers: int = 1   # distinct weight sets (decode sweeps them back to back)
+    qparam_bf16: bool = False  # scale/bias stored as bf16 (else float16)
+    shared_gate: bool = False  # a learned gate vector on the shared expert
     chunk: int = 4096  # prefill chunk size used for this workload
     weights_cfg: int = -1  # config whose weight/x streams are reused (-1: own)
     x_cfg: int = -1
@@ -74,6 +77,12 @@ CONFIGS = {
     # a bf16 router whose expert count is not a multiple of 4 (scalar logit reads in the
     # selection, a partial 64-expert logits tile), over ragged 24-token chunks
     14: MoeShape("e42-bf16", T=50, H=512, E=42, k=6, I=256, router_fp32=False, zipf_bias=False, chunk=24),
+    # the pages' checkpoint format: bf16 scale/bias, and a sigmoid-gated shared expert;
+    # a small shape and the benchmark shape (512 tokens)
+    15: MoeShape("bf16-qparams-small", T=40, H=512, E=32, k=4, I=256, router_fp32=False, zipf_bias=False,
+                 chunk=16, qparam_bf16=True, shared_gate=True),
+    16: MoeShape("bf16-qparams", T=512, H=2048, E=256, k=8, I=512, router_fp32=False, zipf_bias=False,
+                 chunk=512, qparam_bf16=True, shared_gate=True),
 }
 
 
@@ -112,16 +121,24 @@ class LayerWeights:
     down_q: np.ndarray              # [E+1][H][I/8] uint32
     down_s: np.ndarray              # [E+1][H][I/64] float16
     down_b: np.ndarray
+    shared_gate: Optional[np.ndarray] = None  # [H] uint16 (bf16) or None
 
     def nbytes(self) -> int:
         return sum(getattr(self, f.name).nbytes for f in dataclasses.fields(self)
                    if getattr(self, f.name) is not None)
 
 
-def _quant_matrix(rng: np.random.Generator, N: int, K: int):
+def _quant_matrix(rng: np.random.Generator, N: int, K: int, bf16: bool = False):
+    """Codes, scale and bias of one matrix: scale ~ U(0.005, 0.02) rounded to float16 (or
+    to bf16, returned as uint16 bits), bias = -8*scale (exact in either format)."""
     q = rng.integers(0, 1 << 32, size=(N, K // 8), dtype=np.uint32)
-    s = rng.uniform(0.005, 0.02, size=(N, K // 64)).astype(np.float16)
-    b = (s.astype(np.float32) * np.float32(-8.0)).astype(np.float16)
+    u = rng.uniform(0.005, 0.02, size=(N, K // 64))
+    if bf16:
+        s = f32_to_bf16_bits(u.astype(np.float32))
+        b = f32_to_bf16_bits(bf16_bits_to_f32(s) * np.float32(-8.0))
+    else:
+        s = u.astype(np.float16)
+        b = (s.astype(np.float32) * np.float32(-8.0)).astype(np.float16)
     return q, s, b
 
 
@@ -148,13 +165,18 @@ def make_layer(cfg: int, layer: int = 0, seed: int = 0, into: Optional[LayerWeig
             q, s, b = getattr(into, nm + "_q"), getattr(into, nm + "_s"), getattr(into, nm + "_b")
             assert q.shape == (E + 1, N, K // 8)
         else:
+            qdt = np.uint16 if sh.qparam_bf16 else np.float16
             q = np.empty((E + 1, N, K // 8), np.uint32)
-            s = np.empty((E + 1, N, K // 64), np.float16)
-            b = np.empty((E + 1, N, K // 64), np.float16)
+            s = np.empty((E + 1, N, K // 64), qdt)
+            b = np.empty((E + 1, N, K // 64), qdt)
         for e in range(E + 1):
-            q[e], s[e], b[e] = _quant_matrix(_rng(seed, wc, layer, TID_EXPERT0 + 3 * e + m), N, K)
+            q[e], s[e], b[e] = _quant_matrix(_rng(seed, wc, layer, TID_EXPERT0 + 3 * e + m), N, K, sh.qparam_bf16)
         mats[nm] = (q, s, b)
-    return LayerWeights(router_w, router_b, *mats["gate"], *mats["up"], *mats["down"])
+    sg = None
+    if sh.shared_gate:
+        g = _rng(seed, cfg, layer, TID_SHARED_GATE).standard_normal(H, dtype=np.float32) * np.float32(0.02)
+        sg = f32_to_bf16_bits(g)
+    return LayerWeights(router_w, router_b, *mats["gate"], *mats["up"], *mats["down"], shared_gate=sg)
 
 
 def make_x(cfg: int, layer: int = 0, seed: int = 0, rows: Optional[slice] = None) -> np.ndarray:

@@ -113,6 +113,32 @@ def test_dequant_random_against_numpy_unpack():
     assert np.array_equal(w, ref)
 
 
+def test_dequant_bf16_scale_bias_closed_form():
+    # the pages' checkpoint stores scale and bias as bf16 ("Prefill > Dequantize weights
+    # during matmul"): with constant codes c, w = s c + b with s, b decoded by a bit shift
+    rng = np.random.default_rng(21)
+    N, K = 6, 192
+    s = bf16(rng.uniform(0.005, 0.02, size=(N, K // 64)))
+    b = bf16(rng.uniform(-0.2, 0.0, size=(N, K // 64)))
+    sd = synth.bf16_bits_to_f32(s).astype(np.float64)
+    bd = synth.bf16_bits_to_f32(b).astype(np.float64)
+    for c in (0, 1, 7, 15):
+        w = oracle.dequant(pack_codes(np.full((N, K), c)), s, b)
+        assert np.array_equal(w, np.repeat(sd * c + bd, 64, axis=1)), c
+
+
+def test_dequant_bf16_and_fp16_agree_where_both_formats_hold_the_values():
+    # powers of two and small multiples are exact in both formats: the same weights
+    rng = np.random.default_rng(22)
+    N, K = 4, 128
+    sv = 2.0 ** rng.integers(-9, -4, size=(N, K // 64)).astype(np.float64)
+    bv = -8 * sv
+    q = pack_codes(rng.integers(0, 16, size=(N, K)))
+    w16 = oracle.dequant(q, sv.astype(np.float16), bv.astype(np.float16))
+    wbf = oracle.dequant(q, bf16(sv), bf16(bv))
+    assert np.array_equal(w16, wbf)
+
+
 # ---------------------------------------------------------------- router
 
 def test_logits_match_numpy_matmul_fp32_router():
@@ -373,6 +399,67 @@ def test_single_expert_equals_twice_ffn_when_shared_is_the_same():
     assert np.all(r["gates"] == 1.0)
     only_shared = oracle.experts(x, L, r["ids"], np.zeros_like(r["gates"]))
     assert np.array_equal(r["out"], 2 * only_shared)
+
+
+def _zero_routed_down(L):
+    """The layer with every routed expert's down projection zero (code 8, bias -8 s), the
+    shared expert untouched."""
+    E = L.down_q.shape[0] - 1
+    dq, ds, db = L.down_q.copy(), L.down_s.copy(), L.down_b.copy()
+    dq[:E] = 0x88888888
+    if ds.dtype == np.uint16:  # bf16 bits
+        db[:E] = bf16(synth.bf16_bits_to_f32(ds[:E]) * np.float32(-8))
+    else:
+        db[:E] = (ds[:E].astype(np.float32) * -8).astype(np.float16)
+    return synth.LayerWeights(L.router_w, L.router_b, L.gate_q, L.gate_s, L.gate_b, L.up_q, L.up_s, L.up_b,
+                              dq, ds, db, shared_gate=L.shared_gate)
+
+
+def test_shared_gate_is_sigmoid_of_x_dot_w():
+    # with the routed experts' outputs zero, out_t = sigmoid(x_t . w_sg) * FFN_shared(x_t):
+    # the ratio to the ungated layer, per token, against numpy's dot and logistic
+    sh = synth.shape_of(15)
+    L = _zero_routed_down(synth.make_layer(15))
+    x = synth.make_x(15)
+    r = oracle.route(x, L.router_w, None, sh.k)
+    gated = oracle.experts(x, L, r["ids"], r["gates"])
+    L0 = synth.LayerWeights(*[getattr(L, f) for f in ("router_w", "router_b", "gate_q", "gate_s", "gate_b", "up_q",
+                                                       "up_s", "up_b", "down_q", "down_s", "down_b")])
+    plain = oracle.experts(x, L0, r["ids"], r["gates"])
+    z = synth.bf16_bits_to_f32(x).astype(np.float64) @ synth.bf16_bits_to_f32(L.shared_gate).astype(np.float64)
+    sig = scipy.special.expit(z)
+    assert np.all((sig > 0.2) & (sig < 0.8))  # the gate is not saturated on these inputs
+    np.testing.assert_allclose(gated, sig[:, None] * plain, rtol=1e-12, atol=1e-12 * np.max(np.abs(plain)))
+    # a zero gate vector: sigmoid(0) = 1/2 exactly, so the output halves bitwise
+    Lh = synth.LayerWeights(*[getattr(L0, f) for f in ("router_w", "router_b", "gate_q", "gate_s", "gate_b", "up_q",
+                                                        "up_s", "up_b", "down_q", "down_s", "down_b")],
+                            shared_gate=np.zeros(sh.H, np.uint16))
+    assert np.array_equal(oracle.experts(x, Lh, r["ids"], r["gates"]), 0.5 * plain)
+
+
+def test_bf16_qparam_layer_matches_dense_reference():
+    # the whole layer with bf16 scale/bias and the shared gate against a dense numpy MoE
+    L = synth.make_layer(15)
+    x = synth.make_x(15)
+    r = oracle.forward(x, L, 4)
+    xf = synth.bf16_bits_to_f32(x).astype(np.float64)
+    E = L.gate_q.shape[0] - 1
+
+    def deq(q, s, b):
+        sd = synth.bf16_bits_to_f32(s).astype(np.float64)
+        bd = synth.bf16_bits_to_f32(b).astype(np.float64)
+        return unpack_codes_numpy(q) * np.repeat(sd, 64, 1) + np.repeat(bd, 64, 1)
+
+    G = np.zeros((x.shape[0], E + 1))
+    for t in range(x.shape[0]):
+        G[t, r["ids"][t]] = r["gates"][t]
+    G[:, E] = scipy.special.expit(xf @ synth.bf16_bits_to_f32(L.shared_gate).astype(np.float64))
+    ref = np.zeros_like(xf)
+    for e in range(E + 1):
+        a = xf @ deq(L.gate_q[e], L.gate_s[e], L.gate_b[e]).T
+        u = xf @ deq(L.up_q[e], L.up_s[e], L.up_b[e]).T
+        ref += G[:, e:e + 1] * ((a * scipy.special.expit(a) * u) @ deq(L.down_q[e], L.down_s[e], L.down_b[e]).T)
+    assert np.max(np.abs(r["out"] - ref)) <= 1e-12 * np.max(np.abs(ref))
 
 
 def test_token_permutation_equivariance_and_chunk_invariance():
