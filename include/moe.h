@@ -8,12 +8,13 @@
  * with one scale and one bias per group of 64 weights (section "Prefill >
  * Dequantize weights during matmul").  The layer output is
  *
- *     out[t] = sum_{e in S_t} g_{t,e} * FFN_e(x_t) + FFN_shared(x_t)
+ *     out[t] = sum_{e in S_t} g_{t,e} * FFN_e(x_t) + c_t * FFN_shared(x_t)
  *     FFN(v) = W_down * (silu(W_gate v) .* (W_up v)),   silu(a) = a*sigmoid(a)
  *
  * with S_t the k experts of largest router logit l[t][e] = x_t . Wr[e] (+ b[e])
  * -- equal logits: the lower expert index wins -- and g_{t,.} the softmax of
- * the chosen logits.  Logits are ranked as if computed exactly; the library
+ * the chosen logits; c_t = 1, or sigmoid(x_t . w_sg) with the optional shared-expert gate
+ * vector w_sg.  Logits are ranked as if computed exactly; the library
  * certifies its fp32 ranking against a rigorous error bound and re-ranks
  * uncertain tokens in binary64 (sequentially summed, ascending h, when even
  * that cannot separate them).
@@ -59,7 +60,7 @@
  *                    word ((n/16)*(K/128) + k/128)*256 + (n%16)*16 + (k%128)/8, so a
  *                    128-k step of 16 rows is one run of 1 KB (moe_pack_codes
  *                    converts row-major [N][K/8] words);
- *                    w = scale*code + bias with one fp16 scale and bias per row
+ *                    w = scale*code + bias with one fp16 (or bf16) scale and bias per row
  *                    n and group g = k/64, stored in 16-row tiles: the pair of
  *                    (n, g) is element ((n/16)*(K/64) + g)*16 + n%16 of the
  *                    scale and of the bias array (moe_pack_qparams converts
@@ -137,7 +138,8 @@ typedef struct {               /* (host) */
   int32_t top_k;               /* k: 1 <= k <= min(E, 16) */
   int32_t group_size;          /* must be 64 */
   moe_dtype router_dtype;      /* MOE_BF16 or MOE_FP32 */
-  moe_dtype qparam_dtype;      /* scale/bias dtype: MOE_FP16 */
+  moe_dtype qparam_dtype;      /* scale/bias dtype: MOE_FP16, or MOE_BF16 (the pages'
+                                  checkpoint format) */
   int32_t max_chunk_tokens;    /* prefill chunk; fixes the workspace size; 1..65536 */
   uint32_t flags;              /* MOE_F_* bits; unknown bits -> MOE_ERR_SHAPE */
 } moe_config;
@@ -155,6 +157,9 @@ typedef struct {               /* (host struct of device pointers) */
   moe_qmat down;               /* routed, [E][H][I] */
   moe_qmat s_gate, s_up;       /* shared, [I][H] */
   moe_qmat s_down;             /* shared, [H][I] */
+  const void *shared_gate;     /* bf16 [H], 16-byte aligned, or NULL.  If given, the shared
+                                  expert's output is weighted by sigmoid(x_t . shared_gate)
+                                  (fp32 sum of the exact products); NULL: weight 1 */
 } moe_weights;
 
 typedef struct moe_plan_s *moe_plan_t;

@@ -61,7 +61,7 @@ class moe_qmat(ctypes.Structure):
 class moe_weights(ctypes.Structure):
     _fields_ = [("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p), ("gate", moe_qmat),
                 ("up", moe_qmat), ("down", moe_qmat), ("s_gate", moe_qmat), ("s_up", moe_qmat),
-                ("s_down", moe_qmat)]
+                ("s_down", moe_qmat), ("shared_gate", ctypes.c_void_p)]
 
 
 class moe_debug_out(ctypes.Structure):

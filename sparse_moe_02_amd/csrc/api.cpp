@@ -28,7 +28,7 @@ struct moe_plan_s {
   // workspace layout (byte offsets)
   size_t slot_u64;  // 8-byte words per partial-sum slot of a split gate/up piece
   size_t off_ctrl, off_tokmask, off_lg, off_rd, off_ids, off_gates, off_counts, off_offsets, off_row_token,
-      off_row_gate, off_slot_row, off_mblocks, off_h, off_y, off_dec, off_tk, off_dend, total;
+      off_row_gate, off_slot_row, off_mblocks, off_sgate, off_h, off_y, off_dec, off_tk, off_dend, total;
 };
 
 namespace {
@@ -74,6 +74,7 @@ void layout(moe_plan_s &p) {
   p.off_row_gate = take(rows * 4);
   p.off_slot_row = take(rows * 4);
   p.off_mblocks = take(max_mblocks * 16);
+  p.off_sgate = take(C * 4);  // shared-expert weight per token (with a gate vector)
   p.off_h = take(rows * I * 2);
   // y also holds the partial sums of split gate/up items (before the down GEMM writes y):
   // at least kPartSlots slots, one per piece, sized for the tallest M-block of a chunk
@@ -140,6 +141,8 @@ moe_status decode_launch(const moe_plan_s *p, const void *x, int T, void *out, C
   a.k = c.top_k;
   a.I = c.inter;
   a.T = T;
+  a.qbf16 = c.qparam_dtype == MOE_BF16;
+  a.sgate = static_cast<const uint16_t *>(p->w.shared_gate);
   a.lrec = reinterpret_cast<uint64_t *>(base + L.lrec);
   a.srec = reinterpret_cast<uint64_t *>(base + L.srec);
   a.hflag = reinterpret_cast<uint64_t *>(base + L.hflag);
@@ -262,9 +265,10 @@ moe_status moe_plan_create(const moe_config *cfg, const moe_weights *w, moe_plan
   if (c.max_chunk_tokens < 1 || c.max_chunk_tokens > 65536) return MOE_ERR_SHAPE;
   if ((c.flags & ~kKnownFlags) != 0 || forced_rows(c.flags) > kBM) return MOE_ERR_SHAPE;
   if (c.router_dtype != MOE_BF16 && c.router_dtype != MOE_FP32) return MOE_ERR_DTYPE;
-  if (c.qparam_dtype != MOE_FP16) return MOE_ERR_DTYPE;
+  if (c.qparam_dtype != MOE_FP16 && c.qparam_dtype != MOE_BF16) return MOE_ERR_DTYPE;
   if (!w->router_w) return MOE_ERR_NULL;
   if (!aligned16(w->router_w) || (w->router_bias && ((uintptr_t)w->router_bias & 3u))) return MOE_ERR_ALIGN;
+  if (w->shared_gate && !aligned16(w->shared_gate)) return MOE_ERR_ALIGN;
   for (const moe_qmat *m : {&w->gate, &w->up, &w->down, &w->s_gate, &w->s_up, &w->s_down}) {
     const moe_status st = check_qmat(*m);
     if (st != MOE_OK) return st;
@@ -388,6 +392,12 @@ moe_status moe_forward_prefill(moe_plan_t p, const void *x, int64_t T, void *out
     ga.mblocks = at<int4>(ws, p->off_mblocks);
     ga.ctrl = ctrl;
     ga.force_rows = forced_rows(c.flags);
+    if (p->w.shared_gate) {
+      ga.sgate = at<float>(ws, p->off_sgate);
+      if (launch_shared_gate(xc, static_cast<const uint16_t *>(p->w.shared_gate), at<float>(ws, p->off_sgate), Tc,
+                             (int)H, stream) != hipSuccess)
+        return MOE_ERR_HIP;
+    }
     if (dbg) {
       ga.dbg_counts = dbg->counts ? dbg->counts + (size_t)ci * (E + 1) : nullptr;
       ga.dbg_offsets = dbg->offsets ? dbg->offsets + (size_t)ci * (E + 2) : nullptr;
@@ -424,6 +434,7 @@ moe_status moe_forward_prefill(moe_plan_t p, const void *x, int64_t T, void *out
     g1.E = (int)E;
     g1.H = (int)H;
     g1.I = c.inter;
+    g1.qbf16 = c.qparam_dtype == MOE_BF16;
     g1.h = at<uint16_t>(ws, p->off_h);
     // the partial sums of split gate/up items live in y, which only the down GEMM writes
     g1.tail_queue = &ctrl->q_tail;

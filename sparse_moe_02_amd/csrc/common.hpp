@@ -34,6 +34,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)(pac
 
 __device__ __forceinline__ float fp16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
+// A scale or bias value: fp16 bits, or bf16 bits when bf16 (the pages' checkpoint format).
+__device__ __forceinline__ float qp_f32(uint32_t v, bool bf16) {
+  return bf16 ? __uint_as_float((v & 0xffffu) << 16) : fp16_to_f32((uint16_t)v);
+}
+
 // Scale and bias arrays (G groups of 64 per row) are stored in tiles of kQpRows rows:
 // the tile's values of one group are contiguous, groups follow each other.
 constexpr int kQpRows = 16;

@@ -130,6 +130,8 @@ struct DecShared {
   uint32_t act_m[kActMax];                       // their token masks
   int n_act;
   int arrive[kMaxDecodeT];                       // this workgroup completed (token, row block)
+  float sgz[kDecThreads / kWave][kMaxDecodeT];   // shared gate: per-wave partial dot products
+  float sgv[kMaxDecodeT];                        // weight of the shared expert per token
   __attribute__((aligned(16))) uint32_t hb[kHbWords];  // staged h, bf16 pairs
 };
 
@@ -592,8 +594,8 @@ __device__ void gu_task(const DecodeArgs &a, DecShared &sh, int act, int u, uint
           codes_bf16(w.y, &o[m][r][4]);
           codes_bf16(w.z, &o[m][r][8]);
           codes_bf16(w.w, &o[m][r][12]);
-          s[m][r] = fp16_to_f32((uint16_t)(sv[m][pp] >> (16 * r)));
-          b2[m][r] = __builtin_fmaf(-128.0f, s[m][r], fp16_to_f32((uint16_t)(bv[m][pp] >> (16 * r))));
+          s[m][r] = qp_f32(sv[m][pp] >> (16 * r), a.qbf16);
+          b2[m][r] = __builtin_fmaf(-128.0f, s[m][r], qp_f32(bv[m][pp] >> (16 * r), a.qbf16));
         }
 #pragma unroll
       for (int t = 0; t < TT; ++t) {
@@ -698,6 +700,36 @@ __device__ __forceinline__ void dn_task(const DecodeArgs &a, DecShared &sh, int 
   const int n0 = rb * kDecDnTask;
   const int nt = __popc(tm);
   const int per_round = kHbWords / (I / 2);  // tokens whose h fits in LDS at once (>= 4)
+  // the shared expert's weight per token: sigmoid(x_t . w_sg), or 1
+  if (u == a.E) {
+    if (a.sgate) {
+      float z[TT];
+#pragma unroll
+      for (int t = 0; t < TT; ++t) z[t] = 0.f;
+      for (int c = tid; c < H / 8; c += kDecThreads) {
+        const uint4 wv4 = *(const uint4 *)(a.sgate + 8 * c);
+        const uint32_t ww[4] = {wv4.x, wv4.y, wv4.z, wv4.w};
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+          if (t >= a.T) break;
+          const uint4 xv = *(const uint4 *)(a.x + (size_t)t * H + 8 * c);
+          const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) z[t] = dot2(xw[i], ww[i], z[t]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < TT; ++t) {
+        const float zs = wave_sum(z[t]);
+        if (lane == 0) sh.sgz[wv][t] = zs;
+      }
+    }
+    __syncthreads();
+    if (tid < TT) {
+      const float zt = (sh.sgz[0][tid] + sh.sgz[1][tid]) + (sh.sgz[2][tid] + sh.sgz[3][tid]);
+      sh.sgv[tid] = a.sgate ? 1.0f / (1.0f + __expf(-zt)) : 1.0f;
+    }
+  }
   for (int t0 = 0; t0 < nt; t0 += per_round) {
     const int nb = min(per_round, nt - t0);
     if (t0 > 0) dn_load(a, u, rb, cl, pre);
@@ -719,8 +751,8 @@ __device__ __forceinline__ void dn_task(const DecodeArgs &a, DecShared &sh, int 
       float s[4], b2[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        s[i] = fp16_to_f32((uint16_t)W.s[i]);
-        b2[i] = __builtin_fmaf(-128.0f, s[i], fp16_to_f32((uint16_t)W.b[i]));
+        s[i] = qp_f32(W.s[i], a.qbf16);
+        b2[i] = __builtin_fmaf(-128.0f, s[i], qp_f32(W.b[i], a.qbf16));
 #pragma unroll
         for (int v = 0; v < 4; ++v) codes_bf16(W.w[i][v], &o[i][4 * v]);
       }
@@ -751,7 +783,7 @@ __device__ __forceinline__ void dn_task(const DecodeArgs &a, DecShared &sh, int 
       if (ti >= nb) break;
       const int t = nth_bit(tm, t0 + ti);
       const int j = slot_of(a, sh, t, u);
-      const float g = j < k ? sh.gates[t][j] : 1.0f;
+      const float g = j < k ? sh.gates[t][j] : sh.sgv[t];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float y = row16_sum(acc[ti][i]);

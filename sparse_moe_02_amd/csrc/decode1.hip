@@ -83,6 +83,7 @@ struct DecShared {
   int ids[kMaxTopK];
   float gates[kMaxTopK];
   int fast;  // select_topk: the one-wave selection was certified
+  float sgv;  // weight of the shared expert: sigmoid(x . w_sg), or 1
   float unit[kDnRows * kDnSlots];
   __attribute__((aligned(16))) float h[kHStage];
 };
@@ -446,7 +447,7 @@ __device__ __forceinline__ void gu_issue(const DecodeArgs &a, const QMat &Gm, co
   for (int q = 0; q < 4; ++q) L.x[q] = *(const uint4 *)(a.x + 32 * cc + 8 * q);
 }
 
-__device__ __forceinline__ void gu_accumulate(const GuLoad &L, float (&ag)[kGuRows], float (&au)[kGuRows]) {
+__device__ __forceinline__ void gu_accumulate(const GuLoad &L, bool bf, float (&ag)[kGuRows], float (&au)[kGuRows]) {
   if (!L.ok) return;
   float xf[32];
 #pragma unroll
@@ -463,7 +464,7 @@ __device__ __forceinline__ void gu_accumulate(const GuLoad &L, float (&ag)[kGuRo
   for (int i = 0; i < 32; ++i) xs += xf[i];
 #pragma unroll
   for (int r = 0; r < kGuRows; ++r) {
-    auto half = [&](uint2 v) { return fp16_to_f32((uint16_t)(((r >> 1) ? v.y : v.x) >> (16 * (r & 1)))); };
+    auto half = [&](uint2 v) { return qp_f32(((r >> 1) ? v.y : v.x) >> (16 * (r & 1)), bf); };
     ag[r] += half(L.sg) * dot_codes32(L.wg[r], xf) + half(L.bg) * xs;
     au[r] += half(L.su) * dot_codes32(L.wu[r], xf) + half(L.bu) * xs;
   }
@@ -490,7 +491,7 @@ __device__ __forceinline__ void gu_task(const DecodeArgs &a, const DecShared &sh
   const int tpe = I / kGuTask;
   const int j = g / tpe, r0 = (g - j * tpe) * kGuTask + kGuRows * wv;
   float ag[kGuRows] = {}, au[kGuRows] = {};
-  gu_accumulate(first, ag, au);
+  gu_accumulate(first, a.qbf16, ag, au);
   const int np = (H / 32 + kWave - 1) / kWave;
   if (np > 1) {
     const int e = gu_expert(a, sh, j);
@@ -499,7 +500,7 @@ __device__ __forceinline__ void gu_task(const DecodeArgs &a, const DecShared &sh
     for (int p = 1; p < np; ++p) {
       GuLoad L;
       gu_issue(a, Gm, Um, r0, lane + kWave * p, L);
-      gu_accumulate(L, ag, au);
+      gu_accumulate(L, a.qbf16, ag, au);
     }
   }
   float hv = 0.f;
@@ -597,7 +598,7 @@ __device__ __forceinline__ void dn_accumulate(const DecodeArgs &a, DecShared &sh
     float hs = 0.f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) hs += hv[i];
-    acc[m] += fp16_to_f32((uint16_t)L.s[m]) * dot_codes32(L.w[m], hv) + fp16_to_f32((uint16_t)L.b[m]) * hs;
+    acc[m] += qp_f32(L.s[m], a.qbf16) * dot_codes32(L.w[m], hv) + qp_f32(L.b[m], a.qbf16) * hs;
   }
 }
 
@@ -629,7 +630,7 @@ __device__ __forceinline__ void dn_task(const DecodeArgs &a, DecShared &sh, int 
       const int u = q + 16 * m;
       if (cl == 0 && u < kDnRows * nb) {
         const int slot = j0 + u % nb;
-        sh.unit[u] = (slot < k ? sh.gates[slot] : 1.0f) * v;
+        sh.unit[u] = (slot < k ? sh.gates[slot] : sh.sgv) * v;
       }
     }
     __syncthreads();
@@ -653,6 +654,26 @@ __global__ __launch_bounds__(kDecThreads) void k_decode1(DecodeArgs a) {
   const int E = a.E, k = a.k;
   const int n_gu = (k + 1) * (a.I / kGuTask), n_dn = a.H / kDnRows;
   const int first_shared = k * (a.I / kGuTask);  // gate/up tasks from here on are the shared expert's
+
+  // the shared expert's weight, in every workgroup with a down task (x and the gate vector
+  // are read at the start, off the dependency chain)
+  if (b < n_dn) {
+    float z = 0.f;
+    if (a.sgate) {
+      for (int c = tid; c < a.H / 8; c += kDecThreads) {
+        const uint4 xv = *(const uint4 *)(a.x + 8 * c), wv4 = *(const uint4 *)(a.sgate + 8 * c);
+        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, ww[4] = {wv4.x, wv4.y, wv4.z, wv4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z += bf16_lo(xw[i]) * bf16_lo(ww[i]) + bf16_hi(xw[i]) * bf16_hi(ww[i]);
+      }
+      z = wave_sum(z);
+      if ((tid & 63) == 0) sh.wf[tid >> 6] = z;
+    }
+    __syncthreads();
+    if (tid == 0) sh.sgv = a.sgate ? 1.0f / (1.0f + __expf(-((sh.wf[0] + sh.wf[1]) + (sh.wf[2] + sh.wf[3])))) : 1.0f;
+    __syncthreads();
+  }
+
 
   // The shared expert needs no routing: issue its gate/up loads before the router work.
   GuLoad gl;

@@ -195,8 +195,8 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
     DeqPair dp[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      sc[i] = fp16_to_f32(sp[s_lane[i]]);
-      bi[i] = fp16_to_f32(sp[kSStage / 4 + s_lane[i]]);
+      sc[i] = qp_f32(sp[s_lane[i]], a.qbf16);
+      bi[i] = qp_f32(sp[kSStage / 4 + s_lane[i]], a.qbf16);
       dp[i] = deq_pair(sc[i], bi[i]);
     }
     auto afrag = [&](int t, int j) {

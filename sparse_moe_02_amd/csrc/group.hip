@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void k_group(GroupArgs a) {
       g = sc_g[u];
     } else {
       pos = s_off[E] + t;
-      g = 1.0f;
+      g = a.sgate ? a.sgate[t] : 1.0f;
     }
     a.row_token[pos] = t;
     a.row_gate[pos] = g;
@@ -275,7 +275,32 @@ __global__ __launch_bounds__(kThreads) void k_group(GroupArgs a) {
   }
 }
 
+// The shared expert's weight per token, sigmoid(x_t . w) with w the learned gate vector:
+// one wave per token, each lane 8-element chunks c = lane + 64 i, bf16 products summed in
+// fp32 (v_dot2), then the wave sum.
+__global__ __launch_bounds__(256) void k_shared_gate(const uint16_t *x, const uint16_t *w, float *out, int T, int H) {
+  const int lane = threadIdx.x & 63, t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+  float z = 0.f;
+  for (int c = lane; c < H / 8; c += kWave) {
+    const uint4 xv = *(const uint4 *)(x + (size_t)t * H + 8 * c), wv = *(const uint4 *)(w + 8 * c);
+    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, ww[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      z = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xw[i]), __builtin_bit_cast(bf16x2, ww[i]), z,
+                                          false);
+  }
+  z = wave_sum(z);
+  if (lane == 0) out[t] = 1.0f / (1.0f + __expf(-z));
+}
+
 }  // namespace
+
+hipError_t launch_shared_gate(const uint16_t *x, const uint16_t *w, float *out, int T, int H, hipStream_t s) {
+  hipLaunchKernelGGL(k_shared_gate, dim3((T + 3) / 4), dim3(256), 0, s, x, w, out, T, H);
+  return hipGetLastError();
+}
 
 hipError_t launch_group(const GroupArgs &a, hipStream_t s) {
   const int nb = (a.T + kTokensPerBlock - 1) / kTokensPerBlock;

@@ -74,6 +74,7 @@ struct GroupArgs {
   Ctrl *ctrl;
   int32_t *dbg_counts, *dbg_offsets, *dbg_row_token, *dbg_n_refined;
   int force_rows;         // 0: M-block heights from the expert's row count; else fixed height
+  const float *sgate;     // [T] shared-expert weight per token, or null (weight 1)
 };
 
 struct GemmArgs {
@@ -91,6 +92,7 @@ struct GemmArgs {
   QMat w0, w1;              // routed stacked (gate, up) or (down, -)
   QMat s0, s1;              // shared expert
   int E, H, I;
+  bool qbf16;               // scale/bias are bf16 (else fp16)
   uint16_t *h;              // gate/up output [rows][I]
   uint16_t *y;              // down output, gate-weighted, per grouped row [rows][H]
 };
@@ -108,6 +110,8 @@ struct DecodeArgs {
   QMat gate, up, down;      // routed stacked
   QMat s_gate, s_up, s_down;
   int H, E, k, I, T;
+  bool qbf16;               // scale/bias are bf16 (else fp16)
+  const uint16_t *sgate;    // [H] bf16 shared-expert gate vector, or null (weight 1)
   uint64_t *lrec;           // [T][E][3] tagged records: low and high word of the binary64 logit, radius
   uint64_t *srec;           // [T][2k] tagged records: the chosen experts (ascending), then their gates
   uint64_t *hflag;          // [min(T*k, E) + 1][I/16] tagged: gate/up task (active expert, row block) done
@@ -132,6 +136,8 @@ DecodeLayout decode_layout(int H, int E, int k, int I, int t_max);
 
 hipError_t launch_route(const RouteArgs &a, hipStream_t s);
 hipError_t launch_group(const GroupArgs &a, hipStream_t s);
+// out[t] = sigmoid(x[t] . w) for the T tokens of x [T][H] (bf16), w [H] (bf16)
+hipError_t launch_shared_gate(const uint16_t *x, const uint16_t *w, float *out, int T, int H, hipStream_t s);
 hipError_t launch_gemm_gateup(const GemmArgs &a, int n_blocks, hipStream_t s);
 hipError_t launch_gemm_down(const GemmArgs &a, int n_blocks, hipStream_t s);
 hipError_t launch_finalize(const uint16_t *y, const int32_t *slot_row, uint16_t *out, int T, int H, int k,

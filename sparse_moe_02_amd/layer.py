@@ -41,20 +41,24 @@ class MoeLayer:
         self.chunk = max_chunk_tokens
         self.t = {}
         for name in ("router_w", "router_b", "gate_q", "gate_s", "gate_b", "up_q", "up_s", "up_b",
-                     "down_q", "down_s", "down_b"):
-            a = getattr(weights, name)
+                     "down_q", "down_s", "down_b", "shared_gate"):
+            a = getattr(weights, name, None)
             self.t[name] = None if a is None else _dev(a, self.device)
             if name in ("gate_s", "gate_b", "up_s", "up_b", "down_s", "down_b"):
                 self.t[name] = self._tiled(self.t[name])
             elif name in ("gate_q", "up_q", "down_q"):
                 self.t[name] = self._tiled_codes(self.t[name])
         fp32_router = weights.router_w.dtype == np.float32
+        # scale/bias: float16 values, or bf16 bit patterns stored as uint16
+        qbf16 = weights.gate_s.dtype == np.uint16
         self.cfg = B.moe_config(hidden=self.H, inter=self.I, n_experts=self.E, top_k=top_k, group_size=64,
                                 router_dtype=B.MOE_FP32 if fp32_router else B.MOE_BF16,
-                                qparam_dtype=B.MOE_FP16, max_chunk_tokens=max_chunk_tokens, flags=flags)
+                                qparam_dtype=B.MOE_BF16 if qbf16 else B.MOE_FP16,
+                                max_chunk_tokens=max_chunk_tokens, flags=flags)
         self.w = B.moe_weights()
         self.w.router_w = self.t["router_w"].data_ptr()
         self.w.router_bias = self.t["router_b"].data_ptr() if self.t["router_b"] is not None else None
+        self.w.shared_gate = self.t["shared_gate"].data_ptr() if self.t["shared_gate"] is not None else None
         for mat in ("gate", "up", "down"):
             q, s, b = self.t[mat + "_q"], self.t[mat + "_s"], self.t[mat + "_b"]
             setattr(self.w, mat, B.moe_qmat(q.data_ptr(), s.data_ptr(), b.data_ptr()))

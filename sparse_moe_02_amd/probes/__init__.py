@@ -26,7 +26,11 @@ def lib() -> ctypes.CDLL:
         L.probe_mfma.argtypes = [I, P, I, P]
         L.probe_empty.argtypes = [I, I, P]
         L.probe_expert_stream.argtypes = [ctypes.POINTER(P), P, I, I, I, P, I, P]
-        for f in (L.probe_read_stream, L.probe_mfma, L.probe_empty, L.probe_expert_stream):
+        L.probe_flat_stream.argtypes = [P, I, P, I, P]
+        L.probe_ticket.argtypes = [P, I, I, I, P]
+        L.probe_handoff.argtypes = [P, ctypes.c_uint32, I, I, I, P, I, P]
+        for f in (L.probe_read_stream, L.probe_mfma, L.probe_empty, L.probe_expert_stream, L.probe_flat_stream,
+                  L.probe_ticket, L.probe_handoff):
             f.restype = I
         _lib = L
     return _lib
@@ -53,3 +57,23 @@ def expert_stream(mats, x_ptr: int, H: int, I: int, arith: bool, sink_ptr: int, 
     """mats: 81 device pointers, [slot 0..8][gate, up, down][codes, scale, bias]."""
     arr = (ctypes.c_void_p * 81)(*mats)
     _ok(lib().probe_expert_stream(arr, x_ptr, H, I, int(arith), sink_ptr, grid, stream), "probe_expert_stream")
+
+
+def flat_table(ptrs, nbytes):
+    """The device-side segment table of probe_flat_stream (384 words: base addresses, sizes
+    in 16-byte units, first workgroup of each segment) as a numpy array, and the grid."""
+    import numpy as np
+
+    n16 = [b // 16 for b in nbytes]
+    wg = np.concatenate([[0], np.cumsum([-(-n // 1024) for n in n16])])
+    t = np.zeros(384, np.uint64)
+    t[:len(ptrs)] = ptrs
+    t[128:128 + len(ptrs)] = n16
+    t[256:256 + len(ptrs) + 1] = wg
+    return t, int(wg[-1])
+
+
+def flat_stream(table_ptr: int, n: int, sink_ptr: int, grid: int, stream: int) -> None:
+    """Read n device arrays (segment table at table_ptr, see flat_table) once, 16 KB per
+    workgroup."""
+    _ok(lib().probe_flat_stream(table_ptr, n, sink_ptr, grid, stream), "probe_flat_stream")

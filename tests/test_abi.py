@@ -69,7 +69,7 @@ def _weights(B, base=0x10000):
     (dict(inter=64), 2), (dict(n_experts=257), 2), (dict(n_experts=0), 2), (dict(top_k=0), 2),
     (dict(top_k=17, n_experts=32), 2), (dict(top_k=9, n_experts=8), 2), (dict(max_chunk_tokens=0), 2),
     (dict(flags=6), 2), (dict(flags=7), 2), (dict(flags=1 << 7), 2), (dict(flags=1 << 31), 2),
-    (dict(router_dtype=1), 3), (dict(qparam_dtype=0), 3),
+    (dict(router_dtype=1), 3), (dict(qparam_dtype=2), 3), (dict(qparam_dtype=7), 3),
 ])
 def test_plan_rejects_bad_config(B, kw, status):
     with pytest.raises(B.MoeError) as ei:
@@ -79,6 +79,7 @@ def test_plan_rejects_bad_config(B, kw, status):
 
 @pytest.mark.parametrize("kw", [
     dict(flags=1), dict(flags=5), dict(flags=16), dict(flags=64), dict(flags=5 | 16 | 64),
+    dict(qparam_dtype=0),  # bf16 scale/bias (the pages' checkpoint format)
     # the largest accepted chunk with the largest intermediate size and top-k: a down GEMM
     # M-block's h rows lie up to 65536 x 17 x 4096 x 2 bytes (> 2^32) into the workspace
     dict(max_chunk_tokens=65536, top_k=16, inter=4096, n_experts=32),
@@ -117,6 +118,11 @@ def test_plan_rejects_null_and_misaligned_weights(B):
     assert ei.value.status == 1
     w = _weights(B)
     w.down = B.moe_qmat(0x2004, 0x3000, 0x4000)
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_plan_create(_cfg(B), w)
+    assert ei.value.status == 4
+    w = _weights(B)
+    w.shared_gate = 0x9008  # the optional shared-expert gate vector must be 16-byte aligned
     with pytest.raises(B.MoeError) as ei:
         B.moe_plan_create(_cfg(B), w)
     assert ei.value.status == 4

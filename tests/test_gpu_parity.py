@@ -429,6 +429,37 @@ def test_decode_batch(cfg, layer_i, Ts):
     m.close()
 
 
+@pytest.mark.parametrize("cfg", [15, 16])
+def test_bf16_qparams_and_shared_gate(cfg):
+    """The pages' checkpoint format (bf16 scale and bias per 64 weights) with a sigmoid
+    shared-expert gate: prefill over ragged chunks (small shape) and at the benchmark's
+    hidden size (512 tokens); one-token decode and a 4-row batch decode of the same tokens."""
+    import torch
+
+    from sparse_moe_02_amd.layer import MoeLayer, bf16_bits, bf16_tensor
+
+    sh = synth.shape_of(cfg)
+    L, x = synth.make_layer(cfg), synth.make_x(cfg)
+    assert L.gate_s.dtype == np.uint16 and L.shared_gate is not None
+    ref = oracle.forward(x, L, sh.k)
+    r, res = _prefill_case(L, x, sh.k, sh.chunk, sh.name)
+    _check_out(sh.name, res["out"], ref["out"])
+    m = MoeLayer(L, top_k=sh.k, max_chunk_tokens=1)
+    one = []
+    for t in range(4):
+        o, d = m.decode(bf16_tensor(x[t], "cuda:0"), debug=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(d["topk_ids"].cpu().numpy()[0], ref["ids"][t])
+        one.append(bf16_bits(o))
+    _check_out(sh.name + "/decode", to_f64(np.stack(one)), ref["out"][:4])
+    ob, db = m.decode_batch(bf16_tensor(x[:4], "cuda:0"), debug=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(db["topk_ids"].cpu().numpy(), ref["ids"][:4])
+    _check_out(sh.name + "/batch4", to_f64(bf16_bits(ob)), ref["out"][:4])
+    assert m.decode_error() == 0
+    m.close()
+
+
 @pytest.mark.parametrize("flags,name", [(1, "force-bm32"), (5, "force-bm160"), (64, "host-routing")])
 def test_prefill_flag_variants(flags, name):
     """The ablation configurations reach the same result: fixed 32- and 160-row M-blocks
