@@ -195,6 +195,7 @@ def main():
     ap.add_argument("--no-long-prompt", action="store_true", help="skip the 131072-token chunked prefill")
     ap.add_argument("--no-skewed", action="store_true", help="skip the skewed-routing prefill")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the measured ceilings")
+    ap.add_argument("--no-ablations", action="store_true", help="skip the ablation configurations")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -387,6 +388,35 @@ def main():
             "gateup_frac": round(gateup_flop / (sk_stage["gateup"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         sk.close()
         del sk, dsk, dun
+
+    if not args.no_ablations:
+        # the pages' ablations on this chip: each optimisation switched off alone, prefill
+        # of the same layer and tokens at 512 tokens (the pages' prompt for the dequant and
+        # routing ablations) and at 4096
+        log("bench: ablations")
+        variants = {"fixed_32_row_tiles": B.MOE_F_FORCE_BM(32), "host_synced_routing": B.MOE_F_HOST_ROUTING,
+                    "separate_dequant": B.MOE_F_SEPARATE_DEQUANT, "no_binary64_rerank": B.MOE_F_NO_FALLBACK}
+        abl = {}
+        for Tn in (512, T):
+            xs = xp[:Tn].contiguous()
+            os_ = torch.empty_like(xs)
+            base_layer = pre
+            runs = {"default": base_layer}
+            for name, fl in variants.items():
+                runs[name] = pre.with_flags(fl)
+            res = {}
+            for name, lay in runs.items():
+                for _ in range(2):
+                    lay.prefill(xs, os_)
+                ms = time_events(lambda lay=lay: lay.prefill(xs, os_), max(K // 2, 5), stream, B)
+                res[name] = float(np.median(ms)) * 1e3
+            abl[str(Tn)] = {name: {"us": round(v, 2), "default_speedup": round(v / res["default"], 4)}
+                            for name, v in res.items()}
+            for name, lay in runs.items():
+                if lay is not base_layer:
+                    lay.close()
+            del runs
+        result["ablations"] = abl
 
     if not args.no_long_prompt:
         # long prompt (131072 tokens, the same layer) through the chunk driver: one bounded

@@ -114,11 +114,12 @@ typedef enum { MOE_BF16 = 0, MOE_FP16 = 1, MOE_FP32 = 2 } moe_dtype;
  *   does not certify it (no binary64 re-rank).  Routing may then differ from the exact
  *   ranking; for tests and timing only.  No effect with a float32 router (ranked in
  *   binary64 throughout) or on decode.
- * MOE_F_SEPARATE_DEQUANT: prefill dequantises the weights of every expert that has rows
- *   into bf16 matrices in the workspace first, and the grouped GEMMs read those (section
- *   "Prefill > Dequantize weights during matmul": the ablation expands the 4-bit weights
- *   into a bf16 array that the matrix kernel reads back).  The workspace grows by the
- *   bf16 size of all E+1 experts' matrices.
+ * MOE_F_SEPARATE_DEQUANT: each prefill call first expands the weights of all E+1
+ *   experts into bf16 matrices in the workspace, and the grouped GEMMs read those instead
+ *   of the packed codes (section "Prefill > Dequantize weights during matmul": the
+ *   ablation expands the 4-bit weights into a bf16 array that the matrix kernel reads
+ *   back).  The workspace grows by (E+1) * 3 * I * H * 2 bytes (1.6 GB at H = 2048,
+ *   I = 512, E = 256).
  * MOE_F_HOST_ROUTING: prefill stops after grouping each chunk, synchronises the stream
  *   on the host, reads the block-map length and launches the grouped GEMMs with exactly
  *   one workgroup per work item (section "Prefill > Keep expert routing on the GPU": the

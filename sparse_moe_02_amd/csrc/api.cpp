@@ -28,7 +28,7 @@ struct moe_plan_s {
   // workspace layout (byte offsets)
   size_t slot_u64;  // 8-byte words per partial-sum slot of a split gate/up piece
   size_t off_ctrl, off_tokmask, off_lg, off_rd, off_ids, off_gates, off_counts, off_offsets, off_row_token,
-      off_row_gate, off_slot_row, off_mblocks, off_sgate, off_h, off_y, off_dec, off_tk, off_dend, total;
+      off_row_gate, off_slot_row, off_mblocks, off_sgate, off_h, off_y, off_dec, off_tk, off_dend, off_w16, total;
 };
 
 namespace {
@@ -38,7 +38,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // M-block height forced by MOE_F_FORCE_BM (0: chosen from each expert's row count)
 int forced_rows(uint32_t flags) { return 32 * (int)(flags & 0xfu); }
 
-constexpr uint32_t kKnownFlags = 0xfu | MOE_F_NO_FALLBACK | MOE_F_HOST_ROUTING;
+constexpr uint32_t kKnownFlags = 0xfu | MOE_F_NO_FALLBACK | MOE_F_SEPARATE_DEQUANT | MOE_F_HOST_ROUTING;
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -90,6 +90,9 @@ void layout(moe_plan_s &p) {
   p.off_dec = take(p.dec.total);
   p.off_tk = take(kMaxTailItems * 4);
   p.off_dend = o;
+  // MOE_F_SEPARATE_DEQUANT: every expert's gate, up and down matrices expanded to bf16
+  p.off_w16 = o;
+  if (p.cfg.flags & MOE_F_SEPARATE_DEQUANT) take((E + 1) * 3 * I * H * 2);
   p.total = o;
 }
 
@@ -338,6 +341,31 @@ moe_status moe_forward_prefill(moe_plan_t p, const void *x, int64_t T, void *out
   Ctrl *ctrl = at<Ctrl>(ws, p->off_ctrl);
   const bool fp32_router = c.router_dtype == MOE_FP32;
 
+  // MOE_F_SEPARATE_DEQUANT: expand the weights to bf16 first (the grouped GEMMs then read
+  // those): routed stacks to experts 0..E-1, the shared expert to expert E
+  const bool w16 = (c.flags & MOE_F_SEPARATE_DEQUANT) != 0;
+  const size_t I = c.inter, mat16 = I * H;  // bf16 elements of one matrix
+  uint16_t *g16 = at<uint16_t>(ws, p->off_w16), *u16 = g16 + (E + 1) * mat16, *d16 = u16 + (E + 1) * mat16;
+  if (w16) {
+    const bool qb = c.qparam_dtype == MOE_BF16;
+    struct {
+      const moe_qmat &m;
+      uint16_t *dst;
+      int64_t rows;
+      int K;
+    } jobs[6] = {{p->w.gate, g16, (int64_t)E * c.inter, c.hidden},
+                 {p->w.up, u16, (int64_t)E * c.inter, c.hidden},
+                 {p->w.down, d16, (int64_t)E * c.hidden, c.inter},
+                 {p->w.s_gate, g16 + E * mat16, c.inter, c.hidden},
+                 {p->w.s_up, u16 + E * mat16, c.inter, c.hidden},
+                 {p->w.s_down, d16 + E * mat16, c.hidden, c.inter}};
+    for (const auto &j : jobs)
+      if (launch_dequant_w16(j.m.q, static_cast<const uint16_t *>(j.m.scale), static_cast<const uint16_t *>(j.m.bias),
+                             j.dst, j.rows, j.K, qb, stream) != hipSuccess)
+        return MOE_ERR_HIP;
+  }
+  auto bf16_mat = [&](uint16_t *base) { return QMat{reinterpret_cast<const uint32_t *>(base), nullptr, nullptr}; };
+
   for (int64_t c0 = 0, ci = 0; c0 < T; c0 += C, ++ci) {
     const int Tc = (int)((T - c0 < C) ? (T - c0) : C);
     const bool last = c0 + C >= T;
@@ -435,6 +463,13 @@ moe_status moe_forward_prefill(moe_plan_t p, const void *x, int64_t T, void *out
     g1.H = (int)H;
     g1.I = c.inter;
     g1.qbf16 = c.qparam_dtype == MOE_BF16;
+    g1.w16 = w16;
+    if (w16) {
+      g1.w0 = bf16_mat(g16);
+      g1.w1 = bf16_mat(u16);
+      g1.s0 = bf16_mat(g16 + E * mat16);
+      g1.s1 = bf16_mat(u16 + E * mat16);
+    }
     g1.h = at<uint16_t>(ws, p->off_h);
     // the partial sums of split gate/up items live in y, which only the down GEMM writes
     g1.tail_queue = &ctrl->q_tail;
@@ -448,8 +483,8 @@ moe_status moe_forward_prefill(moe_plan_t p, const void *x, int64_t T, void *out
     GemmArgs g2 = g1;
     g2.x = g1.h;
     g2.queue = ctrl->q_down;
-    g2.w0 = qm(p->w.down);
-    g2.s0 = qm(p->w.s_down);
+    g2.w0 = w16 ? bf16_mat(d16) : qm(p->w.down);
+    g2.s0 = w16 ? bf16_mat(d16 + E * mat16) : qm(p->w.s_down);
     g2.w1 = QMat{};
     g2.s1 = QMat{};
     g2.y = at<uint16_t>(ws, p->off_y);

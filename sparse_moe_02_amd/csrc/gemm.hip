@@ -90,7 +90,11 @@ struct Piece {
 // taken from: wave 0 takes the ticket once the item's last multiply is done, so the
 // atomic's round trip overlaps the epilogue, and leaves the value in *s_pend when the
 // item ends.
-template <int MT, bool GU>
+// W16: the weights are bf16 matrices (MOE_F_SEPARATE_DEQUANT: expanded by k_dequant_w16
+// in 16-row x 32-k tiles of 1 KB), a super-step is 32 k (two MFMA slices; each weight
+// row's 64 bytes per step land in the same B layout as the packed codes), and there is
+// no scale/bias stage and no dequantisation.
+template <int MT, bool GU, bool W16>
 __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, float *s_gate, int *s_last, int e,
                           int row0, int rows, int nb, int ks0, int ks1, const Piece &pc, int *claim, int *s_pend) {
   // thread index made opaque so per-lane address arithmetic is computed per item instead
@@ -103,8 +107,9 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
   const int H = a.H, I = a.I;
   const int K = GU ? H : I;
   const int N = GU ? I : H;  // rows of each weight matrix
-  const QMat M0 = GU ? expert_mat(a.w0, a.s0, e, a.E, I, H) : expert_mat(a.w0, a.s0, e, a.E, H, I);
-  const QMat M1 = GU ? expert_mat(a.w1, a.s1, e, a.E, I, H) : M0;
+  constexpr int KF = W16 ? 4 : 1;  // the bf16 tiles are laid out as packed codes of a 4x longer row
+  const QMat M0 = GU ? expert_mat(a.w0, a.s0, e, a.E, I, KF * H) : expert_mat(a.w0, a.s0, e, a.E, H, KF * I);
+  const QMat M1 = GU ? expert_mat(a.w1, a.s1, e, a.E, I, KF * H) : M0;
   auto slot_mat = [&](int slot) -> const QMat & { return (GU && ((slot >> 5) & 1)) ? M1 : M0; };
   auto slot_row = [&](int slot) {
     const int w = slot >> 6, t = (slot >> 5) & 1, j = slot & 31;
@@ -119,14 +124,21 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
   // per-lane offsets stay below 2^31 bytes: a token row (gate/up) is at most 65535 x
   // 16384 x 2 bytes in; the h rows (down) are addressed from the M-block's first row,
   // which goes into the 64-bit base, so the offset is at most 159 x 4096 x 2 bytes.
+  // W16: 2*MT wave-loads of 1 KiB (16 rows x 64 B each), v = wu + 8i for i < 2 while
+  // v < 2 MT; row r's 16-byte chunk c at slot c ^ (r & 3).
   const char *abase = GU ? (const char *)a.x : (const char *)a.x + (size_t)row0 * I * 2;
-  uint32_t aoff[MT];
+  constexpr int NA = W16 ? 2 : MT;
+  uint32_t aoff[NA];
+  bool aon[NA];
 #pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    const int r = 4 * (wu + 8 * i) + (lane >> 4);
+  for (int i = 0; i < NA; ++i) {
+    const int v = wu + 8 * i;
+    const int r = W16 ? 16 * v + (lane >> 2) : 4 * v + (lane >> 4);
     const int rl = min(r, rows - 1);
     const uint32_t row_elem = GU ? (uint32_t)a.row_token[row0 + rl] * (uint32_t)H : (uint32_t)rl * (uint32_t)I;
-    aoff[i] = 2u * (row_elem + 8u * (uint32_t)((lane & 15) ^ (r & 15)));
+    const uint32_t chunk = W16 ? (uint32_t)((lane & 3) ^ (r & 3)) : (uint32_t)((lane & 15) ^ (r & 15));
+    aoff[i] = 2u * (row_elem + 8u * chunk);
+    aon[i] = !W16 || v < 2 * MT;
   }
   // B: 32 wave-loads of 1 KiB (16 slots x 64 B); wave takes v = wu + 8i, i < 4.  The 16
   // slots of a wave-load are 16 consecutive weight rows starting at a multiple of 16, so
@@ -139,7 +151,7 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
     const int v = wu + 8 * i;
     const int slot = 16 * v + (lane >> 2);
     bbase[i] = (const char *)slot_mat(16 * v).q;
-    boff[i] = 4u * (uint32_t)code_index((size_t)slot_row(slot), 4 * ((lane & 3) ^ ((slot >> 2) & 3)), K);
+    boff[i] = 4u * (uint32_t)code_index((size_t)slot_row(slot), 4 * ((lane & 3) ^ ((slot >> 2) & 3)), KF * K);
   }
   // S: 16 wave-loads of 256 B (64 slots x 2 groups): v < 8 scales, v >= 8 biases.
   // Wave-load v covers tile t = (v >> 2) & 1 of the wave pair m = v & 3, so its rows come
@@ -164,11 +176,15 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
   auto issue = [&](int ss, uint8_t *st) {
     const uint32_t l = lds_addr(st);
 #pragma unroll
-    for (int i = 0; i < MT; ++i) dma16(abase + ss * 256, aoff[i], l + (wu + 8 * i) * 1024);
+    for (int i = 0; i < NA; ++i)
+      if (aon[i]) dma16(abase + ss * (W16 ? 64 : 256), aoff[i], l + (wu + 8 * i) * 1024);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma16(bbase[i] + ss * 1024, boff[i], l + kAStage + (wu + 8 * i) * 1024);
+    if (!W16) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma4(sbase[i] + ss * (4 * kQpRows), soff[i], l + kAStage + kBStage + (wu + 8 * i) * 256);
+      for (int i = 0; i < 2; ++i)
+        dma4(sbase[i] + ss * (4 * kQpRows), soff[i], l + kAStage + kBStage + (wu + 8 * i) * 256);
+    }
   };
   if (!GU && tid < MT * 32) s_gate[tid] = a.row_gate[row0 + min(tid, rows - 1)];  // read by the epilogue
   f32x16 acc[MT][2];
@@ -188,7 +204,32 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
     b_lane[i] = (64 * wu + 32 * i + (lane & 31));
     s_lane[i] = 128 * ((i << 2) | (wu >> 1)) + 64 * hf + 32 * (wu & 1) + (lane & 31);
   }
+  // bf16 weights: two 16-k slices per 32-k step, fragments straight from LDS
+  auto compute16 = [&](const uint8_t *st) {
+    const uint8_t *bb = st + kAStage;
+    const int r = lane & 31;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      u32x4 av[MT];
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        av[t] = *(const u32x4 *)(st + (t * 32 + r) * 64 + (((2 * j + hf) ^ (r & 3)) << 4));
+      const u32x4 w0 = *(const u32x4 *)(bb + b_off(b_lane[0], 2 * j + hf));
+      const u32x4 w1 = *(const u32x4 *)(bb + b_off(b_lane[1], 2 * j + hf));
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        acc[t][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w0),
+                                                            __builtin_bit_cast(bf16x8, av[t]), acc[t][0], 0, 0, 0);
+        acc[t][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w1),
+                                                            __builtin_bit_cast(bf16x8, av[t]), acc[t][1], 0, 0, 0);
+      }
+    }
+  };
   auto compute = [&](const uint8_t *st) {
+    if (W16) {
+      compute16(st);
+      return;
+    }
     const uint8_t *bb = st + kAStage;
     const uint16_t *sp = (const uint16_t *)(st + kAStage + kBStage);
     float sc[2], bi[2];
@@ -395,20 +436,20 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
 // M-blocks at the end of the block map, the shortest) are then split along K into S
 // pieces (S <= 4, S * items <= workgroups) taken from one more queue after the others
 // are empty, so the last round runs pieces of a fraction of an item each.
-template <bool GU>
+template <bool GU, bool W16>
 __device__ __forceinline__ void run_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, float *s_gate,
                                          int *s_last, const int4 &mb, int nb, int ks0, int ks1, const Piece &pc,
                                          int *claim, int *s_pend) {
   switch (mb.w) {
-    case 1: gemm_item<1, GU>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc, claim, s_pend); break;
-    case 2: gemm_item<2, GU>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc, claim, s_pend); break;
-    case 3: gemm_item<3, GU>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc, claim, s_pend); break;
-    case 4: gemm_item<4, GU>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc, claim, s_pend); break;
-    default: gemm_item<5, GU>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc, claim, s_pend); break;
+    case 1: gemm_item<1, GU, W16>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc, claim, s_pend); break;
+    case 2: gemm_item<2, GU, W16>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc, claim, s_pend); break;
+    case 3: gemm_item<3, GU, W16>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc, claim, s_pend); break;
+    case 4: gemm_item<4, GU, W16>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc, claim, s_pend); break;
+    default: gemm_item<5, GU, W16>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc, claim, s_pend); break;
   }
 }
 
-template <bool GU>
+template <bool GU, bool W16>
 __device__ void gemm_persistent(const GemmArgs &a) {
   __shared__ __attribute__((aligned(16))) uint8_t stage0[kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t stage1[kStageBytes];
@@ -420,7 +461,7 @@ __device__ void gemm_persistent(const GemmArgs &a) {
   constexpr int kMbCache = GU ? 1 : 384;
   __shared__ int4 s_mbc[kMbCache];
   const int NB = GU ? (a.I + kGateUpCols - 1) / kGateUpCols : (a.H + kDownCols - 1) / kDownCols;
-  const int nss = (GU ? a.H : a.I) / 128;
+  const int nss = (GU ? a.H : a.I) / (W16 ? 32 : 128);
   const int nmb = a.ctrl->n_mblocks;
   int m_cut = nmb, S = 1, n_tail = 0;
   if (GU && a.part) {
@@ -513,14 +554,42 @@ __device__ void gemm_persistent(const GemmArgs &a) {
     // the item takes the next ticket from the queue this one came from (the tail
     // pieces' queue for a piece)
     int *claim = q < kXcds ? &a.queue[q] : a.tail_queue;
-    run_item<GU>(a, stage0, stage1, s_gate, &s_last, mb, nb, ks0, ks1, pc, claim, &s_pend);
+    run_item<GU, W16>(a, stage0, stage1, s_gate, &s_last, mb, nb, ks0, ks1, pc, claim, &s_pend);
     cur = q;
     pq = q;
   }
 }
 
-__global__ __launch_bounds__(kGemmThreads) void k_gemm_gateup(GemmArgs a) { gemm_persistent<true>(a); }
-__global__ __launch_bounds__(kGemmThreads) void k_gemm_down(GemmArgs a) { gemm_persistent<false>(a); }
+__global__ __launch_bounds__(kGemmThreads) void k_gemm_gateup(GemmArgs a) { gemm_persistent<true, false>(a); }
+__global__ __launch_bounds__(kGemmThreads) void k_gemm_down(GemmArgs a) { gemm_persistent<false, false>(a); }
+__global__ __launch_bounds__(kGemmThreads) void k_gemm_gateup_w16(GemmArgs a) { gemm_persistent<true, true>(a); }
+__global__ __launch_bounds__(kGemmThreads) void k_gemm_down_w16(GemmArgs a) { gemm_persistent<false, true>(a); }
+
+// MOE_F_SEPARATE_DEQUANT: a stack of `rows` packed matrix rows (K columns, the tiled
+// code and scale/bias layouts) expanded to bf16 (w = s*q + b in fp32, rounded to nearest
+// even) in tiles of 16 rows x 32 k (1 KB; 16-byte chunk c4 of row r of tile (n16, tk) at
+// ((n16*(K/32) + tk)*16 + r)*4 + c4).  One thread per 16-byte output chunk (one code word).
+__global__ __launch_bounds__(256) void k_dequant_w16(const uint32_t *__restrict__ q, const uint16_t *__restrict__ sc,
+                                                     const uint16_t *__restrict__ bi, uint4 *__restrict__ dst,
+                                                     int64_t total, int K, bool qbf16) {
+  const int tpr = K / 32;  // tiles per row
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t tile = i >> 6;
+    const int within = (int)(i & 63), r = within >> 2, c4 = within & 3;
+    const int64_t n16 = tile / tpr;
+    const int tk = (int)(tile - n16 * tpr);
+    const size_t n = (size_t)(n16 * 16 + r);
+    const uint32_t w = q[code_index(n, 4 * tk + c4, K)];
+    const size_t qi = qp_index(n, (32 * tk + 8 * c4) / 64, K / 64);
+    const float s = qp_f32(sc[qi], qbf16), b = qp_f32(bi[qi], qbf16);
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o[j] = pack_bf16x2(__builtin_fmaf(s, (float)((w >> (8 * j)) & 0xfu), b),
+                         __builtin_fmaf(s, (float)((w >> (8 * j + 4)) & 0xfu), b));
+    dst[i] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
 
 // Combine: out[t] = sum over the NR = k+1 grouped rows of token t (already
 // gate-weighted), fp32 sum in slot order, bf16 result.  One workgroup per token, eight
@@ -569,12 +638,27 @@ hipError_t launch_fin(const uint16_t *y, const int32_t *slot_row, uint16_t *out,
 }  // namespace
 
 hipError_t launch_gemm_gateup(const GemmArgs &a, int n_blocks, hipStream_t s) {
-  hipLaunchKernelGGL(k_gemm_gateup, dim3(n_blocks), dim3(kGemmThreads), 0, s, a);
+  if (a.w16)
+    hipLaunchKernelGGL(k_gemm_gateup_w16, dim3(n_blocks), dim3(kGemmThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_gemm_gateup, dim3(n_blocks), dim3(kGemmThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_down(const GemmArgs &a, int n_blocks, hipStream_t s) {
-  hipLaunchKernelGGL(k_gemm_down, dim3(n_blocks), dim3(kGemmThreads), 0, s, a);
+  if (a.w16)
+    hipLaunchKernelGGL(k_gemm_down_w16, dim3(n_blocks), dim3(kGemmThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_gemm_down, dim3(n_blocks), dim3(kGemmThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_w16(const uint32_t *q, const uint16_t *sc, const uint16_t *bi, void *dst, int64_t rows,
+                              int K, bool qbf16, hipStream_t s) {
+  const int64_t total = rows * (int64_t)(K / 8);
+  const int64_t want = (total + 255) / 256;
+  hipLaunchKernelGGL(k_dequant_w16, dim3((int)(want < 16384 ? want : 16384)), dim3(256), 0, s, q, sc, bi, (uint4 *)dst,
+                     total, K, qbf16);
   return hipGetLastError();
 }
 

@@ -93,6 +93,7 @@ struct GemmArgs {
   QMat s0, s1;              // shared expert
   int E, H, I;
   bool qbf16;               // scale/bias are bf16 (else fp16)
+  bool w16;                 // w0/w1/s0/s1 .q are bf16 matrices (16 x 32 tiles), no scale/bias
   uint16_t *h;              // gate/up output [rows][I]
   uint16_t *y;              // down output, gate-weighted, per grouped row [rows][H]
 };
@@ -140,6 +141,9 @@ hipError_t launch_group(const GroupArgs &a, hipStream_t s);
 hipError_t launch_shared_gate(const uint16_t *x, const uint16_t *w, float *out, int T, int H, hipStream_t s);
 hipError_t launch_gemm_gateup(const GemmArgs &a, int n_blocks, hipStream_t s);
 hipError_t launch_gemm_down(const GemmArgs &a, int n_blocks, hipStream_t s);
+// Expand a stack of packed matrices (rows x K) into bf16 16 x 32 tiles at dst.
+hipError_t launch_dequant_w16(const uint32_t *q, const uint16_t *sc, const uint16_t *bi, void *dst, int64_t rows,
+                              int K, bool qbf16, hipStream_t s);
 hipError_t launch_finalize(const uint16_t *y, const int32_t *slot_row, uint16_t *out, int T, int H, int k,
                            hipStream_t s);
 // Workgroups that may be resident at once for the decode kernel of up to t_max tokens

@@ -67,6 +67,21 @@ class MoeLayer:
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
         B.moe_workspace_init(self.plan, self.ws.data_ptr(), self.ws_bytes, self.stream())
 
+    def with_flags(self, flags: int, max_chunk_tokens: int | None = None) -> "MoeLayer":
+        """Another plan (own workspace) over this layer's device weights, with other flags."""
+        other = MoeLayer.__new__(MoeLayer)
+        other.device, other.E, other.I, other.H, other.k = self.device, self.E, self.I, self.H, self.k
+        other.chunk = max_chunk_tokens or self.chunk
+        other.t = self.t
+        other.cfg = B.moe_config(hidden=self.H, inter=self.I, n_experts=self.E, top_k=self.k, group_size=64,
+                                 router_dtype=self.cfg.router_dtype, qparam_dtype=self.cfg.qparam_dtype,
+                                 max_chunk_tokens=other.chunk, flags=flags)
+        other.w = self.w
+        other.plan, other.ws_bytes = B.moe_plan_create(other.cfg, other.w)
+        other.ws = torch.empty(other.ws_bytes, dtype=torch.uint8, device=self.device)
+        B.moe_workspace_init(other.plan, other.ws.data_ptr(), other.ws_bytes, other.stream())
+        return other
+
     def _tiled(self, rm: torch.Tensor) -> torch.Tensor:
         """fp16 bits [E+1][N][G] row-major -> the same values in 16-row tiles."""
         out = torch.empty_like(rm)

@@ -460,15 +460,29 @@ def test_bf16_qparams_and_shared_gate(cfg):
     m.close()
 
 
-@pytest.mark.parametrize("flags,name", [(1, "force-bm32"), (5, "force-bm160"), (64, "host-routing")])
+@pytest.mark.parametrize("flags,name", [(1, "force-bm32"), (5, "force-bm160"), (64, "host-routing"),
+                                        (32, "separate-dequant"), (32 | 64 | 1, "all-ablations")])
 def test_prefill_flag_variants(flags, name):
     """The ablation configurations reach the same result: fixed 32- and 160-row M-blocks
-    (MOE_F_FORCE_BM) and host-synchronised routing with an exact grid (MOE_F_HOST_ROUTING),
+    (MOE_F_FORCE_BM), host-synchronised routing with an exact grid (MOE_F_HOST_ROUTING),
+    and weights expanded to bf16 before bf16-weight grouped GEMMs (MOE_F_SEPARATE_DEQUANT),
     on the skewed 4K workload (hot experts of 1000+ rows, 152 empty)."""
     L, x = synth.make_layer(3), synth.make_x(3)
     r, res = _prefill_case(L, x, 8, 4096, f"zipf-4k/{name}", flags=flags)
     ref = oracle.experts(x, L, r["ids"], r["gates"])
     _check_out(f"zipf-4k/{name}", res["out"], ref)
+
+
+def test_separate_dequant_ragged_shapes():
+    """MOE_F_SEPARATE_DEQUANT off the benchmark grid: H = 768, I = 384, E = 40 over ragged
+    16-token chunks (partial tiles, idle waves, the bf16 tiles of both weight stacks), and
+    bf16 scale/bias with the shared gate."""
+    for cfg in (10, 15):
+        sh = synth.shape_of(cfg)
+        L, x = synth.make_layer(cfg), synth.make_x(cfg)
+        ref = oracle.forward(x, L, sh.k)
+        r, res = _prefill_case(L, x, sh.k, sh.chunk, sh.name + "/separate-dequant", flags=32)
+        _check_out(sh.name + "/separate-dequant", res["out"], ref["out"])
 
 
 def test_prefill_no_fallback():
