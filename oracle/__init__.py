@@ -5,9 +5,10 @@ benchmark's CPU-baseline leg are the only callers.  The HIP library in
 ``sparse_moe_02_amd`` never imports this package, and this package never imports
 that one; the two share only the seeded inputs from ``synth``.
 
-The arithmetic lives in ``moe_oracle.c`` (see its header for what is computed and
-which passage of "Optimizing on-device inference for Apple Silicon" each step
-follows); this module only builds it with gcc, loads it and marshals numpy arrays.
+The arithmetic lives in ``moe_oracle.c`` (the MoE layer) and ``gdn_oracle.c`` (the
+Gated DeltaNet prefill scan); see their headers for what is computed and which
+passage of "Optimizing on-device inference for Apple Silicon" each step follows.
+This module only builds them with gcc, loads them and marshals numpy arrays.
 
 Parity unpinned: nothing.  Every function here is pinned by tests under
 ``tests/`` that do not reuse its formulas (brute force over subsets, library
@@ -24,7 +25,7 @@ import threading
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "moe_oracle.c")
+_SRCS = [os.path.join(_HERE, "moe_oracle.c"), os.path.join(_HERE, "gdn_oracle.c")]
 _LIB = os.path.join(_HERE, "libmoe_oracle.so")
 _lock = threading.Lock()
 _lib = None
@@ -34,7 +35,7 @@ def build() -> str:
     """Compile the oracle with gcc (always recompiles)."""
     tmp = _LIB + ".tmp"
     cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
-           "-std=c11", "-Wall", "-o", tmp, _SRC, "-lm"]
+           "-std=c11", "-Wall", "-o", tmp, *_SRCS, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB)
     return _LIB
@@ -62,6 +63,8 @@ def lib() -> ctypes.CDLL:
             L.oracle_group.argtypes = [P, I64, I64, I64, P, P, P, P]
             L.oracle_experts.restype = ctypes.c_int
             L.oracle_experts.argtypes = [P, I64, I64, I64, I64, I64, P, P] + [P] * 9 + [ctypes.c_int, P, P]
+            L.oracle_gdn_scan.restype = ctypes.c_int
+            L.oracle_gdn_scan.argtypes = [P] * 5 + [I64] * 5 + [P, P]
             _lib = L
     return _lib
 
@@ -180,3 +183,27 @@ def forward(x_bits, layer, k: int):
     r.update(g)
     r["out"] = out
     return r
+
+
+def gdn_scan(q_bits, k_bits, v_bits, alpha, beta, state=None):
+    """Gated DeltaNet scan over T tokens.  q_bits, k_bits: bf16 bits uint16 [T][n_kheads][d_k];
+    v_bits: uint16 [T][n_vheads][d_v]; alpha, beta: float32 [T][n_vheads]; state: S_0
+    [n_vheads][d_v][d_k] (any float dtype; zeros if None).  Returns (out float64
+    [T][n_vheads][d_v], S_T float64)."""
+    q = _c(q_bits, np.uint16)
+    k = _c(k_bits, np.uint16)
+    v = _c(v_bits, np.uint16)
+    T, hk, dk = k.shape
+    assert q.shape == k.shape
+    hv, dv = v.shape[1], v.shape[2]
+    assert v.shape[0] == T
+    a = _c(alpha, np.float32).reshape(T, hv)
+    b = _c(beta, np.float32).reshape(T, hv)
+    S = np.zeros((hv, dv, dk), np.float64) if state is None else np.array(state, dtype=np.float64, copy=True)
+    assert S.shape == (hv, dv, dk)
+    S = np.ascontiguousarray(S)
+    out = np.empty((T, hv, dv), np.float64)
+    rc = lib().oracle_gdn_scan(_p(q), _p(k), _p(v), _p(a), _p(b), T, hk, hv, dk, dv, _p(S), _p(out))
+    if rc != 0:
+        raise ValueError(f"oracle_gdn_scan failed ({rc})")
+    return out, S

@@ -1,4 +1,5 @@
-"""Seeded synthetic inputs for the sparse MoE feed-forward layer.
+"""Seeded synthetic inputs for the sparse MoE feed-forward layer (and, in
+``gdn_inputs``, for the Gated DeltaNet prefill scan).
 
 This module only draws random bytes and lays them out; it holds none of the
 layer's arithmetic (no dequantisation, no routing, no matmul).  Both the CPU
@@ -35,3 +36,4 @@ from .moe_inputs import (  # noqa: F401
     make_x,
     shape_of,
 )
+from .gdn_inputs import GDN_CONFIGS, GdnInputs, GdnShape, gdn_inputs, make_gdn  # noqa: F401,E402
