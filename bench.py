@@ -196,6 +196,7 @@ def main():
     ap.add_argument("--no-skewed", action="store_true", help="skip the skewed-routing prefill")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the measured ceilings")
     ap.add_argument("--no-ablations", action="store_true", help="skip the ablation configurations")
+    ap.add_argument("--no-gdn", action="store_true", help="skip the Gated DeltaNet prefill scan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -491,6 +492,54 @@ def main():
                               "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
             del g, xb, ob
         result["decode_batch"] = batch
+
+    if not args.no_gdn:
+        # the Gated DeltaNet prefill scan of the pages' 2K-token prompt (one layer: 16 key
+        # and 32 value heads of width 128), state resident in registers.  Algorithmic work:
+        # 3 fmas per state element per token (the dots with k and q, the rank-one update),
+        # 6 flops; peak: the vector fp32 fma rate without packed math (this library is
+        # built without packed-fp32 instructions): 256 CUs x 4 SIMDs x 16 lanes x 2 flops x
+        # 2.4 GHz = 78.6 TFLOP/s (157.3 with packed math)
+        from sparse_moe_02_amd.gdn import gdn_scan
+
+        log("bench: gated deltanet scan")
+        gs = synth.GDN_CONFIGS[1]
+        gi = synth.gdn_inputs(1, seed=0, nonzero_state=True)
+
+        def bf(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        gq, gk, gv = bf(gi.q), bf(gi.k), bf(gi.v)
+        ga, gb = torch.from_numpy(gi.alpha).to(dev), torch.from_numpy(gi.beta).to(dev)
+        gst = torch.from_numpy(gi.state).to(dev)
+        gout = torch.empty((gs.T, gs.n_vheads, gs.d), dtype=torch.bfloat16, device=dev)
+        for _ in range(3):
+            gdn_scan(gq, gk, gv, ga, gb, gst, gout, stream)
+        g_ms = time_events(lambda: gdn_scan(gq, gk, gv, ga, gb, gst, gout, stream), max(K, 10), stream, B)
+        g_us = float(np.median(g_ms)) * 1e3
+        flop = 6.0 * gs.T * gs.n_vheads * gs.d * gs.d
+        gbytes = (gi.q.nbytes + gi.k.nbytes + gi.v.nbytes + gi.alpha.nbytes + gi.beta.nbytes + 2 * gi.state.nbytes
+                  + gs.T * gs.n_vheads * gs.d * 2)
+        peak_alu = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+        gres = {"workload": f"gdn-2k: {gs.T} tokens, {gs.n_kheads} key / {gs.n_vheads} value heads of {gs.d}",
+                "us": round(g_us, 2), "us_p10_p90": [round(pct(g_ms, 10) * 1e3, 2), round(pct(g_ms, 90) * 1e3, 2)],
+                "tokens_per_s": round(gs.T / (g_us * 1e-6), 1),
+                "roofline": {"bound": "alu", "achieved": round(flop / (g_us * 1e-6) / 1e12, 3),
+                             "peak": round(peak_alu, 1), "unit": "TFLOP/s",
+                             "frac": round(flop / (g_us * 1e-6) / 1e12 / peak_alu, 4),
+                             "frac_vs_packed_peak": round(flop / (g_us * 1e-6) / 1e12 / 157.3, 4),
+                             "hbm_bytes": int(gbytes),
+                             "hbm_frac": round(gbytes / (g_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}}
+        if not args.no_cpu_baseline:
+            import oracle
+
+            t1 = time.perf_counter()
+            oracle.gdn_scan(gi.q, gi.k, gi.v, gi.alpha, gi.beta, gi.state)
+            dt = time.perf_counter() - t1
+            gres["cpu_baseline"] = {"value": round(gs.T / dt, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                                    "sample": f"the full {gs.T}-token scan ({dt:.2f} s)"}
+        result["gdn_scan"] = gres
+        del gq, gk, gv, ga, gb, gst, gout
 
     if not args.no_ceilings:
         log("bench: measured ceilings")

@@ -27,7 +27,9 @@ CTRL_DECODE_ERR_OFFSET = 88  # byte offset of the decode wait-failure word in th
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE", 4: "MOE_ERR_ALIGN",
                 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_TOKENS", 7: "MOE_ERR_DEVICE", 8: "MOE_ERR_HIP",
                 9: "MOE_ERR_ALIAS", 10: "MOE_ERR_ALLOC", 11: "MOE_ERR_WAIT"}
-MOE_ERR_WAIT = 11
+(MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_TOKENS, MOE_ERR_DEVICE,
+ MOE_ERR_HIP, MOE_ERR_ALIAS, MOE_ERR_ALLOC, MOE_ERR_WAIT) = range(1, 12)
+assert all(STATUS_NAMES[globals()[n] if n != "MOE_OK" else 0] == n for n in STATUS_NAMES.values())
 
 # moe_config.flags (include/moe.h)
 MOE_F_NONE = 0
@@ -44,7 +46,7 @@ MOE_F_HOST_ROUTING = 1 << 6
 EXPORTED = ("moe_plan_create", "moe_plan_destroy", "moe_workspace_init", "moe_workspace_check",
             "moe_forward_prefill", "moe_forward_decode", "moe_forward_decode_batch", "moe_forward_decode_static",
             "moe_pack_qparams",
-            "moe_pack_codes", "moe_status_string", "moe_version")
+            "moe_pack_codes", "moe_status_string", "moe_version", "moe_gdn_scan")
 
 
 class moe_config(ctypes.Structure):
@@ -111,6 +113,8 @@ def lib() -> ctypes.CDLL:
             L.moe_pack_qparams.argtypes = [P, P, I64, ctypes.c_int32, P]
             L.moe_pack_codes.restype = ctypes.c_int
             L.moe_pack_codes.argtypes = [P, P, I64, ctypes.c_int32, P]
+            L.moe_gdn_scan.restype = ctypes.c_int
+            L.moe_gdn_scan.argtypes = [ctypes.c_int32] * 5 + [P] * 7 + [P]
             L.moe_status_string.restype = ctypes.c_char_p
             L.moe_status_string.argtypes = [ctypes.c_int]
             L.moe_version.restype = ctypes.c_char_p
@@ -186,6 +190,12 @@ def moe_forward_decode_batch(plan, x_ptr: int, T: int, out_ptr: int, ws_ptr: int
 def moe_forward_decode_static(plan, x_ptr: int, out_ptr: int, stream: int, dbg: moe_debug_out | None = None) -> None:
     _check("moe_forward_decode_static", lib().moe_forward_decode_static(plan, x_ptr, out_ptr, stream,
                                                                         ctypes.byref(dbg) if dbg is not None else None))
+
+
+def moe_gdn_scan(T: int, n_kheads: int, n_vheads: int, d_k: int, d_v: int, q_ptr: int, k_ptr: int, v_ptr: int,
+                 alpha_ptr: int, beta_ptr: int, state_ptr: int, out_ptr: int, stream: int) -> None:
+    _check("moe_gdn_scan", lib().moe_gdn_scan(T, n_kheads, n_vheads, d_k, d_v, q_ptr, k_ptr, v_ptr, alpha_ptr,
+                                              beta_ptr, state_ptr, out_ptr, stream))
 
 
 def moe_pack_qparams(src_ptr: int, dst_ptr: int, rows: int, k: int, stream: int) -> None:

@@ -6,13 +6,16 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstddef>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
 #include <new>
+#include <utility>
 
 #include "../../include/moe.h"
+#include "../../include/gdn.h"
 #include "kernels.hpp"
 
 using namespace moe;
@@ -115,6 +118,22 @@ moe_status check_ws(const moe_plan_s *p, void *ws, size_t bytes) {
 bool overlap(const void *a, size_t na, const void *b, size_t nb) {
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
   return x < y + nb && y < x + na;
+}
+
+// gfx950 check of the current device, cached per device (plan-free entry points)
+constexpr int kMaxDevs = 64;
+std::atomic<int> g_dev_ok[kMaxDevs];  // 0 unknown, 1 gfx950, 2 other
+moe_status current_device_ok() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevs) return MOE_ERR_DEVICE;
+  int ok = g_dev_ok[dev].load(std::memory_order_relaxed);
+  if (ok == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ERR_DEVICE;
+    ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_dev_ok[dev].store(ok, std::memory_order_relaxed);
+  }
+  return ok == 1 ? MOE_OK : MOE_ERR_DEVICE;
 }
 
 hipError_t rec(const moe_debug_out *dbg, int i, hipStream_t s) {
@@ -528,6 +547,45 @@ moe_status moe_forward_decode_static(moe_plan_t p, const void *x, void *out, hip
   const moe_status st = static_scratch(stream, &base);
   if (st != MOE_OK) return st;
   return decode_launch(p, x, 1, out, reinterpret_cast<Ctrl *>(base), base + kStaticDec, p->dec_static, stream, dbg);
+}
+
+moe_status moe_gdn_scan(int32_t T, int32_t n_kheads, int32_t n_vheads, int32_t d_k, int32_t d_v, const void *q,
+                        const void *k, const void *v, const float *alpha, const float *beta, float *state,
+                        void *out, hipStream_t stream) {
+  if (T < 0) return MOE_ERR_TOKENS;
+  if (d_k != kGdnDim || d_v != kGdnDim) return MOE_ERR_SHAPE;
+  if (n_kheads < 1 || n_vheads < 1 || n_vheads > 4096 || n_vheads % n_kheads != 0) return MOE_ERR_SHAPE;
+  if (!state) return MOE_ERR_NULL;
+  if (T > 0 && (!q || !k || !v || !alpha || !beta || !out)) return MOE_ERR_NULL;
+  if (!aligned16(state)) return MOE_ERR_ALIGN;
+  if (T > 0 && (!aligned16(q) || !aligned16(k) || !aligned16(v) || ((uintptr_t)alpha & 3u) ||
+                ((uintptr_t)beta & 3u) || ((uintptr_t)out & 1u)))
+    return MOE_ERR_ALIGN;
+  const size_t nqk = (size_t)T * n_kheads * kGdnDim * 2, nv = (size_t)T * n_vheads * kGdnDim * 2;
+  const size_t ng = (size_t)T * n_vheads * 4, ns = (size_t)n_vheads * kGdnDim * kGdnDim * 4;
+  if (T > 0) {
+    // the output and the state may overlap no input and not each other
+    for (const auto &w : {std::make_pair((const void *)out, nv), std::make_pair((const void *)state, ns)})
+      if (overlap(w.first, w.second, q, nqk) || overlap(w.first, w.second, k, nqk) ||
+          overlap(w.first, w.second, v, nv) || overlap(w.first, w.second, alpha, ng) ||
+          overlap(w.first, w.second, beta, ng))
+        return MOE_ERR_ALIAS;
+    if (overlap(out, nv, state, ns)) return MOE_ERR_ALIAS;
+  }
+  const moe_status st = current_device_ok();
+  if (st != MOE_OK) return st;
+  GdnArgs a;
+  a.q = static_cast<const uint16_t *>(q);
+  a.k = static_cast<const uint16_t *>(k);
+  a.v = static_cast<const uint16_t *>(v);
+  a.alpha = alpha;
+  a.beta = beta;
+  a.state = state;
+  a.out = static_cast<uint16_t *>(out);
+  a.T = T;
+  a.hk = n_kheads;
+  a.hv = n_vheads;
+  return launch_gdn_scan(a, stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 }  // extern "C"

@@ -156,6 +156,18 @@ int decode1_capacity(int n_cu);
 int decode1_grid(const DecodeArgs &a, int capacity);
 hipError_t launch_decode1(const DecodeArgs &a, int grid, hipStream_t s);
 hipError_t launch_ctrl_init(Ctrl *c, void *clear, size_t clear_bytes, hipStream_t s);
+
+// Gated DeltaNet prefill scan (gdn.hip): heads of width kGdnDim.
+constexpr int kGdnDim = 128;
+struct GdnArgs {
+  const uint16_t *q, *k;    // [T][hk][128] bf16
+  const uint16_t *v;        // [T][hv][128] bf16
+  const float *alpha, *beta;  // [T][hv]
+  float *state;             // [hv][128][128] fp32, in: S_0, out: S_T
+  uint16_t *out;            // [T][hv][128] bf16
+  int T, hk, hv;
+};
+hipError_t launch_gdn_scan(const GdnArgs &a, hipStream_t s);
 hipError_t launch_pack_qparams(const uint16_t *src, uint16_t *dst, int64_t rows, int G, hipStream_t s);
 hipError_t launch_pack_codes(const uint32_t *src, uint32_t *dst, int64_t rows, int K, hipStream_t s);
 

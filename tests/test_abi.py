@@ -191,3 +191,34 @@ def test_product_package_does_not_import_oracle():
         if f.endswith((".py", ".c")):
             src = open(os.path.join(ROOT, "oracle", f)).read()
             assert "import sparse_moe_02_amd" not in src and "csrc" not in src
+
+
+def test_gdn_scan_validation(B):
+    """moe_gdn_scan's host checks return their statuses before touching a device; valid
+    arguments reach the device check (no GPU here: MOE_ERR_DEVICE)."""
+    L = B.lib()
+    base = 0x100000
+    q, k, v, al, be, st, out = (base + i * 0x10000000 for i in range(7))
+
+    def call(T=8, hk=2, hv=4, dk=128, dv=128, **kw):
+        a = dict(q=q, k=k, v=v, al=al, be=be, st=st, out=out)
+        a.update(kw)
+        return L.moe_gdn_scan(T, hk, hv, dk, dv, a["q"], a["k"], a["v"], a["al"], a["be"], a["st"], a["out"], None)
+
+    assert call(T=-1) == B.MOE_ERR_TOKENS
+    assert call(dk=64) == B.MOE_ERR_SHAPE
+    assert call(dv=256) == B.MOE_ERR_SHAPE
+    assert call(hk=3, hv=4) == B.MOE_ERR_SHAPE
+    assert call(hk=0) == B.MOE_ERR_SHAPE
+    assert call(hv=8192, hk=1) == B.MOE_ERR_SHAPE
+    assert call(st=None) == B.MOE_ERR_NULL
+    assert call(q=None) == B.MOE_ERR_NULL
+    assert call(T=0, q=None, k=None, v=None, al=None, be=None, out=None) == B.MOE_ERR_DEVICE
+    assert call(k=k + 8) == B.MOE_ERR_ALIGN
+    assert call(st=st + 4) == B.MOE_ERR_ALIGN
+    assert call(al=al + 2) == B.MOE_ERR_ALIGN
+    assert call(out=out + 1) == B.MOE_ERR_ALIGN
+    assert call(out=v) == B.MOE_ERR_ALIAS
+    assert call(st=q) == B.MOE_ERR_ALIAS
+    assert call(out=st) == B.MOE_ERR_ALIAS
+    assert call() == B.MOE_ERR_DEVICE
