@@ -124,6 +124,21 @@ def ceilings(dev, stream, B, dec_layers, dec_x, H, I, k):
     probes.mfma(100, sink.data_ptr(), grid, stream)
     ms = time_events(lambda: probes.mfma(iters, sink.data_ptr(), grid, stream), 3, stream, B)
     out["mfma_bf16_TFLOPs"] = round(flop / (float(np.min(ms)) * 1e-3) / 1e12, 1)
+    # the same instruction on random bf16 operands (real data switches more bits and the
+    # chip draws more power: the clock the GEMMs actually run at), and the grouped GEMM's
+    # register pipeline (two words dequantised per 2 x 5 MFMAs) without its LDS traffic
+    gen = torch.Generator(device="cpu").manual_seed(0)
+    ngrid = 512
+    src = (torch.randn(ngrid * 8 * 64 * 8, generator=gen) * 0.5).to(torch.bfloat16).to(dev)
+    iters = 2000
+    probes.mfma_data(src.data_ptr(), 20, sink.data_ptr(), ngrid, stream)
+    ms = time_events(lambda: probes.mfma_data(src.data_ptr(), iters, sink.data_ptr(), ngrid, stream), 3, stream, B)
+    out["mfma_bf16_random_data_TFLOPs"] = round(ngrid * 8 * iters * 10 * 32768 / (float(np.min(ms)) * 1e-3) / 1e12, 1)
+    iters = 250
+    probes.dequant_mfma(src.data_ptr(), 5, sink.data_ptr(), ngrid, stream)
+    ms = time_events(lambda: probes.dequant_mfma(src.data_ptr(), iters, sink.data_ptr(), ngrid, stream), 3, stream, B)
+    out["dequant_mfma_pipeline_TFLOPs"] = round(ngrid * 8 * iters * 80 * 32768 / (float(np.min(ms)) * 1e-3) / 1e12, 1)
+    del src
 
     def graph_of(fn, n):
         g = torch.cuda.CUDAGraph()
@@ -547,6 +562,8 @@ def main():
         result["ceilings"] = c
         result["roofline"]["frac_vs_measured"] = round(gu_tflops / c["mfma_bf16_TFLOPs"], 4)
         result["roofline"]["measured_peak"] = c["mfma_bf16_TFLOPs"]
+        result["roofline"]["frac_vs_random_data_mfma"] = round(gu_tflops / c["mfma_bf16_random_data_TFLOPs"], 4)
+        result["roofline"]["frac_vs_dequant_pipeline"] = round(gu_tflops / c["dequant_mfma_pipeline_TFLOPs"], 4)
         if "decode_roofline" in result:
             dr = result["decode_roofline"]
             dr["frac_vs_measured"] = round(dr["achieved"] / c["hbm_read_GBs"], 4)

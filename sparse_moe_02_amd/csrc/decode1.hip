@@ -40,6 +40,10 @@ constexpr int kDnRows = 8;              // output rows of one down task
 constexpr int kDnUnits = 5;             // (row, slot) units per 16-lane group per round
 constexpr int kDnSlots = 10;            // slots per down round: 8 rows x 10 = 16 groups x 5
 constexpr int kHStage = 5120;           // h floats staged in LDS per down round
+// In LDS every 32-float chunk of staged h takes 36 floats: the 16 lanes of a group read
+// chunks c = lane%16 with 16-byte loads, and a 144-byte chunk stride spreads them over all
+// 64 banks (a 128-byte stride would put them on two).
+__device__ __forceinline__ int h_lds(int t) { return t + 4 * (t >> 5); }
 constexpr int kSpins = 1 << 20;         // polls before a wait gives up (about a second)
 
 // This call's record tag (set by thread 0 at the start of k_decode).
@@ -85,7 +89,7 @@ struct DecShared {
   int fast;  // select_topk: the one-wave selection was certified
   float sgv;  // weight of the shared expert: sigmoid(x . w_sg), or 1
   float unit[kDnRows * kDnSlots];
-  __attribute__((aligned(16))) float h[kHStage];
+  __attribute__((aligned(16))) float h[kHStage / 32 * 36];
 };
 
 // ------------------------------------------------------------------ router (binary64)
@@ -543,35 +547,42 @@ __device__ __forceinline__ void dn_issue(const DecodeArgs &a, const DecShared &s
   }
 }
 
-// h of slots j0 .. j0+nb-1 into LDS from their tagged records: each thread issues the
-// loads of up to 16 records at once, then re-reads (one by one) the few whose tag is not
-// yet this call's.
+// h of slots j0 .. j0+nb-1 into LDS from their tagged records: each thread loads all of
+// its records at once (at most kHStage / 256 = 20), then, while any is not yet tagged
+// with this call's epoch, re-loads every such record together, so each round of the wait
+// costs one memory round trip however many records were stale.
 __device__ __forceinline__ void stage_h(const DecodeArgs &a, DecShared &sh, int j0, int nb) {
   const int tid = threadIdx.x;
   const int n = nb * a.I;
   const uint64_t *rec = a.hrec1 + (size_t)j0 * a.I;
-  constexpr int kBatch = 16;
-  for (int t0 = tid; t0 < n; t0 += kDecThreads * kBatch) {
-    uint64_t rv[kBatch];
+  constexpr int kBatch = kHStage / kDecThreads;
+  static_assert(kBatch * kDecThreads == kHStage, "one batch covers the stage");
+  uint64_t rv[kBatch];
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) {
+    const int t = tid + u * kDecThreads;
+    rv[u] = t < n ? ld_agent(&rec[t]) : tagged(s_epoch, 0u);
+  }
+  for (int i = 0;; ++i) {
+    bool ok = true;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) ok &= tag_of(rv[u]) == s_epoch;
+    if (ok) break;
+    if (i == kSpins) {
+      st_agent(&a.ctrl->d_err, 1);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int t = t0 + u * kDecThreads;
-      rv[u] = t < n ? ld_agent(&rec[t]) : tagged(s_epoch, 0u);
+      const int t = tid + u * kDecThreads;
+      if (t < n && tag_of(rv[u]) != s_epoch) rv[u] = ld_agent(&rec[t]);
     }
+  }
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int t = t0 + u * kDecThreads;
-      if (t >= n) continue;
-      for (int i = 0; tag_of(rv[u]) != s_epoch; ++i) {
-        if (i == kSpins) {
-          st_agent(&a.ctrl->d_err, 1);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-        rv[u] = ld_agent(&rec[t]);
-      }
-      sh.h[t] = __uint_as_float((uint32_t)rv[u]);
-    }
+  for (int u = 0; u < kBatch; ++u) {
+    const int t = tid + u * kDecThreads;
+    if (t < n) sh.h[h_lds(t)] = __uint_as_float((uint32_t)rv[u]);
   }
   __syncthreads();
 }
@@ -585,7 +596,7 @@ __device__ __forceinline__ void dn_accumulate(const DecodeArgs &a, DecShared &sh
     const int u = q + 16 * m;
     if (u >= kDnRows * nb) continue;
     const int jj = u % nb;
-    const float4 *hp = (const float4 *)&sh.h[jj * I + 32 * c];
+    const float4 *hp = (const float4 *)&sh.h[h_lds(jj * I + 32 * c)];
     float hv[32];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {

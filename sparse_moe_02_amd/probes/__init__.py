@@ -1,4 +1,5 @@
-"""Measured ceilings (HBM read stream, MFMA loop, launch cost, the decode step's weight
+"""Measured ceilings (HBM read stream, MFMA loop on constant and on random operands, the
+grouped GEMM's dequant + MFMA register pipeline, launch cost, the decode step's weight
 stream with and without arithmetic) for the benchmark; see ``probes.hip``.
 
 Built into ``libmoe_probes.so`` next to this file by ``sparse_moe_02_amd._build``; the
@@ -25,11 +26,13 @@ def lib() -> ctypes.CDLL:
         L.probe_read_stream.argtypes = [P, SZ, P, I, P]
         L.probe_mfma.argtypes = [I, P, I, P]
         L.probe_empty.argtypes = [I, I, P]
+        L.probe_mfma_data.argtypes = [P, I, P, I, P]
+        L.probe_dequant_mfma.argtypes = [P, I, P, I, P]
         L.probe_expert_stream.argtypes = [ctypes.POINTER(P), P, I, I, I, P, I, P]
         L.probe_flat_stream.argtypes = [P, I, P, I, P]
         L.probe_ticket.argtypes = [P, I, I, I, P]
         L.probe_handoff.argtypes = [P, ctypes.c_uint32, I, I, I, P, I, P]
-        for f in (L.probe_read_stream, L.probe_mfma, L.probe_empty, L.probe_expert_stream, L.probe_flat_stream,
+        for f in (L.probe_read_stream, L.probe_mfma, L.probe_mfma_data, L.probe_dequant_mfma, L.probe_empty, L.probe_expert_stream, L.probe_flat_stream,
                   L.probe_ticket, L.probe_handoff):
             f.restype = I
         _lib = L
@@ -47,6 +50,16 @@ def read_stream(buf_ptr: int, nbytes: int, sink_ptr: int, grid: int, stream: int
 
 def mfma(iters: int, sink_ptr: int, grid: int, stream: int) -> None:
     _ok(lib().probe_mfma(iters, sink_ptr, grid, stream), "probe_mfma")
+
+
+def mfma_data(src_ptr: int, iters: int, sink_ptr: int, grid: int, stream: int) -> None:
+    """src: grid * 8 * 64 * 16 bytes of operand data (10 MFMAs per loop iteration per wave)."""
+    _ok(lib().probe_mfma_data(src_ptr, iters, sink_ptr, grid, stream), "probe_mfma_data")
+
+
+def dequant_mfma(src_ptr: int, iters: int, sink_ptr: int, grid: int, stream: int) -> None:
+    """src as for mfma_data (80 MFMAs and 16 dequantised words per iteration per wave)."""
+    _ok(lib().probe_dequant_mfma(src_ptr, iters, sink_ptr, grid, stream), "probe_dequant_mfma")
 
 
 def empty(grid: int, threads: int, stream: int) -> None:

@@ -10,6 +10,14 @@
 //                          ceiling);
 //   probe_mfma          -- a register-only loop of v_mfma_f32_32x32x16_bf16 (the matrix
 //                          units' sustained rate, clock included);
+//   probe_mfma_data     -- the same loop on operands loaded from memory (random bf16 data
+//                          in the benchmark: the matrix units' rate on real bits, which
+//                          draw more power than the constant operands above), ten
+//                          accumulators, two waves per SIMD;
+//   probe_dequant_mfma  -- the grouped GEMM's register pipeline without LDS: per 16-k
+//                          slice two packed words dequantised (the library's own int4 ->
+//                          bf16 routine) and 2 x 5 MFMAs, in the kernel's issue pattern
+//                          (the ceiling of dequantising inside the MFMA loop);
 //   probe_empty         -- an empty kernel (launch cost, e.g. replayed from a HIP graph);
 //   probe_expert_stream -- the nine active experts' packed weights of one decode step
 //                          (gate, up, down codes + fp16 scale/bias, 16-byte loads), read
@@ -20,6 +28,8 @@
 // so the loads and the arithmetic cannot be dropped by the compiler.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "../csrc/common.hpp"
 
 namespace {
 
@@ -61,6 +71,91 @@ __global__ __launch_bounds__(256) void k_mfma(int iters, float *__restrict__ sin
 #pragma unroll
   for (int j = 0; j < 16; ++j) s += c0[j] + c1[j] + c2[j] + c3[j];
   if (s == -1.0f) sink[blockIdx.x] = s;
+}
+
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4p;
+
+// operands from memory: 5 activation-like and 2 weight-like fragments per lane
+__global__ __launch_bounds__(512) void k_mfma_data(const u32x4p *__restrict__ src, int iters,
+                                                    float *__restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  u32x4p a[5], b[2];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) a[i] = src[(blockIdx.x * 8 + i) * 64 + lane];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) b[i] = src[(blockIdx.x * 8 + 5 + i) * 64 + lane];
+  f32x16 c[10];
+#pragma unroll
+  for (int i = 0; i < 10; ++i) c[i] = (f32x16){};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 10; ++i)
+      c[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b[i & 1]),
+                                                     __builtin_bit_cast(bf16x8, a[i % 5]), c[i], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 10; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += c[i][j];
+  if (s == -1.2345f) sink[blockIdx.x] = s;
+}
+
+// one 128-k super-step's worth of the grouped GEMM's registers, repeated: 8 slices, each
+// with the two tiles' words dequantised and 2 x 5 MFMAs (5 row tiles)
+__global__ __launch_bounds__(512) void k_dequant_mfma(const u32x4p *__restrict__ src, int iters,
+                                                       float *__restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  u32x4p a[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) a[i] = src[(blockIdx.x * 8 + i) * 64 + lane];
+  const u32x4p wsrc = src[(blockIdx.x * 8 + 6) * 64 + lane];
+  uint32_t w0 = wsrc[0], w1 = wsrc[1];
+  const moe::DeqPair dp = moe::deq_pair(0.01f + lane * 1e-4f, -0.08f);
+  f32x16 acc[5][2];
+#pragma unroll
+  for (int t = 0; t < 5; ++t) acc[t][0] = acc[t][1] = (f32x16){};
+  uint32_t d0[4], d1[4];
+  moe::dequant8_bf16_m(w0, dp, d0);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      moe::dequant8_bf16_m(w1, dp, d1);
+#pragma unroll
+      for (int t = 0; t < 5; ++t) {
+        const u32x4p wv = {d0[0], d0[1], d0[2], d0[3]};
+        acc[t][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wv),
+                                                            __builtin_bit_cast(bf16x8, a[t]), acc[t][0], 0, 0, 0);
+      }
+#pragma unroll
+      for (int t = 0; t < 5; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      w0 = (w0 >> 3) | (w0 << 29);
+      w1 = (w1 >> 5) | (w1 << 27);
+      moe::dequant8_bf16_m(w0, dp, d0);
+#pragma unroll
+      for (int t = 0; t < 5; ++t) {
+        const u32x4p wv = {d1[0], d1[1], d1[2], d1[3]};
+        acc[t][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wv),
+                                                            __builtin_bit_cast(bf16x8, a[t]), acc[t][1], 0, 0, 0);
+      }
+#pragma unroll
+      for (int t = 0; t < 5; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int t = 0; t < 5; ++t)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += acc[t][0][j] + acc[t][1][j];
+  if (s == -1.2345f) sink[blockIdx.x] = s;
 }
 
 __global__ void k_empty() {}
@@ -298,6 +393,19 @@ int probe_read_stream(const void *buf, size_t bytes, void *sink, int grid, hipSt
 int probe_mfma(int iters, void *sink, int grid, hipStream_t s) {
   (void)hipGetLastError();
   hipLaunchKernelGGL(k_mfma, dim3(grid), dim3(256), 0, s, iters, (float *)sink);
+  return (int)hipGetLastError();
+}
+
+// src: grid * 8 * 64 16-byte values (the fragments each workgroup's waves read).
+int probe_mfma_data(const void *src, int iters, void *sink, int grid, hipStream_t s) {
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k_mfma_data, dim3(grid), dim3(512), 0, s, (const u32x4p *)src, iters, (float *)sink);
+  return (int)hipGetLastError();
+}
+
+int probe_dequant_mfma(const void *src, int iters, void *sink, int grid, hipStream_t s) {
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k_dequant_mfma, dim3(grid), dim3(512), 0, s, (const u32x4p *)src, iters, (float *)sink);
   return (int)hipGetLastError();
 }
 
