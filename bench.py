@@ -358,7 +358,7 @@ def main():
         return {"kernel": "k_decode (whole decode layer: router, top-k, 9 expert GEMVs)",
                 "bound": "hbm", "achieved": round(k_gbs, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(k_gbs / PEAK_HBM_GBS, 4), "timing": timing,
-                "traffic": profiled_traffic("k_decode"), "traffic_unit": "bytes per launch",
+                "traffic": profiled_traffic("k_decode1"), "traffic_unit": "bytes per launch",
                 "algorithmic_bytes_per_launch": layer_bytes}
 
     if n_dec:
