@@ -25,8 +25,9 @@
 // The launch arguments are therefore the same for every call, so a sequence of calls can
 // be captured once in a HIP graph and replayed.
 //   1. the shared expert's gate/up tasks need no routing and run first;
-//   2. router: the first ceil(E/4) workgroups compute one expert's binary64 logit per
-//      wave for every token and publish it with its error radius;
+//   2. router: every wave of the grid computes one expert's binary64 logits for a pair of
+//      tokens and publishes them with their error radii (done first, before step 1's
+//      tasks, since every selection waits for all of them);
 //   3. workgroup t (t < T) selects token t's top k (one wave, certified against the
 //      radii; the four-wave exact path when the certificate fails) and publishes the
 //      chosen experts (ascending) and their softmax gates;
@@ -140,15 +141,16 @@ struct DecShared {
 // Additions on any path of router_wave's sum: H/64 per lane, a 6-level butterfly.
 __device__ __forceinline__ int router_depth(int H) { return H / 64 + 6; }
 
-// Binary64 logits of expert e for every token, by one wave: lane takes the 8-element
-// chunks c = lane + 64 i of the router row (read once) and sums the exact products of
-// each token sequentially; a butterfly gives every lane the totals.  The loads of four
-// chunks of the row (and of the first token) are issued before any is used.  Lane 0
-// publishes (t, e)'s three records: the two halves of the logit (+ bias) and its error
-// radius.
+// Binary64 logits of expert e for tokens t0 .. t0+TT-1 (those below T), by one wave: lane
+// takes the 8-element chunks c = lane + 64 i of the router row (read once) and sums the
+// exact products of each token sequentially; a butterfly gives every lane the totals.
+// The loads of four chunks of the row (and of the first token) are issued before any is
+// used.  Lane 0 publishes (t, e)'s three records: the two halves of the logit (+ bias)
+// and its error radius.
 template <int TT>
-__device__ void router_wave(const DecodeArgs &a, int e) {
-  const int lane = threadIdx.x & 63, H = a.H, E = a.E, T = a.T;
+__device__ void router_wave(const DecodeArgs &a, int e, int t0) {
+  const int lane = threadIdx.x & 63, H = a.H, E = a.E, T = a.T - t0;
+  const uint16_t *xb = a.x + (size_t)t0 * H;
   constexpr int B4 = 4;
   double s[TT], sa[TT];
 #pragma unroll
@@ -165,7 +167,7 @@ __device__ void router_wave(const DecodeArgs &a, int e) {
         w0[u] = *(const uint4 *)(a.wr32 + (size_t)e * H + 8 * cc);
         w1[u] = *(const uint4 *)(a.wr32 + (size_t)e * H + 8 * cc + 4);
       }
-      xv[u] = *(const uint4 *)(a.x + 8 * cc);
+      xv[u] = *(const uint4 *)(xb + 8 * cc);
     }
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
@@ -174,7 +176,7 @@ __device__ void router_wave(const DecodeArgs &a, int e) {
 #pragma unroll
         for (int u = 0; u < B4; ++u) {
           const int c = c0 + u * kWave;
-          xv[u] = *(const uint4 *)(a.x + (size_t)t * H + 8 * (c < H / 8 ? c : lane));
+          xv[u] = *(const uint4 *)(xb + (size_t)t * H + 8 * (c < H / 8 ? c : lane));
         }
       }
 #pragma unroll
@@ -210,7 +212,7 @@ __device__ void router_wave(const DecodeArgs &a, int e) {
     if (lane == 0) {
       const uint64_t lb = (uint64_t)__double_as_longlong(l);
       const float rad = __double2float_ru(radius64(l, ab, H, router_depth(H)));
-      uint64_t *rec = a.lrec + 3 * ((size_t)t * E + e);
+      uint64_t *rec = a.lrec + 3 * ((size_t)(t0 + t) * E + e);
       st_agent(&rec[0], tagged(s_epoch, (uint32_t)lb));
       st_agent(&rec[1], tagged(s_epoch, (uint32_t)(lb >> 32)));
       st_agent(&rec[2], tagged(s_epoch, __float_as_uint(rad)));
@@ -794,14 +796,12 @@ __device__ __forceinline__ void dn_task(const DecodeArgs &a, DecShared &sh, int 
   }
   vm_drain();  // this thread's partial outputs have completed
   __syncthreads();
-  if (tid == 0) {
-    for (int i = 0; i < nt; ++i) {
-      const int t = nth_bit(tm, i);
-      int *ctr = a.rbctr + ((size_t)t * (H / kDecDnTask) + rb) * kCtrStride;
-      const int c = ticket(ctr);
-      sh.arrive[i] = c == k;  // the (k+1)-th arrival
-      if (c == k) st_agent(ctr, 0);
-    }
+  if (tid < nt) {  // one thread per token: the tickets are taken together
+    const int t = nth_bit(tm, tid);
+    int *ctr = a.rbctr + ((size_t)t * (H / kDecDnTask) + rb) * kCtrStride;
+    const int c = ticket(ctr);
+    sh.arrive[tid] = c == k;  // the (k+1)-th arrival
+    if (c == k) st_agent(ctr, 0);
   }
   __syncthreads();
   // the (token, row block)s this workgroup completed: sum the k+1 slots in slot order
@@ -825,10 +825,10 @@ __device__ __forceinline__ void dn_task(const DecodeArgs &a, DecShared &sh, int 
 
 // Workgroups start XCD by XCD (workgroup b on the XCD b mod 8 under the round-robin
 // placement), the XCD of workgroup 0 first and the others up to a few microseconds
-// later.  Work that every other workgroup waits for -- the router and the selections --
-// goes to the workgroups b = 0 mod 8; the shared expert's gate/up tasks, which need no
-// routing, to b = 1 mod 8, the next XCD to start; the other tasks follow.  pos(b) orders
-// the workgroups by residue 1, 2, ..., 7, 0 (then by b).
+// later.  The router is spread over every wave of the grid (every selection waits for
+// all of it); the selections go to the workgroups b = 0 mod 8; the shared expert's
+// gate/up tasks, which need no routing, to b = 1 mod 8, the next XCD to start; the other
+// tasks follow.  pos(b) orders the workgroups by residue 1, 2, ..., 7, 0 (then by b).
 __device__ __forceinline__ int wg_pos(int b, int G) {
   const int r = b % 8, ri = (r + 7) % 8;  // residue 1 -> 0, ..., 0 -> 7
   int before = 0;
@@ -853,7 +853,6 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
   const int act_max = min(T * k, E) + 1;
   const uint32_t all_tok = (1u << T) - 1u;
   const int gpos = wg_pos(b, G);          // gate/up tasks g = gpos, gpos + G, ...
-  const int nrw = 4 * ((G + 7) / 8);      // router waves: four per workgroup b = 0 mod 8
   const bool spread_sel = 8 * (T - 1) < G;
   const bool selector = spread_sel ? (b % 8 == 0 && b / 8 < T) : b < T;
   const int my_tok = spread_sel ? b / 8 : b;
@@ -864,12 +863,19 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
   if (pre_shared) dn_load(a, E, b, threadIdx.x & 15, pre);
   __syncthreads();  // s_epoch
 
-  // 1. the shared expert (active index 0): gate/up before the routing is known
-  for (int g = gpos; g < ntb; g += G) gu_task<TT>(a, sh, 0, E, all_tok, g);
+  // 1. router logits, published as records: (expert, pair of tokens) per wave over every
+  // wave of the grid, before anything else, since every selection waits for all of them
+  {
+    constexpr int TPW = 2;  // tokens per router wave
+    const int nsub = (T + TPW - 1) / TPW, nw = 4 * G;
+    for (int p = b * 4 + wv; p < E * nsub; p += nw) {
+      const int e = p / nsub, sub = p - e * nsub;
+      router_wave<TPW>(a, e, TPW * sub);
+    }
+  }
 
-  // 2. router logits, published as records
-  if (b % 8 == 0)
-    for (int e = (b / 8) * 4 + wv; e < E; e += nrw) router_wave<TT>(a, e);
+  // 2. the shared expert (active index 0): gate/up before the routing is known
+  for (int g = gpos; g < ntb; g += G) gu_task<TT>(a, sh, 0, E, all_tok, g);
 
   // 3. selection of token my_tok, published as records (ids ascending, then gates), in
   // kSrecRep copies so that few workgroups poll each copy
