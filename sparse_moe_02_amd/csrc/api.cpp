@@ -172,7 +172,7 @@ moe_status decode_launch(const moe_plan_s *p, const void *x, int T, void *out, C
   a.hrec1 = reinterpret_cast<uint64_t *>(base + L.hrec1);
   a.part = reinterpret_cast<float *>(base + L.part);
   a.rbctr = reinterpret_cast<int *>(base + L.rbctr);
-  a.endctr = reinterpret_cast<int *>(base + L.endctr);
+  a.epctr = reinterpret_cast<uint64_t *>(base + L.epctr);
   a.ctrl = ctrl;
   a.out = static_cast<uint16_t *>(out);
   if (dbg) {
@@ -195,7 +195,7 @@ moe_status decode_launch(const moe_plan_s *p, const void *x, int T, void *out, C
 // holds its own copy; host code uses only the address hipGetSymbolAddress returns for the
 // current device (the array's name is a host-side stand-in).  The first call on a device
 // clears the array with a kernel on the caller's stream; later calls rely on the decode
-// protocol itself (tags per call; the last arriver of every counter resets it).
+// protocol itself (a fresh tag per call from counters that only grow).
 constexpr size_t kStaticDec = 256;
 
 constexpr int kMaxDevices = 64;

@@ -32,6 +32,29 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)(pack_bf16x2(f, 0.f) & 0xffffu); }
 
+// c + a.lo b.lo + a.hi b.hi for two pairs of bf16 (v_dot2_f32_bf16; the products are exact
+// in fp32).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// Codes p and p + 4 (p < 4) of a packed word of eight 4-bit codes as the bf16 pair
+// (128 + code p, 128 + code p + 4): each code lands in the low mantissa bits of 128
+// (0x4300), so the numbers are exact.
+__device__ __forceinline__ uint32_t code_pair(uint32_t w, int p) {
+  return ((w >> (4 * p)) & 0x000f000fu) | 0x43004300u;
+}
+
+// Eight bf16 values v0..v7 held as natural pairs (v0,v1) (v2,v3) (v4,v5) (v6,v7), regrouped
+// into the pairs (v_p, v_p+4) that match code_pair.
+__device__ __forceinline__ void pairs_p4(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, uint32_t *o) {
+  o[0] = __builtin_amdgcn_perm(w2, w0, 0x05040100u);
+  o[1] = __builtin_amdgcn_perm(w2, w0, 0x07060302u);
+  o[2] = __builtin_amdgcn_perm(w3, w1, 0x05040100u);
+  o[3] = __builtin_amdgcn_perm(w3, w1, 0x07060302u);
+}
+
 __device__ __forceinline__ float fp16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
 // A scale or bias value: fp16 bits, or bf16 bits when bf16 (the pages' checkpoint format).
@@ -195,6 +218,32 @@ __device__ __forceinline__ T ld_agent(const T *p) {
 __device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0xF70); }  // vmcnt(0)
 __device__ __forceinline__ int ticket(int *p) {
   return __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Tag of this call's hand-off records, taken at the start of the call with no work at its
+// end.  Eight call counters (64-bit, 256 bytes apart): workgroup b adds to counter b % 8,
+// 1 each except the first workgroup of every group, which adds the rest of kEpochUnit
+// (workgroup 0 also adds a whole unit to the counters of groups with no workgroup), so
+// every call moves every counter by exactly kEpochUnit and each ticket of the n-th call
+// on a workspace lies in [n kEpochUnit, (n+1) kEpochUnit) whatever the grid, for both
+// decode kernels.  Calls on one stream run one after the other, so no call's tickets mix
+// with the next one's.  The tag is n mod (2^32 - 1) plus 1: never 0 (the value of
+// cleared records) and different in consecutive calls.
+constexpr uint64_t kEpochUnit = uint64_t(1) << 24;
+// The ticket (the atomic's return value is waited for at its first use) ...
+__device__ __forceinline__ uint64_t epoch_ticket(uint64_t *ctr, int stride_u64, int b, int G) {
+  const int g = b & 7;
+  const int n_g = G / 8 + (g < G % 8 ? 1 : 0);
+  if (b == 0)
+    for (int g2 = G; g2 < 8; ++g2)
+      __hip_atomic_fetch_add(ctr + (size_t)g2 * stride_u64, kEpochUnit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t w = b < 8 ? kEpochUnit - (uint64_t)(n_g - 1) : uint64_t(1);
+  return __hip_atomic_fetch_add(ctr + (size_t)g * stride_u64, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// ... and the tag it gives.
+__device__ __forceinline__ uint32_t epoch_of(uint64_t t) { return (uint32_t)((t / kEpochUnit) % 0xffffffffull) + 1u; }
+__device__ __forceinline__ uint32_t take_epoch(uint64_t *ctr, int stride_u64, int b, int G) {
+  return epoch_of(epoch_ticket(ctr, stride_u64, b, G));
 }
 
 }  // namespace moe

@@ -19,10 +19,9 @@
 // (an 8-byte word holding a 32-bit value and the call's 32-bit tag, written with one
 // device-scope store and read with device-scope loads, so a reader accepts a value
 // exactly when its tag is this call's) or as plain device-scope stores followed by a
-// tagged flag once they have completed.  The tag lives in the workspace: every
-// workgroup reads the last call's tag at its start and uses the next one; the last
-// workgroup to finish (two-level tickets on counters 256 bytes apart) stores it back.
-// The launch arguments are therefore the same for every call, so a sequence of calls can
+// tagged flag once they have completed.  The tag comes from call counters in the
+// workspace, one ticket per workgroup at its start (take_epoch), shared with the
+// one-token kernel.  The launch arguments are therefore the same for every call, so a sequence of calls can
 // be captured once in a HIP graph and replayed.
 //   1. the shared expert's gate/up tasks need no routing and run first;
 //   2. router: every wave of the grid computes one expert's binary64 logits for a pair of
@@ -70,8 +69,6 @@ constexpr int kSpins = 1 << 20;       // polls before a wait gives up (about a s
 constexpr int kActMax = kMaxDecodeT * kMaxTopK + 1;
 constexpr int kSrecRep = 16;          // copies of the selection records
 
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
-
 // This call's record tag (set by thread 0 at the start of k_decode).
 __shared__ uint32_t s_epoch;
 
@@ -86,10 +83,6 @@ __device__ __forceinline__ QMat expert_mat(const QMat &routed, const QMat &share
 
 __device__ __forceinline__ uint64_t tagged(uint32_t epoch, uint32_t v) { return ((uint64_t)epoch << 32) | v; }
 __device__ __forceinline__ uint32_t tag_of(uint64_t r) { return (uint32_t)(r >> 32); }
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
-}
 
 // The eight 4-bit codes of a word as four bf16 pairs holding 128 + code (exact): codes
 // 2j, 2j+1 are byte j of the low and of the high nibbles.
@@ -107,13 +100,13 @@ __device__ __forceinline__ void codes_bf16(uint32_t w, uint32_t *o) {
 __device__ __forceinline__ float dot32(const uint32_t (&o)[16], const uint32_t *v) {
   float d = 0.f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) d = dot2(o[i], v[i], d);
+  for (int i = 0; i < 16; ++i) d = dot2_bf16(o[i], v[i], d);
   return d;
 }
 __device__ __forceinline__ float sum32(const uint32_t *v) {
   float d = 0.f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) d = dot2(0x3f803f80u, v[i], d);  // pairs of 1.0
+  for (int i = 0; i < 16; ++i) d = dot2_bf16(0x3f803f80u, v[i], d);  // pairs of 1.0
   return d;
 }
 
@@ -717,7 +710,7 @@ __device__ __forceinline__ void dn_task(const DecodeArgs &a, DecShared &sh, int 
           const uint4 xv = *(const uint4 *)(a.x + (size_t)t * H + 8 * c);
           const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) z[t] = dot2(xw[i], ww[i], z[t]);
+          for (int i = 0; i < 4; ++i) z[t] = dot2_bf16(xw[i], ww[i], z[t]);
         }
       }
 #pragma unroll
@@ -843,10 +836,7 @@ template <int TT>
 __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
   __shared__ DecShared sh;
   const int b = blockIdx.x, G = gridDim.x, tid = threadIdx.x, wv = tid >> 6;
-  if (tid == 0) {
-    uint32_t ep = ld_agent(&a.ctrl->d_epoch) + 1u;
-    s_epoch = ep ? ep : 1u;
-  }
+  if (tid == 0) s_epoch = take_epoch(a.epctr, kCtrStride / 2, b, G);
   const int T = a.T, E = a.E, k = a.k;
   const int ntb = a.I / kDecGuTask;       // gate/up tasks per active expert
   const int nrb = a.H / kDecDnTask;       // down tasks per active expert
@@ -915,21 +905,6 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
       dn_task<TT>(a, sh, act, sh.act_e[act], sh.act_m[act], d - act * nrb, pre);
     }
   }
-
-  // 7. the last workgroup to finish publishes this call's tag for the next call (every
-  // workgroup read the old one before taking its ticket): eight group counters, then one
-  __syncthreads();
-  if (tid == 0) {
-    const int grp = b % 8, n_g = G / 8 + (grp < G % 8 ? 1 : 0);
-    int *cg = a.endctr + (1 + grp) * kCtrStride;
-    if (ticket(cg) == n_g - 1) {
-      st_agent(cg, 0);
-      if (ticket(a.endctr) == min(G, 8) - 1) {
-        st_agent(a.endctr, 0);
-        st_agent(&a.ctrl->d_epoch, s_epoch);
-      }
-    }
-  }
 }
 
 template <int TT>
@@ -952,21 +927,22 @@ DecodeLayout decode_layout(int H, int E, int k, int I, int t_max) {
     return at;
   };
   const size_t T = (size_t)t_max, K1 = (size_t)k + 1;
-  if (t_max <= 1) {  // the one-token kernel: logit and h records and the end counters only
-    L.lrec = take((size_t)E * 3 * 8);
-    L.hrec1 = take(K1 * I * 8);
-    L.endctr = take(9 * kCtrStride * 4);
+  // the call counters first, at the same offset for every shape: a region shared by the
+  // plans of different layers keeps one consistent count of calls
+  L.epctr = take(8 * kCtrStride * 4);
+  if (t_max <= 1) {  // the one-token kernel: logit and h records only
+    L.lrec = take((size_t)kLrecRep * E * 3 * 8);
+    L.hrec1 = take(K1 * I / 2 * 8);
     L.total = o;
     return L;
   }
-  L.lrec = take(T * E * 3 * 8);
+  L.lrec = take(std::max<size_t>(T, kLrecRep) * E * 3 * 8);
   L.srec = take(kSrecRep * T * 2 * k * 8);
   L.hflag = take((std::min<size_t>(T * k, E) + 1) * (I / kDecGuTask) * 8);
   L.hval = take(T * K1 * I * 4);
-  L.hrec1 = take(K1 * I * 8);
+  L.hrec1 = take(K1 * I / 2 * 8);
   L.part = take(T * K1 * H * 4);
   L.rbctr = take(T * (H / kDecDnTask) * kCtrStride * 4);
-  L.endctr = take(9 * kCtrStride * 4);
   L.total = o;
   return L;
 }

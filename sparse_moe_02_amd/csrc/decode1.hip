@@ -16,12 +16,11 @@
 // records: an 8-byte word holding a 32-bit value and the call's 32-bit epoch, written
 // with one device-scope store and read with device-scope loads, so a reader accepts a
 // value exactly when its tag is this call's epoch; no wait uses a counter or an atomic
-// read-modify-write (those serialise on one address).  The epoch lives in the
-// workspace: every workgroup reads the last call's epoch at its start and uses the next
-// one; the last workgroup to finish stores it back (two-level tickets: eight group
-// counters, then one, each on its own 256-byte line -- one counter for every workgroup
-// measured about 3 us per launch).  The launch arguments are therefore the same for
-// every call, so a sequence of calls can be captured once in a HIP graph and replayed.
+// read-modify-write (those serialise on one address).  The epoch comes from call
+// counters in the workspace, one ticket per workgroup at its start (take_epoch), so
+// nothing is left to do once a workgroup's last output is stored.  The launch arguments
+// are therefore the same for every call, so a sequence of calls can be captured once in
+// a HIP graph and replayed.
 #include <type_traits>
 
 #include "common.hpp"
@@ -39,11 +38,12 @@ static_assert(kGuRows == 4 && kGuTask % 4 == 0 && kQpRows % 4 == 0, "a wave read
 constexpr int kDnRows = 8;              // output rows of one down task
 constexpr int kDnUnits = 5;             // (row, slot) units per 16-lane group per round
 constexpr int kDnSlots = 10;            // slots per down round: 8 rows x 10 = 16 groups x 5
-constexpr int kHStage = 5120;           // h floats staged in LDS per down round
-// In LDS every 32-float chunk of staged h takes 36 floats: the 16 lanes of a group read
-// chunks c = lane%16 with 16-byte loads, and a 144-byte chunk stride spreads them over all
-// 64 banks (a 128-byte stride would put them on two).
-__device__ __forceinline__ int h_lds(int t) { return t + 4 * (t >> 5); }
+constexpr int kHStage = 5120;           // h values staged in LDS per down round
+// In LDS every 32-element chunk of staged h (16 words of bf16 pairs) takes 20 words: the
+// 16 lanes of a group read chunks c = lane%16 with 16-byte loads, and an 80-byte chunk
+// stride puts them on 16 different groups of 4 banks (a 64-byte stride would put four
+// lanes on each).
+constexpr int kHChunkWords = 20;
 constexpr int kSpins = 1 << 20;         // polls before a wait gives up (about a second)
 
 // This call's record tag (set by thread 0 at the start of k_decode).
@@ -58,22 +58,20 @@ __device__ __forceinline__ QMat expert_mat(const QMat &routed, const QMat &share
   return m;
 }
 
-// sum_i v[i] * code_i over the 32 codes of four packed words
-__device__ __forceinline__ float dot_codes32(const uint4 &w, const float (&v)[32]) {
+// GEMV arithmetic: per group of 64, sum_i v_i (s q_i + b) = s sum_i v_i (128 + q_i) +
+// (b - 128 s) sum_i v_i, with 128 + q exact in bf16 (code_pair) and v_dot2_f32_bf16 taking
+// two products per instruction.  dot_chunk: sum over the 32 elements of a chunk of
+// (128 + code) v, the codes of four packed words, v as 16 pairs in pairs_p4 order.
+__device__ __forceinline__ float dot_chunk(const uint4 &w, const uint32_t (&v)[16]) {
   const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-  float s = 0.f;
+  float d = 0.f;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    uint32_t lo = ws[q] & 0x0f0f0f0fu, hi = (ws[q] >> 4) & 0x0f0f0f0fu;
-    asm("" : "+v"(lo), "+v"(hi));  // one v_cvt_f32_ubyteN per code
+  for (int q = 0; q < 4; ++q)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      s = __builtin_fmaf(v[8 * q + 2 * j], (float)((lo >> (8 * j)) & 0xffu), s);
-      s = __builtin_fmaf(v[8 * q + 2 * j + 1], (float)((hi >> (8 * j)) & 0xffu), s);
-    }
-  }
-  return s;
+    for (int p = 0; p < 4; ++p) d = dot2_bf16(code_pair(ws[q], p), v[4 * q + p], d);
+  return d;
 }
+constexpr uint32_t kOnes = 0x3f803f80u;  // the bf16 pair (1, 1)
 
 __device__ __forceinline__ uint64_t tagged(uint32_t epoch, uint32_t v) { return ((uint64_t)epoch << 32) | v; }
 __device__ __forceinline__ uint32_t tag_of(uint64_t r) { return (uint32_t)(r >> 32); }
@@ -89,7 +87,8 @@ struct DecShared {
   int fast;  // select_topk: the one-wave selection was certified
   float sgv;  // weight of the shared expert: sigmoid(x . w_sg), or 1
   float unit[kDnRows * kDnSlots];
-  __attribute__((aligned(16))) float h[kHStage / 32 * 36];
+  __attribute__((aligned(16))) uint32_t hb[kHStage / 32 * kHChunkWords];  // staged h, pairs_p4 order
+  float hsum[kHStage / 32];  // sum of each staged chunk
 };
 
 // ------------------------------------------------------------------ router (binary64)
@@ -100,7 +99,10 @@ __device__ __forceinline__ int router_depth(int H) { return 8 * ((H + 2047) / 20
 
 // Binary64 logit of expert e (exact products, summed lane-sequentially, then over the
 // wave, then over the four waves in order) and sum |x w|, in every thread.
-__device__ void router_logit(const DecodeArgs &a, DecShared &sh, int e, double &l, double &ab) {
+// With set_ep, thread 0 also stores the call's tag (from the ticket tk, in flight until
+// then) before the first barrier.
+__device__ void router_logit(const DecodeArgs &a, DecShared &sh, int e, double &l, double &ab, bool set_ep,
+                             uint64_t tk) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, H = a.H;
   double s = 0.0, sa = 0.0;
   for (int c = tid; c < H / 8; c += kDecThreads) {
@@ -131,6 +133,7 @@ __device__ void router_logit(const DecodeArgs &a, DecShared &sh, int e, double &
     sh.red[0][wv] = s;
     sh.red[1][wv] = sa;
   }
+  if (set_ep && tid == 0) s_epoch = epoch_of(tk);
   __syncthreads();
   l = ((sh.red[0][0] + sh.red[0][1]) + sh.red[0][2]) + sh.red[0][3];
   ab = ((sh.red[1][0] + sh.red[1][1]) + sh.red[1][2]) + sh.red[1][3];
@@ -138,9 +141,14 @@ __device__ void router_logit(const DecodeArgs &a, DecShared &sh, int e, double &
   __syncthreads();
 }
 
+// This workgroup's copy of the logit records.
+__device__ __forceinline__ const uint64_t *lrec_copy(const DecodeArgs &a) {
+  return a.lrec + (size_t)(blockIdx.x % kLrecRep) * a.E * 3;
+}
+
 // Wait for expert e's three logit records of this call.
 __device__ void read_logit(const DecodeArgs &a, int e, double &v, double &r) {
-  const uint64_t *rec = a.lrec + 3 * (size_t)e;
+  const uint64_t *rec = lrec_copy(a) + 3 * (size_t)e;
   for (int i = 0;; ++i) {
     const uint64_t r0 = ld_agent(&rec[0]), r1 = ld_agent(&rec[1]), r2 = ld_agent(&rec[2]);
     if (tag_of(r0) == s_epoch && tag_of(r1) == s_epoch && tag_of(r2) == s_epoch) {
@@ -237,12 +245,13 @@ __device__ bool select_topk_wave(const DecodeArgs &a, DecShared &sh, bool write_
 #pragma unroll
   for (int i = 0; i < NV; ++i) valid[i] = lane + kWave * i < E;
   uint64_t rec[NV][3];
+  const uint64_t *lr = lrec_copy(a);
   for (int it = 0;; ++it) {
     bool ok = true;
 #pragma unroll
     for (int i = 0; i < NV; ++i)
 #pragma unroll
-      for (int j = 0; j < 3; ++j) rec[i][j] = valid[i] ? ld_agent(&a.lrec[3 * (size_t)(lane + kWave * i) + j]) : 0u;
+      for (int j = 0; j < 3; ++j) rec[i][j] = valid[i] ? ld_agent(&lr[3 * (size_t)(lane + kWave * i) + j]) : 0u;
 #pragma unroll
     for (int i = 0; i < NV; ++i)
 #pragma unroll
@@ -453,24 +462,18 @@ __device__ __forceinline__ void gu_issue(const DecodeArgs &a, const QMat &Gm, co
 
 __device__ __forceinline__ void gu_accumulate(const GuLoad &L, bool bf, float (&ag)[kGuRows], float (&au)[kGuRows]) {
   if (!L.ok) return;
-  float xf[32];
+  uint32_t xp[16];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t xw[4] = {L.x[q].x, L.x[q].y, L.x[q].z, L.x[q].w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      xf[8 * q + 2 * i] = bf16_lo(xw[i]);
-      xf[8 * q + 2 * i + 1] = bf16_hi(xw[i]);
-    }
-  }
+  for (int q = 0; q < 4; ++q) pairs_p4(L.x[q].x, L.x[q].y, L.x[q].z, L.x[q].w, &xp[4 * q]);
   float xs = 0.f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) xs += xf[i];
+  for (int i = 0; i < 16; ++i) xs = dot2_bf16(kOnes, xp[i], xs);
 #pragma unroll
   for (int r = 0; r < kGuRows; ++r) {
     auto half = [&](uint2 v) { return qp_f32(((r >> 1) ? v.y : v.x) >> (16 * (r & 1)), bf); };
-    ag[r] += half(L.sg) * dot_codes32(L.wg[r], xf) + half(L.bg) * xs;
-    au[r] += half(L.su) * dot_codes32(L.wu[r], xf) + half(L.bu) * xs;
+    const float sg = half(L.sg), su = half(L.su);
+    ag[r] += sg * dot_chunk(L.wg[r], xp) + (half(L.bg) - 128.0f * sg) * xs;
+    au[r] += su * dot_chunk(L.wu[r], xp) + (half(L.bu) - 128.0f * su) * xs;
   }
 }
 
@@ -514,8 +517,11 @@ __device__ __forceinline__ void gu_task(const DecodeArgs &a, const DecShared &sh
     const float us = wave_sum(au[r]);
     if (lane == r) hv = gs / (1.0f + __expf(-gs)) * us;
   }
-  const size_t row = (size_t)j * I + r0;
-  if (lane < kGuRows) st_agent(&a.hrec1[row + lane], tagged(s_epoch, __float_as_uint(hv)));
+  // rows r0 + 2p and r0 + 2p + 1 as one record (lane p < 2): their h in bf16, the even
+  // row in the low half
+  const float h0 = __shfl(hv, 2 * (lane & 1)), h1 = __shfl(hv, 2 * (lane & 1) + 1);
+  const size_t pr = ((size_t)j * I + r0) / 2;
+  if (lane < kGuRows / 2) st_agent(&a.hrec1[pr + lane], tagged(s_epoch, pack_bf16x2(h0, h1)));
 }
 
 // ------------------------------------------------------------------ down
@@ -547,26 +553,31 @@ __device__ __forceinline__ void dn_issue(const DecodeArgs &a, const DecShared &s
   }
 }
 
-// h of slots j0 .. j0+nb-1 into LDS from their tagged records: each thread loads all of
-// its records at once (at most kHStage / 256 = 20), then, while any is not yet tagged
-// with this call's epoch, re-loads every such record together, so each round of the wait
-// costs one memory round trip however many records were stale.
+// h of slots j0 .. j0+nb-1 into LDS from their tagged records (two bf16 values each, in
+// row order).  Thread t takes the 8-element groups g = t + 256 u, i.e. records 4g..4g+3:
+// it loads all of its records at once and, while any is not yet tagged with this call's
+// epoch, re-loads every such record together, so each round of the wait costs one
+// memory round trip however many records were stale.  A group is stored regrouped for
+// code_pair (pairs_p4) as words 4(g mod 4) .. 4(g mod 4)+3 of its 32-element chunk; then
+// each chunk's sum.
 __device__ __forceinline__ void stage_h(const DecodeArgs &a, DecShared &sh, int j0, int nb) {
-  const int tid = threadIdx.x;
-  const int n = nb * a.I;
-  const uint64_t *rec = a.hrec1 + (size_t)j0 * a.I;
-  constexpr int kBatch = kHStage / kDecThreads;
-  static_assert(kBatch * kDecThreads == kHStage, "one batch covers the stage");
-  uint64_t rv[kBatch];
+  const int tid = threadIdx.x, I = a.I;
+  const int ng = nb * I / 8;
+  const uint64_t *rec = a.hrec1 + (size_t)j0 * I / 2;
+  constexpr int kG = (kHStage / 8 + kDecThreads - 1) / kDecThreads;
+  uint64_t rv[kG][4];
 #pragma unroll
-  for (int u = 0; u < kBatch; ++u) {
-    const int t = tid + u * kDecThreads;
-    rv[u] = t < n ? ld_agent(&rec[t]) : tagged(s_epoch, 0u);
+  for (int u = 0; u < kG; ++u) {
+    const int g = tid + u * kDecThreads;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rv[u][r] = g < ng ? ld_agent(&rec[4 * g + r]) : tagged(s_epoch, 0u);
   }
   for (int i = 0;; ++i) {
     bool ok = true;
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) ok &= tag_of(rv[u]) == s_epoch;
+    for (int u = 0; u < kG; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ok &= tag_of(rv[u][r]) == s_epoch;
     if (ok) break;
     if (i == kSpins) {
       st_agent(&a.ctrl->d_err, 1);
@@ -574,15 +585,35 @@ __device__ __forceinline__ void stage_h(const DecodeArgs &a, DecShared &sh, int 
     }
     __builtin_amdgcn_s_sleep(1);
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int t = tid + u * kDecThreads;
-      if (t < n && tag_of(rv[u]) != s_epoch) rv[u] = ld_agent(&rec[t]);
+    for (int u = 0; u < kG; ++u) {
+      const int g = tid + u * kDecThreads;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (g < ng && tag_of(rv[u][r]) != s_epoch) rv[u][r] = ld_agent(&rec[4 * g + r]);
     }
   }
 #pragma unroll
-  for (int u = 0; u < kBatch; ++u) {
-    const int t = tid + u * kDecThreads;
-    if (t < n) sh.h[h_lds(t)] = __uint_as_float((uint32_t)rv[u]);
+  for (int u = 0; u < kG; ++u) {
+    const int g = tid + u * kDecThreads;
+    if (g < ng) {
+      uint32_t o[4];
+      pairs_p4((uint32_t)rv[u][0], (uint32_t)rv[u][1], (uint32_t)rv[u][2], (uint32_t)rv[u][3], o);
+      *(uint4 *)&sh.hb[(g >> 2) * kHChunkWords + 4 * (g & 3)] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+  __syncthreads();
+  if (tid < nb * I / 32) {
+    const uint4 *hp = (const uint4 *)&sh.hb[tid * kHChunkWords];
+    float hs = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = hp[i];
+      hs = dot2_bf16(kOnes, v.x, hs);
+      hs = dot2_bf16(kOnes, v.y, hs);
+      hs = dot2_bf16(kOnes, v.z, hs);
+      hs = dot2_bf16(kOnes, v.w, hs);
+    }
+    sh.hsum[tid] = hs;
   }
   __syncthreads();
 }
@@ -595,21 +626,19 @@ __device__ __forceinline__ void dn_accumulate(const DecodeArgs &a, DecShared &sh
   for (int m = 0; m < kDnUnits; ++m) {
     const int u = q + 16 * m;
     if (u >= kDnRows * nb) continue;
-    const int jj = u % nb;
-    const float4 *hp = (const float4 *)&sh.h[h_lds(jj * I + 32 * c)];
-    float hv[32];
+    const int ch = (u % nb) * (I / 32) + c;
+    const uint4 *hp = (const uint4 *)&sh.hb[ch * kHChunkWords];
+    uint32_t hv[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float4 v = hp[i];
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = hp[i];
       hv[4 * i] = v.x;
       hv[4 * i + 1] = v.y;
       hv[4 * i + 2] = v.z;
       hv[4 * i + 3] = v.w;
     }
-    float hs = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) hs += hv[i];
-    acc[m] += qp_f32(L.s[m], a.qbf16) * dot_codes32(L.w[m], hv) + qp_f32(L.b[m], a.qbf16) * hs;
+    const float sc = qp_f32(L.s[m], a.qbf16);
+    acc[m] += sc * dot_chunk(L.w[m], hv) + (qp_f32(L.b[m], a.qbf16) - 128.0f * sc) * sh.hsum[ch];
   }
 }
 
@@ -657,11 +686,10 @@ __device__ __forceinline__ void dn_task(const DecodeArgs &a, DecShared &sh, int 
 __global__ __launch_bounds__(kDecThreads) void k_decode1(DecodeArgs a) {
   __shared__ DecShared sh;
   const int b = blockIdx.x, G = gridDim.x, tid = threadIdx.x;
-  if (tid == 0) {
-    uint32_t ep = ld_agent(&a.ctrl->d_epoch) + 1u;
-    s_epoch = ep ? ep : 1u;
-  }
-  __syncthreads();
+  // the call's ticket goes out now; thread 0 stores its tag to s_epoch in the first router
+  // pass (or after the router loop) before any record is written or read
+  uint64_t tk = 0;
+  if (tid == 0) tk = epoch_ticket(a.epctr, kCtrStride / 2, b, G);
   const int E = a.E, k = a.k;
   const int n_gu = (k + 1) * (a.I / kGuTask), n_dn = a.H / kDnRows;
   const int first_shared = k * (a.I / kGuTask);  // gate/up tasks from here on are the shared expert's
@@ -691,18 +719,23 @@ __global__ __launch_bounds__(kDecThreads) void k_decode1(DecodeArgs a) {
   const bool gu_early = b < n_gu && b >= first_shared;
   if (gu_early) gu_start(a, sh, b, gl);
 
-  // 1. router logits, published as records
+  // 1. router logits, published as records, kLrecRep copies of each (every workgroup
+  // reads all of them, so the readers of one memory line are fewer)
   for (int e = b; e < E; e += G) {
     double l, ab;
-    router_logit(a, sh, e, l, ab);
-    if (tid == 0) {
+    router_logit(a, sh, e, l, ab, e == b, tk);
+    if (tid < 3 * kLrecRep) {
+      const int w = tid % 3, cp = tid / 3;
       const uint64_t lb = (uint64_t)__double_as_longlong(l);
-      const float rad = __double2float_ru(radius64(l, ab, a.H, router_depth(a.H)));
-      uint64_t *rec = a.lrec + 3 * (size_t)e;
-      st_agent(&rec[0], tagged(s_epoch, (uint32_t)lb));
-      st_agent(&rec[1], tagged(s_epoch, (uint32_t)(lb >> 32)));
-      st_agent(&rec[2], tagged(s_epoch, __float_as_uint(rad)));
+      const uint32_t v = w == 0 ? (uint32_t)lb
+                       : w == 1 ? (uint32_t)(lb >> 32)
+                                : __float_as_uint(__double2float_ru(radius64(l, ab, a.H, router_depth(a.H))));
+      st_agent(&a.lrec[((size_t)cp * E + e) * 3 + w], tagged(s_epoch, v));
     }
+  }
+  if (b >= E) {
+    if (tid == 0) s_epoch = epoch_of(tk);
+    __syncthreads();
   }
 
   if (gu_early) gu_task(a, sh, b, gl);
@@ -729,21 +762,6 @@ __global__ __launch_bounds__(kDecThreads) void k_decode1(DecodeArgs a) {
   for (int d = b; d < n_dn; d += G) {
     dn_task(a, sh, d, dl, dn_pre);
     dn_pre = false;
-  }
-
-  // the last workgroup to finish publishes this call's epoch for the next call (every
-  // workgroup read the old one before taking its ticket)
-  __syncthreads();
-  if (tid == 0) {
-    const int grp = b % 8, n_g = G / 8 + (grp < G % 8 ? 1 : 0);
-    int *cg = a.endctr + (1 + grp) * kCtrStride;
-    if (ticket(cg) == n_g - 1) {
-      st_agent(cg, 0);
-      if (ticket(a.endctr) == min(G, 8) - 1) {
-        st_agent(a.endctr, 0);
-        st_agent(&a.ctrl->d_epoch, s_epoch);
-      }
-    }
   }
 }
 

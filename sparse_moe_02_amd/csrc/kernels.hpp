@@ -37,8 +37,7 @@ struct Ctrl {
   int q_tail;            // gate/up tail-piece queue (reset by the group kernel)
   int pad2;
   int d_err;             // decode: a wait ran out of polls (sticky; cleared by workspace init)
-  uint32_t d_epoch;      // decode: tag of the last finished call's records (0 after init)
-  int d_done;            // decode: workgroups of the running call that have finished
+  int pad3[2];
   int pad[39];
 };
 static_assert(sizeof(Ctrl) == 256, "control block is one 256-byte slot");
@@ -102,6 +101,7 @@ constexpr int kMaxDecodeT = 8;     // tokens of one decode call (a verification 
 constexpr int kDecGuTask = 16;     // rows of one decode gate/up task
 constexpr int kDecDnTask = 64;     // output rows of one decode down task
 constexpr int kCtrStride = 64;     // ints between two completion counters (256 bytes)
+constexpr int kLrecRep = 8;        // copies of the one-token kernel's logit records
 
 struct DecodeArgs {
   const uint16_t *x;        // [T][H]
@@ -114,13 +114,14 @@ struct DecodeArgs {
   bool qbf16;               // scale/bias are bf16 (else fp16)
   const uint16_t *sgate;    // [H] bf16 shared-expert gate vector, or null (weight 1)
   uint64_t *lrec;           // [T][E][3] tagged records: low and high word of the binary64 logit, radius
+                            // (one-token kernel: [kLrecRep][E][3], copies of the same records)
   uint64_t *srec;           // [T][2k] tagged records: the chosen experts (ascending), then their gates
   uint64_t *hflag;          // [min(T*k, E) + 1][I/16] tagged: gate/up task (active expert, row block) done
   float *hval;              // [T][k+1][I] h of every (token, slot); slot k = shared expert
-  uint64_t *hrec1;          // one-token kernel: [(k+1)*I] tagged h values
+  uint64_t *hrec1;          // one-token kernel: [(k+1)*I/2] tagged pairs of bf16 h values
   float *part;              // [T][k+1][H] gate-weighted down output of every (token, slot)
   int *rbctr;               // [T][H/64] arrivals per (token, row block), kCtrStride ints apart
-  int *endctr;              // [9] end-of-call arrivals (8 groups + 1), kCtrStride ints apart
+  uint64_t *epctr;          // [8] call counters (take_epoch), kCtrStride ints apart
   Ctrl *ctrl;
   uint16_t *out;            // [T][H]
   int32_t *dbg_ids;         // [T][k]
@@ -129,9 +130,9 @@ struct DecodeArgs {
 
 // Decode workspace regions, in bytes, for T <= t_max tokens (offsets from a 256-byte
 // aligned base; each region 256-byte aligned).  t_max = 1: only the regions of the
-// one-token kernel (lrec, hrec1, endctr; the other offsets are 0 and unused).
+// one-token kernel (lrec, hrec1, epctr; the other offsets are 0 and unused).
 struct DecodeLayout {
-  size_t lrec, srec, hflag, hval, hrec1, part, rbctr, endctr, total;
+  size_t lrec, srec, hflag, hval, hrec1, part, rbctr, epctr, total;
 };
 DecodeLayout decode_layout(int H, int E, int k, int I, int t_max);
 
