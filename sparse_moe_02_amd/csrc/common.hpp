@@ -184,24 +184,72 @@ __device__ __forceinline__ float row16_max(float v) {
   return v;
 }
 
-// Sum over the whole wave, result broadcast to every lane.
-__device__ __forceinline__ float wave_sum(float v) {
-  v = row16_sum(v);
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+// Wave reductions read back from lane 63, so every lane gets the same (uniform) value:
+// DPP steps within each row of 16 lanes (every lane of a row ends with its row's result),
+// then the row broadcasts 15 and 31 fold rows 0..2 into row 3 -- six DPP steps and one
+// v_readlane, no LDS round trip.  Called by whole waves only.
+
+// 64-bit DPP move: lanes of rows outside ROW_MASK get `old`.
+template <int C, int ROW_MASK = 0xf>
+__device__ __forceinline__ double dpp_d(double x, double old = 0.0) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x), o = (uint64_t)__double_as_longlong(old);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)o, (int)(uint32_t)b, C, ROW_MASK, 0xf, false);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(o >> 32), (int)(uint32_t)(b >> 32), C, ROW_MASK, 0xf, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ double readlane_d(double x, int l) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) v += __shfl_xor(v, o);
-  return v;
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = row16_max(v);
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x142, 0xa, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x143, 0xc, 0xf, false)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Binary64 sum: six levels of additions on the path of every lane's value.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v += dpp_d<0xB1>(v);        // quad_perm [1,0,3,2]
+  v += dpp_d<0x4E>(v);        // quad_perm [2,3,0,1]
+  v += dpp_d<0x124>(v);       // row_ror:4
+  v += dpp_d<0x128>(v);       // row_ror:8
+  v += dpp_d<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_d<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return readlane_d(v, 63);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, false));  // row_ror:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false));  // row_ror:8
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// wave minimum of mn and maximum of mx together
+__device__ __forceinline__ void wave_minmax_f64(double &mn, double &mx) {
+  mn = fmin(mn, dpp_d<0xB1>(mn)); mx = fmax(mx, dpp_d<0xB1>(mx));
+  mn = fmin(mn, dpp_d<0x4E>(mn)); mx = fmax(mx, dpp_d<0x4E>(mx));
+  mn = fmin(mn, dpp_d<0x124>(mn)); mx = fmax(mx, dpp_d<0x124>(mx));
+  mn = fmin(mn, dpp_d<0x128>(mn)); mx = fmax(mx, dpp_d<0x128>(mx));
+  mn = fmin(mn, dpp_d<0x142, 0xa>(mn, mn)); mx = fmax(mx, dpp_d<0x142, 0xa>(mx, mx));
+  mn = fmin(mn, dpp_d<0x143, 0xc>(mn, mn)); mx = fmax(mx, dpp_d<0x143, 0xc>(mx, mx));
+  mn = readlane_d(mn, 63);
+  mx = readlane_d(mx, 63);
 }
 
 // Cross-workgroup hand-off without cache maintenance: agent-scope relaxed atomic

@@ -235,41 +235,6 @@ __device__ void read_logit(const DecodeArgs &a, int t, int e, double &v, double 
   }
 }
 
-// DPP row maxima, then the four row results through scalar registers: the wave-wide
-// result in every lane.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, false));  // row_ror:4
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false));  // row_ror:8
-  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
-  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
-  return max(a, b);
-}
-
-template <int C>
-__device__ __forceinline__ double dpp_d(double x) {
-  const uint64_t b = (uint64_t)__double_as_longlong(x);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, C, 0xf, 0xf, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), C, 0xf, 0xf, false);
-  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-}
-__device__ __forceinline__ double readlane_d(double x, int l) {
-  const uint64_t b = (uint64_t)__double_as_longlong(x);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
-  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-}
-// wave minimum of mn and maximum of mx together
-__device__ __forceinline__ void wave_minmax_f64(double &mn, double &mx) {
-  mn = fmin(mn, dpp_d<0xB1>(mn)); mx = fmax(mx, dpp_d<0xB1>(mx));
-  mn = fmin(mn, dpp_d<0x4E>(mn)); mx = fmax(mx, dpp_d<0x4E>(mx));
-  mn = fmin(mn, dpp_d<0x124>(mn)); mx = fmax(mx, dpp_d<0x124>(mx));
-  mn = fmin(mn, dpp_d<0x128>(mn)); mx = fmax(mx, dpp_d<0x128>(mx));
-  mn = fmin(fmin(readlane_d(mn, 0), readlane_d(mn, 16)), fmin(readlane_d(mn, 32), readlane_d(mn, 48)));
-  mx = fmax(fmax(readlane_d(mx, 0), readlane_d(mx, 16)), fmax(readlane_d(mx, 32), readlane_d(mx, 48)));
-}
-
 // Order-preserving 32-bit key of a logit of expert e: the fp32 value's ordered bits with
 // the low 8 replaced by the complemented index, so the largest key is the largest logit,
 // ties (and logits equal in their top 24 bits) to the lower index.  The truncation only

@@ -93,8 +93,8 @@ struct DecShared {
 
 // ------------------------------------------------------------------ router (binary64)
 
-// Additions on any path of router_logit's sum: 8 per 2048 elements per lane, a 6-level
-// butterfly, 3 across the four waves.
+// Additions on any path of router_logit's sum: 8 per 2048 elements per lane, 6 levels
+// across the wave, 3 across the four waves.
 __device__ __forceinline__ int router_depth(int H) { return 8 * ((H + 2047) / 2048) + 9; }
 
 // Binary64 logit of expert e (exact products, summed lane-sequentially, then over the
@@ -186,41 +186,6 @@ __device__ double block_max_f64(double v, DecShared &sh) {
   return v;
 }
 
-// DPP row maxima / minima (16 lanes), then the four row results through scalar registers:
-// the wave-wide result in every lane.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, false));  // row_ror:4
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false));  // row_ror:8
-  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
-  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
-  return max(a, b);
-}
-
-template <int C>
-__device__ __forceinline__ double dpp_d(double x) {
-  const uint64_t b = (uint64_t)__double_as_longlong(x);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, C, 0xf, 0xf, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), C, 0xf, 0xf, false);
-  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-}
-__device__ __forceinline__ double readlane_d(double x, int l) {
-  const uint64_t b = (uint64_t)__double_as_longlong(x);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
-  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-}
-// wave minimum of mn and maximum of mx together
-__device__ __forceinline__ void wave_minmax_f64(double &mn, double &mx) {
-  mn = fmin(mn, dpp_d<0xB1>(mn)); mx = fmax(mx, dpp_d<0xB1>(mx));
-  mn = fmin(mn, dpp_d<0x4E>(mn)); mx = fmax(mx, dpp_d<0x4E>(mx));
-  mn = fmin(mn, dpp_d<0x124>(mn)); mx = fmax(mx, dpp_d<0x124>(mx));
-  mn = fmin(mn, dpp_d<0x128>(mn)); mx = fmax(mx, dpp_d<0x128>(mx));
-  mn = fmin(fmin(readlane_d(mn, 0), readlane_d(mn, 16)), fmin(readlane_d(mn, 32), readlane_d(mn, 48)));
-  mx = fmax(fmax(readlane_d(mx, 0), readlane_d(mx, 16)), fmax(readlane_d(mx, 32), readlane_d(mx, 48)));
-}
-
 // Order-preserving 32-bit key of a logit of expert e: the fp32 value's ordered bits with
 // the low 8 replaced by the complemented index, so the largest key is the largest logit,
 // ties (and logits equal in their top 24 bits) to the lower index.  The truncation only
@@ -276,7 +241,10 @@ __device__ bool select_topk_wave(const DecodeArgs &a, DecShared &sh, bool write_
     key[i] = valid[i] ? logit_key(v[i], lane + kWave * i) : 0u;
   }
   uint32_t chosen = 0;
-  for (int rr = 0; rr < k; ++rr) {
+  int top_e = 0;  // the first round's winner: the largest chosen logit
+#pragma unroll
+  for (int rr = 0; rr < kMaxTopK; ++rr) {
+    if (rr >= k) break;
     uint32_t best = 0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) best = max(best, key[i]);
@@ -284,6 +252,7 @@ __device__ bool select_topk_wave(const DecodeArgs &a, DecShared &sh, bool write_
 #pragma unroll
     for (int i = 0; i < NV; ++i)
       if (key[i] == best && best != 0u) key[i] = 0u, chosen |= 1u << i;
+    if (rr == 0) top_e = 255 - (int)(best & 0xffu);
   }
   double mn = INFINITY, mx = -INFINITY;
 #pragma unroll
@@ -296,12 +265,12 @@ __device__ bool select_topk_wave(const DecodeArgs &a, DecShared &sh, bool write_
   }
   wave_minmax_f64(mn, mx);
   if (!(mn > mx)) return false;  // false for NaN or an infinite radius as well
-  // softmax of the chosen logits (as fp32), ids ascending
-  float gmax = -INFINITY;
+  // softmax of the chosen logits (as fp32), ids ascending; the largest is top_e's
+  const int ti = min(top_e >> 6, NV - 1);
+  double tv = v[0];
 #pragma unroll
-  for (int i = 0; i < NV; ++i)
-    if ((chosen >> i) & 1u) gmax = fmaxf(gmax, (float)v[i]);
-  gmax = wave_max(gmax);
+  for (int i = 1; i < NV; ++i) tv = ti == i ? v[i] : tv;
+  const float gmax = (float)readlane_d(tv, top_e & 63);
   float ex[NV], part = 0.0f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
