@@ -26,7 +26,9 @@ namespace {
 constexpr float kU32 = 5.9604644775390625e-8f;       // 2^-24
 // ---------------------------------------------------------------------------- prefill
 
-constexpr int kRouteThreads = 512;   // selection: 8 waves, four tokens each
+constexpr int kRouteThreads = 512;   // 8 waves: loads and re-ranks; waves 0..3 select, four tokens each
+constexpr int kSelTokens = 16;       // tokens per selection workgroup (half of a token-mask block)
+static_assert(2 * kSelTokens == kRouteTokens, "two selection workgroups per token-mask block");
 constexpr int kKC = 128;             // k per chunk (one LDS stage, one fresh fp32 partial sum)
 constexpr int kKP = 128;             // k per fresh fp32 partial sum
 constexpr int kLT = 64;              // logits tile: tokens
@@ -151,21 +153,22 @@ __global__ __launch_bounds__(kLThreads) void k_route_logits(RouteArgs a) {
 }
 
 struct RouteSmem {
-  float l[kRouteTokens][kMaxExperts];  // fp32 logit (+bias)
-  float r[kRouteTokens][kMaxExperts];  // its error radius
+  float l[kSelTokens][kMaxExperts];  // fp32 logit (+bias)
+  float r[kSelTokens][kMaxExperts];  // its error radius
   WaveSel ws[kRouteThreads / kWave];
 };
 
-// One workgroup per 32 tokens.
+// One workgroup per 16 tokens (every CU busy at 4096 tokens; the selection at one wave
+// per SIMD).
 //  1. fp32 logits and radii of its tokens from the workspace (or, for a float32 router,
 //     none: every expert is re-ranked in binary64).
 //  2. fp32 selection, sixteen lanes per token, certified against the radii.
 //  3. tokens the certificate does not settle are re-ranked by one wave each, in parallel.
 __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
   __shared__ __attribute__((aligned(16))) RouteSmem sm;
-  __shared__ int s_sel[kRouteTokens][kMaxTopK];      // chosen experts
-  __shared__ float s_min_in[kRouteTokens], s_max_out[kRouteTokens];
-  __shared__ int s_list[kRouteTokens];
+  __shared__ int s_sel[kSelTokens][kMaxTopK];      // chosen experts
+  __shared__ float s_min_in[kSelTokens], s_max_out[kSelTokens];
+  __shared__ int s_list[kSelTokens];
   __shared__ int s_nflag;
   __shared__ uint32_t s_mask[kMaxExperts];
   auto &s_l = sm.l;
@@ -173,8 +176,8 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = a.H, E = a.E, k = a.k;
-  const int t0 = blockIdx.x * kRouteTokens;
-  const int nt = min(kRouteTokens, a.T - t0);
+  const int t0 = blockIdx.x * kSelTokens;
+  const int nt = min(kSelTokens, a.T - t0);
 
   for (int e = tid; e < kMaxExperts; e += kRouteThreads) s_mask[e] = 0;
   if (tid == 0) s_nflag = 0;
@@ -183,11 +186,11 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
     // 16-byte loads: four of each array in flight per thread (one batch for E = 256)
     constexpr int kB = 4;
     const int E4 = E / 4;
-    for (int i0 = tid; i0 < kRouteTokens * E4; i0 += kRouteThreads * kB) {
+    for (int i0 = tid; i0 < kSelTokens * E4; i0 += kRouteThreads * kB) {
       float4 lv[kB], rv[kB];
 #pragma unroll
       for (int u = 0; u < kB; ++u) {
-        const int i = min(i0 + u * kRouteThreads, kRouteTokens * E4 - 1);
+        const int i = min(i0 + u * kRouteThreads, kSelTokens * E4 - 1);
         const int m = i / E4, e4 = i - m * E4;
         const size_t o = (size_t)(t0 + min(m, nt - 1)) * E + 4 * e4;
         lv[u] = *(const float4 *)(a.lg + o);
@@ -196,7 +199,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
 #pragma unroll
       for (int u = 0; u < kB; ++u) {
         const int i = i0 + u * kRouteThreads;
-        if (i < kRouteTokens * E4) {
+        if (i < kSelTokens * E4) {
           const int m = i / E4, e4 = i - m * E4;
           *(float4 *)&s_l[m][4 * e4] = lv[u];
           *(float4 *)&s_r[m][4 * e4] = rv[u];
@@ -206,11 +209,11 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
   } else if (a.wr16) {
     // sixteen loads of each array in flight per thread (one batch for E = 256)
     constexpr int kB = 16;
-    for (int i0 = tid; i0 < kRouteTokens * E; i0 += kRouteThreads * kB) {
+    for (int i0 = tid; i0 < kSelTokens * E; i0 += kRouteThreads * kB) {
       float lv[kB], rv[kB];
 #pragma unroll
       for (int u = 0; u < kB; ++u) {
-        const int i = min(i0 + u * kRouteThreads, kRouteTokens * E - 1);
+        const int i = min(i0 + u * kRouteThreads, kSelTokens * E - 1);
         const int m = i / E, e = i - m * E;
         const size_t o = (size_t)(t0 + min(m, nt - 1)) * E + e;
         lv[u] = a.lg[o];
@@ -219,7 +222,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
 #pragma unroll
       for (int u = 0; u < kB; ++u) {
         const int i = i0 + u * kRouteThreads;
-        if (i < kRouteTokens * E) {
+        if (i < kSelTokens * E) {
           const int m = i / E, e = i - m * E;
           s_l[m][e] = lv[u];
           s_r[m][e] = rv[u];
@@ -227,14 +230,14 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
       }
     }
   } else {
-    for (int i = tid; i < kRouteTokens * kMaxExperts; i += kRouteThreads) {
+    for (int i = tid; i < kSelTokens * kMaxExperts; i += kRouteThreads) {
       (&s_l[0][0])[i] = 0.0f;
       (&s_r[0][0])[i] = INFINITY;
     }
   }
   __syncthreads();
 
-  // fp32 selection: wave wv takes tokens 4wv..4wv+3, sixteen lanes (one DPP row) per
+  // fp32 selection: wave wv < 4 takes tokens 4wv..4wv+3, sixteen lanes (one DPP row) per
   // token, lane q holding experts q, q+16, ...  Each (logit, expert) pair is one 32-bit
   // key: the order-preserving bits of the logit with the low 8 replaced by the
   // complemented index, so the largest key is the largest logit, ties (and logits equal
@@ -242,7 +245,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
   // clearing each winner.  Truncating the keys only changes the choice between logits
   // closer than their error radii, and such a token fails the certificate below, which
   // uses the exact fp32 values.
-  {
+  if (wv < kSelTokens / 4) {
     const int g = lane >> 4, q = lane & 15;
     const int m = wv * 4 + g;
     constexpr int NV = kMaxExperts / 16;
@@ -372,7 +375,18 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
     atomicOr(&s_mask[s_sel[m][r]], 1u << m);
   }
   __syncthreads();
-  for (int e = tid; e < kMaxExperts; e += kRouteThreads) a.tokmask[(size_t)blockIdx.x * kMaxExperts + e] = e < E ? s_mask[e] : 0u;
+  // this workgroup's 16 bits of each expert's word in the 32-token mask block (the
+  // low half for even workgroups); the last workgroup of an odd count also clears the
+  // high half, which no workgroup owns
+  {
+    uint16_t *tm = (uint16_t *)a.tokmask + (size_t)(blockIdx.x >> 1) * kMaxExperts * 2;
+    const int h = blockIdx.x & 1;
+    const bool clear_hi = h == 0 && blockIdx.x == gridDim.x - 1;
+    for (int e = tid; e < kMaxExperts; e += kRouteThreads) {
+      tm[2 * e + h] = e < E ? (uint16_t)s_mask[e] : (uint16_t)0;
+      if (clear_hi) tm[2 * e + 1] = 0;
+    }
+  }
   if (tid == 0 && nflag) atomicAdd(&a.ctrl->n_refined, nflag);
 }
 
@@ -391,7 +405,7 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t s) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int nb = (a.T + kRouteTokens - 1) / kRouteTokens;
+  const int nb = (a.T + kSelTokens - 1) / kSelTokens;
   hipLaunchKernelGGL(k_route, dim3(nb), dim3(kRouteThreads), 0, s, a);
   return hipGetLastError();
 }

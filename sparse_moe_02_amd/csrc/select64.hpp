@@ -319,15 +319,11 @@ __device__ void rerank_wave(WaveSel &W, KnownIn known_in, KnownOut known_out, Fp
     my_e = W.in_ids[lane];
     my_l = W.in_l[lane];
   }
-  float mx = my_l;
-#pragma unroll
-  for (int o = 1; o < kMaxTopK; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  const float mx = wave_max(my_l);
   const float ex = lane < n ? __expf(my_l - mx) : 0.f;
-  float den = ex;
-#pragma unroll
-  for (int o = 1; o < kMaxTopK; o <<= 1) den += __shfl_xor(den, o);
+  const float den = wave_sum(ex);
   int pos = 0;
-  for (int j = 0; j < n; ++j) pos += __shfl(my_e, j) < my_e;
+  for (int j = 0; j < n; ++j) pos += __builtin_amdgcn_readlane(my_e, j) < my_e;
   wave_sync();
   if (lane < n) {
     const float g = ex / den;
