@@ -797,8 +797,12 @@ __device__ __forceinline__ int wg_pos(int b, int G) {
   return before + b / 8;
 }
 
+// Two waves per SIMD (two workgroups per CU, so one's memory round trips overlap the
+// other's work) where the registers allow it without heavy spilling: up to four rows
+// (measured 35.8 -> 33.6 us at two rows, 52.5 -> 47.6 at four); eight rows would spill
+// 636 bytes per lane and ran 111 -> 132 us, so they keep one wave per SIMD.
 template <int TT>
-__global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
+__global__ __launch_bounds__(kDecThreads, TT <= 4 ? 2 : 1) void k_decode(DecodeArgs a) {
   __shared__ DecShared sh;
   const int b = blockIdx.x, G = gridDim.x, tid = threadIdx.x, wv = tid >> 6;
   if (tid == 0) s_epoch = take_epoch(a.epctr, kCtrStride / 2, b, G);
