@@ -901,7 +901,7 @@ DecodeLayout decode_layout(int H, int E, int k, int I, int t_max) {
   L.epctr = take(8 * kCtrStride * 4);
   if (t_max <= 1) {  // the one-token kernel: logit and h records only
     L.lrec = take((size_t)kLrecRep * E * 3 * 8);
-    L.hrec1 = take(K1 * I / 2 * 8);
+    L.hrec1 = take((size_t)kHrecRep * K1 * I / 2 * 8);
     L.total = o;
     return L;
   }
@@ -909,7 +909,7 @@ DecodeLayout decode_layout(int H, int E, int k, int I, int t_max) {
   L.srec = take(kSrecRep * T * 2 * k * 8);
   L.hflag = take((std::min<size_t>(T * k, E) + 1) * (I / kDecGuTask) * 8);
   L.hval = take(T * K1 * I * 4);
-  L.hrec1 = take(K1 * I / 2 * 8);
+  L.hrec1 = take((size_t)kHrecRep * K1 * I / 2 * 8);
   L.part = take(T * K1 * H * 4);
   L.rbctr = take(T * (H / kDecDnTask) * kCtrStride * 4);
   L.total = o;

@@ -486,11 +486,12 @@ __device__ __forceinline__ void gu_task(const DecodeArgs &a, const DecShared &sh
     const float us = wave_sum(au[r]);
     if (lane == r) hv = gs / (1.0f + __expf(-gs)) * us;
   }
-  // rows r0 + 2p and r0 + 2p + 1 as one record (lane p < 2): their h in bf16, the even
-  // row in the low half
+  // rows r0 + 2p and r0 + 2p + 1 as one record (p = lane % 2): their h in bf16, the even
+  // row in the low half, in kHrecRep copies (lane / 2), so fewer readers share a line
   const float h0 = __shfl(hv, 2 * (lane & 1)), h1 = __shfl(hv, 2 * (lane & 1) + 1);
   const size_t pr = ((size_t)j * I + r0) / 2;
-  if (lane < kGuRows / 2) st_agent(&a.hrec1[pr + lane], tagged(s_epoch, pack_bf16x2(h0, h1)));
+  if (lane < 2 * kHrecRep)
+    st_agent(&a.hrec1[(size_t)(lane >> 1) * ((a.k + 1) * I / 2) + pr + (lane & 1)], tagged(s_epoch, pack_bf16x2(h0, h1)));
 }
 
 // ------------------------------------------------------------------ down
@@ -532,7 +533,7 @@ __device__ __forceinline__ void dn_issue(const DecodeArgs &a, const DecShared &s
 __device__ __forceinline__ void stage_h(const DecodeArgs &a, DecShared &sh, int j0, int nb) {
   const int tid = threadIdx.x, I = a.I;
   const int ng = nb * I / 8;
-  const uint64_t *rec = a.hrec1 + (size_t)j0 * I / 2;
+  const uint64_t *rec = a.hrec1 + (size_t)(blockIdx.x % kHrecRep) * ((a.k + 1) * I / 2) + (size_t)j0 * I / 2;
   constexpr int kG = (kHStage / 8 + kDecThreads - 1) / kDecThreads;
   uint64_t rv[kG][4];
 #pragma unroll

@@ -102,6 +102,7 @@ constexpr int kDecGuTask = 16;     // rows of one decode gate/up task
 constexpr int kDecDnTask = 64;     // output rows of one decode down task
 constexpr int kCtrStride = 64;     // ints between two completion counters (256 bytes)
 constexpr int kLrecRep = 8;        // copies of the one-token kernel's logit records
+constexpr int kHrecRep = 4;        // copies of the one-token kernel's h records
 
 struct DecodeArgs {
   const uint16_t *x;        // [T][H]
@@ -118,7 +119,7 @@ struct DecodeArgs {
   uint64_t *srec;           // [T][2k] tagged records: the chosen experts (ascending), then their gates
   uint64_t *hflag;          // [min(T*k, E) + 1][I/16] tagged: gate/up task (active expert, row block) done
   float *hval;              // [T][k+1][I] h of every (token, slot); slot k = shared expert
-  uint64_t *hrec1;          // one-token kernel: [(k+1)*I/2] tagged pairs of bf16 h values
+  uint64_t *hrec1;          // one-token kernel: [kHrecRep][(k+1)*I/2] tagged pairs of bf16 h values
   float *part;              // [T][k+1][H] gate-weighted down output of every (token, slot)
   int *rbctr;               // [T][H/64] arrivals per (token, row block), kCtrStride ints apart
   uint64_t *epctr;          // [8] call counters (take_epoch), kCtrStride ints apart
