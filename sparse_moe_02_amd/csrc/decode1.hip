@@ -240,20 +240,34 @@ __device__ bool select_topk_wave(const DecodeArgs &a, DecShared &sh, bool write_
     r[i] = valid[i] ? (double)__uint_as_float((uint32_t)rec[i][2]) : 0.0;
     key[i] = valid[i] ? logit_key(v[i], lane + kWave * i) : 0u;
   }
-  uint32_t chosen = 0;
-  int top_e = 0;  // the first round's winner: the largest chosen logit
-#pragma unroll
+  // k rounds over the lanes' heads: each lane sorts its keys once (descending), a round
+  // takes the wave maximum of the heads and the lane holding it (keys are distinct) moves
+  // on to its next key.  The k-th winner is the threshold: an expert is chosen iff its
+  // (nonzero) key is at least that.
+  static_assert(NV == 4, "four keys per lane");
+  uint32_t h0 = key[0], h1 = key[1], h2 = key[2], h3 = key[3];
+  auto cx = [](uint32_t &x, uint32_t &y) {
+    const uint32_t hi = max(x, y), lo = min(x, y);
+    x = hi;
+    y = lo;
+  };
+  cx(h0, h1); cx(h2, h3); cx(h0, h2); cx(h1, h3); cx(h1, h2);
+  int top_e = 0;      // the first round's winner: the largest chosen logit
+  uint32_t kth = 0;   // the last round's winner
   for (int rr = 0; rr < kMaxTopK; ++rr) {
     if (rr >= k) break;
-    uint32_t best = 0;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) best = max(best, key[i]);
-    best = wave_max_u32(best);
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-      if (key[i] == best && best != 0u) key[i] = 0u, chosen |= 1u << i;
+    const uint32_t best = wave_max_u32(h0);
+    const bool win = h0 == best;
+    h0 = win ? h1 : h0;
+    h1 = win ? h2 : h1;
+    h2 = win ? h3 : h2;
+    h3 = win ? 0u : h3;
     if (rr == 0) top_e = 255 - (int)(best & 0xffu);
+    kth = best;
   }
+  uint32_t chosen = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) chosen |= (key[i] != 0u && key[i] >= kth) ? (1u << i) : 0u;
   double mn = INFINITY, mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
