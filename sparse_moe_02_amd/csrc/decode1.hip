@@ -64,12 +64,15 @@ __device__ __forceinline__ QMat expert_mat(const QMat &routed, const QMat &share
 // (128 + code) v, the codes of four packed words, v as 16 pairs in pairs_p4 order.
 __device__ __forceinline__ float dot_chunk(const uint4 &w, const uint32_t (&v)[16]) {
   const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-  float d = 0.f;
+  float d0 = 0.f, d1 = 0.f;  // two chains of eight (half the dependent latency)
 #pragma unroll
   for (int q = 0; q < 4; ++q)
 #pragma unroll
-    for (int p = 0; p < 4; ++p) d = dot2_bf16(code_pair(ws[q], p), v[4 * q + p], d);
-  return d;
+    for (int p = 0; p < 4; ++p) {
+      float &d = (q & 1) ? d1 : d0;
+      d = dot2_bf16(code_pair(ws[q], p), v[4 * q + p], d);
+    }
+  return d0 + d1;
 }
 constexpr uint32_t kOnes = 0x3f803f80u;  // the bf16 pair (1, 1)
 
