@@ -237,8 +237,9 @@ moe_status moe_forward_prefill(moe_plan_t plan, const void *x, int64_t T, void *
  * GPU"); requires E <= 256.  If an internal wait ever exceeded its poll budget, the
  * control word at byte offset 88 of the workspace (int32) becomes non-zero (the output of
  * that call is then invalid); moe_workspace_init clears it.  The hand-off records are
- * tagged with a per-call number kept in the workspace (bytes 92..99), so the launch
- * arguments depend only on (plan, x, out, workspace, dbg): a sequence of decode calls may
+ * tagged with a per-call number drawn from call counters in the workspace (every call
+ * advances them by the same amount, whatever its grid), so the launch arguments depend
+ * only on (plan, x, out, workspace, dbg): a sequence of decode calls may
  * be captured once in a HIP graph and replayed, also interleaved with direct calls on the
  * same workspace, as long as the calls on one workspace stay ordered on one stream.
  * Workgroups of the launch wait for each other, so the launch must have the GPU to
@@ -266,9 +267,9 @@ moe_status moe_forward_decode_batch(moe_plan_t plan, const void *x, int32_t T, v
  * library (2 MiB per device, held until the process ends) instead of a workspace.
  * Allocates nothing: no hipMalloc, no hipFree, no allocating library call.  The first
  * call on a device enqueues a kernel on `stream` that clears the array.
- * MOE_ERR_WORKSPACE if the plan's one-token decode records (24E + 8(k+1)I bytes, plus
- * alignment and 2.3 KB of counters) do not fit the array (never for sizes
- * moe_plan_create accepts today: at most 0.57 MB).  Every call on a GPU shares that GPU's array:
+ * MOE_ERR_WORKSPACE if the plan's one-token decode records (192E + 16(k+1)I bytes, plus
+ * alignment and 2 KB of counters) do not fit the array (never for sizes
+ * moe_plan_create accepts today: at most 0.65 MB).  Every call on a GPU shares that GPU's array:
  * calls that may overlap on one GPU (different streams, different threads) race and
  * must be ordered by the caller.  moe_workspace_check(plan, NULL, 0, stream) reads this
  * array's error word.  Other errors as moe_forward_decode. */
