@@ -496,16 +496,16 @@ __device__ __forceinline__ void gu_task(const DecodeArgs &a, const DecShared &sh
       gu_accumulate(L, a.qbf16, ag, au);
     }
   }
-  float hv = 0.f;
+  float hv[kGuRows];  // uniform: the wave sums are read back to every lane
 #pragma unroll
   for (int r = 0; r < kGuRows; ++r) {
     const float gs = wave_sum(ag[r]);
     const float us = wave_sum(au[r]);
-    if (lane == r) hv = gs / (1.0f + __expf(-gs)) * us;
+    hv[r] = gs / (1.0f + __expf(-gs)) * us;
   }
   // rows r0 + 2p and r0 + 2p + 1 as one record (p = lane % 2): their h in bf16, the even
   // row in the low half, in kHrecRep copies (lane / 2), so fewer readers share a line
-  const float h0 = __shfl(hv, 2 * (lane & 1)), h1 = __shfl(hv, 2 * (lane & 1) + 1);
+  const float h0 = (lane & 1) ? hv[2] : hv[0], h1 = (lane & 1) ? hv[3] : hv[1];
   const size_t pr = ((size_t)j * I + r0) / 2;
   if (lane < 2 * kHrecRep)
     st_agent(&a.hrec1[(size_t)(lane >> 1) * ((a.k + 1) * I / 2) + pr + (lane & 1)], tagged(s_epoch, pack_bf16x2(h0, h1)));

@@ -51,6 +51,7 @@ __global__ __launch_bounds__(kThreads) void k_group(GroupArgs a) {
   __shared__ int s_base[kSubs][kMaxExperts];
   __shared__ int s_cls[6], s_clsoff[6];
   __shared__ int s_pc[kBM / 32 + 1][kMaxExperts + 1];  // per class, per expert: M-blocks (then their scan)
+  __shared__ int s_mbs[kMaxExperts + 2];                // M-blocks of the experts before e (all classes)
   const int tid = threadIdx.x;
   const int T = a.T, E = a.E, k = a.k;
   const int nblk = (T + kRouteTokens - 1) / kRouteTokens;
@@ -126,12 +127,7 @@ __global__ __launch_bounds__(kThreads) void k_group(GroupArgs a) {
     const int lo = tid * per, hi = min(lo + per, E + 1);
     int sum = 0;
     for (int e = lo; e < hi; ++e) sum += s_cnt[e];
-    int incl = sum;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int v = __shfl_up(incl, o);
-      if (tid >= o) incl += v;
-    }
+    const int incl = wave_incl_scan(sum);
     int run = incl - sum;
     for (int e = lo; e < hi; ++e) {
       s_off[e] = run;
@@ -227,12 +223,7 @@ __global__ __launch_bounds__(kThreads) void k_group(GroupArgs a) {
     const int lo = lane * per, hi = min(lo + per, E + 1);
     int sum = 0;
     for (int e = lo; e < hi; ++e) sum += s_pc[c][e];
-    int incl = sum;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int v = __shfl_up(incl, o);
-      if (lane >= o) incl += v;
-    }
+    const int incl = wave_incl_scan(sum);
     int run = incl - sum;
     for (int e = lo; e < hi; ++e) {
       const int v = s_pc[c][e];
@@ -257,21 +248,44 @@ __global__ __launch_bounds__(kThreads) void k_group(GroupArgs a) {
     if (a.dbg_n_refined) *a.dbg_n_refined = a.ctrl->n_refined;
     a.ctrl->n_refined = 0;
   }
-  __syncthreads();
-  if (tid <= E && nmb) {
-    int row = s_off[tid];
-    int seen[kCls + 1] = {};  // this expert's blocks placed so far, per class
-    for (int i = 0; i < nmb; ++i) {
-      const int rows = F ? (i + 1 < nmb ? F : rem) : q + (i < rem ? 1 : 0);
-      const int cls = (rows + 31) / 32;
-      int pos = 0;
+  // every M-block placed by a thread of its own (the shared expert alone has T/160 of
+  // them): flat block index f -> its expert e (the last with s_mbs[e] <= f) and index i
+  // inside e; blocks of one class keep their order inside the expert
+  if (tid <= E) {
+    int before = 0;
 #pragma unroll
-      for (int c = 1; c <= kCls; ++c)
-        if (c == cls) pos = seen[c]++;
-      const int slot = s_clsoff[cls] + s_pc[cls][tid] + pos;
-      a.mblocks[slot] = make_int4(tid, row, rows, cls);
-      row += rows;
+    for (int c = 1; c <= kCls; ++c) before += s_pc[c][tid];
+    s_mbs[tid] = before;
+  }
+  if (tid == 0) s_mbs[E + 1] = s_clsoff[1] + s_cls[1];  // every block (class 1 comes last)
+  __syncthreads();
+  const int n_all = s_mbs[E + 1];
+  for (int f = tid; f < n_all; f += kThreads) {
+    int lo = 0, hi = E;  // s_mbs[lo] <= f < s_mbs[hi + 1]
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_mbs[mid] <= f)
+        lo = mid;
+      else
+        hi = mid - 1;
     }
+    const int e = lo, i = f - s_mbs[e], n = s_cnt[e];
+    int rows, row, pos;
+    if (F) {
+      const int nb = (n + F - 1) / F, last = n - (nb - 1) * F;
+      rows = i + 1 < nb ? F : last;
+      row = s_off[e] + i * F;
+      // the full blocks come first; the last one is first of its class unless it is full
+      pos = (i + 1 < nb || (last + 31) / 32 == F / 32) ? i : 0;
+    } else {
+      const int nb = (n + kBM - 1) / kBM, qq = n / nb, rr = n % nb;
+      rows = qq + (i < rr ? 1 : 0);
+      row = s_off[e] + i * qq + min(i, rr);
+      // rr blocks of qq+1 rows, then nb-rr of qq rows: one class, or two in that order
+      pos = ((qq + 1 + 31) / 32 == (qq + 31) / 32 || i < rr) ? i : i - rr;
+    }
+    const int cls = (rows + 31) / 32;
+    a.mblocks[s_clsoff[cls] + s_pc[cls][e] + pos] = make_int4(e, row, rows, cls);
   }
 }
 
