@@ -237,60 +237,72 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
   }
   __syncthreads();
 
-  // fp32 selection: wave wv < 4 takes tokens 4wv..4wv+3, sixteen lanes (one DPP row) per
-  // token, lane q holding experts q, q+16, ...  Each (logit, expert) pair is one 32-bit
-  // key: the order-preserving bits of the logit with the low 8 replaced by the
-  // complemented index, so the largest key is the largest logit, ties (and logits equal
-  // in their top 24 bits) to the lower index; k rounds of a row maximum pick the top k,
-  // clearing each winner.  Truncating the keys only changes the choice between logits
-  // closer than their error radii, and such a token fails the certificate below, which
-  // uses the exact fp32 values.
-  if (wv < kSelTokens / 4) {
-    const int g = lane >> 4, q = lane & 15;
-    const int m = wv * 4 + g;
-    constexpr int NV = kMaxExperts / 16;
+  // fp32 selection: wave wv takes tokens 2wv and 2wv+1, 32 lanes (two DPP rows) per token,
+  // lane q holding experts q, q+32, ...  Each (logit, expert) pair is one 32-bit key: the
+  // order-preserving bits of the logit with the low 8 replaced by the complemented index,
+  // so the largest key is the largest logit, ties (and logits equal in their top 24 bits)
+  // to the lower index; k rounds of a 32-lane maximum pick the top k, clearing each
+  // winner.  Truncating the keys only changes the choice between logits closer than their
+  // error radii, and such a token fails the certificate below, which uses the exact fp32
+  // values.  A 32-lane reduction is four DPP steps within each row, then the two rows of
+  // the half-wave exchanged with v_permlane16_swap.
+  {
+    const int g = lane >> 5, q = lane & 31;
+    const int m = wv * 2 + g;
+    constexpr int NV = kMaxExperts / 32;
     uint32_t key[NV];
     float lv[NV], rv[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int e = q + 16 * i;
+      const int e = q + 32 * i;
       lv[i] = e < E ? s_l[m][e] : -INFINITY;
       rv[i] = e < E ? s_r[m][e] : 0.0f;
       const uint32_t b = __float_as_uint(lv[i]);
       const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
       key[i] = e < E ? ((ord & 0xffffff00u) | (uint32_t)(255 - e)) : 0u;
     }
-    auto row_max_u32 = [](uint32_t v) {
+    auto half_max_u32 = [](uint32_t v) {
       v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
       v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
       v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, false));  // row_ror:4
       v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false));  // row_ror:8
-      return v;
+      const auto sw = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+      return max((uint32_t)sw[0], (uint32_t)sw[1]);
+    };
+    auto half_max_f = [](float v) {
+      v = row16_max(v);
+      const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+      return fmaxf(__uint_as_float((uint32_t)sw[0]), __uint_as_float((uint32_t)sw[1]));
+    };
+    auto half_sum_f = [](float v) {
+      v = row16_sum(v);
+      const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+      return __uint_as_float((uint32_t)sw[0]) + __uint_as_float((uint32_t)sw[1]);
     };
     int my_e = 0;
     for (int r = 0; r < k; ++r) {
       uint32_t best = 0;
 #pragma unroll
       for (int i = 0; i < NV; ++i) best = max(best, key[i]);
-      best = row_max_u32(best);
+      best = half_max_u32(best);
 #pragma unroll
       for (int i = 0; i < NV; ++i) key[i] = key[i] == best ? 0u : key[i];
       if (q == r) my_e = 255 - (int)(best & 0xffu);
     }
     uint32_t taken = 0;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) taken |= (key[i] == 0u && q + 16 * i < E) ? (1u << i) : 0u;
+    for (int i = 0; i < NV; ++i) taken |= (key[i] == 0u && q + 32 * i < E) ? (1u << i) : 0u;
     const float my_l = q < k ? s_l[m][my_e] : -INFINITY;
     float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int e = q + 16 * i;
+      const int e = q + 32 * i;
       const bool in = (taken >> i) & 1u;
       mn = (e < E && in) ? fminf(mn, lv[i] - rv[i]) : mn;
       mx = (e < E && !in) ? fmaxf(mx, lv[i] + rv[i]) : mx;
     }
-    mn = -row16_max(-mn);
-    mx = row16_max(mx);
+    mn = -half_max_f(-mn);
+    mx = half_max_f(mx);
     const bool cert = mn > mx;  // false for NaN or an infinite radius
     if (q < k) s_sel[m][q] = my_e;
     if (q == 0) {
@@ -300,13 +312,16 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
     if (m < nt && (cert || (a.no_fallback && a.wr16))) {
       // gates: softmax of the chosen logits (lane q < k holds choice q; choice 0 is the
       // largest); ids in ascending order
-      const float top = __shfl(my_l, lane & ~15);
+      const float t0l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_l), 0));
+      const float t1l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_l), 32));
+      const float top = g ? t1l : t0l;
       const float ex = q < k ? __expf(my_l - top) : 0.0f;
-      const float den = row16_sum(ex);
+      const float den = half_sum_f(ex);
       int pos = 0;
 #pragma unroll
       for (int j = 0; j < kMaxTopK; ++j) {
-        const int ej = __shfl(my_e, (lane & ~15) + j);
+        const int e0 = __builtin_amdgcn_readlane(my_e, j), e1 = __builtin_amdgcn_readlane(my_e, 32 + j);
+        const int ej = g ? e1 : e0;
         pos += (j < k && ej < my_e) ? 1 : 0;
       }
       if (q < k) {
