@@ -155,6 +155,39 @@ def test_decode_back_to_back_same_workspace():
     m.close()
 
 
+def test_decode_one_row_and_batches_interleaved():
+    """One-row and batch decode calls (different grids) alternating on one workspace with
+    no host sync: they share the call counters that tag the hand-off records, so every
+    call must draw a tag of its own and see only its own records.  Each output bitwise
+    equal to the same call made alone, and no wait ran out of polls."""
+    import torch
+
+    from sparse_moe_02_amd.layer import MoeLayer, bf16_bits, bf16_tensor
+
+    L = synth.make_layer(1, 5)
+    xall = np.stack([synth.make_x(1, 5 + j)[0] for j in range(8)])  # eight distinct rows
+    m = MoeLayer(L, top_k=8, max_chunk_tokens=1)
+    x1 = [bf16_tensor(xall[i], "cuda:0") for i in range(3)]
+    xb = {T: bf16_tensor(xall[:T], "cuda:0") for T in (2, 4, 8)}
+    alone1 = [bf16_bits(m.decode(x)) for x in x1]
+    aloneb = {T: bf16_bits(m.decode_batch(xb[T])) for T in xb}
+    torch.cuda.synchronize()
+    say("[interleaved] 1/2/4/8-row decode calls alternating on one workspace")
+    seq = []
+    for i in range(24):
+        kind = (1, 2, 1, 4, 8, 1)[i % 6]
+        if kind == 1:
+            seq.append((kind, i % 3, m.decode(x1[i % 3])))
+        else:
+            seq.append((kind, None, m.decode_batch(xb[kind])))
+    torch.cuda.synchronize()
+    for i, (kind, j, o) in enumerate(seq):
+        want = alone1[j] if kind == 1 else aloneb[kind]
+        assert np.array_equal(bf16_bits(o), want), f"call {i} ({kind} rows) differs from the same call alone"
+    assert m.decode_error() == 0
+    m.close()
+
+
 def test_decode_graph_replay():
     """Three decode calls captured once in a HIP graph (their launch arguments do not
     change between calls: the record tag lives in the workspace) and replayed several
