@@ -816,9 +816,12 @@ __global__ __launch_bounds__(kDecThreads, TT <= 4 ? 2 : 1) void k_decode(DecodeA
   const bool selector = spread_sel ? (b % 8 == 0 && b / 8 < T) : b < T;
   const int my_tok = spread_sel ? b / 8 : b;
 
-  // the first down task's weights, if it belongs to the shared expert (known now)
+  // the first down task's weights, if it belongs to the shared expert (known now).  A
+  // wave's loads complete in issue order, so these also hold back the router's loads and
+  // the record polls behind them; with eight rows (one workgroup per CU) that costs more
+  // than the early start gains, and the loads go out with the routed ones instead.
   DnPre pre;
-  const bool pre_shared = b < nrb;
+  const bool pre_shared = TT <= 4 && b < nrb;
   if (pre_shared) dn_load(a, E, b, threadIdx.x & 15, pre);
   __syncthreads();  // s_epoch
 

@@ -521,8 +521,10 @@ struct DnLoad {
   uint32_t s[kDnUnits], b[kDnUnits];
 };
 
+// routed = false: the selection may not have run in this workgroup; every slot reads the
+// shared expert (loads whose results are discarded, from valid addresses).
 __device__ __forceinline__ void dn_issue(const DecodeArgs &a, const DecShared &sh, int n0, int j0, int nb, int c,
-                                         DnLoad &L) {
+                                         DnLoad &L, bool routed = true) {
   const int I = a.I, k = a.k, q = (threadIdx.x >> 4);
   const int cc = c < I / 32 ? c : 0;
 #pragma unroll
@@ -530,7 +532,7 @@ __device__ __forceinline__ void dn_issue(const DecodeArgs &a, const DecShared &s
     int u = q + 16 * m;
     u = u < kDnRows * nb ? u : 0;  // surplus units read unit 0 (result discarded)
     const int r = u / nb, slot = j0 + (u - r * nb);
-    const int e = slot < k ? sh.ids[slot] : a.E;
+    const int e = slot < k && routed ? sh.ids[slot] : a.E;
     const QMat D = expert_mat(a.down, a.s_down, e, a.E, a.H, I);
     const size_t n = (size_t)(n0 + r);
     L.w[m] = *(const uint4 *)(D.q + code_index(n, 4 * cc, I));
@@ -732,17 +734,22 @@ __global__ __launch_bounds__(kDecThreads) void k_decode1(DecodeArgs a) {
   const bool routed_gu = g0 < first_shared;
   if (routed_gu || b < n_dn || b == 0) select_topk(a, sh, b == 0);
 
-  // 3. routed gate/up tasks; the first down task's loads go out with the first of them
+  // 3. routed gate/up tasks; the first down task's loads go out with the first of them.
+  // Both load groups are issued in straight-line code (the down loads unconditionally, from
+  // a valid row), so the gate/up arithmetic waits for its own loads only: behind a branch,
+  // the wait before the first use would cover every load issued on either path.
   DnLoad dl;
   bool dn_pre = false;
   const int nbmax = min(min(k + 1, kDnSlots), kHStage / a.I);
-  for (int g = g0; g < n_gu; g += G) {
-    gu_start(a, sh, g, gl);
-    if (!dn_pre && b < n_dn) {
-      dn_issue(a, sh, b * kDnRows, 0, min(nbmax, k + 1), tid & 15, dl);
-      dn_pre = true;
+  if (g0 < n_gu) {
+    gu_start(a, sh, g0, gl);
+    dn_pre = b < n_dn;
+    dn_issue(a, sh, min(b, n_dn - 1) * kDnRows, 0, min(nbmax, k + 1), tid & 15, dl, dn_pre);
+    gu_task(a, sh, g0, gl);
+    for (int g = g0 + G; g < n_gu; g += G) {
+      gu_start(a, sh, g, gl);
+      gu_task(a, sh, g, gl);
     }
-    gu_task(a, sh, g, gl);
   }
 
   // 4. down tasks
