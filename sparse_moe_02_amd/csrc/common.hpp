@@ -291,7 +291,10 @@ __device__ __forceinline__ int ticket(int *p) {
 // with the next one's.  The tag is n mod (2^32 - 1) plus 1: never 0 (the value of
 // cleared records) and different in consecutive calls.
 constexpr uint64_t kEpochUnit = uint64_t(1) << 24;
-// The ticket (the atomic's return value is waited for at its first use) ...
+// The ticket (the atomic's return value is waited for at its first use) ...  The
+// counter's address carries a per-lane zero the compiler cannot see through: with a
+// uniform address it would combine the active lanes' adds into one and broadcast the
+// result, which waits for the atomic's round trip right where it is issued.
 __device__ __forceinline__ uint64_t epoch_ticket(uint64_t *ctr, int stride_u64, int b, int G) {
   const int g = b & 7;
   const int n_g = G / 8 + (g < G % 8 ? 1 : 0);
@@ -299,12 +302,15 @@ __device__ __forceinline__ uint64_t epoch_ticket(uint64_t *ctr, int stride_u64, 
     for (int g2 = G; g2 < 8; ++g2)
       __hip_atomic_fetch_add(ctr + (size_t)g2 * stride_u64, kEpochUnit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint64_t w = b < 8 ? kEpochUnit - (uint64_t)(n_g - 1) : uint64_t(1);
-  return __hip_atomic_fetch_add(ctr + (size_t)g * stride_u64, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint32_t z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return __hip_atomic_fetch_add(ctr + (size_t)g * stride_u64 + z, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // ... and the tag it gives.
-__device__ __forceinline__ uint32_t epoch_of(uint64_t t) { return (uint32_t)((t / kEpochUnit) % 0xffffffffull) + 1u; }
-__device__ __forceinline__ uint32_t take_epoch(uint64_t *ctr, int stride_u64, int b, int G) {
-  return epoch_of(epoch_ticket(ctr, stride_u64, b, G));
+__device__ __forceinline__ uint64_t lane0_u64(uint64_t v) {
+  return ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32) |
+         __builtin_amdgcn_readfirstlane((uint32_t)v);
 }
+__device__ __forceinline__ uint32_t epoch_of(uint64_t t) { return (uint32_t)((t / kEpochUnit) % 0xffffffffull) + 1u; }
 
 }  // namespace moe

@@ -20,9 +20,9 @@
 // device-scope store and read with device-scope loads, so a reader accepts a value
 // exactly when its tag is this call's) or as plain device-scope stores followed by a
 // tagged flag once they have completed.  The tag comes from call counters in the
-// workspace, one ticket per workgroup at its start (take_epoch), shared with the
-// one-token kernel.  The launch arguments are therefore the same for every call, so a sequence of calls can
-// be captured once in a HIP graph and replayed.
+// workspace, one ticket per workgroup at its start (epoch_ticket), shared with the
+// one-token kernel.  The launch arguments are therefore the same for every call, so a
+// sequence of calls can be captured once in a HIP graph and replayed.
 //   1. the shared expert's gate/up tasks need no routing and run first;
 //   2. router: every wave of the grid computes one expert's binary64 logits for a pair of
 //      tokens and publishes them with their error radii (done first, before step 1's
@@ -131,17 +131,17 @@ struct DecShared {
 
 // ------------------------------------------------------------------ router (binary64)
 
-// Additions on any path of router_wave's sum: H/64 per lane, a 6-level butterfly.
+// Additions on any path of router_dot's sum: H/64 per lane, a 6-level butterfly.
 __device__ __forceinline__ int router_depth(int H) { return H / 64 + 6; }
 
 // Binary64 logits of expert e for tokens t0 .. t0+TT-1 (those below T), by one wave: lane
 // takes the 8-element chunks c = lane + 64 i of the router row (read once) and sums the
 // exact products of each token sequentially; a butterfly gives every lane the totals.
 // The loads of four chunks of the row (and of the first token) are issued before any is
-// used.  Lane 0 publishes (t, e)'s three records: the two halves of the logit (+ bias)
-// and its error radius.
+// used.  router_pub: lane 0 publishes (t, e)'s three records: the two halves of the
+// logit (+ bias) and its error radius.
 template <int TT>
-__device__ void router_wave(const DecodeArgs &a, int e, int t0) {
+__device__ void router_dot(const DecodeArgs &a, int e, int t0, double (&l)[TT], double (&ab)[TT]) {
   const int lane = threadIdx.x & 63, H = a.H, E = a.E, T = a.T - t0;
   const uint16_t *xb = a.x + (size_t)t0 * H;
   constexpr int B4 = 4;
@@ -198,13 +198,20 @@ __device__ void router_wave(const DecodeArgs &a, int e, int t0) {
   }
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
+    l[t] = wave_sum_f64(s[t]);
+    ab[t] = wave_sum_f64(sa[t]);
+    if (a.bias) l[t] += (double)a.bias[e];
+  }
+}
+template <int TT>
+__device__ void router_pub(const DecodeArgs &a, int e, int t0, const double (&l)[TT], const double (&ab)[TT]) {
+  const int lane = threadIdx.x & 63, H = a.H, E = a.E, T = a.T - t0;
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
     if (t >= T) break;
-    double l = wave_sum_f64(s[t]);
-    const double ab = wave_sum_f64(sa[t]);
-    if (a.bias) l += (double)a.bias[e];
     if (lane == 0) {
-      const uint64_t lb = (uint64_t)__double_as_longlong(l);
-      const float rad = __double2float_ru(radius64(l, ab, H, router_depth(H)));
+      const uint64_t lb = (uint64_t)__double_as_longlong(l[t]);
+      const float rad = __double2float_ru(radius64(l[t], ab[t], H, router_depth(H)));
       uint64_t *rec = a.lrec + 3 * ((size_t)(t0 + t) * E + e);
       st_agent(&rec[0], tagged(s_epoch, (uint32_t)lb));
       st_agent(&rec[1], tagged(s_epoch, (uint32_t)(lb >> 32)));
@@ -805,7 +812,10 @@ template <int TT>
 __global__ __launch_bounds__(kDecThreads, TT <= 4 ? 2 : 1) void k_decode(DecodeArgs a) {
   __shared__ DecShared sh;
   const int b = blockIdx.x, G = gridDim.x, tid = threadIdx.x, wv = tid >> 6;
-  if (tid == 0) s_epoch = take_epoch(a.epctr, kCtrStride / 2, b, G);
+  // the call's ticket goes out now; wave 0 reads it back after its router loads (so the
+  // router does not wait for the atomic's round trip), then a barrier shares the tag
+  uint64_t tk;
+  if (tid == 0) tk = epoch_ticket(a.epctr, kCtrStride / 2, b, G);
   const int T = a.T, E = a.E, k = a.k;
   const int ntb = a.I / kDecGuTask;       // gate/up tasks per active expert
   const int nrb = a.H / kDecDnTask;       // down tasks per active expert
@@ -823,16 +833,21 @@ __global__ __launch_bounds__(kDecThreads, TT <= 4 ? 2 : 1) void k_decode(DecodeA
   DnPre pre;
   const bool pre_shared = TT <= 4 && b < nrb;
   if (pre_shared) dn_load(a, E, b, threadIdx.x & 15, pre);
-  __syncthreads();  // s_epoch
 
   // 1. router logits, published as records: (expert, pair of tokens) per wave over every
   // wave of the grid, before anything else, since every selection waits for all of them
   {
     constexpr int TPW = 2;  // tokens per router wave
     const int nsub = (T + TPW - 1) / TPW, nw = 4 * G;
-    for (int p = b * 4 + wv; p < E * nsub; p += nw) {
-      const int e = p / nsub, sub = p - e * nsub;
-      router_wave<TPW>(a, e, TPW * sub);
+    int p = b * 4 + wv;
+    double l[TPW], ab[TPW];
+    if (p < E * nsub) router_dot<TPW>(a, p / nsub, TPW * (p % nsub), l, ab);
+    if (tid < kWave) s_epoch = epoch_of(lane0_u64(tk));
+    __syncthreads();  // s_epoch
+    if (p < E * nsub) router_pub<TPW>(a, p / nsub, TPW * (p % nsub), l, ab);
+    for (p += nw; p < E * nsub; p += nw) {
+      router_dot<TPW>(a, p / nsub, TPW * (p % nsub), l, ab);
+      router_pub<TPW>(a, p / nsub, TPW * (p % nsub), l, ab);
     }
   }
 

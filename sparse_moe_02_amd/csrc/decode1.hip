@@ -17,7 +17,7 @@
 // with one device-scope store and read with device-scope loads, so a reader accepts a
 // value exactly when its tag is this call's epoch; no wait uses a counter or an atomic
 // read-modify-write (those serialise on one address).  The epoch comes from call
-// counters in the workspace, one ticket per workgroup at its start (take_epoch), so
+// counters in the workspace, one ticket per workgroup at its start (epoch_ticket), so
 // nothing is left to do once a workgroup's last output is stored.  The launch arguments
 // are therefore the same for every call, so a sequence of calls can be captured once in
 // a HIP graph and replayed.
@@ -136,7 +136,7 @@ __device__ void router_logit(const DecodeArgs &a, DecShared &sh, int e, double &
     sh.red[0][wv] = s;
     sh.red[1][wv] = sa;
   }
-  if (set_ep && tid == 0) s_epoch = epoch_of(tk);
+  if (set_ep && tid < kWave) s_epoch = epoch_of(lane0_u64(tk));
   __syncthreads();
   l = ((sh.red[0][0] + sh.red[0][1]) + sh.red[0][2]) + sh.red[0][3];
   ab = ((sh.red[1][0] + sh.red[1][1]) + sh.red[1][2]) + sh.red[1][3];
@@ -167,26 +167,6 @@ __device__ void read_logit(const DecodeArgs &a, int e, double &v, double &r) {
     }
     __builtin_amdgcn_s_sleep(2);
   }
-}
-
-__device__ double block_min_f64(double v, DecShared &sh) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) v = fmin(v, __shfl_xor(v, o));
-  if ((threadIdx.x & 63) == 0) sh.red[0][threadIdx.x >> 6] = v;
-  __syncthreads();
-  v = fmin(fmin(sh.red[0][0], sh.red[0][1]), fmin(sh.red[0][2], sh.red[0][3]));
-  __syncthreads();
-  return v;
-}
-
-__device__ double block_max_f64(double v, DecShared &sh) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) v = fmax(v, __shfl_xor(v, o));
-  if ((threadIdx.x & 63) == 0) sh.red[0][threadIdx.x >> 6] = v;
-  __syncthreads();
-  v = fmax(fmax(sh.red[0][0], sh.red[0][1]), fmax(sh.red[0][2], sh.red[0][3]));
-  __syncthreads();
-  return v;
 }
 
 // Order-preserving 32-bit key of a logit of expert e: the fp32 value's ordered bits with
@@ -677,7 +657,10 @@ __global__ __launch_bounds__(kDecThreads) void k_decode1(DecodeArgs a) {
   const int b = blockIdx.x, G = gridDim.x, tid = threadIdx.x;
   // the call's ticket goes out now; thread 0 stores its tag to s_epoch in the first router
   // pass (or after the router loop) before any record is written or read
-  uint64_t tk = 0;
+  // Thread 0's ticket is read back through lane 0 by all of wave 0 where it is used, so
+  // the compiler neither moves that use up to the atomic nor copies the value where the
+  // branch ends: either would wait for the atomic's round trip here.
+  uint64_t tk;
   if (tid == 0) tk = epoch_ticket(a.epctr, kCtrStride / 2, b, G);
   const int E = a.E, k = a.k;
   const int n_gu = (k + 1) * (a.I / kGuTask), n_dn = a.H / kDnRows;
@@ -723,7 +706,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode1(DecodeArgs a) {
     }
   }
   if (b >= E) {
-    if (tid == 0) s_epoch = epoch_of(tk);
+    if (tid < kWave) s_epoch = epoch_of(lane0_u64(tk));
     __syncthreads();
   }
 

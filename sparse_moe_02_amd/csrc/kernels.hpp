@@ -122,7 +122,7 @@ struct DecodeArgs {
   uint64_t *hrec1;          // one-token kernel: [kHrecRep][(k+1)*I/2] tagged pairs of bf16 h values
   float *part;              // [T][k+1][H] gate-weighted down output of every (token, slot)
   int *rbctr;               // [T][H/64] arrivals per (token, row block), kCtrStride ints apart
-  uint64_t *epctr;          // [8] call counters (take_epoch), kCtrStride ints apart
+  uint64_t *epctr;          // [8] call counters (epoch_ticket), kCtrStride ints apart
   Ctrl *ctrl;
   uint16_t *out;            // [T][H]
   int32_t *dbg_ids;         // [T][k]
