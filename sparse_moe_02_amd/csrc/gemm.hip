@@ -314,7 +314,15 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
   // every wave is past its last LDS read before the epilogue reuses stage0
   __builtin_amdgcn_s_barrier();
   int pend = 0;
-  if (tid == 0 && claim) pend = atomicAdd(claim, 1);
+  if (tid == 0 && claim) {
+    // gate/up: the counter's address carries a per-lane zero the compiler cannot see
+    // through, so it leaves the atomic alone (with a uniform address it combines the
+    // lanes' adds and broadcasts the result, which waits for the round trip here instead
+    // of at the end of the epilogue); down keeps the plain form, which spills less
+    uint32_t z = 0;
+    if (GU) asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+    pend = atomicAdd(claim + z, 1);
+  }
   if (GU && pc.ti >= 0) {
     // slot layout: per (wave, tile, matrix) 8 rows of 64 lanes of fp32 pairs, so each
     // store and load instruction covers 512 contiguous bytes
