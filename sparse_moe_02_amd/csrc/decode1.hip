@@ -493,6 +493,12 @@ __device__ __forceinline__ void gu_task(const DecodeArgs &a, const DecShared &sh
 
 // ------------------------------------------------------------------ down
 
+// u / nb for the small unit indices of a down round (u < 2^16 / nb): one 24-bit
+// multiply and a shift with m = ceil(2^16 / nb), exact there, in place of a division by
+// a runtime value (a long sequence of quarter-rate multiplies on the chain).
+__device__ __forceinline__ int unit_div(int u, uint32_t m) { return (int)(__umul24((uint32_t)u, m) >> 16); }
+__device__ __forceinline__ uint32_t unit_div_m(int nb) { return (65536u + (uint32_t)nb - 1u) / (uint32_t)nb; }
+
 // Units of a down round: u = r * nb + jj (row r of the task, slot j0 + jj).  16-lane
 // group q (lane/16 + 4*wave) takes u = q + 16 m; lane cl = lane % 16 takes the
 // 32-element chunk c = cl + 16 p of the I-long rows.
@@ -507,11 +513,12 @@ __device__ __forceinline__ void dn_issue(const DecodeArgs &a, const DecShared &s
                                          DnLoad &L, bool routed = true) {
   const int I = a.I, k = a.k, q = (threadIdx.x >> 4);
   const int cc = c < I / 32 ? c : 0;
+  const uint32_t nbm = unit_div_m(nb);
 #pragma unroll
   for (int m = 0; m < kDnUnits; ++m) {
     int u = q + 16 * m;
     u = u < kDnRows * nb ? u : 0;  // surplus units read unit 0 (result discarded)
-    const int r = u / nb, slot = j0 + (u - r * nb);
+    const int r = unit_div(u, nbm), slot = j0 + (u - r * nb);
     const int e = slot < k && routed ? sh.ids[slot] : a.E;
     const QMat D = expert_mat(a.down, a.s_down, e, a.E, a.H, I);
     const size_t n = (size_t)(n0 + r);
@@ -591,11 +598,12 @@ __device__ __forceinline__ void dn_accumulate(const DecodeArgs &a, DecShared &sh
                                               float (&acc)[kDnUnits]) {
   const int I = a.I, q = threadIdx.x >> 4;
   if (c >= I / 32) return;
+  const uint32_t nbm = unit_div_m(nb);
 #pragma unroll
   for (int m = 0; m < kDnUnits; ++m) {
     const int u = q + 16 * m;
     if (u >= kDnRows * nb) continue;
-    const int ch = (u % nb) * (I / 32) + c;
+    const int ch = (u - unit_div(u, nbm) * nb) * (I / 32) + c;
     const uint4 *hp = (const uint4 *)&sh.hb[ch * kHChunkWords];
     uint32_t hv[16];
 #pragma unroll
@@ -621,6 +629,7 @@ __device__ __forceinline__ void dn_task(const DecodeArgs &a, DecShared &sh, int 
   float out_acc = 0.f;  // thread t < 8: row n0 + t
   for (int j0 = 0; j0 <= k; j0 += nbmax) {
     const int nb = min(nbmax, k + 1 - j0);
+    const uint32_t nbm = unit_div_m(nb);
     stage_h(a, sh, j0, nb);
     float acc[kDnUnits] = {};
     for (int p = 0; p < npass; ++p) {
@@ -638,7 +647,7 @@ __device__ __forceinline__ void dn_task(const DecodeArgs &a, DecShared &sh, int 
       const float v = row16_sum(acc[m]);
       const int u = q + 16 * m;
       if (cl == 0 && u < kDnRows * nb) {
-        const int slot = j0 + u % nb;
+        const int slot = j0 + (u - unit_div(u, nbm) * nb);
         sh.unit[u] = (slot < k ? sh.gates[slot] : sh.sgv) * v;
       }
     }
