@@ -276,6 +276,14 @@ template <class T>
 __device__ __forceinline__ T ld_agent(const T *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// This lane's index in its wave (v_mbcnt over all lanes), computed where it is used: the
+// volatile asm keeps the compiler from computing it once at the start and holding it in a
+// register (or spilling it) through the code in between.
+__device__ __forceinline__ int lane_now() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
 __device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0xF70); }  // vmcnt(0)
 __device__ __forceinline__ int ticket(int *p) {
   return __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -96,11 +96,12 @@ struct Piece {
 // no scale/bias stage and no dequantisation.
 template <int MT, bool GU, bool W16>
 __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, float *s_gate, int *s_last, int e,
-                          int row0, int rows, int nb, int ks0, int ks1, const Piece &pc, int *claim, int *s_pend) {
+                          int row0, int rows, int nb, int ks0, int ks1, const Piece &pc, int *claim, int *s_pend,
+                          int wv0) {
   // thread index made opaque so per-lane address arithmetic is computed per item instead
   // of being hoisted out of the persistent loop (where every row-tile variant's copy
   // would hold registers for the whole kernel)
-  int tid = threadIdx.x;
+  int tid = (wv0 << 6) + lane_now();
   asm volatile("" : "+v"(tid));
   const int lane = tid & 63, hf = lane >> 5;
   const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -447,18 +448,21 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
 template <bool GU, bool W16>
 __device__ __forceinline__ void run_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, float *s_gate,
                                          int *s_last, const int4 &mb, int nb, int ks0, int ks1, const Piece &pc,
-                                         int *claim, int *s_pend) {
+                                         int *claim, int *s_pend, int wv0) {
   switch (mb.w) {
-    case 1: gemm_item<1, GU, W16>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc, claim, s_pend); break;
-    case 2: gemm_item<2, GU, W16>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc, claim, s_pend); break;
-    case 3: gemm_item<3, GU, W16>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc, claim, s_pend); break;
-    case 4: gemm_item<4, GU, W16>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc, claim, s_pend); break;
-    default: gemm_item<5, GU, W16>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc, claim, s_pend); break;
+    case 1: gemm_item<1, GU, W16>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc, claim, s_pend, wv0); break;
+    case 2: gemm_item<2, GU, W16>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc, claim, s_pend, wv0); break;
+    case 3: gemm_item<3, GU, W16>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc, claim, s_pend, wv0); break;
+    case 4: gemm_item<4, GU, W16>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc, claim, s_pend, wv0); break;
+    default: gemm_item<5, GU, W16>(a, stage0, stage1, s_gate, s_last, mb.x, mb.y, mb.z, nb, ks0, ks1, pc, claim, s_pend, wv0); break;
   }
 }
 
 template <bool GU, bool W16>
 __device__ void gemm_persistent(const GemmArgs &a) {
+  // the wave's index (scalar) and, where needed, the lane's (mbcnt) are recomputed rather
+  // than the thread index kept in a vector register for the whole kernel
+  const int wv0 = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   __shared__ __attribute__((aligned(16))) uint8_t stage0[kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t stage1[kStageBytes];
   __shared__ float s_gate[kBM];
@@ -487,7 +491,7 @@ __device__ void gemm_persistent(const GemmArgs &a) {
   auto items_of = [&](int x) { return m_cut > x ? NB * ((m_cut - x + kXcds - 1) / kXcds) : 0; };
   int cur = blockIdx.x % kXcds;  // wave 0: queue being drained (kXcds: the tail pieces)
   if (!GU)
-    for (int i = threadIdx.x; i < min(nmb, kMbCache); i += blockDim.x) s_mbc[i] = a.mblocks[i];
+    for (int i = (int)threadIdx.x; i < min(nmb, kMbCache); i += kGemmThreads) s_mbc[i] = a.mblocks[i];
   auto mblock = [&](int i) {  // after a barrier; wave-uniform, kept in scalar registers
     const int4 m = !GU && i < kMbCache ? s_mbc[i] : a.mblocks[i];
     return make_int4(__builtin_amdgcn_readfirstlane(m.x), __builtin_amdgcn_readfirstlane(m.y),
@@ -495,18 +499,19 @@ __device__ void gemm_persistent(const GemmArgs &a) {
   };
   int pq = -1;                    // wave 0: queue of the ticket in s_pend (-1: none)
   for (;;) {
-    if (threadIdx.x < 64) {
+    if (wv0 == 0) {
       // Claim the next unit.  The current queue first (one atomic); once it is empty, the
       // remaining counts of all eight queues are read in one round trip (one lane per
       // queue, atomic adds of zero, so the values are the queues' own) and the fullest
       // is taken; then the tail pieces.
-      const int lane = threadIdx.x;
+      int lane = lane_now();
+      asm volatile("" : "+v"(lane));  // per-lane values below are recomputed per claim, not kept
       int v = -1, q = -1;
       if (cur < kXcds) {
         int c = 0;
         if (lane == 0) c = pq == cur ? s_pend : atomicAdd(&a.queue[cur], 1);
         pq = -1;
-        c = __shfl(c, 0);
+        c = __builtin_amdgcn_readfirstlane(c);
         if (c < items_of(cur)) v = c, q = cur;
       }
       while (q < 0 && cur < kXcds) {
@@ -515,7 +520,7 @@ __device__ void gemm_persistent(const GemmArgs &a) {
         if (lane < kXcds) rem = items_of(lane) - atomicAdd(&a.queue[lane], zero);
         int best = -1, best_rem = 0;
         for (int i = 0; i < kXcds; ++i) {
-          const int r = __shfl(rem, i);
+          const int r = __builtin_amdgcn_readlane(rem, i);
           if (r > best_rem) best_rem = r, best = i;
         }
         if (best < 0) {
@@ -525,14 +530,14 @@ __device__ void gemm_persistent(const GemmArgs &a) {
         cur = best;
         int c = 0;
         if (lane == 0) c = atomicAdd(&a.queue[cur], 1);
-        c = __shfl(c, 0);
+        c = __builtin_amdgcn_readfirstlane(c);
         if (c < items_of(cur)) v = c, q = cur;
       }
       if (q < 0 && n_tail) {
         int c = 0;
         if (lane == 0) c = pq == kXcds ? s_pend : atomicAdd(a.tail_queue, 1);
         pq = -1;
-        c = __shfl(c, 0);
+        c = __builtin_amdgcn_readfirstlane(c);
         if (c < n_tail * S) v = c, q = kXcds;
       }
       if (lane == 0) {
@@ -562,7 +567,7 @@ __device__ void gemm_persistent(const GemmArgs &a) {
     // the item takes the next ticket from the queue this one came from (the tail
     // pieces' queue for a piece)
     int *claim = q < kXcds ? &a.queue[q] : a.tail_queue;
-    run_item<GU, W16>(a, stage0, stage1, s_gate, &s_last, mb, nb, ks0, ks1, pc, claim, &s_pend);
+    run_item<GU, W16>(a, stage0, stage1, s_gate, &s_last, mb, nb, ks0, ks1, pc, claim, &s_pend, wv0);
     cur = q;
     pq = q;
   }
