@@ -675,26 +675,6 @@ __global__ __launch_bounds__(kDecThreads) void k_decode1(DecodeArgs a) {
   const int n_gu = (k + 1) * (a.I / kGuTask), n_dn = a.H / kDnRows;
   const int first_shared = k * (a.I / kGuTask);  // gate/up tasks from here on are the shared expert's
 
-  // the shared expert's weight, in every workgroup with a down task (x and the gate vector
-  // are read at the start, off the dependency chain)
-  if (b < n_dn) {
-    float z = 0.f;
-    if (a.sgate) {
-      for (int c = tid; c < a.H / 8; c += kDecThreads) {
-        const uint4 xv = *(const uint4 *)(a.x + 8 * c), wv4 = *(const uint4 *)(a.sgate + 8 * c);
-        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, ww[4] = {wv4.x, wv4.y, wv4.z, wv4.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) z += bf16_lo(xw[i]) * bf16_lo(ww[i]) + bf16_hi(xw[i]) * bf16_hi(ww[i]);
-      }
-      z = wave_sum(z);
-      if ((tid & 63) == 0) sh.wf[tid >> 6] = z;
-    }
-    __syncthreads();
-    if (tid == 0) sh.sgv = a.sgate ? 1.0f / (1.0f + __expf(-((sh.wf[0] + sh.wf[1]) + (sh.wf[2] + sh.wf[3])))) : 1.0f;
-    __syncthreads();
-  }
-
-
   // The shared expert needs no routing: issue its gate/up loads before the router work.
   GuLoad gl;
   const bool gu_early = b < n_gu && b >= first_shared;
@@ -743,6 +723,26 @@ __global__ __launch_bounds__(kDecThreads) void k_decode1(DecodeArgs a) {
       gu_task(a, sh, g, gl);
     }
   }
+
+  // the shared expert's weight, in every workgroup with a down task: computed here, while
+  // the h records are still on their way (at the start it delayed the router's loads)
+  if (b < n_dn) {
+    float z = 0.f;
+    if (a.sgate) {
+      for (int c = tid; c < a.H / 8; c += kDecThreads) {
+        const uint4 xv = *(const uint4 *)(a.x + 8 * c), wv4 = *(const uint4 *)(a.sgate + 8 * c);
+        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, ww[4] = {wv4.x, wv4.y, wv4.z, wv4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z += bf16_lo(xw[i]) * bf16_lo(ww[i]) + bf16_hi(xw[i]) * bf16_hi(ww[i]);
+      }
+      z = wave_sum(z);
+      if ((tid & 63) == 0) sh.wf[tid >> 6] = z;
+    }
+    __syncthreads();
+    if (tid == 0) sh.sgv = a.sgate ? 1.0f / (1.0f + __expf(-((sh.wf[0] + sh.wf[1]) + (sh.wf[2] + sh.wf[3])))) : 1.0f;
+    __syncthreads();
+  }
+
 
   // 4. down tasks
   for (int d = b; d < n_dn; d += G) {
