@@ -187,7 +187,6 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
         dma4(sbase[i] + ss * (4 * kQpRows), soff[i], l + kAStage + kBStage + (wu + 8 * i) * 256);
     }
   };
-  if (!GU && tid < MT * 32) s_gate[tid] = a.row_gate[row0 + min(tid, rows - 1)];  // read by the epilogue
   f32x16 acc[MT][2];
 #pragma unroll
   for (int t = 0; t < MT; ++t)
@@ -301,6 +300,12 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
   // compiler adds no waits of its own for them; each wave waits for its loads, then the
   // barrier publishes every wave's.
   issue(ks0, stage0);
+  if (!GU && 64 * wu < MT * 32) {
+    // down: the rows' routing weights (read by the epilogue) go to LDS with the first
+    // stage, so no register load and wait sits before the stage loads
+    const int r = min(64 * wu + lane_now(), rows - 1);
+    dma4(a.row_gate + row0, 4u * (uint32_t)r, lds_addr(s_gate) + 256 * wu);
+  }
   for (int ss = ks0; ss < ks1; ss += 2) {
     vm_wait<0>();
     __syncthreads();  // stage0 holds step ss for every wave; stage1 is free
@@ -465,7 +470,7 @@ __device__ void gemm_persistent(const GemmArgs &a) {
   const int wv0 = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   __shared__ __attribute__((aligned(16))) uint8_t stage0[kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t stage1[kStageBytes];
-  __shared__ float s_gate[kBM];
+  __shared__ __attribute__((aligned(16))) float s_gate[(kBM + 63) / 64 * 64];  // whole waves of 64
   __shared__ int s_item, s_queue, s_last, s_pend;
   // down: the first kMbCache block-map entries, copied once per launch, so an item finds
   // its entry without a round trip to memory (down runs about twice as many items per
@@ -493,7 +498,16 @@ __device__ void gemm_persistent(const GemmArgs &a) {
   if (!GU)
     for (int i = (int)threadIdx.x; i < min(nmb, kMbCache); i += kGemmThreads) s_mbc[i] = a.mblocks[i];
   auto mblock = [&](int i) {  // after a barrier; wave-uniform, kept in scalar registers
-    const int4 m = !GU && i < kMbCache ? s_mbc[i] : a.mblocks[i];
+    // The entry is uniform: an LDS read for the cached ones, else a scalar load.  Neither
+    // is a vector memory load, so neither waits for the previous item's stores (a vector
+    // or generic load here is followed by a wait that also covers every store in flight).
+    u32x4 v;
+    if (!GU && i < kMbCache) {
+      asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(&s_mbc[i])) : "memory");
+    } else {
+      asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(a.mblocks + i) : "memory");
+    }
+    const int4 m = make_int4((int)v[0], (int)v[1], (int)v[2], (int)v[3]);
     return make_int4(__builtin_amdgcn_readfirstlane(m.x), __builtin_amdgcn_readfirstlane(m.y),
                      __builtin_amdgcn_readfirstlane(m.z), __builtin_amdgcn_readfirstlane(m.w));
   };
