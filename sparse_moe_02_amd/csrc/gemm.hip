@@ -306,29 +306,42 @@ __device__ void gemm_item(const GemmArgs &a, uint8_t *stage0, uint8_t *stage1, f
     const int r = min(64 * wu + lane_now(), rows - 1);
     dma4(a.row_gate + row0, 4u * (uint32_t)r, lds_addr(s_gate) + 256 * wu);
   }
+  // Down: the next item's ticket is taken by one thread as the item's last step begins,
+  // so its round trip overlaps that step's multiplies; the value is read back by every
+  // wave once the steps are done, when nothing else of the wave's is in flight (read
+  // behind the epilogue's stores, its wait would also wait for them).  Gate/up (whose
+  // registers do not hold the ticket through a step without spilling) takes it once the
+  // last multiply is done and reads it back at the end of the epilogue.  The counter's
+  // address carries a per-lane zero the compiler cannot see through, so it leaves the
+  // atomic alone (with a uniform address it combines the lanes' adds and broadcasts the
+  // result, waiting for the round trip at once).
+  int pend = 0;
+  auto take_ticket = [&]() {
+    if (tid == 0 && claim) {
+      uint32_t z;
+      asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+      pend = atomicAdd(claim + z, 1);
+    }
+  };
   for (int ss = ks0; ss < ks1; ss += 2) {
     vm_wait<0>();
     __syncthreads();  // stage0 holds step ss for every wave; stage1 is free
     if (ss + 1 < ks1) issue(ss + 1, stage1);
+    if (!GU && ss + 1 == ks1) take_ticket();
     if (active) compute(stage0);
     if (ss + 1 >= ks1) break;
     vm_wait<0>();
     __syncthreads();  // stage1 holds step ss+1; stage0 is free
     if (ss + 2 < ks1) issue(ss + 2, stage0);
+    if (!GU && ss + 2 == ks1) take_ticket();
     if (active) compute(stage1);
   }
   // every wave is past its last LDS read before the epilogue reuses stage0
   __builtin_amdgcn_s_barrier();
-  int pend = 0;
-  if (tid == 0 && claim) {
-    // gate/up: the counter's address carries a per-lane zero the compiler cannot see
-    // through, so it leaves the atomic alone (with a uniform address it combines the
-    // lanes' adds and broadcasts the result, which waits for the round trip here instead
-    // of at the end of the epilogue); down keeps the plain form, which spills less
-    uint32_t z = 0;
-    if (GU) asm volatile("v_mov_b32 %0, 0" : "=v"(z));
-    pend = atomicAdd(claim + z, 1);
-  }
+  if (GU)
+    take_ticket();
+  else
+    pend = __builtin_amdgcn_readfirstlane(pend);  // the ticket (thread 0's), uniform
   if (GU && pc.ti >= 0) {
     // slot layout: per (wave, tile, matrix) 8 rows of 64 lanes of fp32 pairs, so each
     // store and load instruction covers 512 contiguous bytes
