@@ -142,7 +142,7 @@ __device__ __forceinline__ int router_depth(int H) { return H / 64 + 6; }
 // logit (+ bias) and its error radius.
 template <int TT>
 __device__ void router_dot(const DecodeArgs &a, int e, int t0, double (&l)[TT], double (&ab)[TT]) {
-  const int lane = threadIdx.x & 63, H = a.H, E = a.E, T = a.T - t0;
+  const int lane = threadIdx.x & 63, H = a.H, T = a.T - t0;
   const uint16_t *xb = a.x + (size_t)t0 * H;
   constexpr int B4 = 4;
   double s[TT], sa[TT];

@@ -58,8 +58,8 @@ __device__ __forceinline__ QMat expert_mat(const QMat &routed, const QMat &share
   return m;
 }
 
-// activation tile: row r at r*256, 16-byte chunk c at slot c ^ (r & 15)
-__device__ __forceinline__ int a_off(int row, int chunk) { return row * kRowBytes + ((chunk ^ (row & 15)) << 4); }
+// activation tile: row r at r*256, 16-byte chunk c at slot c ^ (r & 15) (the stage loads
+// place the chunks so, and the fragment reads below undo it)
 // weights: slot w (one weight row) at w*64, 16-byte part p at p ^ ((w >> 2) & 3)
 __device__ __forceinline__ int b_off(int slot, int part) { return slot * 64 + ((part ^ ((slot >> 2) & 3)) << 4); }
 

@@ -130,7 +130,7 @@ struct Sel64 {
 
 // Resolve the candidates S.cand[0..S.n) for `r` remaining slots with binary64 logits
 // already in S.v/S.rad; undecided ones are summed sequentially.  Marks S.chosen.
-__device__ void resolve64(Sel64 &S, int r, const uint16_t *x, const uint16_t *w16,
+__device__ __attribute__((unused)) void resolve64(Sel64 &S, int r, const uint16_t *x, const uint16_t *w16,
                           const float *w32, const float *bias, int H, int tid, int nthr) {
   classify(S.v, S.rad, S.n, r, S.state, tid, nthr);
   __syncthreads();
